@@ -1,0 +1,255 @@
+"""TEST INFRASTRUCTURE: the float64 CPU oracle of the QSA select phase and the
+checker that compares a device result with it.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The HIP library never uses it, and it never uses the HIP
+library: the two share nothing but the seeded input generators (qsa_inputs).
+
+Arithmetic contract (Strata pull request #228, part 1, "arithmetic contract"
+paragraph; Strata pull request #856, "Arithmetic contract and parity"):
+    |s_gpu - score_ref| <= B = 2^-9.5 * S + 8 * 2^-24 * |score_ref|
+with S the float64 sum of |k_b[i] * q_h[i]|.  A +2.5*B perturbation must fail
+the same check (negative control, both pages).  Selected ids agree except at
+near-ties whose gap is within 2*B (PR #856, "near-tie-gap guard").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboracle.so")
+
+BOUND_REL = 2.0 ** -9.5
+BOUND_ABS = 8.0 * 2.0 ** -24
+NEG_CONTROL = 2.5
+
+_lib = None
+
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_vp = ctypes.c_void_p
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from . import build as _b
+            _b.build()
+        L = ctypes.CDLL(LIB_PATH)
+        L.oracle_abi_version.restype = ctypes.c_int
+        L.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+        L.oracle_f16_to_f64.restype = ctypes.c_double
+        L.oracle_f32_to_f16_one.argtypes = [ctypes.c_float]
+        L.oracle_f32_to_f16_one.restype = ctypes.c_uint16
+        L.oracle_convert_f32_f16.argtypes = [_vp, _vp, _i64]
+        L.oracle_convert_f32_f16.restype = None
+        L.oracle_scores.argtypes = [_vp, ctypes.c_int, _i64, _vp, _i64, _i32, _i32, _i32, _i32,
+                                    _i64, _vp, _i64, _vp, _vp, _vp, _i64]
+        L.oracle_scores.restype = ctypes.c_int
+        L.oracle_block_model_f32.argtypes = [_vp, _i64, _vp, _i64, _i32, _i32, _i32, _i32, _i64,
+                                             _vp, _i64, _vp]
+        L.oracle_block_model_f32.restype = ctypes.c_int
+        L.oracle_topk.argtypes = [_vp, _i64, _i64, _i64, _i32, _vp, _i64, _vp]
+        L.oracle_topk.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(_vp)
+
+
+def f16_to_f64(bits: np.ndarray) -> np.ndarray:
+    L = lib()
+    flat = np.asarray(bits, dtype=np.uint16).ravel()
+    return np.array([L.oracle_f16_to_f64(int(b)) for b in flat]).reshape(np.shape(bits))
+
+
+def convert_f32_f16(x: np.ndarray) -> np.ndarray:
+    src = np.ascontiguousarray(x, dtype=np.float32)
+    dst = np.empty(src.shape, dtype=np.uint16)
+    lib().oracle_convert_f32_f16(_p(src), _p(dst), src.size)
+    return dst
+
+
+@dataclass
+class Scores:
+    score: np.ndarray  # float64 [n_rows][nb]
+    S: np.ndarray
+    B: np.ndarray
+    rows: np.ndarray   # int64 row ids r = g*nq + t
+
+
+def scores(q: np.ndarray, kblk: np.ndarray, nb: int, rows: np.ndarray | None = None) -> Scores:
+    """R1 of the oracle.  q is uint16 fp16 bits or float32 [nq][G][H][D];
+    kblk is uint16 [G][>=nb][D].  rows: optional int64 list of g*nq + t."""
+    q = np.ascontiguousarray(q)
+    nq, G, H, D = q.shape
+    kblk = np.ascontiguousarray(kblk, dtype=np.uint16)
+    assert kblk.shape[0] == G and kblk.shape[2] == D and kblk.shape[1] >= nb
+    if q.dtype == np.float32:
+        is32 = 1
+    else:
+        assert q.dtype == np.uint16
+        is32 = 0
+    if rows is None:
+        rows = np.arange(G * nq, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    n = rows.size
+    ld = max(nb, 1)
+    sc = np.empty((n, ld))
+    S = np.empty((n, ld))
+    B = np.empty((n, ld))
+    rc = lib().oracle_scores(_p(q), is32, G * H * D, _p(kblk), kblk.shape[1] * D, G, nq, H, D, nb,
+                             _p(rows), n, _p(sc), _p(S), _p(B), ld)
+    assert rc == 0
+    return Scores(sc[:, :nb], S[:, :nb], B[:, :nb], rows)
+
+
+def block_model_f32(q16: np.ndarray, kblk: np.ndarray, b: int,
+                    rows: np.ndarray | None = None) -> np.ndarray:
+    """R2: fixed-order fp32 scores of block b for each requested row."""
+    q16 = np.ascontiguousarray(q16, dtype=np.uint16)
+    nq, G, H, D = q16.shape
+    kblk = np.ascontiguousarray(kblk, dtype=np.uint16)
+    if rows is None:
+        rows = np.arange(G * nq, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty(rows.size, dtype=np.float32)
+    rc = lib().oracle_block_model_f32(_p(q16), G * H * D, _p(kblk), kblk.shape[1] * D, G, nq, H,
+                                      D, b, _p(rows), rows.size, _p(out))
+    assert rc == 0
+    return out
+
+
+def topk(score_rows: np.ndarray, k: int) -> tuple[np.ndarray, np.ndarray]:
+    """R3: ids [rows][k] (int32, -1 padded) and their scores (-inf padded)."""
+    s = np.ascontiguousarray(score_rows, dtype=np.float64)
+    if s.ndim == 1:
+        s = s[None, :]
+    rows, nb = s.shape
+    ids = np.full((rows, k), -1, dtype=np.int32)
+    vals = np.full((rows, k), -np.inf)
+    if rows == 0 or k == 0 or nb == 0:
+        return ids, vals
+    rc = lib().oracle_topk(_p(s), nb, rows, nb, k, _p(ids), k, _p(vals))
+    assert rc == 0
+    return ids, vals
+
+
+# --------------------------------------------------------------------------
+# Checker (R4-R7)
+# --------------------------------------------------------------------------
+
+@dataclass
+class CheckResult:
+    ok: bool
+    utilisation: float   # max |err| / B over cells with B > 0
+    n_fail: int
+    n_cells: int
+    worst: tuple | None  # (row index, block, s_gpu, score_ref, B)
+
+    def __str__(self):
+        return (f"ok={self.ok} util={100 * self.utilisation:.3f}% fail={self.n_fail}/"
+                f"{self.n_cells} worst={self.worst}")
+
+
+def check_scores(s_gpu: np.ndarray, ref: Scores) -> CheckResult:
+    """R4: every cell within B; cells with B == 0 must be exactly equal."""
+    s = np.asarray(s_gpu, dtype=np.float64)
+    assert s.shape == ref.score.shape, (s.shape, ref.score.shape)
+    err = np.abs(s - ref.score)
+    bad = ~(err <= ref.B)          # NaN counts as a failure
+    with np.errstate(divide="ignore", invalid="ignore"):
+        util = np.where(ref.B > 0, err / ref.B, np.where(err == 0, 0.0, np.inf))
+    n_fail = int(bad.sum())
+    worst = None
+    umax = 0.0
+    if s.size:
+        idx = np.unravel_index(int(np.nanargmax(np.where(np.isnan(util), np.inf, util))), s.shape)
+        umax = float(util[idx])
+        worst = (int(idx[0]), int(idx[1]), float(s[idx]), float(ref.score[idx]), float(ref.B[idx]))
+    return CheckResult(n_fail == 0, umax, n_fail, int(s.size), worst)
+
+
+def negative_controls(ref: Scores, s_gpu: np.ndarray, seed: int = 7) -> tuple[bool, bool]:
+    """R5: (i) +2.5*B on every cell with B > 0, (ii) +2.5*B on one seeded cell
+    with B > 0.  Returns (i_failed, ii_failed): both must be True."""
+    s = np.asarray(s_gpu, dtype=np.float64)
+    pos = ref.B > 0
+    if not pos.any():
+        return True, True
+    p1 = s + NEG_CONTROL * ref.B * pos
+    f1 = not check_scores(p1, ref).ok
+    cand = np.flatnonzero(pos.ravel())
+    rng = np.random.default_rng(seed)
+    c = int(cand[rng.integers(cand.size)])
+    p2 = s.copy().ravel()
+    p2[c] = ref.score.ravel()[c] + NEG_CONTROL * ref.B.ravel()[c]
+    f2 = not check_scores(p2.reshape(s.shape), ref).ok
+    return f1, f2
+
+
+@dataclass
+class SelectionResult:
+    ok: bool
+    rows_differing: int
+    ids_differing: int
+    n_ids: int
+    worst_gap_ratio: float  # max over swapped pairs of gap / (2*max(B))
+    detail: str = ""
+
+
+def check_selection(ids_gpu: np.ndarray, ref: Scores, k: int) -> SelectionResult:
+    """R6: the device ids against the oracle's own top-k of score_ref.  Per row
+    the sets must match, except that every x in gpu\\oracle and y in
+    oracle\\gpu satisfy score_ref(y) - score_ref(x) <= 2*max(B(x), B(y)).
+    Slots past min(k, nb) must be -1 in both."""
+    ids_gpu = np.asarray(ids_gpu, dtype=np.int64)
+    ids_ref, _ = topk(ref.score, k)
+    nb = ref.score.shape[1]
+    kk = min(k, nb)
+    rows_diff = ids_diff = 0
+    worst = 0.0
+    ok = True
+    detail = ""
+    for r in range(ids_gpu.shape[0]):
+        g = ids_gpu[r]
+        o = ids_ref[r].astype(np.int64)
+        if np.any(g[kk:] != -1):
+            ok = False
+            detail = f"row {r}: padding not -1"
+            continue
+        gs, os_ = set(g[:kk].tolist()), set(o[:kk].tolist())
+        if len(gs) != kk or any(x < 0 or x >= nb for x in gs):
+            ok = False
+            detail = f"row {r}: invalid or duplicate ids {g[:kk]}"
+            continue
+        xs, ys = gs - os_, os_ - gs
+        if xs:
+            rows_diff += 1
+            ids_diff += len(xs)
+            for x in xs:
+                for y in ys:
+                    gap = ref.score[r, y] - ref.score[r, x]
+                    lim = 2.0 * max(ref.B[r, x], ref.B[r, y])
+                    if gap > lim:
+                        ok = False
+                        detail = f"row {r}: swapped {x}<->{y} gap {gap} > {lim}"
+                    if lim > 0:
+                        worst = max(worst, gap / lim)
+                    elif gap > 0:
+                        worst = np.inf
+    return SelectionResult(ok, rows_diff, ids_diff, ids_gpu.shape[0] * kk, worst, detail)
+
+
+def exact_selection(ids_gpu: np.ndarray, s_rows: np.ndarray, k: int) -> np.ndarray:
+    """R6 first part / R7: the oracle's top-k of the given score rows, to be
+    compared bit for bit with the device ids computed from the same rows."""
+    ids, _ = topk(np.asarray(s_rows, dtype=np.float64), k)
+    return ids

@@ -1,0 +1,250 @@
+/*
+ * qsa_oracle.c -- TEST INFRASTRUCTURE, not part of the product.
+ *
+ * A plain, slow, obviously correct CPU reference for the QSA block-score
+ * select phase.  Only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg may load it.  It shares no code, header or table with the
+ * HIP library: it decodes fp16 itself, sums in float64 in plain index order
+ * and sorts with the C library's qsort.
+ *
+ * What it computes (Strata pull request #228, part 1 "qsa_block_scores_wmma:
+ * the prompt scorer arm on tensor cores", the score formula in its first
+ * paragraph; restated in Strata pull request #856):
+ *
+ *   score(t, b) = sum over query heads h of relu( sum over channels i of
+ *                 k_b[i] * q_{t,h}[i] )
+ *
+ * for every query t of a KV head g and every KV block b, where the H query
+ * heads of KV head g share the block key k_b.  The arithmetic contract (the
+ * same page, "arithmetic contract" paragraph; PR #856 "Arithmetic contract and
+ * parity") bounds each fp16/fp32 result by
+ *
+ *   B(t, b) = 2^-9.5 * S(t, b) + 8 * 2^-24 * |score_ref(t, b)|,
+ *   S(t, b) = sum_h sum_i |k_b[i] * q_{t,h}[i]|   (float64),
+ *
+ * and the phase then keeps, per query, the top-k blocks ("selection/topk",
+ * PR #228 part 1, the paragraph after the bench table).
+ *
+ * Every product of two fp16 values (22 significant bits) or of an fp32 and an
+ * fp16 value (35 bits) is exact in float64, so the only rounding here is the
+ * float64 summation, about D * 2^-53 * S: negligible against B.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_ABI 1
+
+int oracle_abi_version(void) { return ORACLE_ABI; }
+
+/* IEEE 754 binary16 -> exact double, from the format's definition:
+ * sign s, 5-bit biased exponent e, 10-bit fraction m.
+ *   e == 0        : (-1)^s * m * 2^-24            (zero and subnormals)
+ *   0 < e < 31    : (-1)^s * (1024 + m) * 2^(e-25)
+ *   e == 31       : infinity (m == 0) or NaN       */
+double oracle_f16_to_f64(uint16_t h)
+{
+    int s = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);
+    else if (e == 31)
+        v = (m == 0) ? INFINITY : NAN;
+    else
+        v = ldexp((double)(1024 + m), e - 25);
+    return s ? -v : v;
+}
+
+/* fp32 -> fp16 bits, round to nearest, ties to even, written from the
+ * definition rather than bit tricks:
+ *  - NaN keeps its sign and the top 10 fraction bits and is made quiet;
+ *  - |x| >= 65520 (halfway between 65504 and 2^16) overflows to infinity;
+ *  - below 2^-14 the fp16 grid spacing is 2^-24 (subnormals);
+ *  - otherwise the spacing is 2^(E-10) with E = floor(log2 |x|).
+ * The quotient |x| / spacing is exact in double, and rint() rounds it to
+ * the nearest integer with ties to even (the default rounding mode). */
+uint16_t oracle_f32_to_f16_one(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    uint32_t mag = u & 0x7fffffffu;
+    if (mag > 0x7f800000u)                      /* NaN */
+        return (uint16_t)(sign | 0x7c00u | 0x0200u | ((mag >> 13) & 0x3ffu));
+    if (mag == 0x7f800000u)                     /* infinity */
+        return (uint16_t)(sign | 0x7c00u);
+    double a = fabs((double)x);
+    if (a < ldexp(1.0, -14)) {
+        double q = rint(a / ldexp(1.0, -24));   /* 0 .. 1024 */
+        return (uint16_t)(sign | (uint16_t)q);  /* 1024 encodes 2^-14 */
+    }
+    int E;
+    frexp(a, &E);                                /* a = f * 2^E, f in [0.5,1) */
+    E -= 1;                                      /* a in [2^E, 2^(E+1)) */
+    double q = rint(ldexp(a, 10 - E));           /* in [1024, 2048] */
+    if (q == 2048.0) {
+        q = 1024.0;
+        E += 1;
+    }
+    if (E + 15 >= 31)
+        return (uint16_t)(sign | 0x7c00u);
+    return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)(q - 1024.0));
+}
+
+void oracle_convert_f32_f16(const float *src, uint16_t *dst, int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = oracle_f32_to_f16_one(src[i]);
+}
+
+/* Row r of a request is (g, t) = (rows[r] / nq, rows[r] % nq); a NULL row
+ * list means every row r = g*nq + t in order.
+ *
+ * q layout:  element (t, g, h, i) at q[t*q_tok_stride + (g*H + h)*D + i],
+ *            fp16 bits if q_is_f32 == 0, else float32 values.
+ * k layout:  element (g, b, i) at kblk[g*k_head_stride + b*D + i], fp16 bits.
+ * outputs:   score/S/B at [r*ld_out + b] for b in [0, nb); any may be NULL.
+ *
+ * score_ref = sum_h relu(d_h), d_h = sum_i k[i]*q_h[i]; h and i ascending. */
+int oracle_scores(const void *q, int q_is_f32, int64_t q_tok_stride,
+                  const uint16_t *kblk, int64_t k_head_stride,
+                  int32_t G, int32_t nq, int32_t H, int32_t D, int64_t nb,
+                  const int64_t *rows, int64_t n_rows,
+                  double *score, double *S, double *B, int64_t ld_out)
+{
+    if (G < 0 || nq < 0 || H < 1 || D < 1 || nb < 0 || ld_out < nb)
+        return 1;
+    if (rows == NULL)
+        n_rows = (int64_t)G * nq;
+    const uint16_t *q16 = (const uint16_t *)q;
+    const float *q32 = (const float *)q;
+    const double bound_rel = ldexp(1.0, -9) / sqrt(2.0);   /* 2^-9.5 */
+    const double bound_abs = 8.0 * ldexp(1.0, -24);
+
+#pragma omp parallel
+    {
+        double *qrow = (double *)malloc(sizeof(double) * (size_t)H * (size_t)D);
+        double *krow = (double *)malloc(sizeof(double) * (size_t)D);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < n_rows; ++r) {
+            int64_t rid = rows ? rows[r] : r;
+            int64_t g = rid / nq, t = rid % nq;
+            for (int32_t h = 0; h < H; ++h)
+                for (int32_t i = 0; i < D; ++i) {
+                    int64_t off = t * q_tok_stride + ((int64_t)g * H + h) * D + i;
+                    qrow[(size_t)h * D + i] =
+                        q_is_f32 ? (double)q32[off] : oracle_f16_to_f64(q16[off]);
+                }
+            for (int64_t b = 0; b < nb; ++b) {
+                for (int32_t i = 0; i < D; ++i)
+                    krow[i] = oracle_f16_to_f64(kblk[g * k_head_stride + b * D + i]);
+                double sc = 0.0, sabs = 0.0;
+                for (int32_t h = 0; h < H; ++h) {
+                    double d = 0.0;
+                    for (int32_t i = 0; i < D; ++i) {
+                        double p = krow[i] * qrow[(size_t)h * D + i];
+                        d += p;
+                        sabs += fabs(p);
+                    }
+                    sc += (d > 0.0) ? d : 0.0;
+                }
+                if (score) score[r * ld_out + b] = sc;
+                if (S) S[r * ld_out + b] = sabs;
+                if (B) B[r * ld_out + b] = bound_rel * sabs + bound_abs * fabs(sc);
+            }
+        }
+        free(qrow);
+        free(krow);
+    }
+    return 0;
+}
+
+/* The fixed-order single-precision model of one block's scores, used to pin
+ * the separate tail-block kernel bit for bit.  The pages state that the
+ * partial last block is scored by its own shared kernel whose result is
+ * bitwise reproducible (PR #228 part 1, the paragraph naming the tail
+ * kernel; PR #856 "What").  The order fixed here:
+ *   acc_h = +0; for i ascending: acc_h = fmaf(k[i], q_h[i], acc_h)
+ *   r_h   = acc_h > 0 ? acc_h : +0
+ *   s     = +0; for h ascending: s = s + r_h
+ * Operands are fp16 bits (for fp32 queries: the fp16 values the conversion
+ * produced).  out[r] for the same row convention as oracle_scores. */
+int oracle_block_model_f32(const uint16_t *q16, int64_t q_tok_stride,
+                           const uint16_t *kblk, int64_t k_head_stride,
+                           int32_t G, int32_t nq, int32_t H, int32_t D, int64_t b,
+                           const int64_t *rows, int64_t n_rows, float *out)
+{
+    if (G < 0 || nq < 0 || H < 1 || D < 1 || b < 0)
+        return 1;
+    if (rows == NULL)
+        n_rows = (int64_t)G * nq;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t rid = rows ? rows[r] : r;
+        int64_t g = rid / nq, t = rid % nq;
+        float s = 0.0f;
+        for (int32_t h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int32_t i = 0; i < D; ++i) {
+                float kv = (float)oracle_f16_to_f64(kblk[g * k_head_stride + b * D + i]);
+                float qv = (float)oracle_f16_to_f64(
+                    q16[t * q_tok_stride + ((int64_t)g * H + h) * D + i]);
+                acc = fmaf(kv, qv, acc);
+            }
+            float rh = (acc > 0.0f) ? acc : 0.0f;
+            s = s + rh;
+        }
+        out[r] = s;
+    }
+    return 0;
+}
+
+/* Top-k over a score row: blocks ordered by score descending, ties by block
+ * id ascending; scores compare numerically (so -0 == +0) and a NaN ranks
+ * below every number.  The first min(k, nb) ids are written, then -1 up to
+ * k; vals (nullable) gets the selected scores and -inf in padded slots. */
+typedef struct {
+    double s;
+    int64_t id;
+} oracle_entry;
+
+static int oracle_cmp(const void *pa, const void *pb)
+{
+    const oracle_entry *a = (const oracle_entry *)pa, *b = (const oracle_entry *)pb;
+    int na = isnan(a->s), nb = isnan(b->s);
+    if (na != nb)
+        return na ? 1 : -1;                 /* NaN after every number */
+    if (!na && a->s != b->s)
+        return (a->s > b->s) ? -1 : 1;      /* larger score first */
+    return (a->id < b->id) ? -1 : (a->id > b->id);
+}
+
+int oracle_topk(const double *scores, int64_t ld, int64_t rows, int64_t nb, int32_t k,
+                int32_t *ids, int64_t ld_ids, double *vals)
+{
+    if (rows < 0 || nb < 0 || k < 0 || ld < nb || ld_ids < k)
+        return 1;
+#pragma omp parallel
+    {
+        oracle_entry *e = (oracle_entry *)malloc(sizeof(oracle_entry) * (size_t)(nb > 0 ? nb : 1));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < rows; ++r) {
+            for (int64_t b = 0; b < nb; ++b) {
+                e[b].s = scores[r * ld + b];
+                e[b].id = b;
+            }
+            qsort(e, (size_t)nb, sizeof(oracle_entry), oracle_cmp);
+            for (int32_t j = 0; j < k; ++j) {
+                int sel = j < nb;
+                ids[r * ld_ids + j] = sel ? (int32_t)e[j].id : -1;
+                if (vals) vals[r * ld_ids + j] = sel ? e[j].s : -INFINITY;
+            }
+        }
+        free(e);
+    }
+    return 0;
+}

@@ -1,0 +1,509 @@
+"""CPU pins of the float64 oracle.
+
+Each test ties the oracle to something other than itself: exact rational
+arithmetic on tiny inputs, numpy's float64 matmul in the single-head case,
+closed forms of coded fixtures, hand-worked golden examples, invariants of the
+formula, the x86 F16C conversion instruction, numpy's sequential float32
+accumulation, and an O(n^2) rank count for the top-k order.
+
+The formula is the QSA block score of Strata pull request #228 (part 1, first
+paragraph): score(t, b) = sum_h relu(sum_i k_b[i] * q_{t,h}[i]); the bound is
+the same page's arithmetic contract.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import qsa_inputs as qi
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+# --------------------------------------------------------------------------
+# helpers independent of the oracle
+# --------------------------------------------------------------------------
+
+def f16_bits_to_int24(b: int) -> int:
+    """fp16 bits -> integer m with value m * 2^-24 (finite values only),
+    from the bit fields of IEEE 754 binary16."""
+    s, e, m = (b >> 15) & 1, (b >> 10) & 0x1F, b & 0x3FF
+    assert e != 31
+    v = m if e == 0 else (1024 + m) << (e - 1)
+    return -v if s else v
+
+
+def exact_scores(q16: np.ndarray, kblk: np.ndarray, nb: int):
+    """Exact score and S as Fractions, by integer arithmetic."""
+    nq, G, H, D = q16.shape
+    qi_ = np.vectorize(f16_bits_to_int24, otypes=[object])(q16.astype(np.int64))
+    ki_ = np.vectorize(f16_bits_to_int24, otypes=[object])(kblk.astype(np.int64))
+    scale = Fraction(1, 2 ** 48)
+    sc = np.empty((G * nq, nb), dtype=object)
+    S = np.empty((G * nq, nb), dtype=object)
+    for g in range(G):
+        for t in range(nq):
+            for b in range(nb):
+                tot = 0
+                sabs = 0
+                for h in range(H):
+                    d = 0
+                    for i in range(D):
+                        p = int(ki_[g, b, i]) * int(qi_[t, g, h, i])
+                        d += p
+                        sabs += abs(p)
+                    tot += max(d, 0)
+                sc[g * nq + t, b] = tot * scale
+                S[g * nq + t, b] = sabs * scale
+    return sc, S
+
+
+SPECIAL_F16 = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x03FF, 0x83FF, 0x0400, 0x8400,
+                        0x7BFF, 0xFBFF, 0x3C00, 0xBC00, 0x3555, 0x0200], dtype=np.uint16)
+
+
+def random_f16(rng, shape, special_frac=0.2):
+    """fp16 bits: mostly random finite values of mixed magnitude, some special."""
+    n = int(np.prod(shape))
+    e = rng.integers(0, 31, n)            # every finite exponent incl. subnormal
+    m = rng.integers(0, 1024, n)
+    s = rng.integers(0, 2, n)
+    bits = ((s << 15) | (e << 10) | m).astype(np.uint16)
+    pick = rng.random(n) < special_frac
+    bits[pick] = SPECIAL_F16[rng.integers(0, SPECIAL_F16.size, int(pick.sum()))]
+    return bits.reshape(shape)
+
+
+# --------------------------------------------------------------------------
+# fp16 decoding and conversion
+# --------------------------------------------------------------------------
+
+def test_f16_decode_all_patterns():
+    bits = np.arange(65536, dtype=np.uint16)
+    got = oracle.f16_to_f64(bits)
+    want = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))  # -0 kept
+
+
+def test_int24_helper_matches_numpy():
+    bits = np.arange(65536, dtype=np.uint16)
+    fin = np.isfinite(bits.view(np.float16))
+    vals = [f16_bits_to_int24(int(b)) * 2.0 ** -24 for b in bits[fin]]
+    assert np.array_equal(np.array(vals), bits[fin].view(np.float16).astype(np.float64))
+
+
+@pytest.fixture(scope="module")
+def f16c_lib(tmp_path_factory):
+    src = os.path.join(HERE, "pins", "f16c_ref.c")
+    out = str(tmp_path_factory.mktemp("f16c") / "libf16c.so")
+    subprocess.run(["gcc", "-O2", "-mf16c", "-fopenmp", "-fPIC", "-shared", "-o", out, src],
+                   check=True)
+    L = ctypes.CDLL(out)
+    L.f16c_compare_range.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64,
+                                     ctypes.POINTER(ctypes.c_uint64)]
+    L.f16c_compare_range.restype = ctypes.c_int64
+    L.f16c_one.argtypes = [ctypes.c_float]
+    L.f16c_one.restype = ctypes.c_uint16
+    return L
+
+
+def test_convert_exhaustive_vs_f16c(f16c_lib):
+    """The oracle's hand-written fp32 -> fp16 (nearest even) equals the F16C
+    instruction on all 2^32 fp32 bit patterns, NaNs included."""
+    fn = ctypes.cast(oracle.lib().oracle_f32_to_f16_one, ctypes.c_void_p)
+    first = ctypes.c_uint64()
+    bad = f16c_lib.f16c_compare_range(fn, 0, 1 << 32, ctypes.byref(first))
+    assert bad == 0, f"{bad} mismatches, first pattern {first.value:#010x}"
+
+
+def test_convert_vs_numpy_nonnan():
+    """Same converter against numpy's float32 -> float16 on non-NaN samples."""
+    rng = np.random.default_rng(5)
+    pats = np.concatenate([
+        rng.integers(0, 1 << 32, 1 << 20, dtype=np.uint64),
+        # every exponent with the fraction patterns around the rounding points
+        (np.arange(512, dtype=np.uint64)[:, None] << np.uint64(23)
+         | np.array([0, 1, 0xFFF, 0x1000, 0x1001, 0x1FFF, 0x2000, 0x2001, 0x3000,
+                     0x7FFFFF, 0x7FE000, 0x7FF000], dtype=np.uint64)[None, :]).ravel(),
+    ]).astype(np.uint32)
+    x = pats.view(np.float32)
+    x = x[~np.isnan(x)]
+    got = oracle.convert_f32_f16(x)
+    want = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_convert_known_values():
+    cases = {1.0: 0x3C00, -2.0: 0xC000, 65504.0: 0x7BFF, 65519.996: 0x7BFF, 65520.0: 0x7C00,
+             2.0 ** -24: 0x0001, 2.0 ** -25: 0x0000, 2.0 ** -25 * 1.0000001: 0x0001,
+             3 * 2.0 ** -25: 0x0002, 2.0 ** -14: 0x0400, 1.0 + 2.0 ** -11: 0x3C00,
+             1.0 + 3 * 2.0 ** -11: 0x3C02, -0.0: 0x8000, float("inf"): 0x7C00}
+    for v, bits in cases.items():
+        assert oracle.lib().oracle_f32_to_f16_one(v) == bits, (v, hex(bits))
+
+
+# --------------------------------------------------------------------------
+# scores: exact brute force, library special case, closed forms, invariants
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(12))
+def test_scores_vs_exact_bruteforce(seed):
+    rng = np.random.default_rng(100 + seed)
+    D = [1, 2, 3, 16, 64][seed % 5]
+    G, nq, H, nb = int(rng.integers(1, 3)), int(rng.integers(1, 6)), int(rng.integers(1, 5)), \
+        int(rng.integers(1, 6))
+    q16 = random_f16(rng, (nq, G, H, D))
+    kb = random_f16(rng, (G, nb, D))
+    ref = oracle.scores(q16, kb, nb)
+    ex, exS = exact_scores(q16, kb, nb)
+    for r in range(G * nq):
+        for b in range(nb):
+            s_ex, S_ex = ex[r, b], exS[r, b]
+            tol = float(S_ex) * 2.0 ** -45
+            assert abs(Fraction(ref.score[r, b]) - s_ex) <= Fraction(tol), (r, b)
+            assert abs(Fraction(ref.S[r, b]) - S_ex) <= Fraction(tol), (r, b)
+            want_B = oracle.BOUND_REL * float(S_ex) + oracle.BOUND_ABS * float(s_ex)
+            assert math.isclose(ref.B[r, b], want_B, rel_tol=1e-12, abs_tol=1e-300)
+
+
+def test_single_head_is_relu_matmul():
+    """With H = 1 the score is relu(Q K^T): numpy float64 matmul."""
+    rng = np.random.default_rng(3)
+    nq, nb, D = 33, 47, 128
+    q16 = qi.f64_to_f16_bits(rng.standard_normal((nq, 1, 1, D)) / math.sqrt(D))
+    kb = qi.f64_to_f16_bits(rng.standard_normal((1, nb, D)) / math.sqrt(D))
+    ref = oracle.scores(q16, kb, nb)
+    Q = q16.view(np.float16).astype(np.float64).reshape(nq, D)
+    K = kb.view(np.float16).astype(np.float64).reshape(nb, D)
+    want = np.maximum(Q @ K.T, 0.0)
+    assert np.all(np.abs(ref.score - want) <= D * 2.0 ** -52 * ref.S)
+
+
+def test_coded_fixture_closed_form():
+    cfg = qi.CONFIGS["nq256_nkv32768"]
+    small = qi.Config("coded_small", 2, 40, cfg.H, cfg.D, 64 * 37, 64, 8, "normal", 0)
+    w = qi.coded_fixture(small)
+    ref = oracle.scores(w.q16, w.kblk, small.nb)
+    ch, kint = w.extra["channel"], w.extra["kint"]
+    want = np.zeros((small.G * small.nq, small.nb))
+    for g in range(small.G):
+        for t in range(small.nq):
+            want[g * small.nq + t] = np.maximum(kint[g, :small.nb, ch[t]], 0).sum(axis=0)
+    assert np.array_equal(ref.score, want)
+    assert np.array_equal(ref.S, np.abs(kint[:, :small.nb, :][
+        np.repeat(np.arange(small.G), small.nq)[:, None, None],
+        np.arange(small.nb)[None, :, None], np.tile(ch, (small.G, 1))[:, None, :]]).sum(axis=2))
+
+
+def test_integer_fixture_exact():
+    cfg = qi.Config("int_small", 2, 19, 8, 128, 64 * 9 + 7, 64, 8, "normal", 0)
+    w = qi.integer_fixture(cfg)
+    ref = oracle.scores(w.q16, w.kblk, cfg.nb)
+    Q = w.q16.view(np.float16).astype(np.int64)
+    K = w.kblk.view(np.float16).astype(np.int64)
+    want = np.zeros((cfg.G * cfg.nq, cfg.nb), dtype=np.int64)
+    for g in range(cfg.G):
+        d = np.einsum("thi,bi->thb", Q[:, g], K[g, :cfg.nb])
+        want[g * cfg.nq:(g + 1) * cfg.nq] = np.maximum(d, 0).sum(axis=1)
+    assert np.array_equal(ref.score, want.astype(np.float64))
+    assert want.max() > 2048  # large enough that fp16 accumulation would fail
+
+
+def test_trivial_closed_forms():
+    rng = np.random.default_rng(9)
+    nq, G, H, D, nb = 5, 2, 3, 64, 11
+    kb = qi.f64_to_f16_bits(rng.standard_normal((G, nb, D)))
+    zero_q = np.zeros((nq, G, H, D), np.uint16)
+    ref = oracle.scores(zero_q, kb, nb)
+    assert np.all(ref.score == 0) and np.all(ref.S == 0) and np.all(ref.B == 0)
+    ids, _ = oracle.topk(ref.score, 4)
+    assert np.array_equal(ids, np.tile(np.arange(4, dtype=np.int32), (G * nq, 1)))
+    # all key rows equal -> equal scores -> ids 0..k-1
+    q16 = qi.f64_to_f16_bits(rng.standard_normal((nq, G, H, D)))
+    same = np.repeat(kb[:, :1, :], nb, axis=1)
+    ref = oracle.scores(q16, same, nb)
+    assert np.all(ref.score == ref.score[:, :1])
+    ids, _ = oracle.topk(ref.score, 4)
+    assert np.array_equal(ids, np.tile(np.arange(4, dtype=np.int32), (G * nq, 1)))
+    # one dominant block: q = |k_b*| direction on every head
+    kd = kb.copy()
+    kd[:, 7, :] = qi.f64_to_f16_bits(np.full((G, D), 4.0))
+    qp = qi.f64_to_f16_bits(np.abs(rng.standard_normal((nq, G, H, D))) + 1.0)
+    kd[:, :7] = qi.f64_to_f16_bits(np.full((G, 7, D), -1.0))
+    kd[:, 8:] = qi.f64_to_f16_bits(np.full((G, nb - 8, D), -1.0))
+    ref = oracle.scores(qp, kd, nb)
+    ids, _ = oracle.topk(ref.score, 1)
+    assert np.all(ids[:, 0] == 7)
+
+
+def test_invariants():
+    rng = np.random.default_rng(11)
+    nq, G, H, D, nb = 7, 2, 4, 64, 13
+    q16 = qi.f64_to_f16_bits(rng.standard_normal((nq, G, H, D)) * 0.3)
+    kb = qi.f64_to_f16_bits(rng.standard_normal((G, nb, D)) * 0.3)
+    ref = oracle.scores(q16, kb, nb)
+    assert np.all(ref.score >= 0) and np.all(ref.score <= ref.S)
+    # head permutation: same value up to float64 summation order
+    perm = rng.permutation(H)
+    rp = oracle.scores(q16[:, :, perm], kb, nb)
+    assert np.all(np.abs(rp.score - ref.score) <= 2.0 ** -45 * ref.S)
+    # block permutation: each block is independent
+    bp = rng.permutation(nb)
+    rb = oracle.scores(q16, kb[:, bp], nb)
+    assert np.array_equal(rb.score, ref.score[:, bp])
+    # scaling by 2^j scales scores by 2^(2j) exactly
+    q2 = qi.f64_to_f16_bits(q16.view(np.float16).astype(np.float64) * 4.0)
+    k2 = qi.f64_to_f16_bits(kb.view(np.float16).astype(np.float64) * 0.5)
+    r2 = oracle.scores(q2, k2, nb)
+    assert np.array_equal(r2.score, ref.score * 2.0)
+    # relu(x) - relu(-x) = x: score(Q,K) - score(Q,-K) = (sum_h q_h) . k
+    kneg = kb ^ np.uint16(0x8000)
+    rn = oracle.scores(q16, kneg, nb)
+    Qf = q16.view(np.float16).astype(np.float64)
+    Kf = kb.view(np.float16).astype(np.float64)
+    for g in range(G):
+        want = Qf[:, g].sum(axis=1) @ Kf[g].T
+        got = ref.score[g * nq:(g + 1) * nq] - rn.score[g * nq:(g + 1) * nq]
+        assert np.all(np.abs(got - want) <= 2.0 ** -44 * ref.S[g * nq:(g + 1) * nq])
+
+
+def test_f32_queries_use_unrounded_values():
+    """For fp32 queries the oracle uses the fp32 values themselves."""
+    rng = np.random.default_rng(4)
+    nq, G, H, D, nb = 3, 1, 2, 64, 5
+    q32 = (rng.standard_normal((nq, G, H, D)) / 8).astype(np.float32)
+    kb = qi.f64_to_f16_bits(rng.standard_normal((G, nb, D)) / 8)
+    ref = oracle.scores(q32, kb, nb)
+    Q = q32.astype(np.float64)
+    K = kb.view(np.float16).astype(np.float64)
+    want = np.maximum(np.einsum("thi,bi->thb", Q[:, 0], K[0]), 0).sum(axis=1)
+    assert np.all(np.abs(ref.score - want) <= 2.0 ** -45 * ref.S)
+
+
+# --------------------------------------------------------------------------
+# golden hand-worked examples
+# --------------------------------------------------------------------------
+
+def load_hand_examples():
+    path = os.path.join(HERE, "golden", "hand_examples.txt")
+    exs, cur = [], None
+    for line in open(path):
+        line = line.split("#", 1)[0].split()
+        if not line:
+            continue
+        tag = line[0]
+        if tag == "example":
+            kv = dict(zip(line[2::2], map(int, line[3::2])))
+            cur = dict(name=line[1], **kv, q={}, kb={}, score={}, S={}, topk={})
+        elif tag == "q":
+            cur["q"][(int(line[1]), int(line[2]))] = [float(x) for x in line[3:]]
+        elif tag in ("kb", "score", "S", "topk"):
+            cur[tag][int(line[1])] = [float(x) for x in line[2:]]
+        elif tag == "end":
+            exs.append(cur)
+    return exs
+
+
+@pytest.mark.parametrize("ex", load_hand_examples(), ids=lambda e: e["name"])
+def test_hand_examples(ex):
+    H, D, nq, nb, k = ex["H"], ex["D"], ex["nq"], ex["nb"], ex["k"]
+    q = np.zeros((nq, 1, H, D))
+    for (t, h), v in ex["q"].items():
+        q[t, 0, h] = v
+    kb = np.array([ex["kb"][b] for b in range(nb)])[None]
+    ref = oracle.scores(qi.f64_to_f16_bits(q), qi.f64_to_f16_bits(kb), nb)
+    for t in range(nq):
+        assert ref.score[t].tolist() == ex["score"][t]
+        assert ref.S[t].tolist() == ex["S"][t]
+    ids, _ = oracle.topk(ref.score, k)
+    for t in range(nq):
+        assert ids[t].tolist() == [int(x) for x in ex["topk"][t]]
+
+
+def test_contract_constants_match_pages():
+    vals = {}
+    for line in open(os.path.join(HERE, "golden", "contract.txt")):
+        line = line.split("#", 1)[0].strip()
+        if line:
+            key, v = [x.strip() for x in line.split("=")]
+            vals[key] = float(v)
+    assert oracle.BOUND_REL == 2.0 ** vals["bound_rel_log2"]
+    assert oracle.BOUND_ABS == vals["bound_abs_coeff"] * 2.0 ** vals["bound_abs_log2"]
+    assert oracle.NEG_CONTROL == vals["negative_control_factor"]
+
+
+# --------------------------------------------------------------------------
+# fixed-order fp32 block model (the tail kernel's contract)
+# --------------------------------------------------------------------------
+
+def test_block_model_vs_numpy_sequential_float32():
+    """numpy's add.accumulate is a strictly sequential float32 sum; products of
+    two fp16 values are exact in float32, so fmaf(k, q, acc) and
+    round(acc + k*q) coincide and the model must equal it bit for bit."""
+    rng = np.random.default_rng(21)
+    nq, G, H, D, nb = 9, 2, 8, 128, 4
+    q16 = qi.f64_to_f16_bits(rng.standard_normal((nq, G, H, D)) / math.sqrt(D))
+    kb = qi.f64_to_f16_bits(rng.standard_normal((G, nb, D)) / math.sqrt(D))
+    b = 3
+    got = oracle.block_model_f32(q16, kb, b)
+    Q = q16.view(np.float16).astype(np.float32)
+    K = kb.view(np.float16).astype(np.float32)
+    want = np.empty(G * nq, np.float32)
+    for g in range(G):
+        for t in range(nq):
+            prods = K[g, b][None, :] * Q[t, g]                  # exact, [H][D]
+            acc = np.add.accumulate(prods, axis=1, dtype=np.float32)[:, -1]
+            r = np.where(acc > 0, acc, np.float32(0))
+            want[g * nq + t] = np.add.accumulate(np.concatenate([[np.float32(0)], r]),
+                                                 dtype=np.float32)[-1]
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_block_model_integer_exact_and_within_bound():
+    cfg = qi.Config("int_tail", 1, 11, 8, 128, 64 * 3 + 5, 64, 4, "normal", 0)
+    w = qi.integer_fixture(cfg)
+    ref = oracle.scores(w.q16, w.kblk, cfg.nb)
+    got = oracle.block_model_f32(w.q16, w.kblk, cfg.nb - 1)
+    assert np.array_equal(got.astype(np.float64), ref.score[:, -1])
+    wr = qi.make(qi.TINY)
+    refr = oracle.scores(wr.q16, wr.kblk, wr.cfg.nb)
+    gr = oracle.block_model_f32(wr.q16, wr.kblk, wr.cfg.nb - 1)
+    assert np.all(np.abs(gr - refr.score[:, -1]) <= refr.B[:, -1])
+
+
+def test_block_model_x8_is_exactly_64x():
+    w = qi.make(qi.TINY)
+    w8 = qi.scaled_by_8(w)
+    b = w.cfg.nb - 1
+    a = oracle.block_model_f32(w.q16, w.kblk, b)
+    a8 = oracle.block_model_f32(w8.q16, w8.kblk, b)
+    assert np.array_equal(a8, a * np.float32(64))
+
+
+# --------------------------------------------------------------------------
+# top-k order
+# --------------------------------------------------------------------------
+
+def rank_count_topk(row: np.ndarray, k: int) -> list[int]:
+    """O(n^2): rank(b) = #{b' better than b}; NaN below every number."""
+    n = row.size
+
+    def better(a, b):  # is a better than b
+        sa, sb = row[a], row[b]
+        na, nb_ = math.isnan(sa), math.isnan(sb)
+        if na != nb_:
+            return nb_
+        if not na and sa != sb:
+            return sa > sb
+        return a < b
+
+    ranks = [sum(better(o, b) for o in range(n)) for b in range(n)]
+    order = sorted(range(n), key=lambda b: ranks[b])
+    return [order[j] if j < n else -1 for j in range(k)]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_vs_rank_count(seed):
+    rng = np.random.default_rng(300 + seed)
+    rows, nb = 6, int(rng.integers(1, 90))
+    s = rng.integers(-3, 4, (rows, nb)).astype(np.float64) * 0.5
+    s[rng.random((rows, nb)) < 0.1] = -0.0
+    s[rng.random((rows, nb)) < 0.05] = np.nan
+    s[rng.random((rows, nb)) < 0.05] = np.inf
+    for k in (0, 1, 5, 64, nb + 3):
+        ids, vals = oracle.topk(s, k)
+        for r in range(rows):
+            assert ids[r].tolist() == rank_count_topk(s[r], k)
+            sel = ids[r] >= 0
+            assert np.array_equal(vals[r][sel], s[r][ids[r][sel]], equal_nan=True)
+            assert np.all(vals[r][~sel] == -np.inf)
+
+
+def test_topk_empty_row():
+    ids, vals = oracle.topk(np.zeros((3, 0)), 4)
+    assert np.all(ids == -1) and np.all(vals == -np.inf)
+
+
+# --------------------------------------------------------------------------
+# checker
+# --------------------------------------------------------------------------
+
+def test_checker_bound_edges_and_negative_controls():
+    w = qi.make(qi.TINY)
+    ref = oracle.scores(w.q16, w.kblk, w.cfg.nb)
+    s = ref.score.astype(np.float32).astype(np.float64)
+    assert oracle.check_scores(s, ref).ok
+    sign = np.where(np.random.default_rng(1).random(s.shape) < 0.5, -1.0, 1.0)
+    assert oracle.check_scores(ref.score + 0.99 * ref.B * sign, ref).ok
+    r = oracle.check_scores(ref.score + 1.01 * ref.B * sign, ref)
+    assert not r.ok and r.n_fail == s.size
+    f1, f2 = oracle.negative_controls(ref, s)
+    assert f1 and f2
+    # exact-mode cells (B == 0) tolerate nothing
+    z = oracle.Scores(np.zeros((1, 2)), np.zeros((1, 2)), np.zeros((1, 2)), np.zeros(1, np.int64))
+    assert oracle.check_scores(np.zeros((1, 2)), z).ok
+    assert not oracle.check_scores(np.array([[0.0, 1e-30]]), z).ok
+    assert not oracle.check_scores(np.array([[0.0, np.nan]]), z).ok
+
+
+def test_selection_checker_near_ties():
+    w = qi.make(qi.TINY)
+    ref = oracle.scores(w.q16, w.kblk, w.cfg.nb)
+    ids, _ = oracle.topk(ref.score, 4)
+    assert oracle.check_selection(ids, ref, 4).ok
+    # swap the 4th choice for the 5th: allowed only if the gap is within 2B
+    ids5, _ = oracle.topk(ref.score, 5)
+    swapped = ids.copy()
+    swapped[:, 3] = ids5[:, 4]
+    res = oracle.check_selection(swapped, ref, 4)
+    gaps = ref.score[np.arange(ids.shape[0]), ids[:, 3]] - \
+        ref.score[np.arange(ids.shape[0]), ids5[:, 4]]
+    lim = 2 * np.maximum(ref.B[np.arange(ids.shape[0]), ids[:, 3]],
+                         ref.B[np.arange(ids.shape[0]), ids5[:, 4]])
+    assert res.ok == bool(np.all(gaps <= lim))
+    bad = ids.copy()
+    bad[0, 0] = bad[0, 1]  # duplicate id
+    assert not oracle.check_selection(bad, ref, 4).ok
+
+
+# --------------------------------------------------------------------------
+# input generators (shared module, holds no arithmetic of the method)
+# --------------------------------------------------------------------------
+
+def test_splitmix64_published_values():
+    """First outputs of splitmix64 from state 1234567 (the widely published
+    reference sequence of Vigna's splitmix64.c)."""
+    got = qi.splitmix64(1234567, 0, 0, 5).tolist()
+    assert got == [6457827717110365317, 3203168211198807973, 9817491932198370423,
+                   4593380528125082431, 16408922859458223821]
+
+
+def test_stream_slices_are_consistent():
+    a = qi.splitmix64(77, 3, 0, 1000)
+    b = qi.splitmix64(77, 3, 400, 300)
+    assert np.array_equal(a[400:700], b)
+    n = qi.normal(5, 1, 10001)
+    assert abs(n.mean()) < 0.05 and abs(n.std() - 1) < 0.05
+
+
+def test_config_shapes():
+    c = qi.CONFIGS
+    assert (qi.TINY.nb, qi.TINY.nf) == (16, 15)
+    assert c["nq256_nkv4096"].nb == 64 and c["nq256_nkv32768"].nb == 512
+    assert c["nq256_nkv131072"].nb == 2048
+    assert (qi.PREFILL.nb, qi.PREFILL.nf, qi.PREFILL.rows) == (2049, 2048, 65536)
+    assert qi.PREFILL.flop == 2 * 65536 * 8 * 128 * 2049
+    w = qi.make(qi.TINY)
+    assert w.q16.shape == (37, 1, 4, 64) and w.kblk.shape == (1, 16, 64)
+    x8 = qi.scaled_by_8(qi.make("nq256_nkv4096"))
+    assert np.abs(x8.q16.view(np.float16).astype(np.float64)).max() < 8188
