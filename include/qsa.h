@@ -1,0 +1,159 @@
+/*
+ * qsa.h -- C ABI of libqsa.so, the MI355X (gfx950) QSA block-score select
+ * phase.
+ *
+ * The phase (Strata pull request #228, part 1 "qsa_block_scores_wmma: the
+ * prompt scorer arm on tensor cores": the score formula in the first
+ * paragraph, and the paragraph after the bench table, which lists the
+ * phase as scores + selection/top-k + the fp16 conversion + the batch loop):
+ *
+ *   1. convert the fp32 query activations to fp16 (round to nearest even);
+ *   2. for every KV head g, query t and KV block b
+ *        score(g, t, b) = sum_{h < H} relu( sum_{i < D} k[g, b, i] * q[t, g, h, i] )
+ *      with fp16 operands and fp32 accumulation; the last, partial block
+ *      (when n_kv is not a multiple of the block size) by a separate
+ *      fixed-order kernel;
+ *   3. per (g, t) row keep the top-k blocks, by score descending with ties
+ *      to the lower block id.
+ *
+ * Every score lies within the page's arithmetic contract
+ *   B = 2^-9.5 * S + 8 * 2^-24 * |score_ref|,  S = sum_h sum_i |k[i] * q_h[i]|
+ * of the float64 value (same page, "arithmetic contract" paragraph).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are DEVICE pointers (memory the caller allocated on the GPU
+ *    that owns `stream`).  fp16 data is passed as its raw bits (uint16_t).
+ *  - Strides are in ELEMENTS of the pointed-to type.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on it and returns; nothing is synchronised, allocated,
+ *    or kept between calls.  Calls are thread-safe.
+ *  - Refusal is clean: when a call returns anything but QSA_OK, nothing was
+ *    launched and no output byte was written.  Errors that happen on the
+ *    device after a successful launch surface at the caller's next
+ *    synchronisation of the stream.
+ *  - Write sets are exact: an entry point writes the output cells documented
+ *    for it and nothing else (pad columns and memory around the outputs are
+ *    left untouched).
+ *  - Inputs must be finite; non-finite inputs give unspecified scores (the
+ *    call still completes).
+ *
+ * Layouts
+ *  q16[t * q_tok_stride + (g*H + h) * D + i]      token-major queries, the same as
+ *                                                 a GQA query tensor [tokens][G*H][D]
+ *  kblk[g * kblk_head_stride + b * D + i]         one key vector per KV block
+ *  scores[(g*nq + t) * ld_s + b]                  fp32, row r = g*nq + t
+ *  ids[(g*nq + t) * ld_ids + j], vals[...]        j < k
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qsa_status {
+    QSA_OK = 0,
+    QSA_ERR_ARG = 1,         /* NULL where data is needed, negative size, stride
+                                or leading dimension too small, size overflow */
+    QSA_ERR_UNSUPPORTED = 2, /* geometry outside the supported set: D not in
+                                {64, 128}, H outside [1, 16], k > 64, block size
+                                < 1, a pointer or stride not 16-byte aligned
+                                where the kernels load 16-byte vectors */
+    QSA_ERR_HIP = 3          /* the HIP runtime refused a launch */
+} qsa_status;
+
+#define QSA_ABI_VERSION 1
+#define QSA_MAX_K 64
+
+/* Version of this ABI (QSA_ABI_VERSION of the header the library was built
+ * with). */
+int qsa_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char *qsa_status_string(qsa_status s);
+
+/*
+ * qsa_convert_f32_f16 -- step 1 of the phase ("the fp16 conversion",
+ * Strata pull request #228, part 1, paragraph after the bench table).
+ * dst[i] = fp16 bits of src[i] rounded to nearest, ties to even, for
+ * 0 <= i < n.  |x| >= 65520 becomes +-inf; fp16 subnormals are produced;
+ * NaN stays NaN (quiet, sign and top fraction bits kept).
+ *   src  device, n floats;     dst  device, n uint16 (fp16 bits).
+ * n == 0 is a no-op (pointers may then be NULL).  src and dst must not
+ * overlap.  Errors: QSA_ERR_ARG (n < 0, NULL with n > 0).
+ */
+qsa_status qsa_convert_f32_f16(const float *src, uint16_t *dst, int64_t n, void *stream);
+
+/*
+ * qsa_block_scores -- step 2 of the phase: the score of every (g, t, b)
+ * cell, b < nb = ceil(n_kv / bs).  Blocks b < nf = floor(n_kv / bs) go to the
+ * MFMA full-block scorer; the partial block b = nf (present when n_kv % bs
+ * != 0) goes to the separate tail kernel, whose fixed order (per head a
+ * single-precision fused multiply-add chain over i ascending, relu, then the
+ * head sum over h ascending) reproduces the same results bit for bit on
+ * every run (Strata pull request #228, part 1, the paragraph naming the tail
+ * kernel; Strata pull request #856, "What").
+ *   q16        device fp16 bits, layout above; q_tok_stride >= G*H*D,
+ *              q16 and q_tok_stride 16-byte aligned (q_tok_stride % 8 == 0)
+ *   kblk       device fp16 bits [G][>= nb][D] at kblk_head_stride >= nb*D
+ *              (16-byte aligned, kblk_head_stride % 8 == 0)
+ *   scores     device fp32 [G*nq][ld_s], ld_s >= nb; written: [r][0, nb)
+ *   G, nq >= 0; H in [1, 16]; D in {64, 128}; n_kv >= 0; bs >= 1
+ * n_kv == 0 (nb == 0), nq == 0 or G == 0: QSA_OK, nothing written.
+ */
+qsa_status qsa_block_scores(const uint16_t *q16, int64_t q_tok_stride,
+                            const uint16_t *kblk, int64_t kblk_head_stride,
+                            float *scores, int64_t ld_s,
+                            int32_t G, int32_t nq, int32_t H, int32_t D,
+                            int64_t n_kv, int32_t bs, void *stream);
+
+/*
+ * qsa_select_topk -- step 3 of the phase ("selection/topk", Strata pull
+ * request #228, part 1; ids compared across arms in Strata pull request
+ * #856).  For each row r < rows: the first min(k, nb) block ids in the order
+ * (score descending, block id ascending), where scores compare numerically
+ * (-0 == +0) and NaN ranks below every number; slots [min(k, nb), k) get -1.
+ *   scores  device fp32 [rows][ld_s], ld_s >= nb (only [r][0, nb) is read)
+ *   ids     device int32 [rows][ld_ids], ld_ids >= k; written: [r][0, k)
+ *   vals    device fp32 [rows][ld_ids] or NULL; written: [r][0, k): the
+ *           selected scores (bit copies), -inf in padded slots
+ *   rows >= 0, nb >= 0, 0 <= k <= 64
+ * k == 0 or rows == 0: QSA_OK, nothing written.  nb == 0: every slot -1.
+ */
+qsa_status qsa_select_topk(const float *scores, int64_t ld_s, int64_t rows, int32_t nb,
+                           int32_t k, int32_t *ids, int64_t ld_ids, float *vals,
+                           void *stream);
+
+/*
+ * qsa_select_phase -- the whole phase on one stream: convert (when q32 is
+ * given), score (full blocks + tail), select.  The batch loop is folded into
+ * the launch grids; with q_chunk > 0 the host walks the queries in chunks of
+ * q_chunk so that the score workspace holds only G*q_chunk rows.
+ *   q32       device fp32 queries (layout of q16, same q_tok_stride) or NULL
+ *   q16       device fp16 bits: the input when q32 == NULL, else a workspace
+ *             that receives the converted queries (every element of
+ *             [0, (nq-1)*q_tok_stride + G*H*D) is written)
+ *   scores_ws device fp32 [G*qc][ld_s] workspace, qc = q_chunk > 0 ?
+ *             min(q_chunk, nq) : nq; row g*qc + t' holds the scores of query
+ *             t0 + t' of the chunk being selected
+ *   ids, vals as qsa_select_topk with rows = G*nq (vals may be NULL)
+ *   other arguments as qsa_block_scores / qsa_select_topk.
+ * Workspaces must not overlap the inputs or outputs.  Errors as the three
+ * stage entry points; the whole call is validated before the first launch.
+ */
+qsa_status qsa_select_phase(const float *q32, uint16_t *q16, int64_t q_tok_stride,
+                            const uint16_t *kblk, int64_t kblk_head_stride,
+                            float *scores_ws, int64_t ld_s,
+                            int32_t *ids, int64_t ld_ids, float *vals,
+                            int32_t G, int32_t nq, int32_t H, int32_t D,
+                            int64_t n_kv, int32_t bs, int32_t k, int64_t q_chunk,
+                            void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

@@ -271,6 +271,6 @@ def conversion_fixture(cfg: Config, seed: int = 1012) -> Workload:
 
 
 def fp32_bit_patterns(start: int, count: int) -> np.ndarray:
-    """float32 values whose bit patterns are start, start+1, ... (mod 2^32)."""
-    return (np.arange(start, start + count, dtype=np.uint64) & np.uint64(0xFFFFFFFF)) \
-        .astype(np.uint32).view(np.float32)
+    """float32 values whose bit patterns are start, start+1, ... (< 2^32)."""
+    assert 0 <= start and start + count <= 1 << 32
+    return np.arange(start, start + count, dtype=np.uint64).astype(np.uint32).view(np.float32)

@@ -1,0 +1,180 @@
+// qsa_api.hip -- the extern "C" boundary of libqsa.so (declared in qsa.h).
+// Validates every argument before any HIP call, sizes the launches, and
+// orchestrates the select phase on the caller's stream.  No allocation, no
+// state, no synchronisation.
+#include "qsa.h"
+#include "qsa_internal.h"
+
+namespace {
+
+using qsa::ScoreGeom;
+using qsa::TopkGeom;
+
+bool aligned16(const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+bool aligned4(const void *p) { return reinterpret_cast<uintptr_t>(p) % 4 == 0; }
+
+// a*b + c without signed overflow; false when it would overflow int64.
+bool mad_ok(int64_t a, int64_t b, int64_t c, int64_t *out) {
+    int64_t m;
+    if (__builtin_mul_overflow(a, b, &m)) return false;
+    if (__builtin_add_overflow(m, c, out)) return false;
+    return true;
+}
+
+struct ScoreCheck {
+    int64_t nb = 0, nf = 0;
+};
+
+// Validation shared by qsa_block_scores and qsa_select_phase.
+qsa_status check_scores_args(const void *q16, int64_t qts, const uint16_t *kblk, int64_t khs,
+                             const float *scores, int64_t ld_s, int32_t G, int32_t nq, int32_t H,
+                             int32_t D, int64_t n_kv, int32_t bs, ScoreCheck *out) {
+    if (G < 0 || nq < 0 || n_kv < 0 || ld_s < 0 || qts < 0 || khs < 0) return QSA_ERR_ARG;
+    if (bs < 1) return QSA_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return QSA_ERR_UNSUPPORTED;
+    if (H < 1 || H > 16) return QSA_ERR_UNSUPPORTED;
+    const int64_t nb = n_kv / bs + (n_kv % bs != 0);
+    out->nb = nb;
+    out->nf = n_kv / bs;
+    if (G == 0 || nq == 0 || nb == 0) return QSA_OK;   // nothing to read or write
+    if (nb > 0x7fffffffLL) return QSA_ERR_UNSUPPORTED;
+    if (!q16 || !kblk || !scores) return QSA_ERR_ARG;
+    const int64_t row = static_cast<int64_t>(G) * H * D;
+    if (qts < row) return QSA_ERR_ARG;
+    int64_t tmp;
+    if (!mad_ok(nb, D, 0, &tmp) || khs < tmp) return QSA_ERR_ARG;
+    if (ld_s < nb) return QSA_ERR_ARG;
+    // extents of every buffer must be addressable
+    if (!mad_ok(static_cast<int64_t>(nq) - 1, qts, row, &tmp)) return QSA_ERR_ARG;
+    if (!mad_ok(static_cast<int64_t>(G) - 1, khs, nb * D, &tmp)) return QSA_ERR_ARG;
+    if (!mad_ok(static_cast<int64_t>(G) * nq - 1, ld_s, nb, &tmp)) return QSA_ERR_ARG;
+    if (!aligned16(q16) || qts % 8 != 0) return QSA_ERR_UNSUPPORTED;
+    if (!aligned16(kblk) || khs % 8 != 0) return QSA_ERR_UNSUPPORTED;
+    if (!aligned4(scores)) return QSA_ERR_UNSUPPORTED;
+    if (G > 65535) return QSA_ERR_UNSUPPORTED;
+    return QSA_OK;
+}
+
+qsa_status check_topk_args(const float *scores, int64_t ld_s, int64_t rows, int32_t nb, int32_t k,
+                           const int32_t *ids, int64_t ld_ids, const float *vals) {
+    if (rows < 0 || nb < 0 || k < 0 || ld_s < 0 || ld_ids < 0) return QSA_ERR_ARG;
+    if (k > QSA_MAX_K) return QSA_ERR_UNSUPPORTED;
+    if (rows == 0 || k == 0) return QSA_OK;
+    if (!ids || (nb > 0 && !scores)) return QSA_ERR_ARG;
+    if (ld_ids < k) return QSA_ERR_ARG;
+    if (nb > 0 && ld_s < nb) return QSA_ERR_ARG;
+    int64_t tmp;
+    if (!mad_ok(rows - 1, ld_ids, k, &tmp)) return QSA_ERR_ARG;
+    if (nb > 0 && !mad_ok(rows - 1, ld_s, nb, &tmp)) return QSA_ERR_ARG;
+    if (!aligned4(ids) || (vals && !aligned4(vals)) || (scores && !aligned4(scores)))
+        return QSA_ERR_UNSUPPORTED;
+    return QSA_OK;
+}
+
+qsa_status hip_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_HIP; }
+
+hipError_t run_scores(const uint16_t *q16, int64_t qts, const uint16_t *kblk, int64_t khs,
+                      float *scores, int64_t ld_s, int32_t G, int32_t nq, int32_t H, int32_t D,
+                      const ScoreCheck &c, hipStream_t s) {
+    ScoreGeom geo{q16, qts, kblk, khs, scores, ld_s, G, nq, H, D, c.nf};
+    hipError_t e = qsa::launch_score_full(geo, s);
+    if (e != hipSuccess) return e;
+    if (c.nb > c.nf) e = qsa::launch_tail(geo, c.nf, s);
+    return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qsa_abi_version(void) { return QSA_ABI_VERSION; }
+
+const char *qsa_status_string(qsa_status s) {
+    switch (s) {
+        case QSA_OK: return "ok";
+        case QSA_ERR_ARG: return "invalid argument (null pointer, negative size, stride or leading dimension too small)";
+        case QSA_ERR_UNSUPPORTED: return "unsupported geometry (D not in {64,128}, H not in [1,16], k > 64, block size < 1, or misaligned pointer/stride)";
+        case QSA_ERR_HIP: return "HIP runtime error at launch";
+    }
+    return "unknown status";
+}
+
+qsa_status qsa_convert_f32_f16(const float *src, uint16_t *dst, int64_t n, void *stream) {
+    if (n < 0) return QSA_ERR_ARG;
+    if (n == 0) return QSA_OK;
+    if (!src || !dst) return QSA_ERR_ARG;
+    if (!aligned4(src) || reinterpret_cast<uintptr_t>(dst) % 2 != 0) return QSA_ERR_UNSUPPORTED;
+    return hip_status(qsa::launch_convert(src, dst, n, static_cast<hipStream_t>(stream)));
+}
+
+qsa_status qsa_block_scores(const uint16_t *q16, int64_t q_tok_stride, const uint16_t *kblk,
+                            int64_t kblk_head_stride, float *scores, int64_t ld_s, int32_t G,
+                            int32_t nq, int32_t H, int32_t D, int64_t n_kv, int32_t bs,
+                            void *stream) {
+    ScoreCheck c;
+    qsa_status st = check_scores_args(q16, q_tok_stride, kblk, kblk_head_stride, scores, ld_s, G,
+                                      nq, H, D, n_kv, bs, &c);
+    if (st != QSA_OK || G == 0 || nq == 0 || c.nb == 0) return st;
+    return hip_status(run_scores(q16, q_tok_stride, kblk, kblk_head_stride, scores, ld_s, G, nq,
+                                 H, D, c, static_cast<hipStream_t>(stream)));
+}
+
+qsa_status qsa_select_topk(const float *scores, int64_t ld_s, int64_t rows, int32_t nb, int32_t k,
+                           int32_t *ids, int64_t ld_ids, float *vals, void *stream) {
+    qsa_status st = check_topk_args(scores, ld_s, rows, nb, k, ids, ld_ids, vals);
+    if (st != QSA_OK || rows == 0 || k == 0) return st;
+    TopkGeom geo{scores, ld_s, ids, ld_ids, vals, 1, rows, rows, rows, 0, nb, k};
+    return hip_status(qsa::launch_topk(geo, static_cast<hipStream_t>(stream)));
+}
+
+qsa_status qsa_select_phase(const float *q32, uint16_t *q16, int64_t q_tok_stride,
+                            const uint16_t *kblk, int64_t kblk_head_stride, float *scores_ws,
+                            int64_t ld_s, int32_t *ids, int64_t ld_ids, float *vals, int32_t G,
+                            int32_t nq, int32_t H, int32_t D, int64_t n_kv, int32_t bs, int32_t k,
+                            int64_t q_chunk, void *stream) {
+    if (q_chunk < 0) return QSA_ERR_ARG;
+    const int64_t qc = (q_chunk > 0 && q_chunk < nq) ? q_chunk : nq;
+    ScoreCheck c;
+    // scores are validated for the chunk-sized workspace
+    qsa_status st = check_scores_args(q16, q_tok_stride, kblk, kblk_head_stride, scores_ws, ld_s,
+                                      G, static_cast<int32_t>(qc), H, D, n_kv, bs, &c);
+    if (st != QSA_OK) return st;
+    if (G == 0 || nq == 0) return QSA_OK;
+    // the whole query tensor (not only one chunk of it) must be addressable
+    int64_t qext = 0;
+    if (!mad_ok(static_cast<int64_t>(nq) - 1, q_tok_stride, static_cast<int64_t>(G) * H * D,
+                &qext))
+        return QSA_ERR_ARG;
+    const int64_t rows = static_cast<int64_t>(G) * nq;
+    st = check_topk_args(scores_ws, ld_s, rows, static_cast<int32_t>(c.nb), k, ids, ld_ids, vals);
+    if (st != QSA_OK) return st;
+    if (q32) {
+        if (!q16) return QSA_ERR_ARG;
+        if (!aligned4(q32) || reinterpret_cast<uintptr_t>(q16) % 2 != 0)
+            return QSA_ERR_UNSUPPORTED;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    if (q32) {
+        hipError_t e = qsa::launch_convert(q32, q16, qext, s);
+        if (e != hipSuccess) return QSA_ERR_HIP;
+    }
+    for (int64_t t0 = 0; t0 < nq; t0 += qc) {
+        const int32_t n = static_cast<int32_t>((nq - t0 < qc) ? nq - t0 : qc);
+        if (c.nb > 0) {
+            hipError_t e = run_scores(q16 + t0 * q_tok_stride, q_tok_stride, kblk,
+                                      kblk_head_stride, scores_ws, ld_s, G, n, H, D, c, s);
+            if (e != hipSuccess) return QSA_ERR_HIP;
+        }
+        if (k > 0) {
+            // the scorer wrote this chunk's rows at g*n + t' (n = rows in the chunk)
+            TopkGeom geo{scores_ws, ld_s, ids, ld_ids, vals, G, n, n, nq, t0,
+                         static_cast<int32_t>(c.nb), k};
+            hipError_t e = qsa::launch_topk(geo, s);
+            if (e != hipSuccess) return QSA_ERR_HIP;
+        }
+    }
+    return QSA_OK;
+}
+
+}  // extern "C"

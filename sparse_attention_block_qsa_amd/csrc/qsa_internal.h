@@ -1,0 +1,52 @@
+// qsa_internal.h -- launchers shared between the C-ABI layer and the kernel
+// files of libqsa.so (gfx950 / CDNA4 only).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+// Blocks per MFMA scorer tile: the N extent of v_mfma_f32_32x32x16_f16.
+constexpr int kTileBlocks = 32;
+// Queries per wave (M = 32 rows = 16 queries x 2 heads) and waves per group.
+constexpr int kWaveQueries = 16;
+constexpr int kScoreWaves = 4;
+constexpr int kGroupQueries = kWaveQueries * kScoreWaves;
+
+struct ScoreGeom {
+    const uint16_t *q16;
+    int64_t qts;          // elements between tokens
+    const uint16_t *kblk;
+    int64_t khs;          // elements between KV heads
+    float *scores;
+    int64_t ld_s;
+    int32_t G, nq, H, D;
+    int64_t nf;           // full blocks
+};
+
+// Full-block MFMA scorer over blocks [0, nf).  Launches one kernel per head
+// pass (one pass unless H*D > kMaxHeadElems).
+hipError_t launch_score_full(const ScoreGeom &g, hipStream_t s);
+
+// Fixed-order scorer of the single block b_tail.
+hipError_t launch_tail(const ScoreGeom &g, int64_t b_tail, hipStream_t s);
+
+struct TopkGeom {
+    const float *scores;
+    int64_t ld_s;
+    int32_t *ids;
+    int64_t ld_ids;
+    float *vals;
+    // row (grp, t), t < rows_per_group:
+    //   source row      grp * src_group_rows + t
+    //   destination row grp * dst_group_rows + dst_row0 + t
+    int64_t n_groups, rows_per_group, src_group_rows, dst_group_rows, dst_row0;
+    int32_t nb, k;
+};
+
+hipError_t launch_topk(const TopkGeom &g, hipStream_t s);
+
+hipError_t launch_convert(const float *src, uint16_t *dst, int64_t n, hipStream_t s);
+
+}  // namespace qsa

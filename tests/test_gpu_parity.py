@@ -1,0 +1,359 @@
+"""GPU parity of the HIP path against the float64 oracle, through the C ABI.
+
+Bars (contract of Strata pull request #228, part 1, and pull request #856):
+  * every score within B = 2^-9.5*S + 8*2^-24*|score_ref| of the oracle;
+    +2.5*B perturbations of the same scores must fail the same check;
+  * the tail block bit for bit equal to the oracle's fixed-order fp32 model;
+  * ids bit for bit equal to the oracle's top-k of the device's own scores,
+    and equal to the oracle's selection except near-ties within 2*B;
+  * zero tolerance on the coordinate-coded and integer fixtures;
+  * exact write sets (canaries), bitwise determinism across launches,
+    exactly 64x scores for x8 inputs.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import qsa_inputs as qi
+from gpu_util import (SENTINEL, dev, guarded, k_dev, log, q_dev, run_block_scores,
+                      scores_mask)
+
+pytestmark = pytest.mark.gpu
+
+import sparse_attention_block_qsa_amd as qsa  # noqa: E402  (fails loudly if not built)
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def check_bound(s_gpu, ref, name, exact=False):
+    res = oracle.check_scores(s_gpu, ref)
+    log(f"  [{name}] {res}")
+    assert res.ok, f"{name}: {res}"
+    if exact:
+        assert np.array_equal(s_gpu, ref.score), f"{name}: not exact"
+    f1, f2 = oracle.negative_controls(ref, s_gpu)
+    assert f1 and f2, f"{name}: negative control passed the checker"
+    return res
+
+
+def check_ids(ids_gpu, s_gpu, ref, k, name):
+    want = oracle.topk(s_gpu, k)[0]
+    assert np.array_equal(ids_gpu, want), f"{name}: ids differ from the top-k of the device scores"
+    sel = oracle.check_selection(ids_gpu, ref, k)
+    log(f"  [{name}] selection: rows differing {sel.rows_differing}, ids differing "
+        f"{sel.ids_differing}/{sel.n_ids}, worst gap/2B {sel.worst_gap_ratio:.3f}")
+    assert sel.ok, f"{name}: {sel.detail}"
+
+
+def run_topk_dev(s_rows: np.ndarray, nb: int, k: int, ld_pad: int = 5, want_vals=True):
+    rows = s_rows.shape[0]
+    ld = max(nb, 1) + ld_pad
+    src = torch.full((rows, ld), float("nan"), dtype=torch.float32, device=dev())
+    if nb:
+        src[:, :nb] = torch.from_numpy(np.ascontiguousarray(s_rows, dtype=np.float32)).to(dev())
+    ids = guarded((rows, k + 2), torch.int32)
+    vals = guarded((rows, k + 2), torch.float32) if want_vals else None
+    qsa.select_topk(src, nb, k, ids=ids.view, vals=vals.view if vals else None)
+    torch.cuda.synchronize()
+    m = np.zeros((rows, k + 2), dtype=bool)
+    m[:, :k] = True
+    assert ids.outside_intact(m) and ids.written_all(m), "select_topk ids write set"
+    if vals:
+        assert vals.outside_intact(m) and vals.written_all(m), "select_topk vals write set"
+    out_ids = ids.view[:, :k].cpu().numpy()
+    out_vals = vals.view[:, :k].cpu().numpy() if vals else None
+    return out_ids, out_vals
+
+
+# ---------------------------------------------------------------------------
+# conversion
+# ---------------------------------------------------------------------------
+
+def test_convert_all_fp32_patterns():
+    """The conversion kernel equals the oracle's round-to-nearest-even on
+    every one of the 2^32 fp32 bit patterns (NaN payload rule included)."""
+    chunk = 1 << 26
+    n_bad = 0
+    for c in range((1 << 32) // chunk):
+        start = c * chunk
+        pat = (torch.arange(start, start + chunk, dtype=torch.int64, device=dev())
+               & 0xFFFFFFFF).to(torch.int32).view(torch.float32)
+        out = qsa.convert_f32_f16(pat)
+        got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+        want = oracle.convert_f32_f16(qi.fp32_bit_patterns(start, chunk))
+        bad = np.flatnonzero(got != want)
+        n_bad += bad.size
+        if bad.size:
+            i = int(bad[0])
+            log(f"  chunk {c}: {bad.size} mismatches, first {start + i:#010x}: "
+                f"got {got[i]:#06x} want {want[i]:#06x}")
+        if c % 16 == 15:
+            log(f"  convert: {c + 1} / 64 chunks checked")
+    assert n_bad == 0
+
+
+@pytest.mark.parametrize("n,off_src,off_dst", [(1, 0, 0), (7, 0, 0), (8, 0, 0), (4099, 0, 0),
+                                               (1000, 1, 0), (1000, 0, 1), (1000, 3, 5)])
+def test_convert_lengths_and_alignment(n, off_src, off_dst):
+    x = qi.normal(77, 1, n + off_src).astype(np.float32) * 1000
+    src = torch.from_numpy(x).to(dev())[off_src:off_src + n]
+    buf = torch.full((n + off_dst + 8,), 0x5A5A, dtype=torch.int16, device=dev())
+    dst = buf[off_dst:off_dst + n]
+    st = qsa.lib.qsa_convert_f32_f16(qsa._ptr(src), qsa._ptr(dst), n, qsa._stream(None))
+    assert st == 0
+    torch.cuda.synchronize()
+    got = dst.cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, oracle.convert_f32_f16(x[off_src:off_src + n]))
+    rest = buf.cpu().numpy()
+    assert np.all(rest[:off_dst] == 0x5A5A) and np.all(rest[off_dst + n:] == 0x5A5A)
+
+
+# ---------------------------------------------------------------------------
+# scores on the configs
+# ---------------------------------------------------------------------------
+
+SMALL = ["tiny_nq37_nkv1000", "nq256_nkv4096", "nq256_nkv32768", "nq256_nkv131072"]
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_config_scores_ids_and_write_set(name):
+    cfg = qi.CONFIGS[name]
+    log(f"config {name}")
+    w = qi.make(cfg)
+    s_gpu, intact, written = run_block_scores(w.q16, w.kblk, cfg.n_kv, cfg.bs)
+    assert intact, "scores: write outside [r][0, nb)"
+    assert written, "scores: a cell of [r][0, nb) was not written"
+    ref = oracle.scores(w.q16, w.kblk, cfg.nb)
+    check_bound(s_gpu, ref, name)
+    if cfg.nb > cfg.nf:   # tail block: bit for bit the fixed-order model
+        model = oracle.block_model_f32(w.q16, w.kblk, cfg.nf)
+        assert np.array_equal(s_gpu[:, cfg.nf].astype(np.float32).view(np.uint32),
+                              model.view(np.uint32)), "tail block differs from the model"
+    ids, vals = run_topk_dev(s_gpu, cfg.nb, cfg.k)
+    check_ids(ids, s_gpu, ref, cfg.k, name)
+    sel = ids >= 0
+    assert np.array_equal(vals[sel], s_gpu[np.nonzero(sel)[0], ids[sel]].astype(np.float32))
+    # determinism: a second launch is bitwise identical
+    s2, _, _ = run_block_scores(w.q16, w.kblk, cfg.n_kv, cfg.bs)
+    assert np.array_equal(s_gpu.view(np.uint64), s2.view(np.uint64)), "not deterministic"
+
+
+def test_tiny_nkv0_writes_nothing_and_selects_nothing():
+    cfg = qi.TINY
+    w = qi.make(cfg)
+    out = guarded((cfg.G, cfg.nq, 8), torch.float32)
+    qsa.block_scores(q_dev(w.q16), k_dev(w.kblk), 0, cfg.bs, out=out.view)
+    torch.cuda.synchronize()
+    assert out.outside_intact(np.zeros((cfg.G, cfg.nq, 8), dtype=bool))
+    ws = qsa.PhaseWorkspace(cfg.nq, cfg.G, cfg.H, cfg.D, 0, cfg.bs, cfg.k, dev(), with_vals=True)
+    ws.ids.fill_(123)
+    ids, vals = qsa.select_phase(torch.from_numpy(w.q32).to(dev()), k_dev(w.kblk), 0, cfg.bs,
+                                 cfg.k, ws)
+    torch.cuda.synchronize()
+    assert torch.all(ids == -1) and torch.all(vals == -float("inf"))
+
+
+def test_coded_fixture_exact():
+    cfg = qi.CONFIGS["nq256_nkv32768"]
+    w = qi.coded_fixture(cfg)
+    s_gpu, intact, written = run_block_scores(w.q16, w.kblk, cfg.n_kv, cfg.bs)
+    assert intact and written
+    ref = oracle.scores(w.q16, w.kblk, cfg.nb)
+    check_bound(s_gpu, ref, "coded", exact=True)
+    ids, _ = run_topk_dev(s_gpu, cfg.nb, cfg.k)
+    assert np.array_equal(ids, oracle.topk(ref.score, cfg.k)[0]), "coded: ids not exact"
+
+
+@pytest.mark.parametrize("n_kv", [4096, 4096 + 37])
+def test_integer_fixture_exact(n_kv):
+    cfg = qi.CONFIGS["nq256_nkv4096"]
+    cfg = qi.Config("int", cfg.G, cfg.nq, cfg.H, cfg.D, n_kv, cfg.bs, cfg.k, "normal", 0)
+    w = qi.integer_fixture(cfg)
+    s_gpu, intact, written = run_block_scores(w.q16, w.kblk, cfg.n_kv, cfg.bs)
+    assert intact and written
+    ref = oracle.scores(w.q16, w.kblk, cfg.nb)
+    check_bound(s_gpu, ref, f"integer n_kv={n_kv}", exact=True)
+    ids, _ = run_topk_dev(s_gpu, cfg.nb, cfg.k)
+    assert np.array_equal(ids, oracle.topk(ref.score, cfg.k)[0])
+
+
+def test_x8_headroom_exactly_64x():
+    cfg = qi.HEADLINE
+    w = qi.make(cfg)
+    w8 = qi.scaled_by_8(w)
+    s1, _, _ = run_block_scores(w.q16, w.kblk, cfg.n_kv, cfg.bs)
+    s8, intact, written = run_block_scores(w8.q16, w8.kblk, cfg.n_kv, cfg.bs)
+    assert intact and written
+    ref8 = oracle.scores(w8.q16, w8.kblk, cfg.nb)
+    check_bound(s8, ref8, "x8")
+    assert np.array_equal(s8, s1 * 64.0), "x8 inputs did not give exactly 64x scores"
+    ids, _ = run_topk_dev(s8, cfg.nb, cfg.k)
+    check_ids(ids, s8, ref8, cfg.k, "x8")
+
+
+def test_stress60_within_bound():
+    cfg = qi.CONFIGS["nq256_nkv4096"]
+    cfg = qi.Config("stress60", 1, 64, 8, 128, 4096 + 19, 64, 16, "normal", 0)
+    w = qi.stress60_fixture(cfg)
+    s_gpu, intact, written = run_block_scores(w.q16, w.kblk, cfg.n_kv, cfg.bs)
+    assert intact and written
+    ref = oracle.scores(w.q16, w.kblk, cfg.nb)
+    check_bound(s_gpu, ref, "stress60")
+    model = oracle.block_model_f32(w.q16, w.kblk, cfg.nf)
+    assert np.array_equal(s_gpu[:, cfg.nf].astype(np.float32).view(np.uint32),
+                          model.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# ragged geometry, strides, head passes
+# ---------------------------------------------------------------------------
+
+GEOMS = [
+    # G, nq, H, D, n_kv, bs, tok_pad, nb_pad
+    (1, 1, 1, 64, 64, 64, 0, 0),
+    (1, 15, 2, 64, 31 * 64, 64, 8, 1),
+    (2, 17, 3, 128, 33 * 64 + 1, 64, 0, 2),
+    (3, 65, 5, 64, 95 * 16 + 15, 16, 24, 0),
+    (1, 100, 8, 128, 7, 64, 0, 0),           # only a tail block
+    (2, 63, 9, 128, 40 * 32, 32, 8, 3),      # two head passes
+    (1, 70, 12, 64, 65 * 64 + 63, 64, 0, 0),
+    (1, 33, 16, 64, 20 * 64 + 9, 64, 16, 0), # D=64, two head passes
+    (1, 50, 16, 128, 18 * 64, 64, 0, 1),     # D=128, two full passes
+    (2, 129, 4, 128, 100 * 64 + 3, 64, 0, 0),
+]
+
+
+@pytest.mark.parametrize("geo", GEOMS, ids=lambda g: "G{}_nq{}_H{}_D{}_nkv{}_bs{}".format(*g[:6]))
+def test_ragged_geometry(geo):
+    G, nq, H, D, n_kv, bs, tok_pad, nb_pad = geo
+    cfg = qi.Config("geo", G, nq, H, D, n_kv, bs, min(64, 8), "normal", 500 + nq)
+    w = qi.make(cfg)
+    s_gpu, intact, written = run_block_scores(w.q16, w.kblk, n_kv, bs, tok_pad=tok_pad,
+                                              nb_pad=nb_pad)
+    assert intact, "write outside the documented set"
+    assert written, "a cell was not written"
+    ref = oracle.scores(w.q16, w.kblk, cfg.nb)
+    check_bound(s_gpu, ref, "geo")
+    if cfg.nb > cfg.nf:
+        model = oracle.block_model_f32(w.q16, w.kblk, cfg.nf)
+        assert np.array_equal(s_gpu[:, cfg.nf].astype(np.float32).view(np.uint32),
+                              model.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# top-k selector on identical inputs (bit exact)
+# ---------------------------------------------------------------------------
+
+def topk_cases():
+    rng = np.random.default_rng(42)
+    cases = []
+    for nb in (1, 5, 63, 64, 65, 200, 2049, 4096, 5000):
+        cases.append(("random", rng.standard_normal((13, nb)).astype(np.float32), nb))
+    nb = 300
+    cases.append(("all_equal", np.full((4, nb), 0.5, np.float32), nb))
+    cases.append(("all_zero", np.zeros((4, nb), np.float32), nb))
+    z = rng.integers(0, 2, (6, nb)).astype(np.float32) * 0.0
+    z[rng.random((6, nb)) < 0.5] = -0.0
+    cases.append(("signed_zeros", z, nb))
+    d = rng.integers(-3, 3, (6, nb)).astype(np.float32)
+    cases.append(("duplicates", d, nb))
+    s = rng.standard_normal((6, nb)).astype(np.float32)
+    s[rng.random((6, nb)) < 0.1] = np.nan
+    s[rng.random((6, nb)) < 0.05] = np.inf
+    s[rng.random((6, nb)) < 0.05] = -np.inf
+    s[0, :] = np.nan
+    cases.append(("nan_inf", s, nb))
+    t = rng.standard_normal((4, 2049)).astype(np.float32)
+    t[:, ::3] = 1.25
+    cases.append(("many_ties_2049", t, 2049))
+    return cases
+
+
+@pytest.mark.parametrize("case", topk_cases(), ids=lambda c: f"{c[0]}_nb{c[2]}")
+@pytest.mark.parametrize("k", [1, 7, 64])
+def test_topk_bit_exact(case, k):
+    _, s, nb = case
+    ids, vals = run_topk_dev(s, nb, k)
+    want_ids, want_vals = oracle.topk(s.astype(np.float64), k)
+    assert np.array_equal(ids, want_ids)
+    sel = ids >= 0
+    got_bits = vals[sel].view(np.uint32)
+    want_bits = s[np.nonzero(sel)[0], ids[sel]].view(np.uint32)
+    assert np.array_equal(got_bits, want_bits)
+    assert np.all(vals[~sel] == -np.inf)
+
+
+def test_topk_k_larger_than_nb_and_empty_rows():
+    s = np.arange(10, dtype=np.float32)[None, :].repeat(3, 0)
+    ids, vals = run_topk_dev(s, 10, 16)
+    assert np.array_equal(ids[:, :10], np.tile(np.arange(9, -1, -1), (3, 1)))
+    assert np.all(ids[:, 10:] == -1) and np.all(vals[:, 10:] == -np.inf)
+    ids0, vals0 = run_topk_dev(np.zeros((3, 0), np.float32), 0, 5)
+    assert np.all(ids0 == -1) and np.all(vals0 == -np.inf)
+
+
+# ---------------------------------------------------------------------------
+# the whole phase
+# ---------------------------------------------------------------------------
+
+def test_phase_with_fp32_queries_not_fp16_exact():
+    """Conversion fixture: fp32 queries off the fp16 grid.  The oracle uses
+    the unrounded fp32 values (the contract's first term covers operand
+    rounding); the converted operand equals the oracle's conversion bit for
+    bit, and the tail follows the fixed-order model on that operand."""
+    base = qi.CONFIGS["nq256_nkv4096"]
+    cfg = qi.Config("conv", 2, 96, base.H, base.D, 4096 + 21, 64, 16, "normal", 1012)
+    w = qi.conversion_fixture(cfg)
+    q32 = torch.from_numpy(w.q32).to(dev())
+    kd = k_dev(w.kblk)
+    ws = qsa.PhaseWorkspace(cfg.nq, cfg.G, cfg.H, cfg.D, cfg.n_kv, cfg.bs, cfg.k, dev())
+    ids = qsa.select_phase(q32, kd, cfg.n_kv, cfg.bs, cfg.k, ws)
+    torch.cuda.synchronize()
+    q16_gpu = ws.q16.cpu().numpy().view(np.uint16)
+    assert np.array_equal(q16_gpu, oracle.convert_f32_f16(w.q32))
+    s_gpu = ws.scores[:, :, :cfg.nb].reshape(cfg.rows, cfg.nb).cpu().numpy().astype(np.float64)
+    ref = oracle.scores(w.q32, w.kblk, cfg.nb)
+    check_bound(s_gpu, ref, "conversion")
+    model = oracle.block_model_f32(q16_gpu, w.kblk, cfg.nf)
+    assert np.array_equal(s_gpu[:, cfg.nf].astype(np.float32).view(np.uint32),
+                          model.view(np.uint32))
+    check_ids(ids.reshape(cfg.rows, cfg.k).cpu().numpy(), s_gpu, ref, cfg.k, "conversion")
+
+
+@pytest.mark.parametrize("q_chunk", [0, 37, 64, 1000])
+def test_phase_chunked_equals_whole(q_chunk):
+    cfg = qi.Config("chunk", 3, 150, 8, 128, 70 * 64 + 5, 64, 32, "normal", 77)
+    w = qi.make(cfg)
+    q32 = torch.from_numpy(w.q32).to(dev())
+    kd = k_dev(w.kblk)
+    ws0 = qsa.PhaseWorkspace(cfg.nq, cfg.G, cfg.H, cfg.D, cfg.n_kv, cfg.bs, cfg.k, dev(),
+                             with_vals=True)
+    ids0, vals0 = qsa.select_phase(q32, kd, cfg.n_kv, cfg.bs, cfg.k, ws0)
+    wsc = qsa.PhaseWorkspace(cfg.nq, cfg.G, cfg.H, cfg.D, cfg.n_kv, cfg.bs, cfg.k, dev(),
+                             q_chunk=q_chunk, with_vals=True)
+    idsc, valsc = qsa.select_phase(q32, kd, cfg.n_kv, cfg.bs, cfg.k, wsc)
+    torch.cuda.synchronize()
+    assert torch.equal(ids0, idsc) and torch.equal(vals0.view(torch.int32), valsc.view(torch.int32))
+    s0 = ws0.scores[:, :, :cfg.nb].reshape(cfg.rows, cfg.nb).cpu().numpy().astype(np.float64)
+    ref = oracle.scores(w.q16, w.kblk, cfg.nb)
+    check_bound(s0, ref, f"phase chunk={q_chunk}")
+    check_ids(ids0.reshape(cfg.rows, cfg.k).cpu().numpy(), s0, ref, cfg.k, "phase")
+
+
+def test_phase_ids_write_set():
+    cfg = qi.TINY
+    w = qi.make(cfg)
+    ids = guarded((cfg.G, cfg.nq, cfg.k), torch.int32)
+    ws = qsa.PhaseWorkspace(cfg.nq, cfg.G, cfg.H, cfg.D, cfg.n_kv, cfg.bs, cfg.k, dev())
+    ws.ids = ids.view
+    qsa.select_phase(torch.from_numpy(w.q32).to(dev()), k_dev(w.kblk), cfg.n_kv, cfg.bs, cfg.k, ws)
+    torch.cuda.synchronize()
+    m = np.ones((cfg.G, cfg.nq, cfg.k), dtype=bool)
+    assert ids.outside_intact(m) and ids.written_all(m)

@@ -1,0 +1,129 @@
+"""Full-size parity of the select phase on the full-prefill chunk (4 KV heads
+x 16384 queries, H = 8, D = 128, n_kv = 131077: 2048 full blocks + a 5-token
+tail, k = 64), in the launch configuration the benchmark times.
+
+The oracle cannot score all 134 M cells in test time, so:
+  * sampled rows (first, last, tile and group edges, random) are scored in
+    full by the oracle: every cell within B, ids exact against the oracle's
+    top-k of the device scores and within the near-tie rule of the oracle's;
+  * the tail column of EVERY row is compared bit for bit with the oracle's
+    fixed-order model;
+  * for EVERY row the ids are checked on the device scores for the
+    properties that define the selection: strictly ordered by (score desc,
+    id asc), nothing outside the selection beats its last element, and ties
+    at the threshold are the lowest ids;
+  * the phase is run twice and must be bitwise identical.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import qsa_inputs as qi
+from gpu_util import dev, log
+
+pytestmark = pytest.mark.gpu
+
+import sparse_attention_block_qsa_amd as qsa  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def prefill():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cfg = qi.PREFILL
+    log("prefill: generating inputs")
+    w = qi.make(cfg)
+    q32 = torch.from_numpy(w.q32).to(dev())
+    kb = torch.from_numpy(w.kblk.view(np.float16)).to(dev())
+    ws = qsa.PhaseWorkspace(cfg.nq, cfg.G, cfg.H, cfg.D, cfg.n_kv, cfg.bs, cfg.k, dev(),
+                            with_vals=True, ld_pad=3)
+    pad = torch.full((cfg.G, cfg.nq, 3), float("nan"), device=dev())
+    ws.scores[:, :, cfg.nb:] = pad
+    log("prefill: running the phase")
+    qsa.select_phase(q32, kb, cfg.n_kv, cfg.bs, cfg.k, ws)
+    torch.cuda.synchronize()
+    return cfg, w, q32, kb, ws
+
+
+def sampled_rows(cfg, n_random=40, seed=3):
+    rng = np.random.default_rng(seed)
+    ts = {0, 1, 15, 16, 63, 64, 65, cfg.nq - 1, cfg.nq - 2, cfg.nq // 2}
+    rows = set()
+    for g in range(cfg.G):
+        rows.update(g * cfg.nq + t for t in ts)
+    rows.update(int(r) for r in rng.integers(0, cfg.rows, n_random))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def test_prefill_converted_queries_exact(prefill):
+    cfg, w, q32, kb, ws = prefill
+    assert np.array_equal(ws.q16.cpu().numpy().view(np.uint16), w.q16)
+
+
+def test_prefill_sampled_rows_within_bound(prefill):
+    cfg, w, q32, kb, ws = prefill
+    rows = sampled_rows(cfg)
+    log(f"prefill: oracle on {rows.size} sampled rows x {cfg.nb} blocks")
+    ref = oracle.scores(w.q16, w.kblk, cfg.nb, rows=rows)
+    s_all = ws.scores.reshape(cfg.rows, -1)
+    s_gpu = s_all[torch.from_numpy(rows).to(dev())][:, :cfg.nb].cpu().numpy().astype(np.float64)
+    res = oracle.check_scores(s_gpu, ref)
+    log(f"prefill: {res}")
+    assert res.ok, str(res)
+    f1, f2 = oracle.negative_controls(ref, s_gpu)
+    assert f1 and f2
+    ids = ws.ids.reshape(cfg.rows, cfg.k)[torch.from_numpy(rows).to(dev())].cpu().numpy()
+    assert np.array_equal(ids, oracle.topk(s_gpu, cfg.k)[0])
+    sel = oracle.check_selection(ids, ref, cfg.k)
+    log(f"prefill: selection rows differing {sel.rows_differing}, ids differing "
+        f"{sel.ids_differing}/{sel.n_ids}")
+    assert sel.ok, sel.detail
+
+
+def test_prefill_tail_bitwise_all_rows(prefill):
+    cfg, w, q32, kb, ws = prefill
+    model = oracle.block_model_f32(w.q16, w.kblk, cfg.nf)
+    got = ws.scores[:, :, cfg.nf].reshape(-1).cpu().numpy()
+    bad = np.flatnonzero(got.view(np.uint32) != model.view(np.uint32))
+    assert bad.size == 0, f"{bad.size} tail cells differ, first row {bad[:1]}"
+
+
+def test_prefill_pad_columns_untouched(prefill):
+    cfg, w, q32, kb, ws = prefill
+    pad = ws.scores[:, :, cfg.nb:].view(torch.int32)
+    assert torch.all(pad == torch.tensor(float("nan")).view(torch.int32).item())
+
+
+def test_prefill_selection_properties_all_rows(prefill):
+    cfg, w, q32, kb, ws = prefill
+    k, nb = cfg.k, cfg.nb
+    S = ws.scores.reshape(cfg.rows, -1)[:, :nb]
+    ids = ws.ids.reshape(cfg.rows, k).long()
+    vals = ws.vals.reshape(cfg.rows, k)
+    assert torch.all((ids >= 0) & (ids < nb))
+    picked = torch.gather(S, 1, ids)
+    assert torch.equal(picked.view(torch.int32), vals.view(torch.int32))
+    # ordered by (score desc, id asc)
+    a, b = picked[:, :-1], picked[:, 1:]
+    ia, ib = ids[:, :-1], ids[:, 1:]
+    assert torch.all((a > b) | ((a == b) & (ia < ib)))
+    # nothing outside the selection beats the last selected element
+    kth = picked[:, -1:]
+    kth_id = ids[:, -1:]
+    mask = torch.zeros_like(S, dtype=torch.bool).scatter_(1, ids, True)
+    col = torch.arange(nb, device=S.device)[None, :]
+    beats = (S > kth) | ((S == kth) & (col < kth_id))
+    assert not torch.any(beats & ~mask)
+
+
+def test_prefill_phase_is_deterministic(prefill):
+    cfg, w, q32, kb, ws = prefill
+    s1 = ws.scores.clone()
+    i1 = ws.ids.clone()
+    qsa.select_phase(q32, kb, cfg.n_kv, cfg.bs, cfg.k, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(s1.view(torch.int32), ws.scores.view(torch.int32))
+    assert torch.equal(i1, ws.ids)
