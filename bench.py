@@ -1,0 +1,312 @@
+"""Benchmark of the QSA block-score select phase on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one pass of the whole phase over the workload's synthetic batch:
+fp32 -> fp16 conversion of the queries, the MFMA full-block scorer (+ the
+tail-block kernel when n_kv is not a multiple of the block size), and the
+per-row top-k selector, each a C-ABI call of libqsa.so on one stream.  The
+K timed steps are captured in one HIP graph (the phase at nq = 256 is a few
+microseconds of GPU work, far below Python's per-call cost) and replayed once
+between two events, bracketed by device synchronisation; inputs are resident
+in HBM before the timed region starts.
+
+Per-kernel durations come from graphs of K back-to-back launches of one
+stage, timed with events on the same stream; the scorer's roofline uses that
+duration.  The CPU baseline times the float64 oracle (never tuned) on the
+host cores on the same workload.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "QSA select ms + scorer TFLOP/s (fraction of FP16 MFMA peak), nq=256 @128K"
+PEAK_FP16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense fp16 FLOP/clk/CU (published 2.5 PF)
+PEAK_HBM_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="nq256_nkv131072")
+    p.add_argument("--prefill-steps", type=int, default=20,
+                   help="steps for the full-prefill chunk reported beside the workload (0: skip)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="target wall time of the CPU-baseline sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 256 MiB device copy (for counter calibration)")
+    return p.parse_args()
+
+
+def source_digest() -> str:
+    """sha256 over the kernel sources, to tie stored counter figures to code."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_attention_block_qsa_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str):
+    """Per-launch HBM bytes from committed rocprofv3 counter summaries, valid
+    only while the kernel sources are those the counters were taken on."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        line = line.split("#", 1)[0].strip()
+        if "=" in line:
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_digest") != source_digest():
+        return None
+    try:
+        return float(kv["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Phase:
+    """Device buffers and raw C-ABI calls of one workload (no Python checks
+    inside the hot loop: arguments are validated once by a checked call)."""
+
+    def __init__(self, cfg, qsa, torch, w):
+        import numpy as np
+        self.cfg, self.qsa, self.torch = cfg, qsa, torch
+        dev = torch.device("cuda:0")
+        self.q32 = torch.from_numpy(w.q32).to(dev)
+        self.kb = torch.from_numpy(w.kblk.view(np.float16)).to(dev)
+        self.ws = qsa.PhaseWorkspace(cfg.nq, cfg.G, cfg.H, cfg.D, cfg.n_kv, cfg.bs, cfg.k, dev)
+        self.n_q = self.q32.numel()
+        L = qsa.lib
+        P = qsa._ptr
+        c = cfg
+        ws = self.ws
+        qts = c.G * c.H * c.D
+        # checked once through the binding
+        qsa.select_phase(self.q32, self.kb, c.n_kv, c.bs, c.k, ws)
+        torch.cuda.synchronize()
+        self._conv = (L.qsa_convert_f32_f16, (P(self.q32), P(ws.q16), self.n_q))
+        self._score = (L.qsa_block_scores, (P(ws.q16), qts, P(self.kb), self.kb.stride(0),
+                                            P(ws.scores), ws.ld_s, c.G, c.nq, c.H, c.D,
+                                            c.n_kv, c.bs))
+        self._topk = (L.qsa_select_topk, (P(ws.scores), ws.ld_s, c.rows, c.nb, c.k, P(ws.ids),
+                                          c.k, None))
+        self._phase = (L.qsa_select_phase, (P(self.q32), P(ws.q16), qts, P(self.kb),
+                                            self.kb.stride(0), P(ws.scores), ws.ld_s, P(ws.ids),
+                                            c.k, None, c.G, c.nq, c.H, c.D, c.n_kv, c.bs, c.k, 0))
+
+    def _call(self, fa):
+        fn, args = fa
+        st = fn(*args, self.qsa._stream(None))
+        if st != 0:
+            raise RuntimeError(f"{fn.__name__}: {self.qsa.status_string(st)}")
+
+    def convert(self):
+        self._call(self._conv)
+
+    def score(self):
+        self._call(self._score)
+
+    def topk(self):
+        self._call(self._topk)
+
+    def step(self):
+        self._call(self._phase)
+
+
+def graph_of(torch, fn, n):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            fn()
+    return g
+
+
+def time_graph(torch, g, n) -> float:
+    """ms per step of one replay of a graph holding n steps."""
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def measure(cfg, qsa, torch, steps, warmup, w=None):
+    import qsa_inputs as qi
+    if w is None:
+        w = qi.make(cfg)
+    ph = Phase(cfg, qsa, torch, w)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(warmup):
+            ph.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager_ids = ph.ws.ids.clone()
+    eager_scores = ph.ws.scores.clone()
+
+    g_phase = graph_of(torch, ph.step, steps)
+    # ---- timed region: exactly `steps` phase steps ----
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms_step = time_graph(torch, g_phase, steps)
+    wall = time.perf_counter() - t0
+    # the replayed graph must reproduce the eager result bit for bit
+    same = bool(torch.equal(eager_ids, ph.ws.ids) and
+                torch.equal(eager_scores.view(torch.int32), ph.ws.scores.view(torch.int32)))
+    del g_phase
+
+    stages = {}
+    for name, fn in (("convert", ph.convert), ("scorer", ph.score), ("topk", ph.topk)):
+        g = graph_of(torch, fn, steps)
+        stages[name] = time_graph(torch, g, steps)
+        del g
+    flop = cfg.flop
+    return {
+        "ms_per_step": ms_step,
+        "wall_s": wall,
+        "graph_replay_matches_eager": same,
+        "stages_ms": stages,
+        "scorer_tflops": flop / (stages["scorer"] * 1e-3) / 1e12,
+        "phase_tflops": flop / (ms_step * 1e-3) / 1e12,
+        "flop": flop,
+    }
+
+
+def cpu_baseline(cfg, target_s):
+    """The float64 oracle (scores + S + B, then top-k), as it stands, on the
+    host cores: whole workload, repeated until about target_s of wall time."""
+    import oracle
+    import qsa_inputs as qi
+    w = qi.make(cfg)
+    reps, tot = 0, 0.0
+    while True:
+        t0 = time.perf_counter()
+        ref = oracle.scores(w.q16, w.kblk, cfg.nb)
+        oracle.topk(ref.score, cfg.k)
+        tot += time.perf_counter() - t0
+        reps += 1
+        if tot >= target_s or reps >= 50:
+            break
+    per = tot / reps
+    return {"value": cfg.flop / per / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle", "ms_per_step": per * 1e3,
+            "sample": f"whole {cfg.name} workload ({cfg.rows} rows x {cfg.nb} blocks: scores, "
+                      f"S, B in float64 and top-{cfg.k}), {reps} repetition(s), {tot:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the select phase is per-GPU work with no collective; see the sharding note in "
+              "DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import qsa_inputs as qi
+    import sparse_attention_block_qsa_amd as qsa
+
+    cfg = qi.CONFIGS[args.workload]
+    print(f"# workload {cfg.name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr,
+          flush=True)
+    res = measure(cfg, qsa, torch, args.steps, args.warmup)
+    print(f"# {cfg.name}: {res['ms_per_step'] * 1e3:.2f} us/step, stages "
+          f"{ {k: round(v * 1e3, 2) for k, v in res['stages_ms'].items()} } us", file=sys.stderr,
+          flush=True)
+
+    scorer_ms = res["stages_ms"]["scorer"]
+    achieved = res["flop"] / (scorer_ms * 1e-3) / 1e12
+    kernel = "score_full"
+    roofline = {"bound": "mfma", "kernel": "score_full_kernel<128,4> (+ tail when present)",
+                "achieved": achieved, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_FP16_TFLOPS,
+                "traffic": read_traffic(kernel, cfg.name),
+                "per_launch_flop": res["flop"], "launch_ms": scorer_ms}
+
+    prefill = None
+    if args.prefill_steps > 0 and cfg.name != qi.PREFILL.name:
+        pc = qi.PREFILL
+        print(f"# prefill chunk {pc.name}: steps {args.prefill_steps}", file=sys.stderr,
+              flush=True)
+        pr = measure(pc, qsa, torch, args.prefill_steps, 3)
+        ps = pr["stages_ms"]
+        hbm = {"convert": 6.0 * pc.nq * pc.G * pc.H * pc.D,
+               "topk": 4.0 * pc.rows * pc.nb + 4.0 * pc.rows * pc.k}
+        prefill = {
+            "workload": pc.name, "ms_per_step": pr["ms_per_step"], "stages_ms": ps,
+            "scorer_tflops": pr["scorer_tflops"],
+            "scorer_frac_of_peak": pr["scorer_tflops"] / PEAK_FP16_TFLOPS,
+            "convert_gbs": hbm["convert"] / (ps["convert"] * 1e-3) / 1e9,
+            "topk_gbs": hbm["topk"] / (ps["topk"] * 1e-3) / 1e9,
+            "graph_replay_matches_eager": pr["graph_replay_matches_eager"],
+        }
+        print(f"# prefill: {pr['ms_per_step']:.3f} ms/step, scorer {pr['scorer_tflops']:.0f} "
+              f"TFLOP/s", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg, args.cpu_seconds)
+
+    if args.copy_calibration:
+        src = torch.empty(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    line = {
+        "metric": METRIC,
+        "value": res["phase_tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded splitmix64 N(0,1)/sqrt(D), fp16 operands, fp32 accumulation)",
+        "config": {"workload": cfg.name, "G": cfg.G, "nq": cfg.nq, "H": cfg.H, "D": cfg.D,
+                   "n_kv": cfg.n_kv, "bs": cfg.bs, "k": cfg.k, "parallelism": "single GPU"},
+        "select_ms": res["ms_per_step"],
+        "scorer_ms": scorer_ms,
+        "scorer_tflops": achieved,
+        "scorer_frac_of_peak": achieved / PEAK_FP16_TFLOPS,
+        "stages_ms": res["stages_ms"],
+        "graph_replay_matches_eager": res["graph_replay_matches_eager"],
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "full_prefill": prefill,
+        "source_digest": source_digest(),
+        "context": {"pages_rx7900xtx_gfx1100_scores_ms_128k": {"warp": 2.627, "wmma": 0.252},
+                    "note": "other hardware; context only"},
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

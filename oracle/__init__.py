@@ -42,6 +42,7 @@ def lib():
             _b.build()
         L = ctypes.CDLL(LIB_PATH)
         L.oracle_abi_version.restype = ctypes.c_int
+        L.oracle_max_threads.restype = ctypes.c_int
         L.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
         L.oracle_f16_to_f64.restype = ctypes.c_double
         L.oracle_f32_to_f16_one.argtypes = [ctypes.c_float]
@@ -58,6 +59,10 @@ def lib():
         L.oracle_topk.restype = ctypes.c_int
         _lib = L
     return _lib
+
+
+def max_threads() -> int:
+    return lib().oracle_max_threads()
 
 
 def _p(a: np.ndarray | None):

@@ -30,6 +30,7 @@
  * float64 summation, about D * 2^-53 * S: negligible against B.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -37,6 +38,9 @@
 #define ORACLE_ABI 1
 
 int oracle_abi_version(void) { return ORACLE_ABI; }
+
+/* Threads an OpenMP region of the oracle uses (for reporting). */
+int oracle_max_threads(void) { return omp_get_max_threads(); }
 
 /* IEEE 754 binary16 -> exact double, from the format's definition:
  * sign s, 5-bit biased exponent e, 10-bit fraction m.
