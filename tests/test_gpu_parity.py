@@ -273,6 +273,19 @@ def topk_cases():
     t = rng.standard_normal((4, 2049)).astype(np.float32)
     t[:, ::3] = 1.25
     cases.append(("many_ties_2049", t, 2049))
+    # the sampled-threshold path with ties at the threshold: few distinct values
+    q = (rng.integers(0, 1000, (8, 2049)) / 8.0).astype(np.float32)
+    cases.append(("quantised_ties_2049", q, 2049))
+    # +0 / -0 ties straddling the threshold, the rest negative
+    zz = -1.0 - rng.random((6, 500)).astype(np.float32)
+    for r in range(6):
+        pos = rng.choice(500, 70, replace=False)
+        zz[r, pos[:30]] = rng.random(30).astype(np.float32) + 1.0
+        zz[r, pos[30:50]] = 0.0
+        zz[r, pos[50:]] = -0.0
+    cases.append(("signed_zero_threshold_500", zz, 500))
+    cases.append(("all_negative_100", -rng.random((6, 100)).astype(np.float32) - 0.5, 100))
+    cases.append(("all_negative_2049", -rng.random((4, 2049)).astype(np.float32), 2049))
     return cases
 
 
