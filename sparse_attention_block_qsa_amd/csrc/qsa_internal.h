@@ -26,7 +26,7 @@ struct ScoreGeom {
 };
 
 // Full-block MFMA scorer over blocks [0, nf).  Launches one kernel per head
-// pass (one pass unless H*D > kMaxHeadElems).
+// pass of up to eight heads).
 hipError_t launch_score_full(const ScoreGeom &g, hipStream_t s);
 
 // Fixed-order scorer of the single block b_tail.

@@ -23,7 +23,10 @@
 //    let one wave's relu/add epilogue run on the VALU while the matrix core
 //    works on the other wave's MFMAs.
 //  * Stores: for a fixed accumulator register the 64 lanes hold 2 query rows
-//    x 32 consecutive blocks, i.e. two full 128-byte row segments.
+//    x 32 consecutive blocks, i.e. two full 128-byte row segments; they are
+//    raw buffer stores, so masked lanes cost no branch.
+//  * K tiles go through a three-slot LDS ring with one barrier per tile; the
+//    LDS reads are pinned one K-step ahead of the MFMAs that use them.
 //  * Ragged edges: query rows >= nq load zeros, blocks >= nf repeat block
 //    nf-1 (MFMA output columns are independent, and those columns are never
 //    stored), and stores are masked, so the write set is exactly
@@ -69,17 +72,20 @@ __device__ __forceinline__ float relu_bits(float x) {
     return __builtin_bit_cast(float, max(__builtin_bit_cast(int32_t, x), 0));
 }
 
-template <int D, int NP, bool ACCUM>
+template <int D, int NP, bool ACCUM, bool BUF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void score_full_kernel(ScoreArgs a) {
     constexpr int KS = D / 16;              // MFMA K-steps per head
     constexpr int CHUNKS = D / 8;           // 16-byte chunks per block row
     constexpr int TILE_U4 = CHUNKS * kTileBlocks;
     constexpr int LOADS = TILE_U4 / 256;    // uint4 per thread per tile
-    constexpr int PB = NP < 4 ? NP : 4;     // accumulators live at once (16 VGPRs each)
-    static_assert(TILE_U4 % 256 == 0, "tile must split evenly over 256 threads");
+    static_assert(TILE_U4 % 256 == 0 && (LOADS == 1 || LOADS == 2), "D must be 64 or 128");
+    static_assert(NP >= 1 && NP <= 4, "at most four head pairs per pass");
 
-    __shared__ uint4 kbuf[2][TILE_U4];
+    // Three-slot ring of K tiles: while tile t is consumed, tile t+1 is
+    // already published (so its first fragments can be read before the
+    // barrier) and tile t+2 is being staged.
+    __shared__ uint4 kbuf[3][TILE_U4];
 
     const uint32_t L = xcd_logical_id(blockIdx.x, gridDim.x);
     const int split = static_cast<int>(L % a.n_splits);
@@ -87,9 +93,9 @@ void score_full_kernel(ScoreArgs a) {
     const int qg = static_cast<int>(rest % a.n_qgroups);
     const int g = static_cast<int>(rest / a.n_qgroups);
 
-    const int tile_begin = split * a.tiles_per_split;
-    const int tile_end = min(a.n_tiles, tile_begin + a.tiles_per_split);
-    if (tile_begin >= tile_end) return;   // uniform over the workgroup
+    const int tb = split * a.tiles_per_split;
+    const int te = min(a.n_tiles, tb + a.tiles_per_split);
+    if (tb >= te) return;   // uniform over the workgroup
 
     const int w = threadIdx.x >> 6;
     const int l = threadIdx.x & 63;
@@ -116,126 +122,165 @@ void score_full_kernel(ScoreArgs a) {
         }
     }
 
-    // ---- cooperative K tile staging --------------------------------------
-    // Each thread moves LOADS (1 or 2) 16-byte chunks per tile; LDS index
-    // u = threadIdx.x + 256*c is chunk-major (u = chunk*32 + block), which is
-    // also the MFMA B-fragment order: lane l of K-step s reads u = 64*s + l.
-    // Plain scalars (no array, no lambda) keep the staging in VGPRs.
-    static_assert(LOADS == 1 || LOADS == 2, "D must be 64 or 128");
+    // ---- K tile staging ----------------------------------------------------
+    // LDS index u = threadIdx.x + 256*c is chunk-major (u = chunk*32 + block),
+    // which is also the MFMA B-fragment order: lane l of K-step s reads
+    // u = 64*s + l, lane-contiguous.  Blocks past nf (and tiles past the
+    // split) only feed MFMA output columns that are never stored, so their
+    // rows may be any in-bounds data: the indices are clamped.
     const uint16_t *kg = a.kblk + static_cast<int64_t>(g) * a.khs;
     const int u0 = threadIdx.x, u1 = threadIdx.x + 256;
     const int off0 = 8 * (u0 / kTileBlocks), off1 = 8 * (u1 / kTileBlocks);
     const int bb0 = u0 % kTileBlocks, bb1 = u1 % kTileBlocks;
     const int64_t last = a.nf - 1;
-    // Blocks past nf only feed MFMA output columns that are never stored, so
-    // their rows may be any in-bounds data: clamp to the last full block.
-    uint4 kr0, kr1 = make_uint4(0, 0, 0, 0);
+    auto kload = [&](int tile, int bb, int off) {
+        const int64_t b = min(static_cast<int64_t>(min(tile, te - 1)) * kTileBlocks + bb, last);
+        return *reinterpret_cast<const uint4 *>(kg + b * D + off);
+    };
+
+    // ---- output addressing -------------------------------------------------
+    // Lane l holds, for register u (0..7), query t_base + 8*(u/4) + 4*(l/32)
+    // + u%4 and block tile*32 + l%32.  With BUF the stores are raw buffer
+    // stores over this KV head's rows: an offset >= 2^30 (past the region,
+    // which the host limits to 2^30 bytes) is dropped by the hardware, so
+    // masked lanes need no branch.
+    float *srow_base = a.scores + static_cast<int64_t>(g) * a.nq * a.ld_s;
+    const int bl = l & 31;
+    // BUF: byte offsets (the region is below 2^30 bytes, so they fit 32
+    // bits and kOut marks a masked row); otherwise element offsets and -1.
+    constexpr uint32_t kOut = 0x40000000u;
+    uint32_t rowoff[8];
+    int64_t rowel[8];
+    #pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int t = t_base + 8 * (u >> 2) + 4 * (l >> 5) + (u & 3);
+        if constexpr (BUF)
+            rowoff[u] = t < a.nq ? static_cast<uint32_t>(static_cast<int64_t>(t) * a.ld_s * 4) : kOut;
+        else
+            rowel[u] = t < a.nq ? static_cast<int64_t>(t) * a.ld_s : -1;
+    }
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        srow_base, 0, BUF ? static_cast<int>(static_cast<int64_t>(a.nq) * a.ld_s * 4) : 0,
+        0x00020000 /* 32-bit elements, raw */);
+
+    // prologue: tiles tb and tb+1 into slots 0 and 1
     {
-        const int64_t b0 = static_cast<int64_t>(tile_begin) * kTileBlocks;
-        kr0 = *reinterpret_cast<const uint4 *>(kg + min(b0 + bb0, last) * D + off0);
-        if constexpr (LOADS == 2)
-            kr1 = *reinterpret_cast<const uint4 *>(kg + min(b0 + bb1, last) * D + off1);
-        kbuf[0][u0] = kr0;
-        if constexpr (LOADS == 2) kbuf[0][u1] = kr1;
+        const uint4 x0 = kload(tb, bb0, off0), y0 = kload(tb + 1, bb0, off0);
+        kbuf[0][u0] = x0;
+        kbuf[1][u0] = y0;
+        if constexpr (LOADS == 2) {
+            const uint4 x1 = kload(tb, bb1, off1), y1 = kload(tb + 1, bb1, off1);
+            kbuf[0][u1] = x1;
+            kbuf[1][u1] = y1;
+        }
     }
     __syncthreads();
 
-    float *srow_base = a.scores + static_cast<int64_t>(g) * a.nq * a.ld_s;
-    const int bl = l & 31;
+    int slot = 0;   // ring slot of the current tile
+    half8 kf0 = __builtin_bit_cast(half8, kbuf[0][l]);
+    half8 kf1 = __builtin_bit_cast(half8, kbuf[0][64 + l]);
 
-    for (int tile = tile_begin; tile < tile_end; ++tile) {
-        const int cur = (tile - tile_begin) & 1;
-        const bool more = tile + 1 < tile_end;
-        if (more) {
-            const int64_t b0 = static_cast<int64_t>(tile + 1) * kTileBlocks;
-            kr0 = *reinterpret_cast<const uint4 *>(kg + min(b0 + bb0, last) * D + off0);
-            if constexpr (LOADS == 2)
-                kr1 = *reinterpret_cast<const uint4 *>(kg + min(b0 + bb1, last) * D + off1);
-        }
+    for (int tile = tb; tile < te; ++tile) {
+        const int nslot = slot == 2 ? 0 : slot + 1;
+        const int wslot = nslot == 2 ? 0 : nslot + 1;   // held tile - 1: free
+        const uint4 r0 = kload(tile + 2, bb0, off0);
+        uint4 r1 = make_uint4(0, 0, 0, 0);
+        if constexpr (LOADS == 2) r1 = kload(tile + 2, bb1, off1);
 
-        const int64_t bcol = static_cast<int64_t>(tile) * kTileBlocks + bl;
-        const bool col_ok = bcol < a.nf;
+        const int bcol = tile * kTileBlocks + bl;
+        const uint32_t coloff = bcol < a.nf ? static_cast<uint32_t>(bcol) * 4 : kOut;
 
         float tot[8];
         #pragma unroll
         for (int u = 0; u < 8; ++u) {
             tot[u] = 0.0f;
             if constexpr (ACCUM) {
-                const int t = t_base + 8 * (u >> 2) + 4 * (l >> 5) + (u & 3);
-                if (t < a.nq && col_ok) tot[u] = srow_base[static_cast<int64_t>(t) * a.ld_s + bcol];
+                if constexpr (BUF) {
+                    tot[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                          rs, static_cast<int>(rowoff[u] + coloff), 0, 0));
+                } else if (rowel[u] >= 0 && coloff != kOut) {
+                    tot[u] = srow_base[rowel[u] + bcol];
+                }
             }
         }
 
-        // Head pairs in batches of PB accumulators; inside a batch the K-step
-        // is the outer loop, so the PB MFMAs that consume one B fragment are
-        // independent of each other, and the next fragment's LDS read is in
-        // flight while they run.
-        const uint4 *kcur = &kbuf[cur][l];
+        // MFMA phase: K-step outer so the NP MFMAs sharing a B fragment are
+        // independent; fragment s+2 is read from LDS one step ahead of use.
+        const uint4 *kcur = &kbuf[slot][l];
+        floatx16 acc[NP];
+        half8 kf = kf0, kn = kf1;
         #pragma unroll
-        for (int p0 = 0; p0 < NP; p0 += PB) {
-            floatx16 acc[PB];
-            half8 kf = __builtin_bit_cast(half8, kcur[0]);
+        for (int s = 0; s < KS; ++s) {
+            half8 k2 = kn;
+            if (s + 2 < KS) k2 = __builtin_bit_cast(half8, kcur[64 * (s + 2)]);
             #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                half8 kn = kf;
-                if (s + 1 < KS) kn = __builtin_bit_cast(half8, kcur[64 * (s + 1)]);
-                #pragma unroll
-                for (int j = 0; j < PB; ++j) {
-                    if (p0 + j < NP) {
-                        const floatx16 c = (s == 0) ? floatx16{} : acc[j];
-                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[p0 + j][s], kf, c, 0, 0, 0);
-                    }
-                }
-                kf = kn;
+            for (int p = 0; p < NP; ++p) {
+                const floatx16 c = (s == 0) ? floatx16{} : acc[p];
+                acc[p] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[p][s], kf, c, 0, 0, 0);
             }
-            #pragma unroll
-            for (int j = 0; j < PB; ++j) {
-                if (p0 + j < NP) {
-                    #pragma unroll
-                    for (int u = 0; u < 8; ++u) tot[u] += relu_bits(acc[j][u]);       // head 2p
-                    #pragma unroll
-                    for (int u = 0; u < 8; ++u) tot[u] += relu_bits(acc[j][u + 8]);   // head 2p+1
-                }
-            }
+            kf = kn;
+            kn = k2;
+        }
+        // Keep the LDS reads a step ahead of their MFMAs (the scheduler would
+        // otherwise sink each read next to its first use).
+        __builtin_amdgcn_sched_group_barrier(0x020, LOADS, 0);   // staging loads
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // fragments 2, 3
+        #pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            __builtin_amdgcn_sched_group_barrier(0x008, NP, 0);
+            if (s + 4 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
 
-        // Publish the prefetched tile before issuing this tile's stores: the
-        // wait for its loads then does not also wait for the stores.
-        if (more) {
-            kbuf[cur ^ 1][u0] = kr0;
-            if constexpr (LOADS == 2) kbuf[cur ^ 1][u1] = kr1;
-        }
+        // the next tile was published an iteration ago: fetch its first two
+        // fragments now, then stage tile+2 into the free slot
+        kf0 = __builtin_bit_cast(half8, kbuf[nslot][l]);
+        kf1 = __builtin_bit_cast(half8, kbuf[nslot][64 + l]);
+        kbuf[wslot][u0] = r0;
+        if constexpr (LOADS == 2) kbuf[wslot][u1] = r1;
 
+        // epilogue: relu per head, head sum in ascending head order
+        #pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            #pragma unroll
+            for (int u = 0; u < 8; ++u) tot[u] += relu_bits(acc[p][u]);       // head 2p
+            #pragma unroll
+            for (int u = 0; u < 8; ++u) tot[u] += relu_bits(acc[p][u + 8]);   // head 2p+1
+        }
         #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int t = t_base + 8 * (u >> 2) + 4 * (l >> 5) + (u & 3);
-            if (t < a.nq && col_ok) srow_base[static_cast<int64_t>(t) * a.ld_s + bcol] = tot[u];
+            if constexpr (BUF) {
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, tot[u]), rs,
+                                                      static_cast<int>(rowoff[u] + coloff), 0, 0);
+            } else if (rowel[u] >= 0 && coloff != kOut) {
+                srow_base[rowel[u] + bcol] = tot[u];
+            }
         }
         __syncthreads();
+        slot = nslot;
     }
 }
 
 typedef void (*score_fn)(ScoreArgs);
 
-// Heads per pass: 12 at D = 64 and 8 at D = 128 keep the resident queries,
-// four accumulators and the staging registers inside 256 VGPRs (two waves per
-// SIMD); more heads take a second, accumulating pass.
-constexpr int heads_per_pass(int D) { return D == 64 ? 12 : 8; }
+// Heads per pass: 8 keep the resident queries (128 VGPRs at D = 128), four
+// accumulators and the staging registers inside 256 VGPRs, i.e. two waves
+// per SIMD; more heads take a second, accumulating pass.
+constexpr int kHeadsPerPass = 8;
 
-score_fn pick(int D, int np, bool accum) {
-#define QSA_SCORE_CASE(DD, N) \
-    if (D == DD && np == N) return accum ? score_full_kernel<DD, N, true> : score_full_kernel<DD, N, false>;
-    QSA_SCORE_CASE(128, 1)
-    QSA_SCORE_CASE(128, 2)
-    QSA_SCORE_CASE(128, 3)
-    QSA_SCORE_CASE(128, 4)
-    QSA_SCORE_CASE(64, 1)
-    QSA_SCORE_CASE(64, 2)
-    QSA_SCORE_CASE(64, 3)
-    QSA_SCORE_CASE(64, 4)
-    QSA_SCORE_CASE(64, 5)
-    QSA_SCORE_CASE(64, 6)
-#undef QSA_SCORE_CASE
+template <int D, bool BUF>
+score_fn pick_d(int np, bool accum) {
+    switch (np) {
+        case 1: return accum ? score_full_kernel<D, 1, true, BUF> : score_full_kernel<D, 1, false, BUF>;
+        case 2: return accum ? score_full_kernel<D, 2, true, BUF> : score_full_kernel<D, 2, false, BUF>;
+        case 3: return accum ? score_full_kernel<D, 3, true, BUF> : score_full_kernel<D, 3, false, BUF>;
+        case 4: return accum ? score_full_kernel<D, 4, true, BUF> : score_full_kernel<D, 4, false, BUF>;
+    }
+    return nullptr;
+}
+
+score_fn pick(int D, int np, bool accum, bool buf) {
+    if (D == 128) return buf ? pick_d<128, true>(np, accum) : pick_d<128, false>(np, accum);
+    if (D == 64) return buf ? pick_d<64, true>(np, accum) : pick_d<64, false>(np, accum);
     return nullptr;
 }
 
@@ -243,7 +288,9 @@ score_fn pick(int D, int np, bool accum) {
 
 hipError_t launch_score_full(const ScoreGeom &geo, hipStream_t s) {
     if (geo.nf <= 0 || geo.nq <= 0 || geo.G <= 0) return hipSuccess;
-    const int hpp = heads_per_pass(geo.D);
+    const int hpp = kHeadsPerPass;
+    // buffer stores address one KV head's rows with 32-bit offsets below 2^30
+    const bool buf = static_cast<int64_t>(geo.nq) * geo.ld_s * 4 < (int64_t(1) << 30);
     const int64_t n_tiles = (geo.nf + kTileBlocks - 1) / kTileBlocks;
     const int64_t n_qgroups = (geo.nq + kGroupQueries - 1) / kGroupQueries;
     const int64_t base = static_cast<int64_t>(geo.G) * n_qgroups;
@@ -265,7 +312,7 @@ hipError_t launch_score_full(const ScoreGeom &geo, hipStream_t s) {
     for (int h0 = 0; h0 < geo.H; h0 += hpp) {
         const int nh = (geo.H - h0 < hpp) ? geo.H - h0 : hpp;
         const int np = (nh + 1) / 2;
-        score_fn fn = pick(geo.D, np, h0 > 0);
+        score_fn fn = pick(geo.D, np, h0 > 0, buf);
         if (!fn) return hipErrorInvalidValue;
         ScoreArgs a{geo.q16, geo.qts, geo.kblk, geo.khs, geo.scores, geo.ld_s,
                     geo.G, geo.nq, geo.H, h0, nh, h0 > 0 ? 1 : 0, geo.nf,

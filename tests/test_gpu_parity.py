@@ -370,3 +370,26 @@ def test_phase_ids_write_set():
     torch.cuda.synchronize()
     m = np.ones((cfg.G, cfg.nq, cfg.k), dtype=bool)
     assert ids.outside_intact(m) and ids.written_all(m)
+
+
+def test_wide_rows_use_global_store_path():
+    """A score region past 2^30 bytes per KV head takes the scorer's plain
+    global-store path (the buffer-store path needs 30-bit offsets); it must
+    give the same write set and the same bound.  H = 12 also exercises the
+    accumulating second head pass on that path."""
+    cfg = qi.Config("wide", 1, 70, 12, 128, 65 * 64 + 5, 64, 8, "normal", 99)
+    w = qi.make(cfg)
+    ld = 1 << 24                                   # 64 MiB per row: 4.4 GiB region
+    sent = int(SENTINEL)
+    out = torch.full((cfg.G, cfg.nq, ld), sent, dtype=torch.int32, device=dev())
+    qsa.block_scores(q_dev(w.q16), k_dev(w.kblk), cfg.n_kv, cfg.bs, out=out.view(torch.float32))
+    torch.cuda.synchronize()
+    head = out[:, :, :cfg.nb + 256]
+    assert torch.all(head[:, :, cfg.nb:] == sent), "write past nb"
+    assert torch.all(out[:, :, ld - 256:] == sent)
+    assert not torch.any(head[:, :, :cfg.nb] == sent), "cell not written"
+    s_gpu = head[:, :, :cfg.nb].view(torch.float32).reshape(cfg.rows, cfg.nb).cpu().numpy()
+    ref = oracle.scores(w.q16, w.kblk, cfg.nb)
+    check_bound(s_gpu.astype(np.float64), ref, "wide rows")
+    del out
+    torch.cuda.empty_cache()
