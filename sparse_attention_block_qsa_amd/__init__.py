@@ -167,7 +167,9 @@ class PhaseWorkspace:
         self.nb = n_blocks(n_kv, bs)
         qc = q_chunk if 0 < q_chunk < nq else nq
         self.q_chunk = q_chunk
-        self.ld_s = max(self.nb, 1) + ld_pad
+        # Rows start on 128-byte boundaries: every 32-column tile store of the
+        # scorer then fills whole cache lines.
+        self.ld_s = -(-(max(self.nb, 1) + ld_pad) // 32) * 32
         self.scores = torch.empty((G, qc, self.ld_s), dtype=torch.float32, device=device)
         self.q16 = torch.empty((nq, G, H, D), dtype=torch.float16, device=device)
         self.ids = torch.empty((G, nq, k), dtype=torch.int32, device=device)

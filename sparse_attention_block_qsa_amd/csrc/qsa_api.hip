@@ -77,10 +77,9 @@ hipError_t run_scores(const uint16_t *q16, int64_t qts, const uint16_t *kblk, in
                       float *scores, int64_t ld_s, int32_t G, int32_t nq, int32_t H, int32_t D,
                       const ScoreCheck &c, hipStream_t s) {
     ScoreGeom geo{q16, qts, kblk, khs, scores, ld_s, G, nq, H, D, c.nf};
-    hipError_t e = qsa::launch_score_full(geo, s);
-    if (e != hipSuccess) return e;
-    if (c.nb > c.nf) e = qsa::launch_tail(geo, c.nf, s);
-    return e;
+    const bool tail = c.nb > c.nf;
+    if (c.nf > 0) return qsa::launch_score_full(geo, tail, s);
+    return tail ? qsa::launch_tail(geo, c.nf, s) : hipSuccess;
 }
 
 }  // namespace

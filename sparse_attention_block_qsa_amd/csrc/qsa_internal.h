@@ -26,10 +26,12 @@ struct ScoreGeom {
 };
 
 // Full-block MFMA scorer over blocks [0, nf).  Launches one kernel per head
-// pass of up to eight heads).
-hipError_t launch_score_full(const ScoreGeom &g, hipStream_t s);
+// pass of up to eight heads.  With tail (requires nf > 0) the same launches
+// also score block nf in the fixed order of the tail model.
+hipError_t launch_score_full(const ScoreGeom &g, bool tail, hipStream_t s);
 
-// Fixed-order scorer of the single block b_tail.
+// Fixed-order scorer of the single block b_tail, standalone (used when there
+// is no full block to share the query reads with).
 hipError_t launch_tail(const ScoreGeom &g, int64_t b_tail, hipStream_t s);
 
 struct TopkGeom {

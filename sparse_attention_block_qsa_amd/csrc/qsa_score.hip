@@ -13,9 +13,9 @@
 //    the operand with 8x the reuse, so they are the stationary one.
 //  * The B operand is 32 blocks of K_blk, N = block axis: lane l holds
 //    k[b0 + l%32][16s + 8*(l/32) .. +7].  A 32-block tile (8 KiB at D=128) is
-//    staged once per workgroup in LDS, double-buffered, stored in fragment
-//    order so that every ds_read_b128 is lane-contiguous, and reused by the
-//    four waves and by every head pair.
+//    staged once per workgroup in LDS, stored in fragment order so that
+//    every ds_read_b128 is lane-contiguous, and reused by the four waves and
+//    by every head pair.
 //  * The 32x32 accumulator of one head pair holds, per lane, the same
 //    (query, block) cells for both heads (registers r and r+8), so the relu
 //    and the head sum are lane-local: tot[u] += relu(acc[u]); tot[u] +=
@@ -31,6 +31,10 @@
 //    nf-1 (MFMA output columns are independent, and those columns are never
 //    stored), and stores are masked, so the write set is exactly
 //    scores[g*nq + t][0, nf).
+//  * A partial last block (n_kv mod bs != 0) is scored at the end by the
+//    last split of each query group, from the same resident query registers,
+//    in the fixed fma order of the tail model, so the queries are read from
+//    HBM once for all nb blocks.
 //  * Grid: (KV head, 64-query group, block split), with logical ids laid out
 //    so that each XCD (blockIdx % 8) takes a contiguous range: the splits of
 //    one query group and the query groups of one KV head share that XCD's L2.
@@ -72,7 +76,7 @@ __device__ __forceinline__ float relu_bits(float x) {
     return __builtin_bit_cast(float, max(__builtin_bit_cast(int32_t, x), 0));
 }
 
-template <int D, int NP, bool ACCUM, bool BUF>
+template <int D, int NP, bool ACCUM, bool BUF, bool TAIL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void score_full_kernel(ScoreArgs a) {
     constexpr int KS = D / 16;              // MFMA K-steps per head
@@ -258,6 +262,70 @@ void score_full_kernel(ScoreArgs a) {
         __syncthreads();
         slot = nslot;
     }
+
+    if constexpr (TAIL) {
+        // The partial block nf, scored by the last split of each query group
+        // from the query fragments already in registers, in the fixed order
+        // of the tail model: per (query, head) one fp32 fma chain over the
+        // channels in ascending order, relu (acc > 0 ? acc : +0), then the
+        // heads added in ascending order.  v_permlane32_swap of the fragments
+        // of head pairs p0 = 2c and p1 = 2c+1 gives lanes 0-31 whole 16-wide
+        // channel runs of pair p0 and lanes 32-63 those of pair p1, so lane l
+        // runs the chain of query t_base + l%16, head 4c + l/16 (in the pass).
+        if (split == a.n_splits - 1) {   // uniform over the workgroup
+            constexpr int NPC = (NP + 1) / 2;
+            const uint4 *kt = reinterpret_cast<const uint4 *>(kg + a.nf * D);
+            uint4 kc[CHUNKS];
+            #pragma unroll
+            for (int c = 0; c < CHUNKS; ++c) kc[c] = kt[c];
+            float r[NPC];
+            #pragma unroll
+            for (int c = 0; c < NPC; ++c) {
+                float acc = 0.0f;
+                #pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    const uint4 x = __builtin_bit_cast(uint4, qa[2 * c][s]);
+                    const uint4 y = 2 * c + 1 < NP ? __builtin_bit_cast(uint4, qa[2 * c + 1 < NP ? 2 * c + 1 : 0][s])
+                                                   : make_uint4(0, 0, 0, 0);
+                    const auto sw0 = __builtin_amdgcn_permlane32_swap(x.x, y.x, false, false);
+                    const auto sw1 = __builtin_amdgcn_permlane32_swap(x.y, y.y, false, false);
+                    const auto sw2 = __builtin_amdgcn_permlane32_swap(x.z, y.z, false, false);
+                    const auto sw3 = __builtin_amdgcn_permlane32_swap(x.w, y.w, false, false);
+                    // channels 16s .. 16s+7, then 16s+8 .. 16s+15
+                    const uint32_t qw[8] = {sw0[0], sw1[0], sw2[0], sw3[0], sw0[1], sw1[1], sw2[1], sw3[1]};
+                    const uint4 k0 = kc[2 * s], k1 = kc[2 * s + 1];
+                    const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+                    #pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float q0 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(qw[e] & 0xffffu)));
+                        const float q1 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(qw[e] >> 16)));
+                        const float k0f = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(kw[e] & 0xffffu)));
+                        const float k1f = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(kw[e] >> 16)));
+                        acc = __builtin_fmaf(k0f, q0, acc);
+                        acc = __builtin_fmaf(k1f, q1, acc);
+                    }
+                }
+                r[c] = acc > 0.0f ? acc : 0.0f;
+            }
+            // head sum across lanes: the ring is free after the last barrier
+            float *red = reinterpret_cast<float *>(&kbuf[0][0]) + w * (NPC * 64);
+            #pragma unroll
+            for (int c = 0; c < NPC; ++c) red[64 * c + l] = r[c];
+            __syncthreads();
+            const int t = t_base + l;
+            if (l < kWaveQueries && t < a.nq) {
+                float *cell = srow_base + static_cast<int64_t>(t) * a.ld_s + a.nf;
+                float sum = ACCUM ? *cell : 0.0f;
+                #pragma unroll
+                for (int c = 0; c < NPC; ++c) {
+                    #pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (4 * c + j < a.nh) sum = sum + red[64 * c + 16 * j + l];
+                }
+                *cell = sum;
+            }
+        }
+    }
 }
 
 typedef void (*score_fn)(ScoreArgs);
@@ -267,26 +335,32 @@ typedef void (*score_fn)(ScoreArgs);
 // per SIMD; more heads take a second, accumulating pass.
 constexpr int kHeadsPerPass = 8;
 
-template <int D, bool BUF>
+template <int D, bool BUF, bool TAIL>
 score_fn pick_d(int np, bool accum) {
     switch (np) {
-        case 1: return accum ? score_full_kernel<D, 1, true, BUF> : score_full_kernel<D, 1, false, BUF>;
-        case 2: return accum ? score_full_kernel<D, 2, true, BUF> : score_full_kernel<D, 2, false, BUF>;
-        case 3: return accum ? score_full_kernel<D, 3, true, BUF> : score_full_kernel<D, 3, false, BUF>;
-        case 4: return accum ? score_full_kernel<D, 4, true, BUF> : score_full_kernel<D, 4, false, BUF>;
+        case 1: return accum ? score_full_kernel<D, 1, true, BUF, TAIL> : score_full_kernel<D, 1, false, BUF, TAIL>;
+        case 2: return accum ? score_full_kernel<D, 2, true, BUF, TAIL> : score_full_kernel<D, 2, false, BUF, TAIL>;
+        case 3: return accum ? score_full_kernel<D, 3, true, BUF, TAIL> : score_full_kernel<D, 3, false, BUF, TAIL>;
+        case 4: return accum ? score_full_kernel<D, 4, true, BUF, TAIL> : score_full_kernel<D, 4, false, BUF, TAIL>;
     }
     return nullptr;
 }
 
-score_fn pick(int D, int np, bool accum, bool buf) {
-    if (D == 128) return buf ? pick_d<128, true>(np, accum) : pick_d<128, false>(np, accum);
-    if (D == 64) return buf ? pick_d<64, true>(np, accum) : pick_d<64, false>(np, accum);
+template <int D>
+score_fn pick_dt(int np, bool accum, bool buf, bool tail) {
+    if (tail) return buf ? pick_d<D, true, true>(np, accum) : pick_d<D, false, true>(np, accum);
+    return buf ? pick_d<D, true, false>(np, accum) : pick_d<D, false, false>(np, accum);
+}
+
+score_fn pick(int D, int np, bool accum, bool buf, bool tail) {
+    if (D == 128) return pick_dt<128>(np, accum, buf, tail);
+    if (D == 64) return pick_dt<64>(np, accum, buf, tail);
     return nullptr;
 }
 
 }  // namespace
 
-hipError_t launch_score_full(const ScoreGeom &geo, hipStream_t s) {
+hipError_t launch_score_full(const ScoreGeom &geo, bool tail, hipStream_t s) {
     if (geo.nf <= 0 || geo.nq <= 0 || geo.G <= 0) return hipSuccess;
     const int hpp = kHeadsPerPass;
     // buffer stores address one KV head's rows with 32-bit offsets below 2^30
@@ -312,7 +386,7 @@ hipError_t launch_score_full(const ScoreGeom &geo, hipStream_t s) {
     for (int h0 = 0; h0 < geo.H; h0 += hpp) {
         const int nh = (geo.H - h0 < hpp) ? geo.H - h0 : hpp;
         const int np = (nh + 1) / 2;
-        score_fn fn = pick(geo.D, np, h0 > 0, buf);
+        score_fn fn = pick(geo.D, np, h0 > 0, buf, tail);
         if (!fn) return hipErrorInvalidValue;
         ScoreArgs a{geo.q16, geo.qts, geo.kblk, geo.khs, geo.scores, geo.ld_s,
                     geo.G, geo.nq, geo.H, h0, nh, h0 > 0 ? 1 : 0, geo.nf,

@@ -40,8 +40,8 @@ def prefill():
     kb = torch.from_numpy(w.kblk.view(np.float16)).to(dev())
     ws = qsa.PhaseWorkspace(cfg.nq, cfg.G, cfg.H, cfg.D, cfg.n_kv, cfg.bs, cfg.k, dev(),
                             with_vals=True, ld_pad=3)
-    pad = torch.full((cfg.G, cfg.nq, 3), float("nan"), device=dev())
-    ws.scores[:, :, cfg.nb:] = pad
+    assert ws.ld_s % 32 == 0 and ws.ld_s >= cfg.nb + 3
+    ws.scores[:, :, cfg.nb:] = float("nan")
     log("prefill: running the phase")
     qsa.select_phase(q32, kb, cfg.n_kv, cfg.bs, cfg.k, ws)
     torch.cuda.synchronize()
