@@ -227,6 +227,13 @@ GEOMS = [
     (1, 33, 16, 64, 20 * 64 + 9, 64, 16, 0), # D=64, two head passes
     (1, 50, 16, 128, 18 * 64, 64, 0, 1),     # D=128, two full passes
     (2, 129, 4, 128, 100 * 64 + 3, 64, 0, 0),
+    # only a tail block (the standalone tail kernel): H = 16 and 5, D = 64,
+    # one-token blocks, and more items than the kernel's grid (a second loop
+    # trip per workgroup)
+    (2, 300, 16, 64, 33, 64, 8, 0),
+    (3, 129, 5, 128, 63, 64, 0, 1),
+    (1, 1000, 1, 64, 1, 2, 0, 0),
+    (4, 4200, 8, 128, 40, 64, 0, 0),
 ]
 
 
