@@ -39,56 +39,107 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-    const uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
-    const uint32_t plo = static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), m));
-    const uint32_t phi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), m));
-    return (static_cast<uint64_t>(phi) << 32) | plo;
-}
-
-// Sorting networks in the uniform-direction (mirror) form of the bitonic
-// sort: every compare-exchange keeps the larger composite at the lower
-// element index, so the only per-lane input is whether this lane holds the
-// lower element of its pair.  Merge of size s: first partner e ^ (s-1), then
-// partners e ^ (s/4), ..., e ^ 1.
-__device__ __forceinline__ uint64_t cx_keep(uint64_t v, uint64_t p, bool lower) {
-    return ((p > v) == lower) ? p : v;   // lower keeps max, upper keeps min
-}
-
-// 128 composites held two per lane (element e = s*64 + lane), descending:
-// afterwards slot 0 of lanes 0..63 holds the 64 largest in order.
-__device__ __forceinline__ void bitonic128_desc(uint64_t &v0, uint64_t &v1, int lane) {
-    #pragma unroll
-    for (int size = 2; size <= 128; size <<= 1) {
-        if (size == 128) {
-            // mirror across the slots: element lane pairs with 127 - lane,
-            // which is slot 1 of lane ^ 63
-            const uint64_t p0 = shfl_xor_u64(v1, 63);
-            const uint64_t p1 = shfl_xor_u64(v0, 63);
-            v0 = cx_keep(v0, p0, true);
-            v1 = cx_keep(v1, p1, false);
-        } else {
-            const bool lower = (lane & (size >> 1)) == 0;
-            v0 = cx_keep(v0, shfl_xor_u64(v0, size - 1), lower);
-            v1 = cx_keep(v1, shfl_xor_u64(v1, size - 1), lower);
-        }
-        #pragma unroll
-        for (int stride = size >> 2; stride > 0; stride >>= 1) {
-            const bool lower = (lane & stride) == 0;
-            v0 = cx_keep(v0, shfl_xor_u64(v0, stride), lower);
-            v1 = cx_keep(v1, shfl_xor_u64(v1, stride), lower);
-        }
+// The value of lane ^ M, without LDS traffic where the hardware has a lane
+// permutation for it: DPP quad permutes (xor 1, 2, 3), DPP row mirrors
+// (xor 7 within 8 lanes, xor 15 within 16), v_permlane16/32_swap (xor 16,
+// xor 32: swapping a register with itself exchanges the two row halves),
+// ds_swizzle's xor mode for the other masks below 32, and xor 63 as
+// xor 31 followed by xor 32.
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v, int lane) {
+    if constexpr (M == 1) {
+        return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, false));
+    } else if constexpr (M == 2) {
+        return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, false));
+    } else if constexpr (M == 3) {
+        return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x1B, 0xF, 0xF, false));
+    } else if constexpr (M == 7) {
+        return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x141, 0xF, 0xF, false));
+    } else if constexpr (M == 15) {
+        return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x140, 0xF, 0xF, false));
+    } else if constexpr (M == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane & 16) ? r[0] : r[1];
+    } else if constexpr (M == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane & 32) ? r[0] : r[1];
+    } else if constexpr (M < 32) {
+        return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), (M << 10) | 0x1F));
+    } else {
+        static_assert(M == 63, "unsupported lane mask");
+        return xor_lane<32>(xor_lane<31>(v, lane), lane);
     }
 }
 
-__device__ __forceinline__ uint64_t bitonic64_desc(uint64_t v, int lane) {
-    #pragma unroll
-    for (int size = 2; size <= 64; size <<= 1) {
-        v = cx_keep(v, shfl_xor_u64(v, size - 1), (lane & (size >> 1)) == 0);
-        #pragma unroll
-        for (int stride = size >> 2; stride > 0; stride >>= 1)
-            v = cx_keep(v, shfl_xor_u64(v, stride), (lane & stride) == 0);
-    }
+template <int M>
+__device__ __forceinline__ uint64_t xor_lane64(uint64_t v, int lane) {
+    const uint32_t lo = xor_lane<M>(static_cast<uint32_t>(v), lane);
+    const uint32_t hi = xor_lane<M>(static_cast<uint32_t>(v >> 32), lane);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Compare-exchange with the partner's value p: keep the larger or the smaller.
+__device__ __forceinline__ uint64_t cmpx(uint64_t v, uint64_t p, bool keep_max) {
+    return ((p > v) == keep_max) ? p : v;
+}
+
+// Bitonic networks in the uniform-direction (mirror) form: a merge of size s
+// first pairs element e with its mirror e ^ (s-1), then with e ^ (s/4), ...,
+// e ^ 1; the element of the pair with the clear bit keeps the larger value
+// (descending) or the smaller (ascending).  One composite per lane.
+template <int M, int B>
+__device__ __forceinline__ void step2(uint64_t &v0, uint64_t &v1, int lane) {
+    const uint64_t p0 = xor_lane64<M>(v0, lane);
+    const uint64_t p1 = xor_lane64<M>(v1, lane);
+    const bool lower = (lane & B) == 0;
+    v0 = cmpx(v0, p0, lower);    // descending
+    v1 = cmpx(v1, p1, !lower);   // ascending
+}
+template <int M, int B>
+__device__ __forceinline__ void step1(uint64_t &v, int lane) {
+    v = cmpx(v, xor_lane64<M>(v, lane), (lane & B) == 0);
+}
+
+// Sorts v0 descending and v1 ascending over the 64 lanes.
+__device__ __forceinline__ void sort64_pair(uint64_t &v0, uint64_t &v1, int lane) {
+    step2<1, 1>(v0, v1, lane);
+    step2<3, 2>(v0, v1, lane);   step2<1, 1>(v0, v1, lane);
+    step2<7, 4>(v0, v1, lane);   step2<2, 2>(v0, v1, lane);   step2<1, 1>(v0, v1, lane);
+    step2<15, 8>(v0, v1, lane);  step2<4, 4>(v0, v1, lane);   step2<2, 2>(v0, v1, lane);
+    step2<1, 1>(v0, v1, lane);
+    step2<31, 16>(v0, v1, lane); step2<8, 8>(v0, v1, lane);   step2<4, 4>(v0, v1, lane);
+    step2<2, 2>(v0, v1, lane);   step2<1, 1>(v0, v1, lane);
+    step2<63, 32>(v0, v1, lane); step2<16, 16>(v0, v1, lane); step2<8, 8>(v0, v1, lane);
+    step2<4, 4>(v0, v1, lane);   step2<2, 2>(v0, v1, lane);   step2<1, 1>(v0, v1, lane);
+}
+
+// Sorts v descending over the 64 lanes (lane 0 largest).
+__device__ __forceinline__ uint64_t sort64_desc(uint64_t v, int lane) {
+    step1<1, 1>(v, lane);
+    step1<3, 2>(v, lane);   step1<1, 1>(v, lane);
+    step1<7, 4>(v, lane);   step1<2, 2>(v, lane);   step1<1, 1>(v, lane);
+    step1<15, 8>(v, lane);  step1<4, 4>(v, lane);   step1<2, 2>(v, lane);   step1<1, 1>(v, lane);
+    step1<31, 16>(v, lane); step1<8, 8>(v, lane);   step1<4, 4>(v, lane);   step1<2, 2>(v, lane);
+    step1<1, 1>(v, lane);
+    step1<63, 32>(v, lane); step1<16, 16>(v, lane); step1<8, 8>(v, lane);   step1<4, 4>(v, lane);
+    step1<2, 2>(v, lane);   step1<1, 1>(v, lane);
+    return v;
+}
+
+// The 64 largest of 128 composites (two per lane), sorted descending: sort
+// the slots in opposite directions, so that element i of the 128-sequence
+// meets element i + 64 in the same lane; the larger of each pair forms a
+// bitonic sequence holding the 64 largest, which a half-cleaner cascade
+// (partners lane ^ 32, ..., lane ^ 1) sorts.
+__device__ __forceinline__ uint64_t top64_of_128(uint64_t v0, uint64_t v1, int lane) {
+    sort64_pair(v0, v1, lane);
+    uint64_t v = v0 > v1 ? v0 : v1;
+    step1<32, 32>(v, lane);
+    step1<16, 16>(v, lane);
+    step1<8, 8>(v, lane);
+    step1<4, 4>(v, lane);
+    step1<2, 2>(v, lane);
+    step1<1, 1>(v, lane);
     return v;
 }
 
@@ -118,13 +169,15 @@ __device__ __forceinline__ int wave_excl_scan(int x, int lane, int *total) {
 // satisfies kk <= C <= 128, every element of the true top-kk is a candidate
 // (kk elements are >= th, so the kk-th largest is too), whatever th was; the
 // candidates' exact (key, ~id) composites are compacted into LDS and sorted
-// by a 128-wide bitonic network.  Any other C takes the exact path: a 32-step
+// by bitonic networks.  Any other C takes the exact path: a 32-step
 // ballot bisection for the kk-th largest key over every value, then ties in
 // id order.
 template <int NPL>
 __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     __shared__ uint64_t slot[4][128];
-    const int w = threadIdx.x >> 6;
+    // the wave index is uniform over the wave: say so, so that the row's
+    // addresses and buffer descriptor live in scalar registers
+    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
     const int64_t R = static_cast<int64_t>(blockIdx.x) * 4 + w;
     if (R >= a.total_rows) return;               // whole wave; no block barriers below
@@ -146,16 +199,20 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 
     uint32_t xr[NPL > 0 ? NPL : 1];              // raw fp32 bits
     if constexpr (NPL > 0) {
+        // Raw buffer loads bounded by the row (reads past nb return 0, no
+        // branch), then the pad substituted past nb.
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(srow), 0, nb * 4, 0x00020000 /* 32-bit elements, raw */);
         #pragma unroll
         for (int j = 0; j < NPL; ++j) {
-            const int id = j * 64 + lane;
-            xr[j] = id < nb ? __builtin_bit_cast(uint32_t, srow[id]) : kPad;
+            const uint32_t x = __builtin_amdgcn_raw_buffer_load_b32(rs, (j * 64 + lane) * 4, 0, 0);
+            xr[j] = lane < nb - 64 * j ? x : kPad;
         }
     }
     auto key = [&](int j) -> uint32_t {
         const int id = j * 64 + lane;
         if constexpr (NPL > 0) {
-            return id < nb ? order_key(__builtin_bit_cast(float, xr[j])) : 0u;
+            return order_key(__builtin_bit_cast(float, xr[j]));   // pads are NaN: key 0
         } else {
             return id < nb ? order_key(srow[id]) : 0u;
         }
@@ -171,15 +228,16 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
             #pragma unroll
             for (int j = 0; j < NPL; ++j) {
                 const int32_t x = static_cast<int32_t>(xr[j]);
-                m2 = max(m2, min(m1, x));
+                m2 = max(min(m1, x), min(max(m1, x), m2));   // median of three: v_med3_i32
                 m1 = max(m1, x);
             }
-            // 2. th = the kk-th largest of the 128 samples (bisection on the
-            //    biased bits, two ballots per step)
+            // 2. th = the kk-th largest of the 128 samples, to 16 leading
+            //    bits (bisection on the biased bits, two ballots per step):
+            //    any th is correct, the low bits only tighten C slightly
             const uint32_t s1 = static_cast<uint32_t>(m1) ^ 0x80000000u;
             const uint32_t s2 = static_cast<uint32_t>(m2) ^ 0x80000000u;
             uint32_t T = 0;
-            for (int bit = 31; bit >= 0; --bit) {
+            for (int bit = 31; bit >= 16; --bit) {
                 const uint32_t cand = T | (1u << bit);
                 const int cnt = __popcll(ballot(s1 >= cand)) + __popcll(ballot(s2 >= cand));
                 if (cnt >= kk) T = cand;
@@ -222,10 +280,13 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                uint64_t v0 = lane < C ? slot[w][lane] : 0ull;
-                uint64_t v1 = lane + 64 < C ? slot[w][lane + 64] : 0ull;
-                bitonic128_desc(v0, v1, lane);
-                v = v0;
+                const uint64_t v0 = lane < C ? slot[w][lane] : 0ull;
+                if (C <= 64) {
+                    v = sort64_desc(v0, lane);
+                } else {
+                    const uint64_t v1 = lane + 64 < C ? slot[w][lane + 64] : 0ull;
+                    v = top64_of_128(v0, v1, lane);
+                }
                 done = true;
             }
         }
@@ -264,7 +325,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        v = bitonic64_desc(lane < kk ? slot[w][lane] : 0ull, lane);
+        v = sort64_desc(lane < kk ? slot[w][lane] : 0ull, lane);
     }
 
     if (lane < a.k) {
