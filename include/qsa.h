@@ -132,10 +132,12 @@ qsa_status qsa_select_topk(const float *scores, int64_t ld_s, int64_t rows, int3
  * given), score (full blocks + tail), select.  The batch loop is folded into
  * the launch grids; with q_chunk > 0 the host walks the queries in chunks of
  * q_chunk so that the score workspace holds only G*q_chunk rows.
- *   q32       device fp32 queries (layout of q16, same q_tok_stride) or NULL
+ *   q32       device fp32 queries (layout of q16, same q_tok_stride), 4-byte
+ *             aligned, or NULL
  *   q16       device fp16 bits: the input when q32 == NULL, else a workspace
- *             that receives the converted queries (every element of
- *             [0, (nq-1)*q_tok_stride + G*H*D) is written)
+ *             that receives the converted queries: exactly the G*H*D
+ *             elements of each of the nq token rows are written (elements
+ *             between rows, when q_tok_stride > G*H*D, are not touched)
  *   scores_ws device fp32 [G*qc][ld_s] workspace, qc = q_chunk > 0 ?
  *             min(q_chunk, nq) : nq; row g*qc + t' holds the scores of query
  *             t0 + t' of the chunk being selected

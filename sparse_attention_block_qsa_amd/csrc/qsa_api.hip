@@ -154,8 +154,10 @@ qsa_status qsa_select_phase(const float *q32, uint16_t *q16, int64_t q_tok_strid
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
 
+    // the conversion writes exactly the token rows (G*H*D elements each)
     if (q32) {
-        hipError_t e = qsa::launch_convert(q32, q16, qext, s);
+        hipError_t e = qsa::launch_convert_rows(q32, q16, nq, static_cast<int64_t>(G) * H * D,
+                                                q_tok_stride, s);
         if (e != hipSuccess) return QSA_ERR_HIP;
     }
     for (int64_t t0 = 0; t0 < nq; t0 += qc) {

@@ -1,23 +1,12 @@
 // qsa_convert.hip -- fp32 -> fp16 conversion of the query activations, the
 // "fp16 conversion" stage of the QSA select phase (Strata pull request #228,
-// part 1, paragraph after the bench table).  HBM-bound streaming kernel:
-// 32 bytes in, 16 bytes out per lane per iteration, grid-stride.
+// part 1, paragraph after the bench table).  HBM-bound streaming kernels:
+// 32 bytes in, 16 bytes out per lane per iteration, grid-stride; the phase
+// converts exactly the token rows of a strided query tensor.
 #include "qsa_internal.h"
 
 namespace qsa {
 namespace {
-
-// Round to nearest even.  v_cvt_f16_f32 rounds by the MODE register, which
-// is round-to-nearest-even for compute kernels, keeps fp16 subnormals and
-// overflows to infinity.  NaN is rewritten explicitly so its bits are
-// defined: quiet, with the sign and the top 10 fraction bits of the input.
-__device__ __forceinline__ uint32_t f16_rne(float x) {
-    uint32_t u = __builtin_bit_cast(uint32_t, x);
-    uint32_t h = __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        h = ((u >> 16) & 0x8000u) | 0x7e00u | ((u >> 13) & 0x3ffu);
-    return h;
-}
 
 __global__ __launch_bounds__(256) void convert_v8_kernel(const float4 *__restrict__ src,
                                                           uint4 *__restrict__ dst, int64_t n8) {
@@ -40,6 +29,19 @@ __global__ __launch_bounds__(256) void convert_scalar_kernel(const float *__rest
     const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += stride)
         dst[i] = static_cast<uint16_t>(f16_rne(src[i]));
+}
+
+// Token rows of a strided query tensor: element e of row r at r * stride + e.
+__global__ __launch_bounds__(256) void convert_rows_kernel(const float *__restrict__ src,
+                                                            uint16_t *__restrict__ dst,
+                                                            int64_t n, int64_t row_len,
+                                                            int64_t stride) {
+    const int64_t step = static_cast<int64_t>(gridDim.x) * 256;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += step) {
+        const int64_t r = i / row_len;
+        const int64_t off = r * stride + (i - r * row_len);
+        dst[off] = static_cast<uint16_t>(f16_rne(src[off]));
+    }
 }
 
 unsigned grid_for(int64_t items) {
@@ -74,6 +76,16 @@ hipError_t launch_convert(const float *src, uint16_t *dst, int64_t n, hipStream_
                                dim3(grid_for(rem)), dim3(256), args, 0, s);
     }
     return hipSuccess;
+}
+
+hipError_t launch_convert_rows(const float *src, uint16_t *dst, int64_t rows, int64_t row_len,
+                               int64_t stride, hipStream_t s) {
+    if (rows <= 0 || row_len <= 0) return hipSuccess;
+    if (stride == row_len) return launch_convert(src, dst, rows * row_len, s);
+    int64_t n = rows * row_len;
+    void *args[] = {&src, &dst, &n, &row_len, &stride};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&convert_rows_kernel),
+                           dim3(grid_for(n)), dim3(256), args, 0, s);
 }
 
 }  // namespace qsa

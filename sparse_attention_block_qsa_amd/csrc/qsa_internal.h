@@ -14,6 +14,19 @@ constexpr int kWaveQueries = 16;
 constexpr int kScoreWaves = 4;
 constexpr int kGroupQueries = kWaveQueries * kScoreWaves;
 
+// fp32 -> fp16 bits, round to nearest even.  v_cvt_f16_f32 rounds by the
+// MODE register, which is round-to-nearest-even for compute kernels, keeps
+// fp16 subnormals and overflows to infinity.  NaN is rewritten explicitly so
+// its bits are defined: quiet, with the sign and the top 10 fraction bits of
+// the input.
+__device__ __forceinline__ uint32_t f16_rne(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    uint32_t h = __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        h = ((u >> 16) & 0x8000u) | 0x7e00u | ((u >> 13) & 0x3ffu);
+    return h;
+}
+
 struct ScoreGeom {
     const uint16_t *q16;
     int64_t qts;          // elements between tokens
@@ -50,5 +63,9 @@ struct TopkGeom {
 hipError_t launch_topk(const TopkGeom &g, hipStream_t s);
 
 hipError_t launch_convert(const float *src, uint16_t *dst, int64_t n, hipStream_t s);
+
+// rows of row_len elements at a stride of stride elements (both arrays)
+hipError_t launch_convert_rows(const float *src, uint16_t *dst, int64_t rows, int64_t row_len,
+                               int64_t stride, hipStream_t s);
 
 }  // namespace qsa

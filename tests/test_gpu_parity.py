@@ -12,6 +12,8 @@ Bars (contract of Strata pull request #228, part 1, and pull request #856):
 """
 from __future__ import annotations
 
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -345,6 +347,64 @@ def test_phase_with_fp32_queries_not_fp16_exact():
     assert np.array_equal(s_gpu[:, cfg.nf].astype(np.float32).view(np.uint32),
                           model.view(np.uint32))
     check_ids(ids.reshape(cfg.rows, cfg.k).cpu().numpy(), s_gpu, ref, cfg.k, "conversion")
+
+
+# G, nq, H, D, n_kv, bs, k, tok_pad, q32 offset in floats.  Padded token rows
+# take the strided conversion kernel, contiguous ones the vector kernel; an
+# offset of one float leaves the fp32 rows only 4-byte aligned.
+PHASE_CONV = [
+    (2, 70, 12, 64, 65 * 64 + 5, 64, 8, 24, 0),    # padded rows, two head passes
+    (2, 70, 12, 64, 65 * 64 + 5, 64, 8, 24, 1),    # padded rows, 4-byte aligned fp32
+    (1, 33, 8, 128, 40, 64, 4, 8, 0),              # only a tail block
+    (3, 129, 5, 128, 100 * 64 + 3, 64, 16, 0, 0),  # contiguous, odd H
+    (1, 40, 8, 128, 10 * 64 + 7, 64, 8, 0, 1),     # contiguous, 4-byte aligned fp32
+]
+
+
+@pytest.mark.parametrize("case", PHASE_CONV,
+                         ids=lambda c: "G{}_nq{}_H{}_D{}_nkv{}_bs{}_k{}_pad{}_off{}".format(*c))
+def test_phase_conversion_paths(case):
+    """The phase's conversion of fp32 queries gives the oracle's fp16 bits,
+    writes exactly the token rows of the fp16 workspace (padding between rows
+    untouched), and the scores, tail and ids follow from the fp32 inputs."""
+    G, nq, H, D, n_kv, bs, k, tok_pad, off = case
+    cfg = qi.Config("conv_path", G, nq, H, D, n_kv, bs, k, "normal", 4000 + nq)
+    w = qi.conversion_fixture(cfg, seed=4000 + nq)
+    row = G * H * D + tok_pad
+    # fp32 rows at the requested offset from a 256-byte aligned allocation
+    q32_buf = torch.full((off + nq * row,), float("nan"), dtype=torch.float32, device=dev())
+    q32_rows = q32_buf[off:].view(nq, row)
+    q32_rows[:, :G * H * D] = torch.from_numpy(w.q32.reshape(nq, -1)).to(dev())
+    # fp16 workspace inside a canary-filled allocation (a signalling-NaN
+    # pattern the conversion never produces: it quietens every NaN)
+    sent16, pad16 = 0x7D5B, 4096
+    q16_flat = torch.full((pad16 + nq * row + pad16,), sent16, dtype=torch.int16, device=dev())
+    q16_view = q16_flat[pad16:pad16 + nq * row].view(nq, row)
+    kd = k_dev(w.kblk)
+    ld = -(-(cfg.nb + 1) // 32) * 32
+    scores = torch.full((G, nq, ld), float("nan"), dtype=torch.float32, device=dev())
+    ids = torch.full((G, nq, k), 123, dtype=torch.int32, device=dev())
+    st = qsa.lib.qsa_select_phase(
+        ctypes.c_void_p(q32_rows.data_ptr()), ctypes.c_void_p(q16_view.data_ptr()), row,
+        ctypes.c_void_p(kd.data_ptr()), kd.stride(0), ctypes.c_void_p(scores.data_ptr()), ld,
+        ctypes.c_void_p(ids.data_ptr()), k, None, G, nq, H, D, n_kv, bs, k, 0, None)
+    torch.cuda.synchronize()
+    assert st == 0, qsa.status_string(st)
+    flat = q16_flat.cpu().numpy()
+    inside = flat[pad16:pad16 + nq * row].reshape(nq, row)
+    assert np.all(flat[:pad16] == sent16) and np.all(flat[pad16 + nq * row:] == sent16)
+    assert np.all(inside[:, G * H * D:] == sent16), "fp16 workspace written between token rows"
+    got16 = inside[:, :G * H * D].view(np.uint16).reshape(nq, G, H, D)
+    want16 = oracle.convert_f32_f16(w.q32)
+    assert np.array_equal(got16, want16), "converted queries differ from the oracle's rounding"
+    s_gpu = scores[:, :, :cfg.nb].reshape(cfg.rows, cfg.nb).cpu().numpy().astype(np.float64)
+    ref = oracle.scores(w.q32, w.kblk, cfg.nb)
+    check_bound(s_gpu, ref, "phase conversion")
+    if cfg.nb > cfg.nf:
+        model = oracle.block_model_f32(want16, w.kblk, cfg.nf)
+        assert np.array_equal(s_gpu[:, cfg.nf].astype(np.float32).view(np.uint32),
+                              model.view(np.uint32))
+    check_ids(ids.reshape(cfg.rows, k).cpu().numpy(), s_gpu, ref, k, "phase conversion")
 
 
 @pytest.mark.parametrize("q_chunk", [0, 37, 64, 1000])
