@@ -69,6 +69,11 @@ __device__ __forceinline__ uint32_t xcd_logical_id(uint32_t bid, uint32_t nblk) 
     return x * q + (x < r ? x : r) + idx;
 }
 
+// Cache policy of the score stores: non-temporal.  The scores are written
+// once and read back by the selector long after they would have left the
+// caches, so they stream to memory without displacing the queries and keys.
+constexpr int kStoreNT = 2;
+
 // relu on fp32 bits: as signed integers, negative floats (and -0) are < 0 and
 // non-negative floats keep their order, so max(bits, 0) is relu(x) with -0
 // mapped to +0.  One v_max_i32, no NaN canonicalisation.
@@ -90,6 +95,7 @@ void score_full_kernel(ScoreArgs a) {
     // already published (so its first fragments can be read before the
     // barrier) and tile t+2 is being staged.
     __shared__ uint4 kbuf[3][TILE_U4];
+    __shared__ uint4 ktail[TAIL ? CHUNKS : 1];   // the partial block's key
 
     const uint32_t L = xcd_logical_id(blockIdx.x, gridDim.x);
     const int split = static_cast<int>(L % a.n_splits);
@@ -167,8 +173,12 @@ void score_full_kernel(ScoreArgs a) {
         srow_base, 0, BUF ? static_cast<int>(static_cast<int64_t>(a.nq) * a.ld_s * 4) : 0,
         0x00020000 /* 32-bit elements, raw */);
 
-    // prologue: tiles tb and tb+1 into slots 0 and 1
+    // prologue: tiles tb and tb+1 into slots 0 and 1 (and the tail key)
     {
+        if constexpr (TAIL) {
+            if (split == a.n_splits - 1 && threadIdx.x < CHUNKS)
+                ktail[threadIdx.x] = reinterpret_cast<const uint4 *>(kg + a.nf * D)[threadIdx.x];
+        }
         const uint4 x0 = kload(tb, bb0, off0), y0 = kload(tb + 1, bb0, off0);
         kbuf[0][u0] = x0;
         kbuf[1][u0] = y0;
@@ -210,6 +220,11 @@ void score_full_kernel(ScoreArgs a) {
 
         // MFMA phase: K-step outer so the NP MFMAs sharing a B fragment are
         // independent; fragment s+2 is read from LDS one step ahead of use.
+        // The wave raises its issue priority for the phase: of the two waves
+        // on a SIMD, the one with MFMAs to issue goes first, and the other
+        // runs its epilogue in the gaps (a lasting ping-pong instead of both
+        // waves reaching their epilogues together).
+        __builtin_amdgcn_s_setprio(1);
         const uint4 *kcur = &kbuf[slot][l];
         floatx16 acc[NP];
         half8 kf = kf0, kn = kf1;
@@ -235,6 +250,8 @@ void score_full_kernel(ScoreArgs a) {
             if (s + 4 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
 
+        __builtin_amdgcn_s_setprio(0);
+
         // the next tile was published an iteration ago: fetch its first two
         // fragments now, then stage tile+2 into the free slot
         kf0 = __builtin_bit_cast(half8, kbuf[nslot][l]);
@@ -254,9 +271,10 @@ void score_full_kernel(ScoreArgs a) {
         for (int u = 0; u < 8; ++u) {
             if constexpr (BUF) {
                 __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, tot[u]), rs,
-                                                      static_cast<int>(rowoff[u] + coloff), 0, 0);
+                                                      static_cast<int>(rowoff[u] + coloff), 0,
+                                                      kStoreNT);
             } else if (rowel[u] >= 0 && coloff != kOut) {
-                srow_base[rowel[u] + bcol] = tot[u];
+                __builtin_nontemporal_store(tot[u], srow_base + rowel[u] + bcol);
             }
         }
         __syncthreads();
@@ -274,10 +292,9 @@ void score_full_kernel(ScoreArgs a) {
         // runs the chain of query t_base + l%16, head 4c + l/16 (in the pass).
         if (split == a.n_splits - 1) {   // uniform over the workgroup
             constexpr int NPC = (NP + 1) / 2;
-            const uint4 *kt = reinterpret_cast<const uint4 *>(kg + a.nf * D);
             uint4 kc[CHUNKS];
             #pragma unroll
-            for (int c = 0; c < CHUNKS; ++c) kc[c] = kt[c];
+            for (int c = 0; c < CHUNKS; ++c) kc[c] = ktail[c];   // staged at the prologue
             float r[NPC];
             #pragma unroll
             for (int c = 0; c < NPC; ++c) {
