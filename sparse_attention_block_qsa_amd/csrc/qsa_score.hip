@@ -386,12 +386,11 @@ hipError_t launch_score_full(const ScoreGeom &geo, bool tail, hipStream_t s) {
     const int64_t n_qgroups = (geo.nq + kGroupQueries - 1) / kGroupQueries;
     const int64_t base = static_cast<int64_t>(geo.G) * n_qgroups;
     // Splits along the block axis only when the query groups alone cannot
-    // fill the 256 CUs (two resident workgroups each); keep >= 2 tiles per
-    // split so the K-tile pipeline has something to overlap.
+    // fill the 256 CUs (two resident workgroups each).
     int64_t splits = 1;
     if (base < 512) {
         splits = (512 + base - 1) / base;
-        const int64_t max_splits = (n_tiles + 1) / 2;
+        const int64_t max_splits = n_tiles;
         if (splits > max_splits) splits = max_splits;
         if (splits < 1) splits = 1;
     }

@@ -174,12 +174,12 @@ __device__ __forceinline__ int wave_excl_scan(int x, int lane, int *total) {
 // id order.
 template <int NPL>
 __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
-    __shared__ uint64_t slot[4][128];
+    __shared__ uint64_t slot[4][128];   // one per wave of the workgroup (at most four)
     // the wave index is uniform over the wave: say so, so that the row's
     // addresses and buffer descriptor live in scalar registers
     const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
-    const int64_t R = static_cast<int64_t>(blockIdx.x) * 4 + w;
+    const int64_t R = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + w;
     if (R >= a.total_rows) return;               // whole wave; no block barriers below
     int64_t grp = 0, t = R;
     if (a.rows_per_group != a.total_rows) {   // grouped rows (the phase's chunks)
@@ -367,7 +367,10 @@ topk_fn pick(int nb, int *npl_out) {
 hipError_t launch_topk(const TopkGeom &geo, hipStream_t s) {
     const int64_t total = geo.n_groups * geo.rows_per_group;
     if (total <= 0 || geo.k <= 0) return hipSuccess;
-    const int64_t blocks = (total + 3) / 4;
+    // One row per wave.  Few rows: one wave per workgroup, so that the rows
+    // spread over all CUs; many rows: four per workgroup.
+    const int wpb = total < 4096 ? 1 : 4;
+    const int64_t blocks = (total + wpb - 1) / wpb;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     TopkArgs a{geo.scores, geo.ld_s, geo.ids, geo.ld_ids, geo.vals, total,
                geo.rows_per_group, geo.src_group_rows, geo.dst_group_rows, geo.dst_row0,
@@ -376,7 +379,7 @@ hipError_t launch_topk(const TopkGeom &geo, hipStream_t s) {
     topk_fn fn = pick(geo.nb, &npl);
     void *args[] = {&a};
     return hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(static_cast<unsigned>(blocks)),
-                           dim3(256), args, 0, s);
+                           dim3(64 * wpb), args, 0, s);
 }
 
 }  // namespace qsa
