@@ -175,6 +175,9 @@ __device__ __forceinline__ int wave_excl_scan(int x, int lane, int *total) {
 template <int NPL>
 __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     __shared__ uint64_t slot[4][128];   // one per wave of the workgroup (at most four)
+    // the row's values, for the candidates' second look (lane l keeps its own
+    // column values at [j*64 + l]: only the writing lane reads them back)
+    __shared__ uint32_t stash[NPL > 0 ? 4 : 1][NPL > 0 ? 64 * NPL : 1];
     // the wave index is uniform over the wave: say so, so that the row's
     // addresses and buffer descriptor live in scalar registers
     const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -208,6 +211,8 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
             const uint32_t x = __builtin_amdgcn_raw_buffer_load_b32(rs, (j * 64 + lane) * 4, 0, 0);
             xr[j] = lane < nb - 64 * j ? x : kPad;
         }
+        #pragma unroll
+        for (int j = 0; j < NPL; ++j) stash[w][j * 64 + lane] = xr[j];
     }
     auto key = [&](int j) -> uint32_t {
         const int id = j * 64 + lane;
@@ -256,7 +261,8 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
             int off = wave_excl_scan(cnt, lane, &C);
             if (C >= kk && C <= 128) {
                 // 4. compact the candidates' exact composites into LDS: up to
-                //    four per lane per round, their reloads issued together
+                //    four per lane per round, their values read back from the
+                //    lane's own stash
                 uint64_t more = ballot(cnt > 0);
                 while (more) {
                     int id4[4];
@@ -271,7 +277,8 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
                     }
                     float x4[4];
                     #pragma unroll
-                    for (int r = 0; r < 4; ++r) x4[r] = id4[r] >= 0 ? srow[id4[r]] : 0.0f;
+                    for (int r = 0; r < 4; ++r)
+                        x4[r] = id4[r] >= 0 ? __builtin_bit_cast(float, stash[w][id4[r]]) : 0.0f;
                     #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         if (id4[r] >= 0) slot[w][off++] = composite(order_key(x4[r]), id4[r]);
