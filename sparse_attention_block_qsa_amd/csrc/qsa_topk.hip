@@ -39,15 +39,27 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
-// The value of lane ^ M, without LDS traffic where the hardware has a lane
-// permutation for it: DPP quad permutes (xor 1, 2, 3), DPP row mirrors
-// (xor 7 within 8 lanes, xor 15 within 16), v_permlane16/32_swap (xor 16,
-// xor 32: swapping a register with itself exchanges the two row halves),
-// ds_swizzle's xor mode for the other masks below 32, and xor 63 as
-// xor 31 followed by xor 32.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+
+// The value of lane ^ M through lane permutations of the VALU: DPP quad
+// permutes (xor 1, 2, 3), DPP row mirrors (xor 7 within 8 lanes, xor 15
+// within 16), DPP row rotates (xor 8 = rotate by 8; xor 4 = rotate by 4 or
+// by 12, picked by lane bit 2), v_permlane16/32_swap (xor 16, xor 32:
+// swapping a register with itself exchanges the two row halves), and the
+// compositions xor 31 = xor 15 then xor 16, xor 63 = xor 31 then xor 32.
 template <int M>
 __device__ __forceinline__ uint32_t xor_lane(uint32_t v, int lane) {
-    if constexpr (M == 1) {
+    if constexpr (M == 4) {
+        const uint32_t a = dpp_mov<0x124>(v), b = dpp_mov<0x12C>(v);   // row_ror:4, row_ror:12
+        return (lane & 4) ? a : b;
+    } else if constexpr (M == 8) {
+        return dpp_mov<0x128>(v);                                       // row_ror:8
+    } else if constexpr (M == 31) {
+        return xor_lane<16>(dpp_mov<0x140>(v), lane);                  // row_mirror, then xor 16
+    } else if constexpr (M == 1) {
         return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, false));
     } else if constexpr (M == 2) {
         return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, false));
@@ -63,8 +75,6 @@ __device__ __forceinline__ uint32_t xor_lane(uint32_t v, int lane) {
     } else if constexpr (M == 32) {
         const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
         return (lane & 32) ? r[0] : r[1];
-    } else if constexpr (M < 32) {
-        return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), (M << 10) | 0x1F));
     } else {
         static_assert(M == 63, "unsupported lane mask");
         return xor_lane<32>(xor_lane<31>(v, lane), lane);
@@ -147,16 +157,26 @@ __device__ __forceinline__ uint64_t composite(uint32_t key, int id) {
     return (static_cast<uint64_t>(key) << 32) | (0xffffffffu - static_cast<uint32_t>(id));
 }
 
-// Exclusive prefix sum over the wave.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_or_zero(uint32_t v) {
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Exclusive prefix sum over the wave with DPP: shifts by 1, 2, 4, 8 within
+// each row of 16 lanes (lanes without a source add 0), then row 1 and 3 add
+// the last lane of the row below (row_bcast:15), rows 2 and 3 add lane 31
+// (row_bcast:31).
 __device__ __forceinline__ int wave_excl_scan(int x, int lane, int *total) {
-    int incl = x;
-    #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(incl, d);
-        if (lane >= d) incl += y;
-    }
-    *total = __shfl(incl, 63);
-    return incl - x;
+    uint32_t v = static_cast<uint32_t>(x);
+    v += dpp_or_zero<0x111, 0xF>(v);   // row_shr:1
+    v += dpp_or_zero<0x112, 0xF>(v);   // row_shr:2
+    v += dpp_or_zero<0x114, 0xF>(v);   // row_shr:4
+    v += dpp_or_zero<0x118, 0xF>(v);   // row_shr:8
+    v += dpp_or_zero<0x142, 0xA>(v);   // row_bcast:15 into rows 1, 3
+    v += dpp_or_zero<0x143, 0xC>(v);   // row_bcast:31 into rows 2, 3
+    *total = __builtin_amdgcn_readlane(static_cast<int>(v), 63);
+    return static_cast<int>(v) - x;
 }
 
 // NPL > 0: the row's values held in registers (row length <= 64*NPL).
@@ -340,7 +360,8 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
         float val = -__builtin_inff();
         if (lane < kk) {
             id = static_cast<int32_t>(0xffffffffu - static_cast<uint32_t>(v));
-            val = srow[id];
+            if constexpr (NPL > 0) val = __builtin_bit_cast(float, stash[w][id]);
+            else val = srow[id];
         }
         a.ids[drow * a.ld_ids + lane] = id;
         if (a.vals) a.vals[drow * a.ld_ids + lane] = val;
