@@ -139,8 +139,9 @@ qsa_status qsa_select_topk(const float *scores, int64_t ld_s, int64_t rows, int3
  *             elements of each of the nq token rows are written (elements
  *             between rows, when q_tok_stride > G*H*D, are not touched)
  *   scores_ws device fp32 [G*qc][ld_s] workspace, qc = q_chunk > 0 ?
- *             min(q_chunk, nq) : nq; row g*qc + t' holds the scores of query
- *             t0 + t' of the chunk being selected
+ *             min(q_chunk, nq) : nq; for the chunk of n <= qc queries starting
+ *             at query t0, row g*n + t' holds the scores of query t0 + t'
+ *             (after the call: those of the last chunk)
  *   ids, vals as qsa_select_topk with rows = G*nq (vals may be NULL)
  *   other arguments as qsa_block_scores / qsa_select_topk.
  * Workspaces must not overlap the inputs or outputs.  Errors as the three

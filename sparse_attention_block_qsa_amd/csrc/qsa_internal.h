@@ -39,8 +39,9 @@ struct ScoreGeom {
 };
 
 // Full-block MFMA scorer over blocks [0, nf).  Launches one kernel per head
-// pass of up to eight heads.  With tail (requires nf > 0) the same launches
-// also score block nf in the fixed order of the tail model.
+// pass of up to eight heads.  With tail (requires nf > 0) block nf is scored
+// too, in the fixed order of the tail model: inside the same launches for
+// many query rows, by a standalone tail launch for few.
 hipError_t launch_score_full(const ScoreGeom &g, bool tail, hipStream_t s);
 
 // Fixed-order scorer of the single block b_tail, standalone (used when there

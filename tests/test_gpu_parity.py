@@ -236,6 +236,11 @@ GEOMS = [
     (3, 129, 5, 128, 63, 64, 0, 1),
     (1, 1000, 1, 64, 1, 2, 0, 0),
     (4, 4200, 8, 128, 40, 64, 0, 0),
+    # enough query rows (>= 256 groups of 64 over the KV heads) for the wide
+    # scorer, which scores the tail block in the same launch
+    (4, 4096, 8, 128, 40 * 64 + 5, 64, 0, 0),
+    (2, 8192, 12, 64, 20 * 64 + 9, 64, 8, 1),     # two head passes, padded rows
+    (4, 4100, 5, 128, 33 * 64, 64, 0, 0),         # ragged query groups, odd H
 ]
 
 
@@ -439,11 +444,64 @@ def test_phase_ids_write_set():
     assert ids.outside_intact(m) and ids.written_all(m)
 
 
+def test_wide_and_narrow_scorers_agree_bitwise():
+    """The whole query set takes the wide scorer (4096 rows per KV head),
+    chunks of 1000 take the narrow one; both add the relu'd heads in the same
+    order, so the chunked phase reproduces the whole phase bit for bit
+    (scores of the last chunk, ids and values of every row)."""
+    cfg = qi.Config("wn", 4, 4096, 8, 128, 30 * 64 + 11, 64, 16, "normal", 321)
+    w = qi.make(cfg)
+    q32 = torch.from_numpy(w.q32).to(dev())
+    kd = k_dev(w.kblk)
+    ws0 = qsa.PhaseWorkspace(cfg.nq, cfg.G, cfg.H, cfg.D, cfg.n_kv, cfg.bs, cfg.k, dev(),
+                             with_vals=True)
+    ids0, vals0 = qsa.select_phase(q32, kd, cfg.n_kv, cfg.bs, cfg.k, ws0)
+    wsc = qsa.PhaseWorkspace(cfg.nq, cfg.G, cfg.H, cfg.D, cfg.n_kv, cfg.bs, cfg.k, dev(),
+                             q_chunk=1000, with_vals=True)
+    idsc, valsc = qsa.select_phase(q32, kd, cfg.n_kv, cfg.bs, cfg.k, wsc)
+    torch.cuda.synchronize()
+    assert torch.equal(ids0, idsc)
+    assert torch.equal(vals0.view(torch.int32), valsc.view(torch.int32))
+    # the chunked workspace holds the last chunk, queries 4000..4095, as
+    # G x 96 consecutive rows
+    n = cfg.nq - 4000
+    last = wsc.scores.reshape(-1, wsc.ld_s)[:cfg.G * n].reshape(cfg.G, n, wsc.ld_s)[:, :, :cfg.nb]
+    assert torch.equal(last.view(torch.int32), ws0.scores[:, 4000:, :cfg.nb].view(torch.int32))
+    s0 = ws0.scores[:, :, :cfg.nb].reshape(cfg.rows, cfg.nb).cpu().numpy().astype(np.float64)
+    model = oracle.block_model_f32(w.q16, w.kblk, cfg.nf)
+    assert np.array_equal(s0[:, cfg.nf].astype(np.float32).view(np.uint32), model.view(np.uint32))
+
+
+def test_wide_scorer_global_store_path():
+    """The wide scorer's plain global-store path (a KV head's score region of
+    2^30 bytes or more), with two head passes and the tail in the same
+    launches: write set and bound."""
+    cfg = qi.Config("wide_g", 4, 4096, 12, 128, 9 * 64 + 5, 64, 8, "normal", 98)
+    w = qi.make(cfg)
+    ld = 1 << 16                                   # 4096 rows x 256 KiB: 1 GiB per KV head
+    sent = int(SENTINEL)
+    out = torch.full((cfg.G, cfg.nq, ld), sent, dtype=torch.int32, device=dev())
+    qsa.block_scores(q_dev(w.q16), k_dev(w.kblk), cfg.n_kv, cfg.bs, out=out.view(torch.float32))
+    torch.cuda.synchronize()
+    head = out[:, :, :cfg.nb + 256]
+    assert torch.all(head[:, :, cfg.nb:] == sent), "write past nb"
+    assert torch.all(out[:, :, ld - 256:] == sent)
+    assert not torch.any(head[:, :, :cfg.nb] == sent), "cell not written"
+    s_gpu = head[:, :, :cfg.nb].view(torch.float32).reshape(cfg.rows, cfg.nb).cpu().numpy()
+    del out, head
+    torch.cuda.empty_cache()
+    ref = oracle.scores(w.q16, w.kblk, cfg.nb)
+    check_bound(s_gpu.astype(np.float64), ref, "wide scorer, global stores")
+    model = oracle.block_model_f32(w.q16, w.kblk, cfg.nf)
+    assert np.array_equal(s_gpu[:, cfg.nf].view(np.uint32), model.view(np.uint32))
+
+
 def test_wide_rows_use_global_store_path():
     """A score region past 2^30 bytes per KV head takes the scorer's plain
     global-store path (the buffer-store path needs 30-bit offsets); it must
     give the same write set and the same bound.  H = 12 also exercises the
-    accumulating second head pass on that path."""
+    accumulating second head pass on that path (here in the narrow scorer,
+    few query rows)."""
     cfg = qi.Config("wide", 1, 70, 12, 128, 65 * 64 + 5, 64, 8, "normal", 99)
     w = qi.make(cfg)
     ld = 1 << 24                                   # 64 MiB per row: 4.4 GiB region
