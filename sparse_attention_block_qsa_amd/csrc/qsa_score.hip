@@ -111,27 +111,6 @@ void score_full_kernel(ScoreArgs a) {
     const int l = threadIdx.x & 63;
     const int t_base = qg * kGroupQueries + w * kWaveQueries;
 
-    // ---- stationary query fragments --------------------------------------
-    half8 qa[NP][KS];
-    {
-        const int tq = l & 15, hh = (l >> 4) & 1, kc = l >> 5;
-        const int t = t_base + tq;
-        #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const int h = 2 * p + hh;
-            const bool valid = (t < a.nq) && (h < a.nh);
-            const uint16_t *src = a.q16 + static_cast<int64_t>(valid ? t : 0) * a.qts +
-                                  static_cast<int64_t>(g * a.H + a.h0 + (valid ? h : 0)) * D +
-                                  8 * kc;
-            #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                half8 v = {};
-                if (valid) v = *reinterpret_cast<const half8 *>(src + 16 * s);
-                qa[p][s] = v;
-            }
-        }
-    }
-
     // ---- K tile staging ----------------------------------------------------
     // LDS index u = threadIdx.x + 256*c is chunk-major (u = chunk*32 + block),
     // which is also the MFMA B-fragment order: lane l of K-step s reads
@@ -147,6 +126,50 @@ void score_full_kernel(ScoreArgs a) {
         const int64_t b = min(static_cast<int64_t>(min(tile, te - 1)) * kTileBlocks + bb, last);
         return *reinterpret_cast<const uint4 *>(kg + b * D + off);
     };
+
+    // prologue loads: tiles tb and tb+1 (and the tail key), published below
+    uint4 x0 = kload(tb, bb0, off0), y0 = kload(tb + 1, bb0, off0);
+    uint4 x1 = make_uint4(0, 0, 0, 0), y1 = make_uint4(0, 0, 0, 0);
+    if constexpr (LOADS == 2) {
+        x1 = kload(tb, bb1, off1);
+        y1 = kload(tb + 1, bb1, off1);
+    }
+    uint4 kt = make_uint4(0, 0, 0, 0);
+    const bool tail_wg = TAIL && split == a.n_splits - 1;   // uniform
+    if (tail_wg && threadIdx.x < CHUNKS)
+        kt = reinterpret_cast<const uint4 *>(kg + a.nf * D)[threadIdx.x];
+
+    // ---- stationary query fragments --------------------------------------
+    // Issued after the first K tiles' loads and in K-step order, so that the
+    // K tiles are published while the queries are still in flight and the
+    // first MFMAs wait only for the fragments of their own K-step.  Every
+    // lane loads from an in-bounds address, without branches.  Rows of
+    // queries past nq read query 0: they only feed MFMA rows that are never
+    // stored.  A head past the pass (only the second head of the last pair,
+    // when nh is odd) is zeroed, since it would enter the head sum.
+    half8 qa[NP][KS];
+    {
+        const int tq = l & 15, hh = (l >> 4) & 1, kc = l >> 5;
+        const int t = t_base + tq;
+        const int64_t trow = static_cast<int64_t>(t < a.nq ? t : 0) * a.qts;
+        const uint16_t *src[NP];
+        #pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int h = 2 * p + hh;
+            src[p] = a.q16 + trow + static_cast<int64_t>(g * a.H + a.h0 + (h < a.nh ? h : 0)) * D +
+                     8 * kc;
+        }
+        #pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            #pragma unroll
+            for (int p = 0; p < NP; ++p) qa[p][s] = *reinterpret_cast<const half8 *>(src[p] + 16 * s);
+        }
+        if (2 * NP > a.nh) {   // uniform
+            #pragma unroll
+            for (int s = 0; s < KS; ++s)
+                if (hh) qa[NP - 1][s] = half8{};
+        }
+    }
 
     // ---- output addressing -------------------------------------------------
     // Lane l holds, for register u (0..7), query t_base + 8*(u/4) + 4*(l/32)
@@ -175,15 +198,10 @@ void score_full_kernel(ScoreArgs a) {
 
     // prologue: tiles tb and tb+1 into slots 0 and 1 (and the tail key)
     {
-        if constexpr (TAIL) {
-            if (split == a.n_splits - 1 && threadIdx.x < CHUNKS)
-                ktail[threadIdx.x] = reinterpret_cast<const uint4 *>(kg + a.nf * D)[threadIdx.x];
-        }
-        const uint4 x0 = kload(tb, bb0, off0), y0 = kload(tb + 1, bb0, off0);
+        if (tail_wg && threadIdx.x < CHUNKS) ktail[threadIdx.x] = kt;
         kbuf[0][u0] = x0;
         kbuf[1][u0] = y0;
         if constexpr (LOADS == 2) {
-            const uint4 x1 = kload(tb, bb1, off1), y1 = kload(tb + 1, bb1, off1);
             kbuf[0][u1] = x1;
             kbuf[1][u1] = y1;
         }
@@ -293,7 +311,7 @@ void score_full_kernel(ScoreArgs a) {
         // of head pairs p0 = 2c and p1 = 2c+1 gives lanes 0-31 whole 16-wide
         // channel runs of pair p0 and lanes 32-63 those of pair p1, so lane l
         // runs the chain of query t_base + l%16, head 4c + l/16 (in the pass).
-        if (split == a.n_splits - 1) {   // uniform over the workgroup
+        if (tail_wg) {   // uniform over the workgroup
             constexpr int NPC = (NP + 1) / 2;
             uint4 kc[CHUNKS];
             #pragma unroll
