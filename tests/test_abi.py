@@ -26,7 +26,11 @@ def declared_functions():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):   # CPU container only: hipcc cross-compiles gfx950
-        from sparse_attention_block_qsa_amd import build_lib
+        import importlib.util  # by path: the package __init__ needs the built library
+        spec = importlib.util.spec_from_file_location(
+            "_qsa_build_lib", os.path.join(ROOT, "sparse_attention_block_qsa_amd", "build_lib.py"))
+        build_lib = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(build_lib)
         build_lib.build()
     L = ctypes.CDLL(LIB)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
