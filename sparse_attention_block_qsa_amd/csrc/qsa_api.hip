@@ -79,7 +79,9 @@ hipError_t run_scores(const uint16_t *q16, int64_t qts, const uint16_t *kblk, in
     ScoreGeom geo{q16, qts, kblk, khs, scores, ld_s, G, nq, H, D, c.nf};
     const bool tail = c.nb > c.nf;
     if (c.nf > 0) return qsa::launch_score_full(geo, tail, s);
-    return tail ? qsa::launch_tail(geo, c.nf, s) : hipSuccess;
+    if (!tail) return hipSuccess;
+    return qsa::small_rows(geo) ? qsa::launch_score_small(geo, true, s)
+                                : qsa::launch_tail(geo, c.nf, s);
 }
 
 }  // namespace

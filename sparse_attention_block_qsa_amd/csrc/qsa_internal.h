@@ -38,11 +38,19 @@ struct ScoreGeom {
     int64_t nf;           // full blocks
 };
 
-// Full-block MFMA scorer over blocks [0, nf).  Launches one kernel per head
-// pass of up to eight heads.  With tail (requires nf > 0) block nf is scored
-// too, in the fixed order of the tail model: inside the same launches for
-// many query rows, by a standalone tail launch for few.
+// Full-block MFMA scorer over blocks [0, nf).  Many query rows: one kernel
+// per head pass of up to eight heads; few: the small scorer.  With tail
+// (requires nf > 0) block nf is scored too, in the fixed order of the tail
+// model, inside the same launches.
 hipError_t launch_score_full(const ScoreGeom &g, bool tail, hipStream_t s);
+
+// Few query rows (fewer than 256 groups of 64 over the KV heads): the
+// scorer of qsa_small.hip, latency-bound shapes.
+bool small_rows(const ScoreGeom &g);
+
+// The small scorer: blocks [0, nf) and, with tail, the partial block nf in
+// the fixed order of the tail model (also when nf == 0).
+hipError_t launch_score_small(const ScoreGeom &g, bool tail, hipStream_t s);
 
 // Fixed-order scorer of the single block b_tail, standalone (used when there
 // is no full block to share the query reads with).

@@ -279,7 +279,7 @@ void score_full_kernel(ScoreArgs a) {
 
         // epilogue: relu per head; the two heads of a pair are added, then
         // the pair sums in ascending pair order (the head-sum order shared
-        // with the narrow kernel below)
+        // with the small scorer in qsa_small.hip)
         #pragma unroll
         for (int p = 0; p < NP; ++p) {
             #pragma unroll
@@ -366,164 +366,6 @@ void score_full_kernel(ScoreArgs a) {
     }
 }
 
-// Narrow variant for few query rows (the query groups of the kernel above
-// cannot fill the GPU): a workgroup owns 16 queries, and its four waves split
-// the head pairs instead of the queries: wave w holds pair w only (8 KiB of
-// queries at D = 128 instead of 32 KiB), so a workgroup's start-up load is a
-// quarter and four times as many workgroups share the work.  The waves share
-// the K tiles through the same LDS ring; each wave's pair sums go through LDS
-// and every register u of the result is finished by one wave, adding the
-// pair sums in ascending pair order: the same head-sum order, hence the same
-// bits, as score_full_kernel.  No tail here (a standalone launch does it).
-template <int D, bool ACCUM, bool BUF>
-__global__ __launch_bounds__(256) void score_narrow_kernel(ScoreArgs a) {
-    constexpr int KS = D / 16;
-    constexpr int CHUNKS = D / 8;
-    constexpr int TILE_U4 = CHUNKS * kTileBlocks;
-    constexpr int LOADS = TILE_U4 / 256;
-    static_assert(TILE_U4 % 256 == 0 && (LOADS == 1 || LOADS == 2), "D must be 64 or 128");
-
-    __shared__ uint4 kbuf[3][TILE_U4];
-    __shared__ float part[2][kScoreWaves][8][64];   // per tile parity: pair sums of each wave
-
-    const uint32_t L = xcd_logical_id(blockIdx.x, gridDim.x);
-    const int split = static_cast<int>(L % a.n_splits);
-    const uint32_t rest = L / a.n_splits;
-    const int qg = static_cast<int>(rest % a.n_qgroups);
-    const int g = static_cast<int>(rest / a.n_qgroups);
-    const int tb = split * a.tiles_per_split;
-    const int te = min(a.n_tiles, tb + a.tiles_per_split);
-    if (tb >= te) return;   // uniform over the workgroup
-
-    const int w = threadIdx.x >> 6;
-    const int l = threadIdx.x & 63;
-    const int t_base = qg * kWaveQueries;
-
-    half8 qa[KS];   // head pair w of the pass
-    {
-        const int tq = l & 15, hh = (l >> 4) & 1, kc = l >> 5;
-        const int t = t_base + tq;
-        const int h = 2 * w + hh;
-        const bool valid = (t < a.nq) && (h < a.nh);
-        const uint16_t *src = a.q16 + static_cast<int64_t>(valid ? t : 0) * a.qts +
-                              static_cast<int64_t>(g * a.H + a.h0 + (valid ? h : 0)) * D + 8 * kc;
-        #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            half8 v = {};
-            if (valid) v = *reinterpret_cast<const half8 *>(src + 16 * s);
-            qa[s] = v;
-        }
-    }
-
-    const uint16_t *kg = a.kblk + static_cast<int64_t>(g) * a.khs;
-    const int u0 = threadIdx.x, u1 = threadIdx.x + 256;
-    const int off0 = 8 * (u0 / kTileBlocks), off1 = 8 * (u1 / kTileBlocks);
-    const int bb0 = u0 % kTileBlocks, bb1 = u1 % kTileBlocks;
-    const int64_t last = a.nf - 1;
-    auto kload = [&](int tile, int bb, int off) {
-        const int64_t b = min(static_cast<int64_t>(min(tile, te - 1)) * kTileBlocks + bb, last);
-        return *reinterpret_cast<const uint4 *>(kg + b * D + off);
-    };
-
-    // this wave finishes registers u = 2w and 2w + 1 of every tile
-    float *srow_base = a.scores + static_cast<int64_t>(g) * a.nq * a.ld_s;
-    const int bl = l & 31;
-    constexpr uint32_t kOut = 0x40000000u;
-    uint32_t rowoff[2];
-    int64_t rowel[2];
-    #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int u = 2 * w + i;
-        const int t = t_base + 8 * (u >> 2) + 4 * (l >> 5) + (u & 3);
-        if constexpr (BUF)
-            rowoff[i] = t < a.nq ? static_cast<uint32_t>(static_cast<int64_t>(t) * a.ld_s * 4) : kOut;
-        else
-            rowel[i] = t < a.nq ? static_cast<int64_t>(t) * a.ld_s : -1;
-    }
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        srow_base, 0, BUF ? static_cast<int>(static_cast<int64_t>(a.nq) * a.ld_s * 4) : 0,
-        0x00020000 /* 32-bit elements, raw */);
-
-    {
-        const uint4 x0 = kload(tb, bb0, off0), y0 = kload(tb + 1, bb0, off0);
-        kbuf[0][u0] = x0;
-        kbuf[1][u0] = y0;
-        if constexpr (LOADS == 2) {
-            const uint4 x1 = kload(tb, bb1, off1), y1 = kload(tb + 1, bb1, off1);
-            kbuf[0][u1] = x1;
-            kbuf[1][u1] = y1;
-        }
-    }
-    __syncthreads();
-
-    int slot = 0;
-    int par = 0;
-    half8 kf0 = __builtin_bit_cast(half8, kbuf[0][l]);
-    half8 kf1 = __builtin_bit_cast(half8, kbuf[0][64 + l]);
-
-    for (int tile = tb; tile < te; ++tile) {
-        const int nslot = slot == 2 ? 0 : slot + 1;
-        const int wslot = nslot == 2 ? 0 : nslot + 1;
-        const uint4 r0 = kload(tile + 2, bb0, off0);
-        uint4 r1 = make_uint4(0, 0, 0, 0);
-        if constexpr (LOADS == 2) r1 = kload(tile + 2, bb1, off1);
-
-        __builtin_amdgcn_s_setprio(1);
-        const uint4 *kcur = &kbuf[slot][l];
-        floatx16 acc;
-        half8 kf = kf0, kn = kf1;
-        #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            half8 k2 = kn;
-            if (s + 2 < KS) k2 = __builtin_bit_cast(half8, kcur[64 * (s + 2)]);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[s], kf, s == 0 ? floatx16{} : acc, 0, 0, 0);
-            kf = kn;
-            kn = k2;
-        }
-        __builtin_amdgcn_s_setprio(0);
-
-        kf0 = __builtin_bit_cast(half8, kbuf[nslot][l]);
-        kf1 = __builtin_bit_cast(half8, kbuf[nslot][64 + l]);
-        kbuf[wslot][u0] = r0;
-        if constexpr (LOADS == 2) kbuf[wslot][u1] = r1;
-
-        #pragma unroll
-        for (int u = 0; u < 8; ++u) part[par][w][u][l] = relu_bits(acc[u]) + relu_bits(acc[u + 8]);
-        __syncthreads();   // pair sums visible; the K ring advances
-
-        const int bcol = tile * kTileBlocks + bl;
-        const uint32_t coloff = bcol < a.nf ? static_cast<uint32_t>(bcol) * 4 : kOut;
-        #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int u = 2 * w + i;
-            float tot;
-            if constexpr (ACCUM) {
-                if constexpr (BUF) {
-                    tot = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                        rs, static_cast<int>(rowoff[i] + coloff), 0, 0));
-                } else {
-                    tot = (rowel[i] >= 0 && coloff != kOut) ? srow_base[rowel[i] + bcol] : 0.0f;
-                }
-                #pragma unroll
-                for (int v = 0; v < kScoreWaves; ++v) tot = tot + part[par][v][u][l];
-            } else {
-                tot = part[par][0][u][l];
-                #pragma unroll
-                for (int v = 1; v < kScoreWaves; ++v) tot = tot + part[par][v][u][l];
-            }
-            if constexpr (BUF) {
-                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, tot), rs,
-                                                      static_cast<int>(rowoff[i] + coloff), 0,
-                                                      kStoreNT);
-            } else if (rowel[i] >= 0 && coloff != kOut) {
-                __builtin_nontemporal_store(tot, srow_base + rowel[i] + bcol);
-            }
-        }
-        slot = nslot;
-        par ^= 1;
-    }
-}
-
 typedef void (*score_fn)(ScoreArgs);
 
 // Heads per pass: 8 keep the resident queries (128 VGPRs at D = 128), four
@@ -554,18 +396,6 @@ score_fn pick(int D, int np, bool accum, bool buf, bool tail) {
     return nullptr;
 }
 
-template <int D>
-score_fn pick_narrow_d(bool accum, bool buf) {
-    if (accum) return buf ? score_narrow_kernel<D, true, true> : score_narrow_kernel<D, true, false>;
-    return buf ? score_narrow_kernel<D, false, true> : score_narrow_kernel<D, false, false>;
-}
-
-score_fn pick_narrow(int D, bool accum, bool buf) {
-    if (D == 128) return pick_narrow_d<128>(accum, buf);
-    if (D == 64) return pick_narrow_d<64>(accum, buf);
-    return nullptr;
-}
-
 // Splits of the block axis so that base * splits workgroups reach target
 // (at most one split per tile); returns the splits and the tiles per split.
 void split_blocks(int64_t base, int64_t n_tiles, int64_t target, int64_t *splits, int64_t *tps) {
@@ -583,30 +413,25 @@ void split_blocks(int64_t base, int64_t n_tiles, int64_t target, int64_t *splits
 
 hipError_t launch_score_full(const ScoreGeom &geo, bool tail, hipStream_t s) {
     if (geo.nf <= 0 || geo.nq <= 0 || geo.G <= 0) return hipSuccess;
+    if (small_rows(geo)) return launch_score_small(geo, tail, s);
     const int hpp = kHeadsPerPass;
     // buffer stores address one KV head's rows with 32-bit offsets below 2^30
     const bool buf = static_cast<int64_t>(geo.nq) * geo.ld_s * 4 < (int64_t(1) << 30);
     const int64_t n_tiles = (geo.nf + kTileBlocks - 1) / kTileBlocks;
     if (n_tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    // Few query rows (fewer than 256 groups of 64 over the KV heads): the
-    // narrow kernel, 16 queries per workgroup, about one workgroup per CU
-    // (measured at 256 queries x 2048 blocks: 256 workgroups 6.0 us, 128 8.0,
-    // 512 6.5, 1024 9.1; every split reloads its queries).  Otherwise the
-    // wide kernel, split along the block axis only when its query groups
-    // cannot fill the CUs twice.
-    const int64_t wide_groups = (geo.nq + kGroupQueries - 1) / kGroupQueries;
-    const bool narrow = static_cast<int64_t>(geo.G) * wide_groups < 256;
-    const int64_t n_qgroups = narrow ? (geo.nq + kWaveQueries - 1) / kWaveQueries : wide_groups;
+    // Groups of 64 queries per workgroup, split along the block axis only
+    // when the groups cannot fill the CUs twice.
+    const int64_t n_qgroups = (geo.nq + kGroupQueries - 1) / kGroupQueries;
     const int64_t base = static_cast<int64_t>(geo.G) * n_qgroups;
     int64_t splits = 1, tps = n_tiles;
-    split_blocks(base, n_tiles, narrow ? 256 : 512, &splits, &tps);
+    split_blocks(base, n_tiles, 512, &splits, &tps);
     const int64_t grid = base * splits;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
 
     for (int h0 = 0; h0 < geo.H; h0 += hpp) {
         const int nh = (geo.H - h0 < hpp) ? geo.H - h0 : hpp;
         const int np = (nh + 1) / 2;
-        score_fn fn = narrow ? pick_narrow(geo.D, h0 > 0, buf) : pick(geo.D, np, h0 > 0, buf, tail);
+        score_fn fn = pick(geo.D, np, h0 > 0, buf, tail);
         if (!fn) return hipErrorInvalidValue;
         ScoreArgs a{geo.q16, geo.qts, geo.kblk, geo.khs, geo.scores, geo.ld_s,
                     geo.G, geo.nq, geo.H, h0, nh, h0 > 0 ? 1 : 0, geo.nf,
@@ -617,8 +442,6 @@ hipError_t launch_score_full(const ScoreGeom &geo, bool tail, hipStream_t s) {
                                        dim3(static_cast<unsigned>(grid)), dim3(256), args, 0, s);
         if (e != hipSuccess) return e;
     }
-    // the narrow kernel leaves the partial block to the standalone tail kernel
-    if (narrow && tail) return launch_tail(geo, geo.nf, s);
     return hipSuccess;
 }
 

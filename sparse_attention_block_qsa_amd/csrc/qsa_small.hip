@@ -1,0 +1,291 @@
+// qsa_small.hip -- the QSA block scorer for few query rows (latency-bound
+// shapes such as 256 queries against a 128K-token context).
+//
+// score(g, t, b) = sum_h relu( sum_i k[g, b, i] * q[t, g, h, i] )
+// (Strata pull request #228, part 1, score formula.)
+//
+// Design (gfx950, wave64, v_mfma_f32_32x32x16_f16):
+//  * One MFMA row block holds every head of a small query group: its 32 A
+//    rows are QPG queries x 2*NP heads (QPG = 16/NP: 4 queries x 8 heads at
+//    H = 8, 8 x 4 at H <= 4, 2 x 16 at H > 8).  A row R = 8j + 4*half + i
+//    carries query q and head 2p + half for c = 4j + i = p*QPG + q, which
+//    is also the output register of that (query, head pair) in the 32x32
+//    accumulator, the half (lanes 0-31 / 32-63) picking the head of the
+//    pair.  A wave's whole A operand is KS fragments (32 VGPRs at D = 128).
+//  * The workgroup's four waves own four query groups (one each) and walk
+//    the same segment of the block axis: 32-block K tiles are staged once
+//    through LDS in fragment order (coalesced loads), four tiles per
+//    barrier, double-buffered, and read by the four waves.
+//  * Epilogue per tile: relu per head; v_permlane32_swap of the registers of
+//    queries q and q+1 brings the two heads of each pair into one lane; the
+//    pair sums are added in ascending pair order.  That is the head-sum
+//    order of the wide scorer, so both produce the same bits.
+//  * The partial last block (n_kv mod bs != 0) is scored by the last segment
+//    in the fixed fma order of the tail model, one lane per (query, head).
+#include "qsa_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace qsa {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// K tiles staged per barrier (32 KiB at D = 128): at 8 MFMAs per tile, one
+// tile's work is far shorter than a load's latency.
+constexpr int kSmallChunk = 4;
+
+struct SmallArgs {
+    const uint16_t *q16;
+    int64_t qts;
+    const uint16_t *kblk;
+    int64_t khs;
+    float *scores;
+    int64_t ld_s;
+    int32_t G, nq, H;
+    int64_t nf;            // full blocks
+    int32_t tail;          // block nf is a partial block
+    int32_t n_qgroups;     // groups of four query groups (one per wave)
+    int32_t n_segs, tiles_per_seg, n_tiles;
+};
+
+__device__ __forceinline__ float relu_bits(float x) {
+    return __builtin_bit_cast(float, max(__builtin_bit_cast(int32_t, x), 0));
+}
+
+__device__ __forceinline__ uint32_t xcd_logical_id(uint32_t bid, uint32_t nblk) {
+    const uint32_t q = nblk / 8, r = nblk % 8;
+    const uint32_t x = bid % 8, idx = bid / 8;
+    return x * q + (x < r ? x : r) + idx;
+}
+
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
+}
+
+template <int D, int NP>
+__global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
+    constexpr int KS = D / 16;
+    constexpr int QPG = 16 / NP;
+    constexpr int CHUNKS = D / 8;                  // 16-byte chunks per block row
+    constexpr int TILE_U4 = CHUNKS * kTileBlocks;
+    constexpr int LOADS = TILE_U4 / 256;           // staging loads per thread per tile
+    static_assert(NP == 1 || NP == 2 || NP == 4 || NP == 8, "head pairs per row block");
+    static_assert(TILE_U4 % 256 == 0 && (LOADS == 1 || LOADS == 2), "D must be 64 or 128");
+
+    // two chunks of K tiles shared by the four waves, and per wave the
+    // relu'd tail chains
+    __shared__ uint4 kbuf[2][kSmallChunk][TILE_U4];
+    __shared__ float red[kScoreWaves][QPG][2 * NP];
+
+    const uint32_t L = xcd_logical_id(blockIdx.x, gridDim.x);
+    const int seg = static_cast<int>(L % a.n_segs);
+    const uint32_t rest = L / a.n_segs;
+    const int qg4 = static_cast<int>(rest % a.n_qgroups);   // groups of four query groups
+    const int g = static_cast<int>(rest / a.n_qgroups);
+    const int w = threadIdx.x >> 6;
+    const int l = threadIdx.x & 63;
+    const int qg = qg4 * kScoreWaves + w;                    // this wave's query group
+
+    // ---- A operand: this lane's (query, head) row, channels 16s + 8*(l/32) ..
+    const int R = l & 31, kc = l >> 5;
+    const int c = 4 * (R >> 3) + (R & 3);
+    const int p_in = c / QPG, q_in = c % QPG;
+    const int h_in = 2 * p_in + ((R >> 2) & 1);
+    const int t_in = qg * QPG + q_in;
+    const bool a_ok = t_in < a.nq && h_in < a.H;
+    const int64_t a_off = static_cast<int64_t>(a_ok ? t_in : 0) * a.qts +
+                          static_cast<int64_t>(g * a.H + (a_ok ? h_in : 0)) * D + 8 * kc;
+    half8 qa[KS];
+    #pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const half8 v = *reinterpret_cast<const half8 *>(a.q16 + a_off + 16 * s);
+        qa[s] = a_ok ? v : half8{};
+    }
+
+    const int tb = seg * a.tiles_per_seg;
+    const int te = min(a.n_tiles, tb + a.tiles_per_seg);
+    const uint16_t *kg = a.kblk + static_cast<int64_t>(g) * a.khs;
+    float *sbase = a.scores + static_cast<int64_t>(g) * a.nq * a.ld_s;
+
+    if (tb < te) {   // uniform over the workgroup
+        // K staging in chunks of CH tiles, double-buffered: the loads of
+        // chunk c+1 are in flight while chunk c is scored, one barrier per
+        // chunk.  LDS index u = threadIdx.x + 256*j of a tile is chunk-major
+        // (u = chunk*32 + block), the B-fragment order: lane l of K-step s
+        // reads u = 64*s + l.  Blocks past nf, and tiles past the segment,
+        // feed output columns that are never stored: their indices are
+        // clamped.
+        const int64_t last = a.nf - 1;
+        auto kload = [&](int tile, int j) {
+            const int u = static_cast<int>(threadIdx.x) + 256 * j;
+            const int64_t b = min(static_cast<int64_t>(min(tile, te - 1)) * kTileBlocks +
+                                      (u % kTileBlocks), last);
+            return *reinterpret_cast<const uint4 *>(kg + b * D + 8 * (u / kTileBlocks));
+        };
+        uint4 st[kSmallChunk][LOADS];
+        auto fetch = [&](int t0) {
+            #pragma unroll
+            for (int i = 0; i < kSmallChunk; ++i)
+                #pragma unroll
+                for (int j = 0; j < LOADS; ++j) st[i][j] = kload(t0 + i, j);
+        };
+        auto publish = [&](int buf) {
+            #pragma unroll
+            for (int i = 0; i < kSmallChunk; ++i)
+                #pragma unroll
+                for (int j = 0; j < LOADS; ++j) kbuf[buf][i][threadIdx.x + 256 * j] = st[i][j];
+        };
+        fetch(tb);
+        publish(0);
+        __syncthreads();
+        int buf = 0;
+        for (int t0 = tb; t0 < te; t0 += kSmallChunk) {
+            const bool more = t0 + kSmallChunk < te;   // uniform
+            if (more) fetch(t0 + kSmallChunk);
+            for (int i = 0; i < kSmallChunk && t0 + i < te; ++i) {
+                const int tile = t0 + i;
+                const uint4 *kcur = &kbuf[buf][i][l];
+                floatx16 acc = {};
+                #pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        qa[s], __builtin_bit_cast(half8, kcur[64 * s]), s == 0 ? floatx16{} : acc, 0,
+                        0, 0);
+
+                // relu per head, then the two heads of each pair into one
+                // lane: for queries q, q+1 of pair p (registers r, r+1) the
+                // swap gives lanes 0-31 both heads of q and lanes 32-63 both
+                // heads of q+1; pair sums are added in ascending pair order
+                float pr[16];
+                #pragma unroll
+                for (int r = 0; r < 16; ++r) pr[r] = relu_bits(acc[r]);
+                float tot[QPG / 2];
+                #pragma unroll
+                for (int p = 0; p < NP; ++p) {
+                    #pragma unroll
+                    for (int m = 0; m < QPG / 2; ++m) {
+                        const int r = p * QPG + 2 * m;
+                        const auto sw = __builtin_amdgcn_permlane32_swap(
+                            __builtin_bit_cast(uint32_t, pr[r]),
+                            __builtin_bit_cast(uint32_t, pr[r + 1]), false, false);
+                        const float pair = __builtin_bit_cast(float, static_cast<uint32_t>(sw[0])) +
+                                           __builtin_bit_cast(float, static_cast<uint32_t>(sw[1]));
+                        tot[m] = p == 0 ? pair : tot[m] + pair;
+                    }
+                }
+                const int64_t b = static_cast<int64_t>(tile) * kTileBlocks + (l & 31);
+                #pragma unroll
+                for (int m = 0; m < QPG / 2; ++m) {
+                    const int t = qg * QPG + 2 * m + kc;
+                    if (t < a.nq && b < a.nf) sbase[static_cast<int64_t>(t) * a.ld_s + b] = tot[m];
+                }
+            }
+            if (more) {
+                publish(buf ^ 1);
+                __syncthreads();
+                buf ^= 1;
+            }
+        }
+    }
+
+    // ---- the partial block nf: last segment, one lane per (query, head) chain
+    if (a.tail && seg == a.n_segs - 1) {   // uniform over the workgroup
+        float r = 0.0f;
+        if (l < 32 && a_ok) {
+            const uint16_t *kt = kg + a.nf * D;
+            const int64_t row = static_cast<int64_t>(t_in) * a.qts +
+                                static_cast<int64_t>(g * a.H + h_in) * D;
+            float acc = 0.0f;
+            #pragma unroll 4
+            for (int i8 = 0; i8 < D; i8 += 8) {
+                const uint4 kv = *reinterpret_cast<const uint4 *>(kt + i8);
+                const uint4 qv = *reinterpret_cast<const uint4 *>(a.q16 + row + i8);
+                const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+                const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+                #pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc = __builtin_fmaf(h2f(kw[e] & 0xffffu), h2f(qw[e] & 0xffffu), acc);
+                    acc = __builtin_fmaf(h2f(kw[e] >> 16), h2f(qw[e] >> 16), acc);
+                }
+            }
+            r = acc > 0.0f ? acc : 0.0f;
+        }
+        if (l < 32) red[w][q_in][h_in] = r;   // padded heads and rows hold +0
+        __syncthreads();
+        if (l < QPG) {
+            const int t = qg * QPG + l;
+            if (t < a.nq) {
+                float sum = 0.0f;
+                for (int h = 0; h < a.H; ++h) sum = sum + red[w][l][h];
+                sbase[static_cast<int64_t>(t) * a.ld_s + a.nf] = sum;
+            }
+        }
+    }
+}
+
+typedef void (*small_fn)(SmallArgs);
+
+template <int D>
+small_fn pick_np(int np) {
+    switch (np) {
+        case 1: return score_small_kernel<D, 1>;
+        case 2: return score_small_kernel<D, 2>;
+        case 4: return score_small_kernel<D, 4>;
+        case 8: return score_small_kernel<D, 8>;
+    }
+    return nullptr;
+}
+
+small_fn pick_small(int D, int np) {
+    if (D == 128) return pick_np<128>(np);
+    if (D == 64) return pick_np<64>(np);
+    return nullptr;
+}
+
+// Head pairs per MFMA row block: the smallest of 1, 2, 4, 8 that holds H.
+int small_pairs(int H) {
+    const int np = (H + 1) / 2;
+    return np <= 1 ? 1 : np <= 2 ? 2 : np <= 4 ? 4 : 8;
+}
+
+}  // namespace
+
+bool small_rows(const ScoreGeom &geo) {
+    const int64_t wide_groups = (geo.nq + kGroupQueries - 1) / kGroupQueries;
+    return static_cast<int64_t>(geo.G) * wide_groups < 256;
+}
+
+hipError_t launch_score_small(const ScoreGeom &geo, bool tail, hipStream_t s) {
+    if (geo.nq <= 0 || geo.G <= 0 || (geo.nf <= 0 && !tail)) return hipSuccess;
+    const int np = small_pairs(geo.H);
+    const int qpg = 16 / np;
+    const int64_t n_tiles = (geo.nf + kTileBlocks - 1) / kTileBlocks;
+    const int64_t n_qgroups = (geo.nq + qpg - 1) / qpg;
+    const int64_t n_qg4 = (n_qgroups + kScoreWaves - 1) / kScoreWaves;   // per workgroup: four
+    const int64_t base = static_cast<int64_t>(geo.G) * n_qg4;
+    // Segments of the block axis: enough workgroups to reach about one per
+    // CU, each segment keeping at least one chunk of tiles.
+    int64_t segs = 1;
+    const int64_t target = 256;
+    if (base < target) segs = (target + base - 1) / base;
+    const int64_t max_segs = n_tiles / kSmallChunk > 0 ? n_tiles / kSmallChunk : 1;
+    if (segs > max_segs) segs = max_segs;
+    if (segs < 1) segs = 1;
+    const int64_t tps = n_tiles > 0 ? (n_tiles + segs - 1) / segs : 0;
+    if (n_tiles > 0) segs = (n_tiles + tps - 1) / tps;
+    const int64_t grid = base * segs;
+    if (grid > 0x7fffffffLL || n_tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    small_fn fn = pick_small(geo.D, np);
+    if (!fn) return hipErrorInvalidValue;
+    SmallArgs a{geo.q16, geo.qts, geo.kblk, geo.khs, geo.scores,
+                geo.ld_s, geo.G, geo.nq, geo.H, geo.nf, tail ? 1 : 0,
+                static_cast<int32_t>(n_qg4), static_cast<int32_t>(segs),
+                static_cast<int32_t>(tps), static_cast<int32_t>(n_tiles)};
+    void *args[] = {&a};
+    return hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(static_cast<unsigned>(grid)),
+                           dim3(256), args, 0, s);
+}
+
+}  // namespace qsa

@@ -444,9 +444,9 @@ def test_phase_ids_write_set():
     assert ids.outside_intact(m) and ids.written_all(m)
 
 
-def test_wide_and_narrow_scorers_agree_bitwise():
+def test_wide_and_small_scorers_agree_bitwise():
     """The whole query set takes the wide scorer (4096 rows per KV head),
-    chunks of 1000 take the narrow one; both add the relu'd heads in the same
+    chunks of 1000 take the small one; both add the relu'd heads in the same
     order, so the chunked phase reproduces the whole phase bit for bit
     (scores of the last chunk, ids and values of every row)."""
     cfg = qi.Config("wn", 4, 4096, 8, 128, 30 * 64 + 11, 64, 16, "normal", 321)
@@ -470,6 +470,30 @@ def test_wide_and_narrow_scorers_agree_bitwise():
     s0 = ws0.scores[:, :, :cfg.nb].reshape(cfg.rows, cfg.nb).cpu().numpy().astype(np.float64)
     model = oracle.block_model_f32(w.q16, w.kblk, cfg.nf)
     assert np.array_equal(s0[:, cfg.nf].astype(np.float32).view(np.uint32), model.view(np.uint32))
+
+
+# H, D: every row packing of the small scorer (head pairs 1, 2, 4, 8 per MFMA
+# row block, padded heads for odd H), both head dims, one or two wide passes
+SMALL_VS_WIDE = [(1, 128), (2, 64), (3, 128), (4, 64), (5, 128), (8, 128), (8, 64), (12, 128),
+                 (16, 64)]
+
+
+@pytest.mark.parametrize("H,D", SMALL_VS_WIDE, ids=lambda v: str(v))
+def test_small_scorer_matches_wide_bitwise(H, D):
+    """4 KV heads x 4096 queries take the wide scorer; a slice of 100 queries
+    (few rows) takes the small scorer, which packs 16/NP queries x 2*NP heads
+    into one MFMA row block instead of 16 queries x 2 heads.  The same MFMA
+    dot products and the same head-sum order give the same bits, tail block
+    included (no oracle needed: the two paths check each other)."""
+    G, nq, t0, n = 4, 4096, 1234, 100
+    cfg = qi.Config("small_vs_wide", G, nq, H, D, 20 * 64 + 9, 64, 4, "normal", 600 + 10 * H + D)
+    w = qi.make(cfg)
+    kd = k_dev(w.kblk)
+    whole = qsa.block_scores(q_dev(w.q16), kd, cfg.n_kv, cfg.bs)
+    part = qsa.block_scores(q_dev(w.q16[t0:t0 + n]), kd, cfg.n_kv, cfg.bs)
+    torch.cuda.synchronize()
+    assert torch.equal(part.contiguous().view(torch.int32),
+                       whole[:, t0:t0 + n].contiguous().view(torch.int32))
 
 
 def test_wide_scorer_global_store_path():
@@ -499,9 +523,9 @@ def test_wide_scorer_global_store_path():
 def test_wide_rows_use_global_store_path():
     """A score region past 2^30 bytes per KV head takes the scorer's plain
     global-store path (the buffer-store path needs 30-bit offsets); it must
-    give the same write set and the same bound.  H = 12 also exercises the
-    accumulating second head pass on that path (here in the narrow scorer,
-    few query rows)."""
+    give the same write set and the same bound.  Few query rows: the small
+    scorer, whose 64-bit addressing covers the region, with H = 12 in one
+    row block of two queries x 16 head slots."""
     cfg = qi.Config("wide", 1, 70, 12, 128, 65 * 64 + 5, 64, 8, "normal", 99)
     w = qi.make(cfg)
     ld = 1 << 24                                   # 64 MiB per row: 4.4 GiB region
