@@ -81,6 +81,17 @@ def read_traffic(kernel: str, workload: str):
         return None
 
 
+def scorer_kernel(cfg):
+    """The scorer kernel the library runs for this workload: the small scorer
+    when the KV heads x groups of 64 queries number fewer than 256, else the
+    wide one (head passes of up to eight heads); the tail block, when there
+    is one, is scored inside the same launch."""
+    if cfg.G * -(-cfg.nq // 64) < 256:
+        np_ = 1 if cfg.H <= 2 else 2 if cfg.H <= 4 else 4 if cfg.H <= 8 else 8
+        return "score_small", f"score_small_kernel<{cfg.D},{np_}>"
+    return "score_full", f"score_full_kernel<{cfg.D},{min(4, (cfg.H + 1) // 2)}> (+ tail when present)"
+
+
 class Phase:
     """Device buffers and raw C-ABI calls of one workload (no Python checks
     inside the hot loop: arguments are validated once by a checked call)."""
@@ -238,8 +249,8 @@ def main():
 
     scorer_ms = res["stages_ms"]["scorer"]
     achieved = res["flop"] / (scorer_ms * 1e-3) / 1e12
-    kernel = "score_full"
-    roofline = {"bound": "mfma", "kernel": "score_full_kernel<128,4> (+ tail when present)",
+    kernel, kernel_desc = scorer_kernel(cfg)
+    roofline = {"bound": "mfma", "kernel": kernel_desc,
                 "achieved": achieved, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_FP16_TFLOPS,
                 "traffic": read_traffic(kernel, cfg.name),
@@ -258,6 +269,8 @@ def main():
             "workload": pc.name, "ms_per_step": pr["ms_per_step"], "stages_ms": ps,
             "scorer_tflops": pr["scorer_tflops"],
             "scorer_frac_of_peak": pr["scorer_tflops"] / PEAK_FP16_TFLOPS,
+            "scorer_kernel": scorer_kernel(pc)[1],
+            "scorer_traffic_bytes": read_traffic(scorer_kernel(pc)[0], pc.name),
             "convert_gbs": hbm["convert"] / (ps["convert"] * 1e-3) / 1e9,
             "topk_gbs": hbm["topk"] / (ps["topk"] * 1e-3) / 1e9,
             "graph_replay_matches_eager": pr["graph_replay_matches_eager"],
