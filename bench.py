@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--workload", default="nq256_nkv131072")
     p.add_argument("--prefill-steps", type=int, default=20,
                    help="steps for the full-prefill chunk reported beside the workload (0: skip)")
+    p.add_argument("--decode-steps", type=int, default=200,
+                   help="steps for the decode step reported beside the workload (0: skip)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target wall time of the CPU-baseline sample")
@@ -278,6 +280,26 @@ def main():
         print(f"# prefill: {pr['ms_per_step']:.3f} ms/step, scorer {pr['scorer_tflops']:.0f} "
               f"TFLOP/s", file=sys.stderr, flush=True)
 
+    decode = None
+    if args.decode_steps > 0 and cfg.name != qi.DECODE.name:
+        dc = qi.DECODE
+        print(f"# decode step {dc.name}: steps {args.decode_steps}", file=sys.stderr, flush=True)
+        dr = measure(dc, qsa, torch, args.decode_steps, 20)
+        ds = dr["stages_ms"]
+        # the scorer streams every KV head's block keys once: HBM-bound
+        kbytes = 2.0 * dc.G * dc.nb * dc.D
+        sbytes = kbytes + 2.0 * dc.rows * dc.H * dc.D + 4.0 * dc.rows * dc.nb
+        decode = {
+            "workload": dc.name, "ms_per_step": dr["ms_per_step"], "stages_ms": ds,
+            "scorer_kernel": scorer_kernel(dc)[1],
+            "scorer_bytes": sbytes,
+            "scorer_gbs": sbytes / (ds["scorer"] * 1e-3) / 1e9,
+            "scorer_frac_of_hbm": sbytes / (ds["scorer"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "graph_replay_matches_eager": dr["graph_replay_matches_eager"],
+        }
+        print(f"# decode: {dr['ms_per_step'] * 1e3:.2f} us/step, scorer {ds['scorer'] * 1e3:.2f} us",
+              file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -314,6 +336,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "full_prefill": prefill,
+        "decode": decode,
         "source_digest": source_digest(),
         "context": {"pages_rx7900xtx_gfx1100_scores_ms_128k": {"warp": 2.627, "wmma": 0.252},
                     "note": "other hardware; context only"},

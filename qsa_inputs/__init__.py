@@ -138,11 +138,15 @@ CONFIGS = {
         Config("nq256_nkv32768", 1, 256, 8, 128, 32768, 64, 32, "normal", 1003),
         Config("nq256_nkv131072", 1, 256, 8, 128, 131072, 64, 64, "normal", 1004),
         Config("prefill_g4_nq16384_nkv131077", 4, 16384, 8, 128, 131077, 64, 64, "normal", 1005),
+        # one decode step: one query per KV head of a GQA layer with 64 query
+        # heads, 128K tokens plus a partial block
+        Config("decode_g8_nq1_nkv131109", 8, 1, 8, 128, 131109, 64, 64, "normal", 1006),
     ]
 }
 TINY = CONFIGS["tiny_nq37_nkv1000"]
 HEADLINE = CONFIGS["nq256_nkv131072"]
 PREFILL = CONFIGS["prefill_g4_nq16384_nkv131077"]
+DECODE = CONFIGS["decode_g8_nq1_nkv131109"]
 
 
 @dataclass

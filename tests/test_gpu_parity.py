@@ -147,6 +147,46 @@ def test_config_scores_ids_and_write_set(name):
     assert np.array_equal(s_gpu.view(np.uint64), s2.view(np.uint64)), "not deterministic"
 
 
+# decode shapes: few queries per KV head (G, nq, H, D, n_kv, k)
+DECODE_SHAPES = [
+    (8, 1, 8, 128, 131109, 64),    # the bench's decode step: 2049 blocks, 37-token tail
+    (8, 4, 8, 128, 20 * 64, 64),   # k > nb/2, no tail
+    (2, 3, 16, 64, 5000, 16),      # H = 16: two queries x 16 heads per MFMA row block
+    (4, 8, 4, 64, 3 * 64 + 63, 8), # H = 4, three full blocks and a 63-token tail
+    (3, 2, 5, 128, 40, 4),         # a single partial block (no full block)
+]
+
+
+@pytest.mark.parametrize("shape", DECODE_SHAPES, ids=lambda v: "G{}_nq{}_H{}_D{}_nkv{}_k{}".format(*v))
+def test_decode_shapes_phase(shape):
+    """One decode step per KV head through the whole phase (fp32 queries,
+    conversion, the small scorer with the tail block, top-k): scores within
+    the bound, the tail bit for bit the fixed-order model, ids exactly the
+    top-k of the device scores and near-tie consistent with the oracle's."""
+    G, nq, H, D, n_kv, k = shape
+    cfg = qi.Config("decode", G, nq, H, D, n_kv, 64, k, "normal", 7000 + G * 10 + nq)
+    log(f"decode {shape}")
+    w = qi.make(cfg)
+    ws = qsa.PhaseWorkspace(cfg.nq, cfg.G, cfg.H, cfg.D, cfg.n_kv, cfg.bs, cfg.k, dev(),
+                            with_vals=True)
+    ids, vals = qsa.select_phase(torch.from_numpy(w.q32).to(dev()), k_dev(w.kblk), cfg.n_kv,
+                                 cfg.bs, cfg.k, ws)
+    torch.cuda.synchronize()
+    s_gpu = ws.scores[:, :, :cfg.nb].reshape(cfg.rows, cfg.nb).cpu().numpy().astype(np.float64)
+    ref = oracle.scores(w.q16, w.kblk, cfg.nb)
+    check_bound(s_gpu, ref, "decode")
+    if cfg.nb > cfg.nf:
+        model = oracle.block_model_f32(w.q16, w.kblk, cfg.nf)
+        assert np.array_equal(s_gpu[:, cfg.nf].astype(np.float32).view(np.uint32),
+                              model.view(np.uint32))
+    got = ids.reshape(cfg.rows, cfg.k).cpu().numpy()
+    check_ids(got, s_gpu, ref, cfg.k, "decode")
+    sel = got >= 0
+    v = vals.reshape(cfg.rows, cfg.k).cpu().numpy()
+    assert np.array_equal(v[sel], s_gpu[np.nonzero(sel)[0], got[sel]].astype(np.float32))
+    assert np.all(v[~sel] == -np.inf)
+
+
 def test_tiny_nkv0_writes_nothing_and_selects_nothing():
     cfg = qi.TINY
     w = qi.make(cfg)
