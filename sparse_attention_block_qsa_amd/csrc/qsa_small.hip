@@ -14,7 +14,7 @@
 //    pair.  A wave's whole A operand is KS fragments (32 VGPRs at D = 128).
 //  * The workgroup's four waves own four query groups (one each) and walk
 //    the same segment of the block axis: 32-block K tiles are staged once
-//    through LDS in fragment order (coalesced loads), four tiles per
+//    through LDS in fragment order (coalesced loads), two tiles per
 //    barrier, double-buffered, and read by the four waves.
 //  * Epilogue per tile: relu per head; v_permlane32_swap of the registers of
 //    queries q and q+1 brings the two heads of each pair into one lane; the
@@ -32,9 +32,10 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-// K tiles staged per barrier (32 KiB at D = 128): at 8 MFMAs per tile, one
-// tile's work is far shorter than a load's latency.
-constexpr int kSmallChunk = 4;
+// K tiles staged per barrier (16 KiB at D = 128), double-buffered: at 8
+// MFMAs per tile, one tile's work is far shorter than a load's latency.
+// Measured at nq = 256: 2 tiles 5.1 us, 4 tiles 5.3 us, 8 tiles 7.5 us.
+constexpr int kSmallChunk = 2;
 
 struct SmallArgs {
     const uint16_t *q16;
@@ -266,11 +267,12 @@ hipError_t launch_score_small(const ScoreGeom &geo, bool tail, hipStream_t s) {
     const int64_t n_qg4 = (n_qgroups + kScoreWaves - 1) / kScoreWaves;   // per workgroup: four
     const int64_t base = static_cast<int64_t>(geo.G) * n_qg4;
     // Segments of the block axis: enough workgroups to reach about one per
-    // CU, each segment keeping at least one chunk of tiles.
+    // CU (more cost more query reloads than they overlap), each segment
+    // keeping at least one tile.
     int64_t segs = 1;
     const int64_t target = 256;
     if (base < target) segs = (target + base - 1) / base;
-    const int64_t max_segs = n_tiles / kSmallChunk > 0 ? n_tiles / kSmallChunk : 1;
+    const int64_t max_segs = n_tiles > 0 ? n_tiles : 1;
     if (segs > max_segs) segs = max_segs;
     if (segs < 1) segs = 1;
     const int64_t tps = n_tiles > 0 ? (n_tiles + segs - 1) / segs : 0;
