@@ -156,6 +156,23 @@ qsa_status qsa_select_phase(const float *q32, uint16_t *q16, int64_t q_tok_strid
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
 
+    // Few query rows in one pass: the small scorer reads the fp32 queries,
+    // converts them on load and writes the fp16 workspace rows itself, so
+    // the conversion launch is folded into the scorer.
+    if (q32 && qc == nq && c.nb > 0) {
+        ScoreGeom geo{q16, q_tok_stride, kblk, kblk_head_stride, scores_ws, ld_s, G, nq, H, D,
+                      c.nf};
+        if (qsa::small_rows(geo) && qsa::small_src32_ok(q32, q_tok_stride)) {
+            hipError_t e = qsa::launch_score_small(geo, c.nb > c.nf, s, q32, q16);
+            if (e == hipSuccess && k > 0) {
+                TopkGeom tg{scores_ws, ld_s, ids, ld_ids, vals, G, nq, nq, nq, 0,
+                            static_cast<int32_t>(c.nb), k};
+                e = qsa::launch_topk(tg, s);
+            }
+            return e == hipSuccess ? QSA_OK : QSA_ERR_HIP;
+        }
+    }
+
     // the conversion writes exactly the token rows (G*H*D elements each)
     if (q32) {
         hipError_t e = qsa::launch_convert_rows(q32, q16, nq, static_cast<int64_t>(G) * H * D,

@@ -48,9 +48,16 @@ hipError_t launch_score_full(const ScoreGeom &g, bool tail, hipStream_t s);
 // scorer of qsa_small.hip, latency-bound shapes.
 bool small_rows(const ScoreGeom &g);
 
+// fp32 queries the small scorer can read directly (16-byte vector loads).
+bool small_src32_ok(const float *q32, int64_t qts);
+
 // The small scorer: blocks [0, nf) and, with tail, the partial block nf in
-// the fixed order of the tail model (also when nf == 0).
-hipError_t launch_score_small(const ScoreGeom &g, bool tail, hipStream_t s);
+// the fixed order of the tail model (also when nf == 0).  With q32 set the
+// queries are read as fp32 (layout of g.q16), converted on load, and their
+// fp16 bits written to q16w: the G*H*D elements of every token row, nothing
+// between rows.
+hipError_t launch_score_small(const ScoreGeom &g, bool tail, hipStream_t s,
+                              const float *q32 = nullptr, uint16_t *q16w = nullptr);
 
 // Fixed-order scorer of the single block b_tail, standalone (used when there
 // is no full block to share the query reads with).

@@ -20,6 +20,10 @@
 //    queries q and q+1 brings the two heads of each pair into one lane; the
 //    pair sums are added in ascending pair order.  That is the head-sum
 //    order of the wide scorer, so both produce the same bits.
+//  * With fp32 queries (the select phase) the fragments are converted on
+//    load with the rounding of the conversion kernel, and the first segment
+//    of each query group writes the converted rows to the fp16 workspace, so
+//    the phase needs no conversion launch for few rows.
 //  * The partial last block (n_kv mod bs != 0) is scored by the last segment
 //    in the fixed fma order of the tail model, one lane per (query, head).
 #include "qsa_internal.h"
@@ -38,7 +42,9 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 constexpr int kSmallChunk = 2;
 
 struct SmallArgs {
-    const uint16_t *q16;
+    const uint16_t *q16;   // query source when q32 is null
+    const float *q32;      // query source when set, converted on load
+    uint16_t *q16w;        // with q32: receives the converted rows, or null
     int64_t qts;
     const uint16_t *kblk;
     int64_t khs;
@@ -61,11 +67,32 @@ __device__ __forceinline__ uint32_t xcd_logical_id(uint32_t bid, uint32_t nblk) 
     return x * q + (x < r ? x : r) + idx;
 }
 
+// Eight fp32 values to fp16 bits, rounded to nearest even: the hardware
+// conversion, which is f16_rne for every input but NaN; a fragment in which
+// some lane holds a NaN takes f16_rne itself (its NaN rule), so the bits
+// equal those of the conversion kernel.
+__device__ __forceinline__ uint4 f16x8(const float4 &x0, const float4 &x1) {
+    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    uint32_t m = 0;
+    #pragma unroll
+    for (int e = 0; e < 8; ++e) m = max(m, __builtin_bit_cast(uint32_t, xs[e]) & 0x7fffffffu);
+    uint32_t h[8];
+    if (__builtin_amdgcn_ballot_w64(m > 0x7f800000u)) {   // uniform: a NaN somewhere
+        #pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = f16_rne(xs[e]);
+    } else {
+        #pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(xs[e]));
+    }
+    return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                      h[6] | (h[7] << 16));
+}
+
 __device__ __forceinline__ float h2f(uint32_t bits16) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
 }
 
-template <int D, int NP>
+template <int D, int NP, bool SRC32>
 __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
     constexpr int KS = D / 16;
     constexpr int QPG = 16 / NP;
@@ -101,8 +128,18 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
     half8 qa[KS];
     #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        const half8 v = *reinterpret_cast<const half8 *>(a.q16 + a_off + 16 * s);
-        qa[s] = a_ok ? v : half8{};
+        if constexpr (SRC32) {
+            const float4 x0 = *reinterpret_cast<const float4 *>(a.q32 + a_off + 16 * s);
+            const float4 x1 = *reinterpret_cast<const float4 *>(a.q32 + a_off + 16 * s + 4);
+            const uint4 hv = f16x8(x0, x1);
+            // one writer per element: the first segment, real rows only
+            if (a.q16w && seg == 0 && a_ok)
+                *reinterpret_cast<uint4 *>(a.q16w + a_off + 16 * s) = hv;
+            qa[s] = a_ok ? __builtin_bit_cast(half8, hv) : half8{};
+        } else {
+            const half8 v = *reinterpret_cast<const half8 *>(a.q16 + a_off + 16 * s);
+            qa[s] = a_ok ? v : half8{};
+        }
     }
 
     const int tb = seg * a.tiles_per_seg;
@@ -192,27 +229,38 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
     }
 
     // ---- the partial block nf: last segment, one lane per (query, head) chain
+    // Lane l < 32 runs the chain of its A row R = l from the query fragments
+    // already in registers: v_permlane32_swap gives it the other half of
+    // every 16-channel run (held by lane l + 32), so it walks channels
+    // 16s .. 16s + 15 in ascending order.
     if (a.tail && seg == a.n_segs - 1) {   // uniform over the workgroup
-        float r = 0.0f;
-        if (l < 32 && a_ok) {
-            const uint16_t *kt = kg + a.nf * D;
-            const int64_t row = static_cast<int64_t>(t_in) * a.qts +
-                                static_cast<int64_t>(g * a.H + h_in) * D;
-            float acc = 0.0f;
-            #pragma unroll 4
-            for (int i8 = 0; i8 < D; i8 += 8) {
-                const uint4 kv = *reinterpret_cast<const uint4 *>(kt + i8);
-                const uint4 qv = *reinterpret_cast<const uint4 *>(a.q16 + row + i8);
-                const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
-                const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
-                #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    acc = __builtin_fmaf(h2f(kw[e] & 0xffffu), h2f(qw[e] & 0xffffu), acc);
-                    acc = __builtin_fmaf(h2f(kw[e] >> 16), h2f(qw[e] >> 16), acc);
-                }
-            }
-            r = acc > 0.0f ? acc : 0.0f;
+        const uint16_t *kt = kg + a.nf * D;
+        uint4 kv[KS][2];
+        #pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            kv[s][0] = *reinterpret_cast<const uint4 *>(kt + 16 * s);
+            kv[s][1] = *reinterpret_cast<const uint4 *>(kt + 16 * s + 8);
         }
+        float acc = 0.0f;
+        #pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const uint4 x = __builtin_bit_cast(uint4, qa[s]);
+            const auto w0 = __builtin_amdgcn_permlane32_swap(x.x, x.x, false, false);
+            const auto w1 = __builtin_amdgcn_permlane32_swap(x.y, x.y, false, false);
+            const auto w2 = __builtin_amdgcn_permlane32_swap(x.z, x.z, false, false);
+            const auto w3 = __builtin_amdgcn_permlane32_swap(x.w, x.w, false, false);
+            // lanes 0-31: [0] is the lane's own half (channels 16s .. +7),
+            // [1] the half of lane l + 32 (channels 16s + 8 .. +15)
+            const uint32_t qw[8] = {w0[0], w1[0], w2[0], w3[0], w0[1], w1[1], w2[1], w3[1]};
+            const uint32_t kw[8] = {kv[s][0].x, kv[s][0].y, kv[s][0].z, kv[s][0].w,
+                                    kv[s][1].x, kv[s][1].y, kv[s][1].z, kv[s][1].w};
+            #pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                acc = __builtin_fmaf(h2f(kw[e] & 0xffffu), h2f(qw[e] & 0xffffu), acc);
+                acc = __builtin_fmaf(h2f(kw[e] >> 16), h2f(qw[e] >> 16), acc);
+            }
+        }
+        const float r = (l < 32 && a_ok && acc > 0.0f) ? acc : 0.0f;
         if (l < 32) red[w][q_in][h_in] = r;   // padded heads and rows hold +0
         __syncthreads();
         if (l < QPG) {
@@ -228,20 +276,20 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
 
 typedef void (*small_fn)(SmallArgs);
 
-template <int D>
+template <int D, bool SRC32>
 small_fn pick_np(int np) {
     switch (np) {
-        case 1: return score_small_kernel<D, 1>;
-        case 2: return score_small_kernel<D, 2>;
-        case 4: return score_small_kernel<D, 4>;
-        case 8: return score_small_kernel<D, 8>;
+        case 1: return score_small_kernel<D, 1, SRC32>;
+        case 2: return score_small_kernel<D, 2, SRC32>;
+        case 4: return score_small_kernel<D, 4, SRC32>;
+        case 8: return score_small_kernel<D, 8, SRC32>;
     }
     return nullptr;
 }
 
-small_fn pick_small(int D, int np) {
-    if (D == 128) return pick_np<128>(np);
-    if (D == 64) return pick_np<64>(np);
+small_fn pick_small(int D, int np, bool src32) {
+    if (D == 128) return src32 ? pick_np<128, true>(np) : pick_np<128, false>(np);
+    if (D == 64) return src32 ? pick_np<64, true>(np) : pick_np<64, false>(np);
     return nullptr;
 }
 
@@ -258,7 +306,12 @@ bool small_rows(const ScoreGeom &geo) {
     return static_cast<int64_t>(geo.G) * wide_groups < 256;
 }
 
-hipError_t launch_score_small(const ScoreGeom &geo, bool tail, hipStream_t s) {
+bool small_src32_ok(const float *q32, int64_t qts) {
+    return reinterpret_cast<uintptr_t>(q32) % 16 == 0 && qts % 4 == 0;
+}
+
+hipError_t launch_score_small(const ScoreGeom &geo, bool tail, hipStream_t s, const float *q32,
+                              uint16_t *q16w) {
     if (geo.nq <= 0 || geo.G <= 0 || (geo.nf <= 0 && !tail)) return hipSuccess;
     const int np = small_pairs(geo.H);
     const int qpg = 16 / np;
@@ -279,9 +332,9 @@ hipError_t launch_score_small(const ScoreGeom &geo, bool tail, hipStream_t s) {
     if (n_tiles > 0) segs = (n_tiles + tps - 1) / tps;
     const int64_t grid = base * segs;
     if (grid > 0x7fffffffLL || n_tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    small_fn fn = pick_small(geo.D, np);
+    small_fn fn = pick_small(geo.D, np, q32 != nullptr);
     if (!fn) return hipErrorInvalidValue;
-    SmallArgs a{geo.q16, geo.qts, geo.kblk, geo.khs, geo.scores,
+    SmallArgs a{geo.q16, q32, q32 ? q16w : nullptr, geo.qts, geo.kblk, geo.khs, geo.scores,
                 geo.ld_s, geo.G, geo.nq, geo.H, geo.nf, tail ? 1 : 0,
                 static_cast<int32_t>(n_qg4), static_cast<int32_t>(segs),
                 static_cast<int32_t>(tps), static_cast<int32_t>(n_tiles)};

@@ -452,6 +452,51 @@ def test_phase_conversion_paths(case):
     check_ids(ids.reshape(cfg.rows, k).cpu().numpy(), s_gpu, ref, k, "phase conversion")
 
 
+SPECIALS = np.array([0x7FC00001, 0xFFA00000, 0x7F800001, 0xFFFFFFFF,    # NaNs: payloads, signs, signalling
+                     0x7F800000, 0xFF800000,                            # +-inf
+                     0x47888000, 0xC77FF000, 0x477FE000, 0x477FEFFF,    # 70000 -> inf, -65520 -> -inf, 65504, just below the midpoint
+                     0x358637BD, 0x33800000, 0x33000000, 0x33000001,    # 1e-6 (subnormal), 2^-24, 2^-25 (tie to 0), just above
+                     0x80000000, 0x38800000], dtype=np.uint32)          # -0, 2^-14 (smallest normal)
+
+
+@pytest.mark.parametrize("off", [0, 1], ids=["small_scorer", "conversion_kernel"])
+def test_phase_converts_special_values(off):
+    """fp32 queries with NaNs (payloads, signs, signalling), infinities,
+    overflow, the rounding at the fp16 maximum, subnormals and -0 in a few
+    token rows.  With 16-byte aligned queries and few rows the small scorer
+    converts them on load; one float off, the conversion kernel does.  Either
+    way the fp16 workspace holds the oracle's conversion bit for bit, and the
+    rows without special values score within the bound."""
+    G, nq, H, D, n_kv, k = 1, 40, 8, 128, 5 * 64 + 3, 4
+    cfg = qi.Config("specials", G, nq, H, D, n_kv, 64, k, "normal", 4321)
+    w = qi.conversion_fixture(cfg, seed=4321)
+    q32 = w.q32.copy()
+    dirty = [3, 7, 30]
+    for r in dirty:
+        flat = q32[r].reshape(-1).view(np.uint32)
+        flat[5 * r:5 * r + len(SPECIALS)] = SPECIALS
+    buf = torch.zeros((off + q32.size,), dtype=torch.float32, device=dev())
+    qd = buf[off:].view(nq, G, H, D)
+    qd.copy_(torch.from_numpy(q32))
+    ws = qsa.PhaseWorkspace(cfg.nq, cfg.G, cfg.H, cfg.D, cfg.n_kv, cfg.bs, cfg.k, dev())
+    ws.q16.fill_(0x7D5B)
+    kd = k_dev(w.kblk)
+    row = G * H * D
+    st = qsa.lib.qsa_select_phase(
+        ctypes.c_void_p(qd.data_ptr()), ctypes.c_void_p(ws.q16.data_ptr()), row,
+        ctypes.c_void_p(kd.data_ptr()), kd.stride(0), ctypes.c_void_p(ws.scores.data_ptr()),
+        ws.ld_s, ctypes.c_void_p(ws.ids.data_ptr()), k, None, G, nq, H, D, n_kv, 64, k, 0, None)
+    torch.cuda.synchronize()
+    assert st == 0, qsa.status_string(st)
+    got16 = ws.q16.cpu().numpy().view(np.uint16)
+    want16 = oracle.convert_f32_f16(q32)
+    assert np.array_equal(got16, want16), "converted queries differ from the oracle's rounding"
+    clean = np.setdiff1d(np.arange(nq), dirty)
+    s_gpu = ws.scores[0, :, :cfg.nb].cpu().numpy().astype(np.float64)[clean]
+    ref = oracle.scores(q32[clean], w.kblk, cfg.nb)
+    check_bound(s_gpu, ref, "specials, clean rows")
+
+
 @pytest.mark.parametrize("q_chunk", [0, 37, 64, 1000])
 def test_phase_chunked_equals_whole(q_chunk):
     cfg = qi.Config("chunk", 3, 150, 8, 128, 70 * 64 + 5, 64, 32, "normal", 77)
