@@ -357,6 +357,23 @@ def test_topk_bit_exact(case, k):
     assert np.all(vals[~sel] == -np.inf)
 
 
+@pytest.mark.parametrize("case", [c for c in topk_cases() if c[2] > 512], ids=lambda c: c[0])
+def test_topk_many_rows_path_bit_exact(case):
+    """The same rows repeated to 4096+ rows: the selector's many-rows launch
+    (four rows per workgroup instead of one): ids and values bit for bit
+    the oracle's top-k for k = 64 and k = 5."""
+    _, s, nb = case
+    reps = -(-4096 // s.shape[0])
+    big = np.ascontiguousarray(np.tile(s, (reps, 1)))
+    for k in (64, 5):
+        ids, vals = run_topk_dev(big, nb, k)
+        want_ids, _ = oracle.topk(big.astype(np.float64), k)
+        assert np.array_equal(ids, want_ids)
+        sel = ids >= 0
+        assert np.array_equal(vals[sel].view(np.uint32),
+                              big[np.nonzero(sel)[0], ids[sel]].view(np.uint32))
+
+
 def test_topk_k_larger_than_nb_and_empty_rows():
     s = np.arange(10, dtype=np.float32)[None, :].repeat(3, 0)
     ids, vals = run_topk_dev(s, 10, 16)
