@@ -368,6 +368,164 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     }
 }
 
+// The exact top-kk (kk <= 64) of `ncol` 64-wide columns of values held by one
+// wave (column jj of this wave is column col0 + jj of the row, block id
+// (col0 + jj)*64 + lane), returned as composites sorted descending over the
+// lanes (lane 0 largest, zero past the set).  The same steps as topk_kernel's
+// fast path (sampled threshold, candidates compacted into slot, bitonic sort)
+// with its exact bisection as the fallback; val(id) reads a value back by id.
+template <int NC, typename Val>
+__device__ __forceinline__ uint64_t wave_topk(const uint32_t (&xr)[NC], int col0, int kk, int nb,
+                                              int lane, uint64_t *slot, Val val) {
+    const uint64_t lt = (1ull << lane) - 1ull;
+    int32_t m1 = INT32_MIN, m2 = INT32_MIN;
+    #pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        const int32_t x = static_cast<int32_t>(xr[j]);
+        m2 = max(min(m1, x), min(max(m1, x), m2));
+        m1 = max(m1, x);
+    }
+    const uint32_t s1 = static_cast<uint32_t>(m1) ^ 0x80000000u;
+    const uint32_t s2 = static_cast<uint32_t>(m2) ^ 0x80000000u;
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 16; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        const int c = __popcll(ballot(s1 >= cand)) + __popcll(ballot(s2 >= cand));
+        if (c >= kk) T = cand;
+    }
+    const float th = __builtin_bit_cast(float, T ^ 0x80000000u);
+    uint32_t mask = 0;
+    #pragma unroll
+    for (int j = 0; j < NC; ++j)
+        mask |= static_cast<uint32_t>(__builtin_bit_cast(float, xr[j]) >= th) << j;
+    int C = 0;
+    int off = wave_excl_scan(__popc(mask), lane, &C);
+    if (C >= kk && C <= 128) {
+        while (mask) {
+            const int j = __builtin_ctz(mask);
+            mask &= mask - 1;
+            const int id = (col0 + j) * 64 + lane;
+            slot[off++] = composite(order_key(val(id)), id);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const uint64_t v0 = lane < C ? slot[lane] : 0ull;
+        if (C <= 64) return sort64_desc(v0, lane);
+        const uint64_t v1 = lane + 64 < C ? slot[lane + 64] : 0ull;
+        return top64_of_128(v0, v1, lane);
+    }
+    // exact path over the wave's columns
+    auto key = [&](int j) -> uint32_t { return order_key(__builtin_bit_cast(float, xr[j])); };
+    T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        int c = 0;
+        #pragma unroll
+        for (int j = 0; j < NC; ++j) c += __popcll(ballot(key(j) >= cand));
+        if (c >= kk) T = cand;
+    }
+    int cgt = 0;
+    #pragma unroll
+    for (int j = 0; j < NC; ++j) cgt += __popcll(ballot(key(j) > T));
+    int need = kk - cgt;
+    int base = 0;
+    #pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        const uint32_t kj = key(j);
+        const int id = (col0 + j) * 64 + lane;
+        const bool eq = (kj == T) && (id < nb);
+        const uint64_t meq = ballot(eq);
+        const bool tsel = eq && (__popcll(meq & lt) < need);
+        const int ceq = __popcll(meq);
+        need -= ceq < need ? ceq : need;
+        const bool sel = (kj > T) || tsel;
+        const uint64_t ms = ballot(sel);
+        if (sel) slot[base + __popcll(ms & lt)] = composite(kj, id);
+        base += __popcll(ms);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    return sort64_desc(lane < kk ? slot[lane] : 0ull, lane);
+}
+
+// Two composite lists, each sorted descending over the lanes: the 64 largest
+// of their union, sorted descending (the first merge step pairs element i of
+// one with element 63 - i of the other; the larger halves form a bitonic
+// sequence, which the half-cleaner cascade sorts).
+__device__ __forceinline__ uint64_t merge64(uint64_t v, uint64_t u_rev, int lane) {
+    uint64_t m = v > u_rev ? v : u_rev;
+    step1<32, 32>(m, lane);
+    step1<16, 16>(m, lane);
+    step1<8, 8>(m, lane);
+    step1<4, 4>(m, lane);
+    step1<2, 2>(m, lane);
+    step1<1, 1>(m, lane);
+    return m;
+}
+
+// Few rows of more than 512 blocks (latency-bound): one workgroup of four
+// waves per row.  Wave w takes columns [w*NC, (w+1)*NC) of the row and finds
+// their exact top-kk (wave_topk); the union of the four holds the row's
+// top-kk, and two levels of merge64 give it sorted.  Each wave's work is a
+// quarter of the one-wave kernel's load and candidate steps.
+template <int NC>
+__global__ __launch_bounds__(256) void topk_quad_kernel(TopkArgs a) {
+    __shared__ uint32_t row[4 * NC * 64];        // the row's raw fp32 bits (pad past nb)
+    __shared__ uint64_t slot[4][128];
+    __shared__ uint64_t lists[4][64];
+    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    const int64_t R = blockIdx.x;
+    if (R >= a.total_rows) return;               // whole workgroup
+    int64_t grp = 0, t = R;
+    if (a.rows_per_group != a.total_rows) {
+        grp = R / a.rows_per_group;
+        t = R - grp * a.rows_per_group;
+    }
+    const float *srow = a.scores + (grp * a.src_group_rows + t) * a.ld_s;
+    const int64_t drow = grp * a.dst_group_rows + a.dst_row0 + t;
+    const int nb = a.nb;
+    const int kk = min(a.k, nb);
+    const uint32_t kPad = 0xffffffffu;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(srow), 0, nb * 4, 0x00020000 /* 32-bit elements, raw */);
+    const int col0 = w * NC;
+    uint32_t xr[NC];
+    #pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        const int c = col0 + j;
+        const uint32_t x = __builtin_amdgcn_raw_buffer_load_b32(rs, (c * 64 + lane) * 4, 0, 0);
+        xr[j] = lane < nb - 64 * c ? x : kPad;
+        row[c * 64 + lane] = xr[j];
+    }
+    uint64_t v = 0;
+    if (kk > 0) {   // uniform
+        v = wave_topk<NC>(xr, col0, kk, nb, lane, slot[w],
+                          [&](int id) { return __builtin_bit_cast(float, row[id]); });
+        lists[w][lane] = v;
+    }
+    __syncthreads();
+    if (kk > 0 && (w & 1) == 0) {   // waves 0, 2: merge with wave w + 1
+        v = merge64(v, lists[w + 1][63 - lane], lane);
+        lists[w][lane] = v;
+    }
+    __syncthreads();
+    if (w != 0) return;
+    if (kk > 0) v = merge64(v, lists[2][63 - lane], lane);
+    if (lane < a.k) {
+        int32_t id = -1;
+        float val = -__builtin_inff();
+        if (lane < kk) {
+            id = static_cast<int32_t>(0xffffffffu - static_cast<uint32_t>(v));
+            val = __builtin_bit_cast(float, row[id]);
+        }
+        a.ids[drow * a.ld_ids + lane] = id;
+        if (a.vals) a.vals[drow * a.ld_ids + lane] = val;
+    }
+}
+
 typedef void (*topk_fn)(TopkArgs);
 
 topk_fn pick(int nb, int *npl_out) {
@@ -395,6 +553,19 @@ topk_fn pick(int nb, int *npl_out) {
 hipError_t launch_topk(const TopkGeom &geo, hipStream_t s) {
     const int64_t total = geo.n_groups * geo.rows_per_group;
     if (total <= 0 || geo.k <= 0) return hipSuccess;
+    const int ncol = (geo.nb + 63) / 64;
+    if (total < 4096 && ncol > 8 && ncol <= 64) {
+        // Few rows of more than 512 blocks: four waves per row.
+        TopkArgs qa{geo.scores, geo.ld_s, geo.ids, geo.ld_ids, geo.vals, total,
+                    geo.rows_per_group, geo.src_group_rows, geo.dst_group_rows, geo.dst_row0,
+                    geo.nb, geo.k};
+        topk_fn fn = ncol <= 16 ? topk_quad_kernel<4> : ncol <= 32 ? topk_quad_kernel<8>
+                   : ncol <= 36 ? topk_quad_kernel<9> : ncol <= 48 ? topk_quad_kernel<12>
+                                                       : topk_quad_kernel<16>;
+        void *qargs[] = {&qa};
+        return hipLaunchKernel(reinterpret_cast<const void *>(fn),
+                               dim3(static_cast<unsigned>(total)), dim3(256), qargs, 0, s);
+    }
     // One row per wave.  Few rows: one wave per workgroup, so that the rows
     // spread over all CUs; many rows: four per workgroup.
     const int wpb = total < 4096 ? 1 : 4;
