@@ -84,19 +84,30 @@ def read_traffic(kernel: str, workload: str):
 
 
 def scorer_kernel(cfg):
-    """The scorer kernel the library runs for this workload: the small scorer
-    when the KV heads x groups of 64 queries number fewer than 256, else the
-    wide one (head passes of up to eight heads); the tail block, when there
-    is one, is scored inside the same launch."""
+    """The scorer kernel the phase runs for this workload (fp32 queries,
+    converted on load): the small scorer when the KV heads x groups of 64
+    queries number fewer than 256, else the wide one (head passes of up to
+    eight heads); the tail block, when there is one, is scored inside the
+    same launch.  Returns the profile key and the kernel's name."""
+    tail = "true" if cfg.n_kv % cfg.bs else "false"
     if cfg.G * -(-cfg.nq // 64) < 256:
         np_ = 1 if cfg.H <= 2 else 2 if cfg.H <= 4 else 4 if cfg.H <= 8 else 8
-        return "score_small", f"score_small_kernel<{cfg.D},{np_}>"
-    return "score_full", f"score_full_kernel<{cfg.D},{min(4, (cfg.H + 1) // 2)}> (+ tail when present)"
+        return "score_small", f"score_small_kernel<{cfg.D},{np_},true>"
+    np_ = min(4, (cfg.H + 1) // 2)
+    return "score_full", f"score_full_kernel<{cfg.D},{np_},false,true,{tail},true>"
 
 
 class Phase:
     """Device buffers and raw C-ABI calls of one workload (no Python checks
-    inside the hot loop: arguments are validated once by a checked call)."""
+    inside the hot loop: arguments are validated once by a checked call).
+
+    The phase runs as a caller would run it: fp32 queries in, no fp16 copy
+    kept, so it is two launches, the scorer (converting the queries as it
+    loads them) and the selector.  Each is also timed alone: the scorer as
+    the phase with k = 0 (exactly the phase's scorer launch), the selector as
+    qsa_select_topk on the phase's scores.  The stand-alone conversion and
+    the fp16-input scorer (qsa_block_scores) are timed for reference; they
+    are not part of the phase."""
 
     def __init__(self, cfg, qsa, torch, w):
         import numpy as np
@@ -105,6 +116,7 @@ class Phase:
         self.q32 = torch.from_numpy(w.q32).to(dev)
         self.kb = torch.from_numpy(w.kblk.view(np.float16)).to(dev)
         self.ws = qsa.PhaseWorkspace(cfg.nq, cfg.G, cfg.H, cfg.D, cfg.n_kv, cfg.bs, cfg.k, dev)
+        self.q16 = torch.empty(self.q32.shape, dtype=torch.float16, device=dev)
         self.n_q = self.q32.numel()
         L = qsa.lib
         P = qsa._ptr
@@ -113,16 +125,18 @@ class Phase:
         qts = c.G * c.H * c.D
         # checked once through the binding
         qsa.select_phase(self.q32, self.kb, c.n_kv, c.bs, c.k, ws)
+        qsa.convert_f32_f16(self.q32, out=self.q16)
         torch.cuda.synchronize()
-        self._conv = (L.qsa_convert_f32_f16, (P(self.q32), P(ws.q16), self.n_q))
-        self._score = (L.qsa_block_scores, (P(ws.q16), qts, P(self.kb), self.kb.stride(0),
-                                            P(ws.scores), ws.ld_s, c.G, c.nq, c.H, c.D,
-                                            c.n_kv, c.bs))
+        self._conv = (L.qsa_convert_f32_f16, (P(self.q32), P(self.q16), self.n_q))
+        self._score16 = (L.qsa_block_scores, (P(self.q16), qts, P(self.kb), self.kb.stride(0),
+                                              P(ws.scores), ws.ld_s, c.G, c.nq, c.H, c.D,
+                                              c.n_kv, c.bs))
         self._topk = (L.qsa_select_topk, (P(ws.scores), ws.ld_s, c.rows, c.nb, c.k, P(ws.ids),
                                           c.k, None))
-        self._phase = (L.qsa_select_phase, (P(self.q32), P(ws.q16), qts, P(self.kb),
-                                            self.kb.stride(0), P(ws.scores), ws.ld_s, P(ws.ids),
-                                            c.k, None, c.G, c.nq, c.H, c.D, c.n_kv, c.bs, c.k, 0))
+        phase = (P(self.q32), None, qts, P(self.kb), self.kb.stride(0), P(ws.scores), ws.ld_s,
+                 P(ws.ids), c.k, None, c.G, c.nq, c.H, c.D, c.n_kv, c.bs)
+        self._phase = (L.qsa_select_phase, phase + (c.k, 0))
+        self._score = (L.qsa_select_phase, phase + (0, 0))   # k = 0: the scorer launch only
 
     def _call(self, fa):
         fn, args = fa
@@ -135,6 +149,9 @@ class Phase:
 
     def score(self):
         self._call(self._score)
+
+    def score16(self):
+        self._call(self._score16)
 
     def topk(self):
         self._call(self._topk)
@@ -189,10 +206,11 @@ def measure(cfg, qsa, torch, steps, warmup, w=None):
                 torch.equal(eager_scores.view(torch.int32), ph.ws.scores.view(torch.int32)))
     del g_phase
 
-    stages = {}
-    for name, fn in (("convert", ph.convert), ("scorer", ph.score), ("topk", ph.topk)):
+    stages, alone = {}, {}
+    for d, name, fn in ((stages, "scorer", ph.score), (stages, "topk", ph.topk),
+                        (alone, "convert", ph.convert), (alone, "block_scores_f16", ph.score16)):
         g = graph_of(torch, fn, steps)
-        stages[name] = time_graph(torch, g, steps)
+        d[name] = time_graph(torch, g, steps)
         del g
     flop = cfg.flop
     return {
@@ -200,6 +218,7 @@ def measure(cfg, qsa, torch, steps, warmup, w=None):
         "wall_s": wall,
         "graph_replay_matches_eager": same,
         "stages_ms": stages,
+        "entry_points_ms": alone,
         "scorer_tflops": flop / (stages["scorer"] * 1e-3) / 1e12,
         "phase_tflops": flop / (ms_step * 1e-3) / 1e12,
         "flop": flop,
@@ -246,8 +265,9 @@ def main():
           flush=True)
     res = measure(cfg, qsa, torch, args.steps, args.warmup)
     print(f"# {cfg.name}: {res['ms_per_step'] * 1e3:.2f} us/step, stages "
-          f"{ {k: round(v * 1e3, 2) for k, v in res['stages_ms'].items()} } us", file=sys.stderr,
-          flush=True)
+          f"{ {k: round(v * 1e3, 2) for k, v in res['stages_ms'].items()} } us, alone "
+          f"{ {k: round(v * 1e3, 2) for k, v in res['entry_points_ms'].items()} } us",
+          file=sys.stderr, flush=True)
 
     scorer_ms = res["stages_ms"]["scorer"]
     achieved = res["flop"] / (scorer_ms * 1e-3) / 1e12
@@ -267,13 +287,17 @@ def main():
         ps = pr["stages_ms"]
         hbm = {"convert": 6.0 * pc.nq * pc.G * pc.H * pc.D,
                "topk": 4.0 * pc.rows * pc.nb + 4.0 * pc.rows * pc.k}
+        pe = pr["entry_points_ms"]
         prefill = {
             "workload": pc.name, "ms_per_step": pr["ms_per_step"], "stages_ms": ps,
+            "entry_points_ms": pe,
             "scorer_tflops": pr["scorer_tflops"],
             "scorer_frac_of_peak": pr["scorer_tflops"] / PEAK_FP16_TFLOPS,
             "scorer_kernel": scorer_kernel(pc)[1],
             "scorer_traffic_bytes": read_traffic(scorer_kernel(pc)[0], pc.name),
-            "convert_gbs": hbm["convert"] / (ps["convert"] * 1e-3) / 1e9,
+            "convert_gbs": hbm["convert"] / (pe["convert"] * 1e-3) / 1e9,
+            "block_scores_f16_frac_of_peak":
+                pc.flop / (pe["block_scores_f16"] * 1e-3) / 1e12 / PEAK_FP16_TFLOPS,
             "topk_gbs": hbm["topk"] / (ps["topk"] * 1e-3) / 1e9,
             "graph_replay_matches_eager": pr["graph_replay_matches_eager"],
         }
@@ -287,10 +311,12 @@ def main():
         dr = measure(dc, qsa, torch, args.decode_steps, 20)
         ds = dr["stages_ms"]
         # the scorer streams every KV head's block keys once: HBM-bound
+        # (fp32 queries read, fp32 scores written)
         kbytes = 2.0 * dc.G * dc.nb * dc.D
-        sbytes = kbytes + 2.0 * dc.rows * dc.H * dc.D + 4.0 * dc.rows * dc.nb
+        sbytes = kbytes + 4.0 * dc.rows * dc.H * dc.D + 4.0 * dc.rows * dc.nb
         decode = {
             "workload": dc.name, "ms_per_step": dr["ms_per_step"], "stages_ms": ds,
+            "entry_points_ms": dr["entry_points_ms"],
             "scorer_kernel": scorer_kernel(dc)[1],
             "scorer_bytes": sbytes,
             "scorer_gbs": sbytes / (ds["scorer"] * 1e-3) / 1e9,
@@ -332,6 +358,7 @@ def main():
         "scorer_tflops": achieved,
         "scorer_frac_of_peak": achieved / PEAK_FP16_TFLOPS,
         "stages_ms": res["stages_ms"],
+        "entry_points_ms": res["entry_points_ms"],
         "graph_replay_matches_eager": res["graph_replay_matches_eager"],
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -65,7 +65,7 @@ typedef enum qsa_status {
     QSA_ERR_HIP = 3          /* the HIP runtime refused a launch */
 } qsa_status;
 
-#define QSA_ABI_VERSION 1
+#define QSA_ABI_VERSION 2
 #define QSA_MAX_K 64
 
 /* Version of this ABI (QSA_ABI_VERSION of the header the library was built
@@ -134,10 +134,17 @@ qsa_status qsa_select_topk(const float *scores, int64_t ld_s, int64_t rows, int3
  * q_chunk so that the score workspace holds only G*q_chunk rows.
  *   q32       device fp32 queries (layout of q16, same q_tok_stride), 4-byte
  *             aligned, or NULL
- *   q16       device fp16 bits: the input when q32 == NULL, else a workspace
- *             that receives the converted queries: exactly the G*H*D
- *             elements of each of the nq token rows are written (elements
- *             between rows, when q_tok_stride > G*H*D, are not touched)
+ *   q16       device fp16 bits: the input when q32 == NULL (required then);
+ *             with q32 either NULL or a buffer that receives the converted
+ *             queries: exactly the G*H*D elements of each of the nq token
+ *             rows are written (elements between rows, when q_tok_stride >
+ *             G*H*D, are not touched).  With q32 and 16-byte aligned fp32 rows
+ *             (q32 16-byte aligned, q_tok_stride % 8 == 0) the scorers convert
+ *             the queries as they load them, so the conversion costs no HBM
+ *             round trip of its own; storing them into q16 adds one write of
+ *             the fp16 rows.  q16 == NULL with fp32 rows that are only 4-byte
+ *             aligned: QSA_ERR_UNSUPPORTED (the conversion kernel would need
+ *             the buffer).
  *   scores_ws device fp32 [G*qc][ld_s] workspace, qc = q_chunk > 0 ?
  *             min(q_chunk, nq) : nq; for the chunk of n <= qc queries starting
  *             at query t0, row g*n + t' holds the scores of query t0 + t'

@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libqsa.so")
 
 QSA_OK, QSA_ERR_ARG, QSA_ERR_UNSUPPORTED, QSA_ERR_HIP = 0, 1, 2, 3
 MAX_K = 64
+ABI_VERSION = 2   # qsa.h QSA_ABI_VERSION this binding is written for
 EXPORTS = ("qsa_abi_version", "qsa_status_string", "qsa_convert_f32_f16", "qsa_block_scores",
            "qsa_select_topk", "qsa_select_phase")
 
@@ -50,6 +51,9 @@ def _load() -> ctypes.CDLL:
     L.qsa_select_phase.argtypes = [vp, vp, i64, vp, i64, vp, i64, vp, i64, vp, i32, i32, i32,
                                    i32, i64, i32, i32, i64, vp]
     L.qsa_select_phase.restype = ctypes.c_int
+    if L.qsa_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH}: ABI version {L.qsa_abi_version()}, this binding needs "
+                          f"{ABI_VERSION}; rebuild with __graft_entry__.build()")
     return L
 
 
@@ -160,10 +164,14 @@ def select_topk(scores: torch.Tensor, nb: int, k: int, ids: torch.Tensor | None 
 
 
 class PhaseWorkspace:
-    """Device buffers of one select phase, allocated once and reused."""
+    """Device buffers of one select phase, allocated once and reused.  With
+    keep_q16 the phase also stores the fp16 conversion of fp32 queries in
+    q16 (one more write of the queries); without it q16 is None and the
+    scorers convert the queries in registers only."""
 
     def __init__(self, nq: int, G: int, H: int, D: int, n_kv: int, bs: int, k: int,
-                 device="cuda", q_chunk: int = 0, with_vals: bool = False, ld_pad: int = 0):
+                 device="cuda", q_chunk: int = 0, with_vals: bool = False, ld_pad: int = 0,
+                 keep_q16: bool = False):
         self.nb = n_blocks(n_kv, bs)
         qc = q_chunk if 0 < q_chunk < nq else nq
         self.q_chunk = q_chunk
@@ -171,7 +179,8 @@ class PhaseWorkspace:
         # scorer then fills whole cache lines.
         self.ld_s = -(-(max(self.nb, 1) + ld_pad) // 32) * 32
         self.scores = torch.empty((G, qc, self.ld_s), dtype=torch.float32, device=device)
-        self.q16 = torch.empty((nq, G, H, D), dtype=torch.float16, device=device)
+        self.q16 = (torch.empty((nq, G, H, D), dtype=torch.float16, device=device)
+                    if keep_q16 else None)
         self.ids = torch.empty((G, nq, k), dtype=torch.int32, device=device)
         self.vals = torch.empty((G, nq, k), dtype=torch.float32, device=device) if with_vals else None
 
@@ -190,7 +199,7 @@ def select_phase(q: torch.Tensor, kblk: torch.Tensor, n_kv: int, bs: int, k: int
     if ws is None:
         ws = PhaseWorkspace(nq, G, H, D, n_kv, bs, k, q.device, q_chunk)
     q16 = ws.q16 if fp32 else q
-    if fp32 and q16.stride(0) != qts:
+    if fp32 and q16 is not None and q16.stride(0) != qts:
         raise ValueError("workspace q16 layout does not match the queries")
     _check("qsa_select_phase",
            lib.qsa_select_phase(_ptr(q) if fp32 else None, _ptr(q16), qts, _ptr(kblk), khs,

@@ -73,15 +73,18 @@ qsa_status check_topk_args(const float *scores, int64_t ld_s, int64_t rows, int3
 
 qsa_status hip_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_HIP; }
 
-hipError_t run_scores(const uint16_t *q16, int64_t qts, const uint16_t *kblk, int64_t khs,
-                      float *scores, int64_t ld_s, int32_t G, int32_t nq, int32_t H, int32_t D,
-                      const ScoreCheck &c, hipStream_t s) {
-    ScoreGeom geo{q16, qts, kblk, khs, scores, ld_s, G, nq, H, D, c.nf};
+// Scores of every block (full blocks and the tail).  With q32 the queries
+// are read as fp32 and converted on load (src32_ok holds), their fp16 bits
+// written to q16w when it is set; with no full block the small scorer then
+// scores the tail whatever the number of rows, since the standalone tail
+// kernel reads fp16 queries only.
+hipError_t run_scores(const ScoreGeom &geo, const ScoreCheck &c, hipStream_t s,
+                      const float *q32 = nullptr, uint16_t *q16w = nullptr) {
     const bool tail = c.nb > c.nf;
-    if (c.nf > 0) return qsa::launch_score_full(geo, tail, s);
+    if (c.nf > 0) return qsa::launch_score_full(geo, tail, s, q32, q16w);
     if (!tail) return hipSuccess;
-    return qsa::small_rows(geo) ? qsa::launch_score_small(geo, true, s)
-                                : qsa::launch_tail(geo, c.nf, s);
+    if (q32 || qsa::small_rows(geo)) return qsa::launch_score_small(geo, true, s, q32, q16w);
+    return qsa::launch_tail(geo, c.nf, s);
 }
 
 }  // namespace
@@ -116,8 +119,8 @@ qsa_status qsa_block_scores(const uint16_t *q16, int64_t q_tok_stride, const uin
     qsa_status st = check_scores_args(q16, q_tok_stride, kblk, kblk_head_stride, scores, ld_s, G,
                                       nq, H, D, n_kv, bs, &c);
     if (st != QSA_OK || G == 0 || nq == 0 || c.nb == 0) return st;
-    return hip_status(run_scores(q16, q_tok_stride, kblk, kblk_head_stride, scores, ld_s, G, nq,
-                                 H, D, c, static_cast<hipStream_t>(stream)));
+    ScoreGeom geo{q16, q_tok_stride, kblk, kblk_head_stride, scores, ld_s, G, nq, H, D, c.nf};
+    return hip_status(run_scores(geo, c, static_cast<hipStream_t>(stream)));
 }
 
 qsa_status qsa_select_topk(const float *scores, int64_t ld_s, int64_t rows, int32_t nb, int32_t k,
@@ -136,8 +139,10 @@ qsa_status qsa_select_phase(const float *q32, uint16_t *q16, int64_t q_tok_strid
     if (q_chunk < 0) return QSA_ERR_ARG;
     const int64_t qc = (q_chunk > 0 && q_chunk < nq) ? q_chunk : nq;
     ScoreCheck c;
-    // scores are validated for the chunk-sized workspace
-    qsa_status st = check_scores_args(q16, q_tok_stride, kblk, kblk_head_stride, scores_ws, ld_s,
+    // scores are validated for the chunk-sized workspace; the query source
+    // is the fp16 buffer when there is one, else the fp32 queries
+    const void *qsrc = q16 ? static_cast<const void *>(q16) : static_cast<const void *>(q32);
+    qsa_status st = check_scores_args(qsrc, q_tok_stride, kblk, kblk_head_stride, scores_ws, ld_s,
                                       G, static_cast<int32_t>(qc), H, D, n_kv, bs, &c);
     if (st != QSA_OK) return st;
     if (G == 0 || nq == 0) return QSA_OK;
@@ -150,47 +155,41 @@ qsa_status qsa_select_phase(const float *q32, uint16_t *q16, int64_t q_tok_strid
     st = check_topk_args(scores_ws, ld_s, rows, static_cast<int32_t>(c.nb), k, ids, ld_ids, vals);
     if (st != QSA_OK) return st;
     if (q32) {
-        if (!q16) return QSA_ERR_ARG;
         if (!aligned4(q32) || reinterpret_cast<uintptr_t>(q16) % 2 != 0)
             return QSA_ERR_UNSUPPORTED;
+        // without an fp16 buffer the scorers must read the fp32 rows directly
+        if (!q16 && !qsa::src32_ok(q32, q_tok_stride)) return QSA_ERR_UNSUPPORTED;
+    } else if (!q16) {
+        return QSA_ERR_ARG;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
 
-    // Few query rows in one pass: the small scorer reads the fp32 queries,
-    // converts them on load and writes the fp16 workspace rows itself, so
-    // the conversion launch is folded into the scorer.
-    if (q32 && qc == nq && c.nb > 0) {
-        ScoreGeom geo{q16, q_tok_stride, kblk, kblk_head_stride, scores_ws, ld_s, G, nq, H, D,
-                      c.nf};
-        if (qsa::small_rows(geo) && qsa::small_src32_ok(q32, q_tok_stride)) {
-            hipError_t e = qsa::launch_score_small(geo, c.nb > c.nf, s, q32, q16);
-            if (e == hipSuccess && k > 0) {
-                TopkGeom tg{scores_ws, ld_s, ids, ld_ids, vals, G, nq, nq, nq, 0,
-                            static_cast<int32_t>(c.nb), k};
-                e = qsa::launch_topk(tg, s);
-            }
-            return e == hipSuccess ? QSA_OK : QSA_ERR_HIP;
-        }
-    }
-
-    // the conversion writes exactly the token rows (G*H*D elements each)
-    if (q32) {
-        hipError_t e = qsa::launch_convert_rows(q32, q16, nq, static_cast<int64_t>(G) * H * D,
-                                                q_tok_stride, s);
-        if (e != hipSuccess) return QSA_ERR_HIP;
-    }
     for (int64_t t0 = 0; t0 < nq; t0 += qc) {
         const int32_t n = static_cast<int32_t>((nq - t0 < qc) ? nq - t0 : qc);
+        const int64_t qoff = t0 * q_tok_stride;
+        uint16_t *q16c = q16 ? q16 + qoff : nullptr;   // may be null when nb == 0
+        ScoreGeom geo{q16c, q_tok_stride, kblk, kblk_head_stride, scores_ws, ld_s, G, n, H, D,
+                      c.nf};
+        // With 16-byte aligned fp32 queries the scorer reads them itself,
+        // converts them on load and writes this chunk's rows of the fp16
+        // buffer (if any), so the conversion needs no launch of its own;
+        // otherwise the conversion kernel writes exactly the chunk's token
+        // rows (G*H*D elements each) first.
+        const bool fused = q32 && c.nb > 0 && qsa::src32_ok(q32 + qoff, q_tok_stride);
+        if (q32 && !fused && q16c) {
+            hipError_t e = qsa::launch_convert_rows(q32 + qoff, q16c, n,
+                                                    static_cast<int64_t>(G) * H * D, q_tok_stride, s);
+            if (e != hipSuccess) return QSA_ERR_HIP;
+        }
         if (c.nb > 0) {
-            hipError_t e = run_scores(q16 + t0 * q_tok_stride, q_tok_stride, kblk,
-                                      kblk_head_stride, scores_ws, ld_s, G, n, H, D, c, s);
+            hipError_t e = fused ? run_scores(geo, c, s, q32 + qoff, q16c) : run_scores(geo, c, s);
             if (e != hipSuccess) return QSA_ERR_HIP;
         }
         if (k > 0) {
             // the scorer wrote this chunk's rows at g*n + t' (n = rows in the chunk)
-            TopkGeom geo{scores_ws, ld_s, ids, ld_ids, vals, G, n, n, nq, t0,
-                         static_cast<int32_t>(c.nb), k};
-            hipError_t e = qsa::launch_topk(geo, s);
+            TopkGeom tg{scores_ws, ld_s, ids, ld_ids, vals, G, n, n, nq, t0,
+                        static_cast<int32_t>(c.nb), k};
+            hipError_t e = qsa::launch_topk(tg, s);
             if (e != hipSuccess) return QSA_ERR_HIP;
         }
     }

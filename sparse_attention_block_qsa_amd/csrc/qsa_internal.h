@@ -27,6 +27,30 @@ __device__ __forceinline__ uint32_t f16_rne(float x) {
     return h;
 }
 
+// Eight fp32 values to fp16 bits (two dwords each), f16_rne per element.
+__device__ __forceinline__ uint4 f16x8_exact(const float4 &x0, const float4 &x1) {
+    return make_uint4(f16_rne(x0.x) | (f16_rne(x0.y) << 16), f16_rne(x0.z) | (f16_rne(x0.w) << 16),
+                      f16_rne(x1.x) | (f16_rne(x1.y) << 16), f16_rne(x1.z) | (f16_rne(x1.w) << 16));
+}
+
+// The same with the bare hardware conversion: equal to f16x8_exact for every
+// input that is not a NaN (max_mag_bits tells whether there is one).
+__device__ __forceinline__ uint4 f16x8_cvt(const float4 &x0, const float4 &x1) {
+    auto h = [](float x) -> uint32_t { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x)); };
+    return make_uint4(h(x0.x) | (h(x0.y) << 16), h(x0.z) | (h(x0.w) << 16),
+                      h(x1.x) | (h(x1.y) << 16), h(x1.z) | (h(x1.w) << 16));
+}
+
+// Largest magnitude bit pattern of eight fp32 values: a NaN among them iff
+// the result is > 0x7f800000.
+__device__ __forceinline__ uint32_t max_mag_bits(const float4 &x0, const float4 &x1) {
+    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    uint32_t m = 0;
+    #pragma unroll
+    for (int e = 0; e < 8; ++e) m = max(m, __builtin_bit_cast(uint32_t, xs[e]) & 0x7fffffffu);
+    return m;
+}
+
 struct ScoreGeom {
     const uint16_t *q16;
     int64_t qts;          // elements between tokens
@@ -41,15 +65,19 @@ struct ScoreGeom {
 // Full-block MFMA scorer over blocks [0, nf).  Many query rows: one kernel
 // per head pass of up to eight heads; few: the small scorer.  With tail
 // (requires nf > 0) block nf is scored too, in the fixed order of the tail
-// model, inside the same launches.
-hipError_t launch_score_full(const ScoreGeom &g, bool tail, hipStream_t s);
+// model, inside the same launches.  With q32 set (src32_ok) the queries are
+// read as fp32 in the layout of g.q16, converted on load (f16_rne bits), and
+// their fp16 bits written to q16w when it is set: the G*H*D elements of every
+// token row, nothing between rows.
+hipError_t launch_score_full(const ScoreGeom &g, bool tail, hipStream_t s,
+                             const float *q32 = nullptr, uint16_t *q16w = nullptr);
 
 // Few query rows (fewer than 256 groups of 64 over the KV heads): the
 // scorer of qsa_small.hip, latency-bound shapes.
 bool small_rows(const ScoreGeom &g);
 
-// fp32 queries the small scorer can read directly (16-byte vector loads).
-bool small_src32_ok(const float *q32, int64_t qts);
+// fp32 queries the scorers can read directly (16-byte vector loads).
+bool src32_ok(const float *q32, int64_t qts);
 
 // The small scorer: blocks [0, nf) and, with tail, the partial block nf in
 // the fixed order of the tail model (also when nf == 0).  With q32 set the

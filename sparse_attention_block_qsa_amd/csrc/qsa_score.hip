@@ -35,6 +35,10 @@
 //    last split of each query group, from the same resident query registers,
 //    in the fixed fma order of the tail model, so the queries are read from
 //    HBM once for all nb blocks.
+//  * fp32 queries (the select phase) are read and converted to fp16 bits on
+//    load, with the rounding of the conversion kernel (f16_rne), and the first split
+//    of each query group writes those bits to the fp16 workspace: the
+//    phase needs no conversion launch and reads the queries from HBM once.
 //  * Grid: (KV head, 64-query group, block split), with logical ids laid out
 //    so that each XCD (blockIdx % 8) takes a contiguous range: the splits of
 //    one query group and the query groups of one KV head share that XCD's L2.
@@ -47,7 +51,9 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 struct ScoreArgs {
-    const uint16_t *q16;
+    const uint16_t *q16;   // query source when q32 is null
+    const float *q32;      // query source when set, converted on load
+    uint16_t *q16w;        // with q32: receives the converted rows, or null
     int64_t qts;
     const uint16_t *kblk;
     int64_t khs;
@@ -81,7 +87,7 @@ __device__ __forceinline__ float relu_bits(float x) {
     return __builtin_bit_cast(float, max(__builtin_bit_cast(int32_t, x), 0));
 }
 
-template <int D, int NP, bool ACCUM, bool BUF, bool TAIL>
+template <int D, int NP, bool ACCUM, bool BUF, bool TAIL, bool SRC32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void score_full_kernel(ScoreArgs a) {
     constexpr int KS = D / 16;              // MFMA K-steps per head
@@ -146,28 +152,98 @@ void score_full_kernel(ScoreArgs a) {
     // lane loads from an in-bounds address, without branches.  Rows of
     // queries past nq read query 0: they only feed MFMA rows that are never
     // stored.  A head past the pass (only the second head of the last pair,
-    // when nh is odd) is zeroed, since it would enter the head sum.
+    // when nh is odd) is zeroed, since it would enter the head sum.  fp32
+    // queries (SRC32) are converted on load; the first split of each query
+    // group writes their fp16 bits for the real rows and heads, so every
+    // element of the workspace is written exactly once.
     half8 qa[NP][KS];
+    const int hh = (l >> 4) & 1;   // this lane's head within a pair
+    // This lane's row of head hh in the workspace, channel 8*(l/32) (head
+    // 2p + hh is 2p*D further on), or null when it writes nothing: the first
+    // split of each query group writes the real rows.
+    uint16_t *qw = nullptr;
     {
-        const int tq = l & 15, hh = (l >> 4) & 1, kc = l >> 5;
+        const int tq = l & 15, kc = l >> 5;
         const int t = t_base + tq;
         const int64_t trow = static_cast<int64_t>(t < a.nq ? t : 0) * a.qts;
-        const uint16_t *src[NP];
+        int64_t qoff[NP];
         #pragma unroll
         for (int p = 0; p < NP; ++p) {
             const int h = 2 * p + hh;
-            src[p] = a.q16 + trow + static_cast<int64_t>(g * a.H + a.h0 + (h < a.nh ? h : 0)) * D +
-                     8 * kc;
+            qoff[p] = trow + static_cast<int64_t>(g * a.H + a.h0 + (h < a.nh ? h : 0)) * D + 8 * kc;
         }
-        #pragma unroll
-        for (int s = 0; s < KS; ++s) {
+        if (SRC32 && a.q16w != nullptr && split == 0 && t < a.nq && hh < a.nh)
+            qw = a.q16w + qoff[0];
+        if constexpr (!SRC32) {
             #pragma unroll
-            for (int p = 0; p < NP; ++p) qa[p][s] = *reinterpret_cast<const half8 *>(src[p] + 16 * s);
+            for (int s = 0; s < KS; ++s) {
+                #pragma unroll
+                for (int p = 0; p < NP; ++p)
+                    qa[p][s] = *reinterpret_cast<const half8 *>(a.q16 + qoff[p] + 16 * s);
+            }
+        } else {
+            // fp32 fragments (8 VGPRs each, twice the fp16 size) in batches
+            // of kQBatch, kQDepth batches in flight: each batch is converted
+            // as it lands and the registers it frees take the next batch's
+            // loads.  Left free, the compiler hoists every load above the
+            // conversions and runs out of registers.
+            constexpr int F = KS * NP;                    // fragments, K-step major
+            // (the accumulating pass with 64-bit store addressing holds more
+            // registers: one batch fewer in flight)
+            constexpr int kQBatch = 4, kQDepth = (ACCUM && !BUF) ? 3 : 4;
+            constexpr int NBAT = (F + kQBatch - 1) / kQBatch;
+            float4 x0[F], x1[F];
+            auto issue = [&](int b) {
+                #pragma unroll
+                for (int j = 0; j < kQBatch; ++j) {
+                    const int f = b * kQBatch + j;
+                    if (f < F) {
+                        const float *src = a.q32 + qoff[f % NP] + 16 * (f / NP);
+                        x0[f] = *reinterpret_cast<const float4 *>(src);
+                        x1[f] = *reinterpret_cast<const float4 *>(src + 4);
+                    }
+                }
+            };
+            #pragma unroll
+            for (int b = 0; b < kQDepth && b < NBAT; ++b) issue(b);
+            #pragma unroll
+            for (int b = 0; b < NBAT; ++b) {
+                #pragma unroll
+                for (int j = 0; j < kQBatch; ++j) {
+                    const int f = b * kQBatch + j;
+                    if (f < F) {
+                        const uint4 h = f16x8_exact(x0[f], x1[f]);
+                        qa[f % NP][f / NP] = __builtin_bit_cast(half8, h);
+                        // an empty statement that uses the converted fragment
+                        // and orders memory: the conversion stays before the
+                        // next batch's loads, which cannot move above it
+                        asm volatile("" ::"v"(h.x), "v"(h.y), "v"(h.z), "v"(h.w) : "memory");
+                    }
+                }
+                if (b + kQDepth < NBAT) issue(b + kQDepth);
+            }
         }
         if (2 * NP > a.nh) {   // uniform
             #pragma unroll
             for (int s = 0; s < KS; ++s)
                 if (hh) qa[NP - 1][s] = half8{};
+        }
+    }
+
+    // The converted queries into the fp16 workspace (SRC32, when the caller
+    // gave one), after the last query load: the workspace may alias the fp32
+    // queries as far as the compiler knows, so a store between the loads
+    // would hold back every load after it.  Temporal stores: the 32-byte
+    // pieces of each line merge in L2.
+    if constexpr (SRC32) {
+        if (qw != nullptr) {
+            #pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                #pragma unroll
+                for (int p = 0; p < NP; ++p)
+                    if (2 * p + hh < a.nh)
+                        *reinterpret_cast<uint4 *>(qw + 2 * p * D + 16 * s) = __builtin_bit_cast(uint4, qa[p][s]);
+            }
         }
     }
 
@@ -373,26 +449,26 @@ typedef void (*score_fn)(ScoreArgs);
 // per SIMD; more heads take a second, accumulating pass.
 constexpr int kHeadsPerPass = 8;
 
-template <int D, bool BUF, bool TAIL>
+template <int D, bool BUF, bool TAIL, bool SRC32>
 score_fn pick_d(int np, bool accum) {
     switch (np) {
-        case 1: return accum ? score_full_kernel<D, 1, true, BUF, TAIL> : score_full_kernel<D, 1, false, BUF, TAIL>;
-        case 2: return accum ? score_full_kernel<D, 2, true, BUF, TAIL> : score_full_kernel<D, 2, false, BUF, TAIL>;
-        case 3: return accum ? score_full_kernel<D, 3, true, BUF, TAIL> : score_full_kernel<D, 3, false, BUF, TAIL>;
-        case 4: return accum ? score_full_kernel<D, 4, true, BUF, TAIL> : score_full_kernel<D, 4, false, BUF, TAIL>;
+        case 1: return accum ? score_full_kernel<D, 1, true, BUF, TAIL, SRC32> : score_full_kernel<D, 1, false, BUF, TAIL, SRC32>;
+        case 2: return accum ? score_full_kernel<D, 2, true, BUF, TAIL, SRC32> : score_full_kernel<D, 2, false, BUF, TAIL, SRC32>;
+        case 3: return accum ? score_full_kernel<D, 3, true, BUF, TAIL, SRC32> : score_full_kernel<D, 3, false, BUF, TAIL, SRC32>;
+        case 4: return accum ? score_full_kernel<D, 4, true, BUF, TAIL, SRC32> : score_full_kernel<D, 4, false, BUF, TAIL, SRC32>;
     }
     return nullptr;
 }
 
-template <int D>
+template <int D, bool SRC32>
 score_fn pick_dt(int np, bool accum, bool buf, bool tail) {
-    if (tail) return buf ? pick_d<D, true, true>(np, accum) : pick_d<D, false, true>(np, accum);
-    return buf ? pick_d<D, true, false>(np, accum) : pick_d<D, false, false>(np, accum);
+    if (tail) return buf ? pick_d<D, true, true, SRC32>(np, accum) : pick_d<D, false, true, SRC32>(np, accum);
+    return buf ? pick_d<D, true, false, SRC32>(np, accum) : pick_d<D, false, false, SRC32>(np, accum);
 }
 
-score_fn pick(int D, int np, bool accum, bool buf, bool tail) {
-    if (D == 128) return pick_dt<128>(np, accum, buf, tail);
-    if (D == 64) return pick_dt<64>(np, accum, buf, tail);
+score_fn pick(int D, int np, bool accum, bool buf, bool tail, bool src32) {
+    if (D == 128) return src32 ? pick_dt<128, true>(np, accum, buf, tail) : pick_dt<128, false>(np, accum, buf, tail);
+    if (D == 64) return src32 ? pick_dt<64, true>(np, accum, buf, tail) : pick_dt<64, false>(np, accum, buf, tail);
     return nullptr;
 }
 
@@ -411,9 +487,10 @@ void split_blocks(int64_t base, int64_t n_tiles, int64_t target, int64_t *splits
 
 }  // namespace
 
-hipError_t launch_score_full(const ScoreGeom &geo, bool tail, hipStream_t s) {
+hipError_t launch_score_full(const ScoreGeom &geo, bool tail, hipStream_t s, const float *q32,
+                             uint16_t *q16w) {
     if (geo.nf <= 0 || geo.nq <= 0 || geo.G <= 0) return hipSuccess;
-    if (small_rows(geo)) return launch_score_small(geo, tail, s);
+    if (small_rows(geo)) return launch_score_small(geo, tail, s, q32, q16w);
     const int hpp = kHeadsPerPass;
     // buffer stores address one KV head's rows with 32-bit offsets below 2^30
     const bool buf = static_cast<int64_t>(geo.nq) * geo.ld_s * 4 < (int64_t(1) << 30);
@@ -431,9 +508,9 @@ hipError_t launch_score_full(const ScoreGeom &geo, bool tail, hipStream_t s) {
     for (int h0 = 0; h0 < geo.H; h0 += hpp) {
         const int nh = (geo.H - h0 < hpp) ? geo.H - h0 : hpp;
         const int np = (nh + 1) / 2;
-        score_fn fn = pick(geo.D, np, h0 > 0, buf, tail);
+        score_fn fn = pick(geo.D, np, h0 > 0, buf, tail, q32 != nullptr);
         if (!fn) return hipErrorInvalidValue;
-        ScoreArgs a{geo.q16, geo.qts, geo.kblk, geo.khs, geo.scores, geo.ld_s,
+        ScoreArgs a{geo.q16, q32, q32 ? q16w : nullptr, geo.qts, geo.kblk, geo.khs, geo.scores, geo.ld_s,
                     geo.G, geo.nq, geo.H, h0, nh, h0 > 0 ? 1 : 0, geo.nf,
                     static_cast<int32_t>(n_qgroups), static_cast<int32_t>(splits),
                     static_cast<int32_t>(tps), static_cast<int32_t>(n_tiles)};

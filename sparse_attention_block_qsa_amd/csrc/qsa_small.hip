@@ -22,8 +22,9 @@
 //    order of the wide scorer, so both produce the same bits.
 //  * With fp32 queries (the select phase) the fragments are converted on
 //    load with the rounding of the conversion kernel, and the first segment
-//    of each query group writes the converted rows to the fp16 workspace, so
-//    the phase needs no conversion launch for few rows.
+//    of each query group writes the converted rows to the caller's fp16
+//    buffer when there is one: the phase needs no conversion launch.  With
+//    no full block (a tail only) this kernel serves any number of rows.
 //  * The partial last block (n_kv mod bs != 0) is scored by the last segment
 //    in the fixed fma order of the tail model, one lane per (query, head).
 #include "qsa_internal.h"
@@ -67,27 +68,6 @@ __device__ __forceinline__ uint32_t xcd_logical_id(uint32_t bid, uint32_t nblk) 
     return x * q + (x < r ? x : r) + idx;
 }
 
-// Eight fp32 values to fp16 bits, rounded to nearest even: the hardware
-// conversion, which is f16_rne for every input but NaN; a fragment in which
-// some lane holds a NaN takes f16_rne itself (its NaN rule), so the bits
-// equal those of the conversion kernel.
-__device__ __forceinline__ uint4 f16x8(const float4 &x0, const float4 &x1) {
-    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-    uint32_t m = 0;
-    #pragma unroll
-    for (int e = 0; e < 8; ++e) m = max(m, __builtin_bit_cast(uint32_t, xs[e]) & 0x7fffffffu);
-    uint32_t h[8];
-    if (__builtin_amdgcn_ballot_w64(m > 0x7f800000u)) {   // uniform: a NaN somewhere
-        #pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = f16_rne(xs[e]);
-    } else {
-        #pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(xs[e]));
-    }
-    return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                      h[6] | (h[7] << 16));
-}
-
 __device__ __forceinline__ float h2f(uint32_t bits16) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
 }
@@ -125,57 +105,82 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
     const bool a_ok = t_in < a.nq && h_in < a.H;
     const int64_t a_off = static_cast<int64_t>(a_ok ? t_in : 0) * a.qts +
                           static_cast<int64_t>(g * a.H + (a_ok ? h_in : 0)) * D + 8 * kc;
-    half8 qa[KS];
-    #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        if constexpr (SRC32) {
-            const float4 x0 = *reinterpret_cast<const float4 *>(a.q32 + a_off + 16 * s);
-            const float4 x1 = *reinterpret_cast<const float4 *>(a.q32 + a_off + 16 * s + 4);
-            const uint4 hv = f16x8(x0, x1);
-            // one writer per element: the first segment, real rows only
-            if (a.q16w && seg == 0 && a_ok)
-                *reinterpret_cast<uint4 *>(a.q16w + a_off + 16 * s) = hv;
-            qa[s] = a_ok ? __builtin_bit_cast(half8, hv) : half8{};
-        } else {
-            const half8 v = *reinterpret_cast<const half8 *>(a.q16 + a_off + 16 * s);
-            qa[s] = a_ok ? v : half8{};
-        }
-    }
 
     const int tb = seg * a.tiles_per_seg;
     const int te = min(a.n_tiles, tb + a.tiles_per_seg);
     const uint16_t *kg = a.kblk + static_cast<int64_t>(g) * a.khs;
     float *sbase = a.scores + static_cast<int64_t>(g) * a.nq * a.ld_s;
 
+    // K staging in chunks of kSmallChunk tiles, double-buffered: the loads of
+    // chunk c+1 are in flight while chunk c is scored, one barrier per chunk.
+    // LDS index u = threadIdx.x + 256*j of a tile is chunk-major (u = chunk*32
+    // + block), the B-fragment order: lane l of K-step s reads u = 64*s + l.
+    // Blocks past nf, and tiles past the segment, feed output columns that
+    // are never stored: their indices are clamped.
+    const int64_t last = a.nf - 1;
+    auto kload = [&](int tile, int j) {
+        const int u = static_cast<int>(threadIdx.x) + 256 * j;
+        const int64_t b = min(static_cast<int64_t>(min(tile, te - 1)) * kTileBlocks +
+                                  (u % kTileBlocks), last);
+        return *reinterpret_cast<const uint4 *>(kg + b * D + 8 * (u / kTileBlocks));
+    };
+    uint4 st[kSmallChunk][LOADS];
+    auto fetch = [&](int t0) {
+        #pragma unroll
+        for (int i = 0; i < kSmallChunk; ++i)
+            #pragma unroll
+            for (int j = 0; j < LOADS; ++j) st[i][j] = kload(t0 + i, j);
+    };
+    auto publish = [&](int buf) {
+        #pragma unroll
+        for (int i = 0; i < kSmallChunk; ++i)
+            #pragma unroll
+            for (int j = 0; j < LOADS; ++j) kbuf[buf][i][threadIdx.x + 256 * j] = st[i][j];
+    };
+    // the first chunk's loads go out before the queries', so that the two
+    // latencies overlap
+    if (tb < te) fetch(tb);   // uniform over the workgroup
+
+    // ---- A operand: all KS fragments' loads in flight together.  fp32
+    // queries are converted once they have landed, by the bare hardware
+    // conversion unless the wave holds a NaN (one decision per wave, so no
+    // branch between the loads), and the first segment of each query group
+    // writes the converted rows (real rows only) to the fp16 workspace when
+    // there is one.
+    half8 qa[KS];
+    if constexpr (SRC32) {
+        float4 x0[KS], x1[KS];
+        #pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            x0[s] = *reinterpret_cast<const float4 *>(a.q32 + a_off + 16 * s);
+            x1[s] = *reinterpret_cast<const float4 *>(a.q32 + a_off + 16 * s + 4);
+        }
+        uint32_t m = 0;
+        #pragma unroll
+        for (int s = 0; s < KS; ++s) m = max(m, max_mag_bits(x0[s], x1[s]));
+        uint4 hv[KS];
+        if (__builtin_amdgcn_ballot_w64(m > 0x7f800000u)) {   // uniform: a NaN somewhere
+            #pragma unroll
+            for (int s = 0; s < KS; ++s) hv[s] = f16x8_exact(x0[s], x1[s]);
+        } else {
+            #pragma unroll
+            for (int s = 0; s < KS; ++s) hv[s] = f16x8_cvt(x0[s], x1[s]);
+        }
+        #pragma unroll
+        for (int s = 0; s < KS; ++s) qa[s] = a_ok ? __builtin_bit_cast(half8, hv[s]) : half8{};
+        if (a.q16w && seg == 0 && a_ok) {
+            #pragma unroll
+            for (int s = 0; s < KS; ++s) *reinterpret_cast<uint4 *>(a.q16w + a_off + 16 * s) = hv[s];
+        }
+    } else {
+        #pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const half8 v = *reinterpret_cast<const half8 *>(a.q16 + a_off + 16 * s);
+            qa[s] = a_ok ? v : half8{};
+        }
+    }
+
     if (tb < te) {   // uniform over the workgroup
-        // K staging in chunks of CH tiles, double-buffered: the loads of
-        // chunk c+1 are in flight while chunk c is scored, one barrier per
-        // chunk.  LDS index u = threadIdx.x + 256*j of a tile is chunk-major
-        // (u = chunk*32 + block), the B-fragment order: lane l of K-step s
-        // reads u = 64*s + l.  Blocks past nf, and tiles past the segment,
-        // feed output columns that are never stored: their indices are
-        // clamped.
-        const int64_t last = a.nf - 1;
-        auto kload = [&](int tile, int j) {
-            const int u = static_cast<int>(threadIdx.x) + 256 * j;
-            const int64_t b = min(static_cast<int64_t>(min(tile, te - 1)) * kTileBlocks +
-                                      (u % kTileBlocks), last);
-            return *reinterpret_cast<const uint4 *>(kg + b * D + 8 * (u / kTileBlocks));
-        };
-        uint4 st[kSmallChunk][LOADS];
-        auto fetch = [&](int t0) {
-            #pragma unroll
-            for (int i = 0; i < kSmallChunk; ++i)
-                #pragma unroll
-                for (int j = 0; j < LOADS; ++j) st[i][j] = kload(t0 + i, j);
-        };
-        auto publish = [&](int buf) {
-            #pragma unroll
-            for (int i = 0; i < kSmallChunk; ++i)
-                #pragma unroll
-                for (int j = 0; j < LOADS; ++j) kbuf[buf][i][threadIdx.x + 256 * j] = st[i][j];
-        };
-        fetch(tb);
         publish(0);
         __syncthreads();
         int buf = 0;
@@ -306,7 +311,7 @@ bool small_rows(const ScoreGeom &geo) {
     return static_cast<int64_t>(geo.G) * wide_groups < 256;
 }
 
-bool small_src32_ok(const float *q32, int64_t qts) {
+bool src32_ok(const float *q32, int64_t qts) {
     return reinterpret_cast<uintptr_t>(q32) % 16 == 0 && qts % 4 == 0;
 }
 

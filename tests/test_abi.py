@@ -136,8 +136,10 @@ def phase_call(lib, **kw):
 
 @pytest.mark.parametrize("kw,want", [
     (dict(q_chunk=-1), ARG), (dict(k=65), UNSUP), (dict(D=80), UNSUP), (dict(ids=None), ARG),
-    (dict(q16=None), ARG), (dict(ws=None), ARG), (dict(ld_ids=8), ARG), (dict(ld_s=10), ARG),
-    (dict(q32=A16 + 2), UNSUP), (dict(H=20), UNSUP),
+    (dict(q16=None, q32=None), ARG), (dict(ws=None), ARG), (dict(ld_ids=8), ARG),
+    (dict(ld_s=10), ARG), (dict(q32=A16 + 2), UNSUP), (dict(H=20), UNSUP),
+    # no fp16 buffer: the fp32 rows must be 16-byte aligned
+    (dict(q16=None, q32=A16 + 4), UNSUP), (dict(q16=None, qts=8 * 128 + 2), UNSUP),
 ])
 def test_select_phase_refusals(lib, kw, want):
     assert phase_call(lib, **kw) == want

@@ -397,7 +397,8 @@ def test_phase_with_fp32_queries_not_fp16_exact():
     w = qi.conversion_fixture(cfg)
     q32 = torch.from_numpy(w.q32).to(dev())
     kd = k_dev(w.kblk)
-    ws = qsa.PhaseWorkspace(cfg.nq, cfg.G, cfg.H, cfg.D, cfg.n_kv, cfg.bs, cfg.k, dev())
+    ws = qsa.PhaseWorkspace(cfg.nq, cfg.G, cfg.H, cfg.D, cfg.n_kv, cfg.bs, cfg.k, dev(),
+                            keep_q16=True)
     ids = qsa.select_phase(q32, kd, cfg.n_kv, cfg.bs, cfg.k, ws)
     torch.cuda.synchronize()
     q16_gpu = ws.q16.cpu().numpy().view(np.uint16)
@@ -411,15 +412,23 @@ def test_phase_with_fp32_queries_not_fp16_exact():
     check_ids(ids.reshape(cfg.rows, cfg.k).cpu().numpy(), s_gpu, ref, cfg.k, "conversion")
 
 
-# G, nq, H, D, n_kv, bs, k, tok_pad, q32 offset in floats.  Padded token rows
-# take the strided conversion kernel, contiguous ones the vector kernel; an
-# offset of one float leaves the fp32 rows only 4-byte aligned.
+# G, nq, H, D, n_kv, bs, k, tok_pad, q32 offset in floats.  16-byte aligned
+# fp32 rows are read and converted by the scorers themselves (small rows, or
+# no full block: the small scorer; G*ceil(nq/64) >= 256: the wide one); an
+# offset of one float leaves the fp32 rows only 4-byte aligned, and the
+# conversion kernel (strided for padded rows) runs first.
 PHASE_CONV = [
     (2, 70, 12, 64, 65 * 64 + 5, 64, 8, 24, 0),    # padded rows, two head passes
     (2, 70, 12, 64, 65 * 64 + 5, 64, 8, 24, 1),    # padded rows, 4-byte aligned fp32
     (1, 33, 8, 128, 40, 64, 4, 8, 0),              # only a tail block
     (3, 129, 5, 128, 100 * 64 + 3, 64, 16, 0, 0),  # contiguous, odd H
     (1, 40, 8, 128, 10 * 64 + 7, 64, 8, 0, 1),     # contiguous, 4-byte aligned fp32
+    # wide rows: two block splits (only the first writes the workspace),
+    # padded rows, two head passes
+    (4, 4096, 12, 64, 40 * 64 + 5, 64, 8, 24, 0),
+    (4, 4096, 3, 128, 70 * 64, 64, 8, 8, 0),       # wide, odd H, three tiles, no tail
+    (4, 4096, 5, 128, 3 * 64 + 3, 64, 4, 0, 1),    # wide, 4-byte aligned: conversion kernel
+    (4, 4096, 8, 128, 40, 64, 4, 0, 0),            # many rows, no full block: tail only
 ]
 
 
@@ -427,8 +436,10 @@ PHASE_CONV = [
                          ids=lambda c: "G{}_nq{}_H{}_D{}_nkv{}_bs{}_k{}_pad{}_off{}".format(*c))
 def test_phase_conversion_paths(case):
     """The phase's conversion of fp32 queries gives the oracle's fp16 bits,
-    writes exactly the token rows of the fp16 workspace (padding between rows
-    untouched), and the scores, tail and ids follow from the fp32 inputs."""
+    writes exactly the token rows of the fp16 buffer (padding between rows
+    untouched), and the scores, tail and ids follow from the fp32 inputs.
+    Without the fp16 buffer the phase gives the same bits (16-byte aligned
+    rows), or refuses cleanly (4-byte aligned rows)."""
     G, nq, H, D, n_kv, bs, k, tok_pad, off = case
     cfg = qi.Config("conv_path", G, nq, H, D, n_kv, bs, k, "normal", 4000 + nq)
     w = qi.conversion_fixture(cfg, seed=4000 + nq)
@@ -468,6 +479,23 @@ def test_phase_conversion_paths(case):
                               model.view(np.uint32))
     check_ids(ids.reshape(cfg.rows, k).cpu().numpy(), s_gpu, ref, k, "phase conversion")
 
+    scores2 = torch.full_like(scores, float("nan"))
+    ids2 = torch.full_like(ids, 123)
+    st = qsa.lib.qsa_select_phase(
+        ctypes.c_void_p(q32_rows.data_ptr()), None, row,
+        ctypes.c_void_p(kd.data_ptr()), kd.stride(0), ctypes.c_void_p(scores2.data_ptr()), ld,
+        ctypes.c_void_p(ids2.data_ptr()), k, None, G, nq, H, D, n_kv, bs, k, 0, None)
+    torch.cuda.synchronize()
+    if off % 4 != 0:
+        assert st == qsa.QSA_ERR_UNSUPPORTED, qsa.status_string(st)
+        assert torch.all(torch.isnan(scores2)) and torch.all(ids2 == 123)
+    else:
+        assert st == 0, qsa.status_string(st)
+        nb = cfg.nb
+        assert torch.equal(scores2[:, :, :nb].view(torch.int32), scores[:, :, :nb].view(torch.int32))
+        assert torch.all(torch.isnan(scores2[:, :, nb:]))
+        assert torch.equal(ids2, ids)
+
 
 SPECIALS = np.array([0x7FC00001, 0xFFA00000, 0x7F800001, 0xFFFFFFFF,    # NaNs: payloads, signs, signalling
                      0x7F800000, 0xFF800000,                            # +-inf
@@ -476,27 +504,30 @@ SPECIALS = np.array([0x7FC00001, 0xFFA00000, 0x7F800001, 0xFFFFFFFF,    # NaNs: 
                      0x80000000, 0x38800000], dtype=np.uint32)          # -0, 2^-14 (smallest normal)
 
 
-@pytest.mark.parametrize("off", [0, 1], ids=["small_scorer", "conversion_kernel"])
-def test_phase_converts_special_values(off):
+@pytest.mark.parametrize("G,nq,off", [(1, 40, 0), (1, 40, 1), (4, 4096, 0)],
+                         ids=["small_scorer", "conversion_kernel", "wide_scorer"])
+def test_phase_converts_special_values(G, nq, off):
     """fp32 queries with NaNs (payloads, signs, signalling), infinities,
     overflow, the rounding at the fp16 maximum, subnormals and -0 in a few
-    token rows.  With 16-byte aligned queries and few rows the small scorer
+    token rows.  With 16-byte aligned queries the scorer (small or wide)
     converts them on load; one float off, the conversion kernel does.  Either
     way the fp16 workspace holds the oracle's conversion bit for bit, and the
     rows without special values score within the bound."""
-    G, nq, H, D, n_kv, k = 1, 40, 8, 128, 5 * 64 + 3, 4
+    H, D, n_kv, k = 8, 128, 5 * 64 + 3, 4
     cfg = qi.Config("specials", G, nq, H, D, n_kv, 64, k, "normal", 4321)
     w = qi.conversion_fixture(cfg, seed=4321)
     q32 = w.q32.copy()
     dirty = [3, 7, 30]
-    for r in dirty:
+    for r in dirty:   # near the start of the token row and at its end (last KV head)
         flat = q32[r].reshape(-1).view(np.uint32)
         flat[5 * r:5 * r + len(SPECIALS)] = SPECIALS
+        flat[flat.size - 5 * r - len(SPECIALS):flat.size - 5 * r] = SPECIALS
     buf = torch.zeros((off + q32.size,), dtype=torch.float32, device=dev())
     qd = buf[off:].view(nq, G, H, D)
     qd.copy_(torch.from_numpy(q32))
-    ws = qsa.PhaseWorkspace(cfg.nq, cfg.G, cfg.H, cfg.D, cfg.n_kv, cfg.bs, cfg.k, dev())
-    ws.q16.fill_(0x7D5B)
+    ws = qsa.PhaseWorkspace(cfg.nq, cfg.G, cfg.H, cfg.D, cfg.n_kv, cfg.bs, cfg.k, dev(),
+                            keep_q16=True)
+    ws.q16.view(torch.int16).fill_(0x7D5B)
     kd = k_dev(w.kblk)
     row = G * H * D
     st = qsa.lib.qsa_select_phase(
@@ -509,9 +540,9 @@ def test_phase_converts_special_values(off):
     want16 = oracle.convert_f32_f16(q32)
     assert np.array_equal(got16, want16), "converted queries differ from the oracle's rounding"
     clean = np.setdiff1d(np.arange(nq), dirty)
-    s_gpu = ws.scores[0, :, :cfg.nb].cpu().numpy().astype(np.float64)[clean]
+    s_gpu = ws.scores[:, clean, :cfg.nb].reshape(G * clean.size, cfg.nb).cpu().numpy()
     ref = oracle.scores(q32[clean], w.kblk, cfg.nb)
-    check_bound(s_gpu, ref, "specials, clean rows")
+    check_bound(s_gpu.astype(np.float64), ref, "specials, clean rows")
 
 
 @pytest.mark.parametrize("q_chunk", [0, 37, 64, 1000])

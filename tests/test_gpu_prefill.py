@@ -12,7 +12,11 @@ The oracle cannot score all 134 M cells in test time, so:
     properties that define the selection: strictly ordered by (score desc,
     id asc), nothing outside the selection beats its last element, and ties
     at the threshold are the lowest ids;
-  * the phase is run twice and must be bitwise identical.
+  * the phase is run twice and must be bitwise identical;
+  * run once more with the fp16 buffer kept, it stores exactly the oracle's
+    conversion of every query and changes no score or id bit.
+The fixture runs the phase as the benchmark does: fp32 queries converted in
+the scorer's registers, no fp16 buffer.
 """
 from __future__ import annotations
 
@@ -59,8 +63,18 @@ def sampled_rows(cfg, n_random=40, seed=3):
 
 
 def test_prefill_converted_queries_exact(prefill):
+    """The phase asked to keep the fp16 queries stores exactly the oracle's
+    conversion, and storing them changes no score or id bit."""
     cfg, w, q32, kb, ws = prefill
-    assert np.array_equal(ws.q16.cpu().numpy().view(np.uint16), w.q16)
+    ws16 = qsa.PhaseWorkspace(cfg.nq, cfg.G, cfg.H, cfg.D, cfg.n_kv, cfg.bs, cfg.k, dev(),
+                              with_vals=True, ld_pad=3, keep_q16=True)
+    log("prefill: running the phase with the fp16 buffer")
+    qsa.select_phase(q32, kb, cfg.n_kv, cfg.bs, cfg.k, ws16)
+    torch.cuda.synchronize()
+    assert np.array_equal(ws16.q16.cpu().numpy().view(np.uint16), w.q16)
+    nb = cfg.nb
+    assert torch.equal(ws16.scores[:, :, :nb].view(torch.int32), ws.scores[:, :, :nb].view(torch.int32))
+    assert torch.equal(ws16.ids, ws.ids)
 
 
 def test_prefill_sampled_rows_within_bound(prefill):
