@@ -14,12 +14,7 @@ __global__ __launch_bounds__(256) void convert_v8_kernel(const float4 *__restric
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n8; i += stride) {
         const float4 a = src[2 * i];
         const float4 b = src[2 * i + 1];
-        uint4 o;
-        o.x = f16_rne(a.x) | (f16_rne(a.y) << 16);
-        o.y = f16_rne(a.z) | (f16_rne(a.w) << 16);
-        o.z = f16_rne(b.x) | (f16_rne(b.y) << 16);
-        o.w = f16_rne(b.z) | (f16_rne(b.w) << 16);
-        dst[i] = o;
+        dst[i] = f16x8(a, b);   // the scorers' on-load conversion
     }
 }
 

@@ -27,28 +27,22 @@ __device__ __forceinline__ uint32_t f16_rne(float x) {
     return h;
 }
 
-// Eight fp32 values to fp16 bits (two dwords each), f16_rne per element.
-__device__ __forceinline__ uint4 f16x8_exact(const float4 &x0, const float4 &x1) {
-    return make_uint4(f16_rne(x0.x) | (f16_rne(x0.y) << 16), f16_rne(x0.z) | (f16_rne(x0.w) << 16),
-                      f16_rne(x1.x) | (f16_rne(x1.y) << 16), f16_rne(x1.z) | (f16_rne(x1.w) << 16));
+// Two fp32 values to packed fp16 bits by v_cvt_pk_f16_f32: round to nearest
+// even by the MODE register, fp16 subnormals kept, overflow to infinity, and
+// a NaN becomes the quiet NaN with the input's sign and top 10 fraction bits,
+// i.e. f16_rne on both halves.  The vector conversion kernel is built from
+// this instruction, and its test compares all 2^32 fp32 patterns with the
+// oracle's rounding, so the scorers that convert on load with it inherit that
+// check.
+typedef _Float16 qsa_half2 __attribute__((ext_vector_type(2)));
+typedef float qsa_float2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(qsa_float2{a, b}, qsa_half2));
 }
 
-// The same with the bare hardware conversion: equal to f16x8_exact for every
-// input that is not a NaN (max_mag_bits tells whether there is one).
-__device__ __forceinline__ uint4 f16x8_cvt(const float4 &x0, const float4 &x1) {
-    auto h = [](float x) -> uint32_t { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x)); };
-    return make_uint4(h(x0.x) | (h(x0.y) << 16), h(x0.z) | (h(x0.w) << 16),
-                      h(x1.x) | (h(x1.y) << 16), h(x1.z) | (h(x1.w) << 16));
-}
-
-// Largest magnitude bit pattern of eight fp32 values: a NaN among them iff
-// the result is > 0x7f800000.
-__device__ __forceinline__ uint32_t max_mag_bits(const float4 &x0, const float4 &x1) {
-    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-    uint32_t m = 0;
-    #pragma unroll
-    for (int e = 0; e < 8; ++e) m = max(m, __builtin_bit_cast(uint32_t, xs[e]) & 0x7fffffffu);
-    return m;
+// Eight fp32 values to fp16 bits, as four packed conversions.
+__device__ __forceinline__ uint4 f16x8(const float4 &x0, const float4 &x1) {
+    return make_uint4(f16x2(x0.x, x0.y), f16x2(x0.z, x0.w), f16x2(x1.x, x1.y), f16x2(x1.z, x1.w));
 }
 
 struct ScoreGeom {

@@ -36,9 +36,10 @@
 //    in the fixed fma order of the tail model, so the queries are read from
 //    HBM once for all nb blocks.
 //  * fp32 queries (the select phase) are read and converted to fp16 bits on
-//    load, with the rounding of the conversion kernel (f16_rne), and the first split
-//    of each query group writes those bits to the fp16 workspace: the
-//    phase needs no conversion launch and reads the queries from HBM once.
+//    load with the conversion kernel's own instruction (f16x8), and the
+//    first split of each query group writes those bits to the caller's fp16
+//    buffer when there is one: the phase needs no conversion launch and
+//    reads the queries from HBM once.
 //  * Grid: (KV head, 64-query group, block split), with logical ids laid out
 //    so that each XCD (blockIdx % 8) takes a contiguous range: the splits of
 //    one query group and the query groups of one KV head share that XCD's L2.
@@ -190,7 +191,7 @@ void score_full_kernel(ScoreArgs a) {
             constexpr int F = KS * NP;                    // fragments, K-step major
             // (the accumulating pass with 64-bit store addressing holds more
             // registers: one batch fewer in flight)
-            constexpr int kQBatch = 4, kQDepth = (ACCUM && !BUF) ? 3 : 4;
+            constexpr int kQBatch = 4, kQDepth = 3;
             constexpr int NBAT = (F + kQBatch - 1) / kQBatch;
             float4 x0[F], x1[F];
             auto issue = [&](int b) {
@@ -212,7 +213,7 @@ void score_full_kernel(ScoreArgs a) {
                 for (int j = 0; j < kQBatch; ++j) {
                     const int f = b * kQBatch + j;
                     if (f < F) {
-                        const uint4 h = f16x8_exact(x0[f], x1[f]);
+                        const uint4 h = f16x8(x0[f], x1[f]);
                         qa[f % NP][f / NP] = __builtin_bit_cast(half8, h);
                         // an empty statement that uses the converted fragment
                         // and orders memory: the conversion stays before the

@@ -142,11 +142,9 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
     if (tb < te) fetch(tb);   // uniform over the workgroup
 
     // ---- A operand: all KS fragments' loads in flight together.  fp32
-    // queries are converted once they have landed, by the bare hardware
-    // conversion unless the wave holds a NaN (one decision per wave, so no
-    // branch between the loads), and the first segment of each query group
-    // writes the converted rows (real rows only) to the fp16 workspace when
-    // there is one.
+    // queries are converted (f16x8) once they have landed, and the first
+    // segment of each query group writes the converted rows (real rows only)
+    // to the fp16 buffer when there is one.
     half8 qa[KS];
     if constexpr (SRC32) {
         float4 x0[KS], x1[KS];
@@ -155,17 +153,9 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
             x0[s] = *reinterpret_cast<const float4 *>(a.q32 + a_off + 16 * s);
             x1[s] = *reinterpret_cast<const float4 *>(a.q32 + a_off + 16 * s + 4);
         }
-        uint32_t m = 0;
-        #pragma unroll
-        for (int s = 0; s < KS; ++s) m = max(m, max_mag_bits(x0[s], x1[s]));
         uint4 hv[KS];
-        if (__builtin_amdgcn_ballot_w64(m > 0x7f800000u)) {   // uniform: a NaN somewhere
-            #pragma unroll
-            for (int s = 0; s < KS; ++s) hv[s] = f16x8_exact(x0[s], x1[s]);
-        } else {
-            #pragma unroll
-            for (int s = 0; s < KS; ++s) hv[s] = f16x8_cvt(x0[s], x1[s]);
-        }
+        #pragma unroll
+        for (int s = 0; s < KS; ++s) hv[s] = f16x8(x0[s], x1[s]);
         #pragma unroll
         for (int s = 0; s < KS; ++s) qa[s] = a_ok ? __builtin_bit_cast(half8, hv[s]) : half8{};
         if (a.q16w && seg == 0 && a_ok) {
