@@ -92,7 +92,15 @@ def scorer_kernel(cfg):
     tail = "true" if cfg.n_kv % cfg.bs else "false"
     if cfg.G * -(-cfg.nq // 64) < 256:
         np_ = 1 if cfg.H <= 2 else 2 if cfg.H <= 4 else 4 if cfg.H <= 8 else 8
-        return "score_small", f"score_small_kernel<{cfg.D},{np_},true>"
+        # K tiles per staged chunk: 2 when a block segment holds an even
+        # number of at least four tiles (segments give about 256 workgroups,
+        # at least one tile each)
+        n_tiles = -(-cfg.nf // 32)
+        base = cfg.G * -(-(-(-cfg.nq // (16 // np_))) // 4)
+        segs = min(-(-256 // base) if base < 256 else 1, max(n_tiles, 1))
+        tps = -(-n_tiles // segs) if n_tiles else 0
+        ch = 2 if tps >= 4 and tps % 2 == 0 else 1
+        return "score_small", f"score_small_kernel<{cfg.D},{np_},true,{ch}>"
     np_ = min(4, (cfg.H + 1) // 2)
     return "score_full", f"score_full_kernel<{cfg.D},{np_},false,true,{tail},true>"
 

@@ -37,10 +37,15 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-// K tiles staged per barrier (16 KiB at D = 128), double-buffered: at 8
-// MFMAs per tile, one tile's work is far shorter than a load's latency.
-// Measured at nq = 256: 2 tiles 5.1 us, 4 tiles 5.3 us, 8 tiles 7.5 us.
-constexpr int kSmallChunk = 2;
+// K tiles staged per barrier (CH = 1 or 2, 8 or 16 KiB at D = 128),
+// double-buffered: at 8 MFMAs per tile, one tile's work is far shorter than a
+// load's latency.  The host takes CH = 2 when a segment holds an even number
+// of at least four tiles, else 1 (a chunk of 2 over an odd count stages a
+// tile that is not scored).  Measured on the phase at nq = 256: 4 tiles per
+// segment (128K keys) 11.8 us with CH = 2, 12.2 us with 1, 12.0 us with 4;
+// 1 tile per segment (32K keys) 8.25 us with CH = 1, 8.5 us with 2; 2 tiles
+// per segment (the decode step, 8 KV heads) 9.9 us with CH = 1, 10.05 us
+// with 2.
 
 struct SmallArgs {
     const uint16_t *q16;   // query source when q32 is null
@@ -72,7 +77,7 @@ __device__ __forceinline__ float h2f(uint32_t bits16) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
 }
 
-template <int D, int NP, bool SRC32>
+template <int D, int NP, bool SRC32, int CH>
 __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
     constexpr int KS = D / 16;
     constexpr int QPG = 16 / NP;
@@ -81,10 +86,11 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
     constexpr int LOADS = TILE_U4 / 256;           // staging loads per thread per tile
     static_assert(NP == 1 || NP == 2 || NP == 4 || NP == 8, "head pairs per row block");
     static_assert(TILE_U4 % 256 == 0 && (LOADS == 1 || LOADS == 2), "D must be 64 or 128");
+    static_assert(CH == 1 || CH == 2, "tiles per staged chunk");
 
     // two chunks of K tiles shared by the four waves, and per wave the
     // relu'd tail chains
-    __shared__ uint4 kbuf[2][kSmallChunk][TILE_U4];
+    __shared__ uint4 kbuf[2][CH][TILE_U4];
     __shared__ float red[kScoreWaves][QPG][2 * NP];
 
     const uint32_t L = xcd_logical_id(blockIdx.x, gridDim.x);
@@ -111,7 +117,7 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
     const uint16_t *kg = a.kblk + static_cast<int64_t>(g) * a.khs;
     float *sbase = a.scores + static_cast<int64_t>(g) * a.nq * a.ld_s;
 
-    // K staging in chunks of kSmallChunk tiles, double-buffered: the loads of
+    // K staging in chunks of CH tiles, double-buffered: the loads of
     // chunk c+1 are in flight while chunk c is scored, one barrier per chunk.
     // LDS index u = threadIdx.x + 256*j of a tile is chunk-major (u = chunk*32
     // + block), the B-fragment order: lane l of K-step s reads u = 64*s + l.
@@ -124,16 +130,16 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
                                   (u % kTileBlocks), last);
         return *reinterpret_cast<const uint4 *>(kg + b * D + 8 * (u / kTileBlocks));
     };
-    uint4 st[kSmallChunk][LOADS];
+    uint4 st[CH][LOADS];
     auto fetch = [&](int t0) {
         #pragma unroll
-        for (int i = 0; i < kSmallChunk; ++i)
+        for (int i = 0; i < CH; ++i)
             #pragma unroll
             for (int j = 0; j < LOADS; ++j) st[i][j] = kload(t0 + i, j);
     };
     auto publish = [&](int buf) {
         #pragma unroll
-        for (int i = 0; i < kSmallChunk; ++i)
+        for (int i = 0; i < CH; ++i)
             #pragma unroll
             for (int j = 0; j < LOADS; ++j) kbuf[buf][i][threadIdx.x + 256 * j] = st[i][j];
     };
@@ -174,10 +180,10 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
         publish(0);
         __syncthreads();
         int buf = 0;
-        for (int t0 = tb; t0 < te; t0 += kSmallChunk) {
-            const bool more = t0 + kSmallChunk < te;   // uniform
-            if (more) fetch(t0 + kSmallChunk);
-            for (int i = 0; i < kSmallChunk && t0 + i < te; ++i) {
+        for (int t0 = tb; t0 < te; t0 += CH) {
+            const bool more = t0 + CH < te;   // uniform
+            if (more) fetch(t0 + CH);
+            for (int i = 0; i < CH && t0 + i < te; ++i) {
                 const int tile = t0 + i;
                 const uint4 *kcur = &kbuf[buf][i][l];
                 floatx16 acc = {};
@@ -271,20 +277,26 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
 
 typedef void (*small_fn)(SmallArgs);
 
-template <int D, bool SRC32>
+template <int D, bool SRC32, int CH>
 small_fn pick_np(int np) {
     switch (np) {
-        case 1: return score_small_kernel<D, 1, SRC32>;
-        case 2: return score_small_kernel<D, 2, SRC32>;
-        case 4: return score_small_kernel<D, 4, SRC32>;
-        case 8: return score_small_kernel<D, 8, SRC32>;
+        case 1: return score_small_kernel<D, 1, SRC32, CH>;
+        case 2: return score_small_kernel<D, 2, SRC32, CH>;
+        case 4: return score_small_kernel<D, 4, SRC32, CH>;
+        case 8: return score_small_kernel<D, 8, SRC32, CH>;
     }
     return nullptr;
 }
 
-small_fn pick_small(int D, int np, bool src32) {
-    if (D == 128) return src32 ? pick_np<128, true>(np) : pick_np<128, false>(np);
-    if (D == 64) return src32 ? pick_np<64, true>(np) : pick_np<64, false>(np);
+template <int D>
+small_fn pick_d(int np, bool src32, int ch) {
+    if (ch == 2) return src32 ? pick_np<D, true, 2>(np) : pick_np<D, false, 2>(np);
+    return src32 ? pick_np<D, true, 1>(np) : pick_np<D, false, 1>(np);
+}
+
+small_fn pick_small(int D, int np, bool src32, int ch) {
+    if (D == 128) return pick_d<128>(np, src32, ch);
+    if (D == 64) return pick_d<64>(np, src32, ch);
     return nullptr;
 }
 
@@ -327,7 +339,7 @@ hipError_t launch_score_small(const ScoreGeom &geo, bool tail, hipStream_t s, co
     if (n_tiles > 0) segs = (n_tiles + tps - 1) / tps;
     const int64_t grid = base * segs;
     if (grid > 0x7fffffffLL || n_tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    small_fn fn = pick_small(geo.D, np, q32 != nullptr);
+    small_fn fn = pick_small(geo.D, np, q32 != nullptr, tps >= 4 && tps % 2 == 0 ? 2 : 1);
     if (!fn) return hipErrorInvalidValue;
     SmallArgs a{geo.q16, q32, q32 ? q16w : nullptr, geo.qts, geo.kblk, geo.khs, geo.scores,
                 geo.ld_s, geo.G, geo.nq, geo.H, geo.nf, tail ? 1 : 0,

@@ -629,6 +629,38 @@ def test_small_scorer_matches_wide_bitwise(H, D):
                        whole[:, t0:t0 + n].contiguous().view(torch.int32))
 
 
+# 256 queries of one KV head at H = 8 give 16 groups of four query groups,
+# so the block axis is cut into 16 segments of n_tiles/16 tiles: 2, 3, 4 and
+# 6 tiles per segment, K staged one tile per barrier (2, 3) or two (4, 6).
+SMALL_CHUNKS = [32, 48, 64, 96]
+
+
+@pytest.mark.parametrize("n_tiles", SMALL_CHUNKS, ids=lambda v: f"tiles{v}")
+def test_small_scorer_chunking(n_tiles):
+    """The small scorer over 2-6 tiles per block segment, both K staging
+    depths, with a tail block: the phase on fp32 queries gives scores within
+    the bound, the tail bit for bit the fixed-order model, ids exact on the
+    device scores, and the same bits as the fp16-input entry point."""
+    cfg = qi.Config("chunks", 1, 256, 8, 128, n_tiles * 32 * 64 + 13, 64, 16, "normal",
+                    900 + n_tiles)
+    log(f"small scorer, {n_tiles} tiles")
+    w = qi.make(cfg)
+    kd = k_dev(w.kblk)
+    ws = qsa.PhaseWorkspace(cfg.nq, cfg.G, cfg.H, cfg.D, cfg.n_kv, cfg.bs, cfg.k, dev())
+    ids = qsa.select_phase(torch.from_numpy(w.q32).to(dev()), kd, cfg.n_kv, cfg.bs, cfg.k, ws)
+    s16 = qsa.block_scores(q_dev(w.q16), kd, cfg.n_kv, cfg.bs)
+    torch.cuda.synchronize()
+    nb = cfg.nb
+    assert torch.equal(ws.scores[:, :, :nb].contiguous().view(torch.int32),
+                       s16.contiguous().view(torch.int32))
+    s_gpu = ws.scores[:, :, :nb].reshape(cfg.rows, nb).cpu().numpy().astype(np.float64)
+    ref = oracle.scores(w.q16, w.kblk, nb)
+    check_bound(s_gpu, ref, "small chunks")
+    model = oracle.block_model_f32(w.q16, w.kblk, cfg.nf)
+    assert np.array_equal(s_gpu[:, cfg.nf].astype(np.float32).view(np.uint32), model.view(np.uint32))
+    check_ids(ids.reshape(cfg.rows, cfg.k).cpu().numpy(), s_gpu, ref, cfg.k, "small chunks")
+
+
 def test_wide_scorer_global_store_path():
     """The wide scorer's plain global-store path (a KV head's score region of
     2^30 bytes or more), with two head passes and the tail in the same
