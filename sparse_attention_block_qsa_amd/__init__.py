@@ -189,7 +189,10 @@ def select_phase(q: torch.Tensor, kblk: torch.Tensor, n_kv: int, bs: int, k: int
                  ws: PhaseWorkspace | None = None, q_chunk: int = 0,
                  stream: torch.cuda.Stream | None = None):
     """The whole phase: (fp32 -> fp16 conversion when q is float32), scores,
-    top-k.  Returns ids [G, nq, k] (and vals when the workspace has them)."""
+    top-k.  Returns ids [G, nq, k] (and vals when the workspace has them).
+    fp32 queries are converted by the scorers as they load them; without a
+    kept fp16 copy (ws.q16 is None) their rows must be 16-byte aligned, which
+    a contiguous tensor from the caching allocator always is."""
     fp32 = q.dtype == torch.float32
     nq, G, H, D, qts = _check_q(q, torch.float32 if fp32 else torch.float16)
     if fp32 and not q.is_contiguous():
