@@ -14,6 +14,18 @@ constexpr int kWaveQueries = 16;
 constexpr int kScoreWaves = 4;
 constexpr int kGroupQueries = kWaveQueries * kScoreWaves;
 
+// Logical workgroup id such that the workgroups the hardware places on one
+// XCD (consecutive ids modulo 8 land on consecutive XCDs) get a contiguous
+// logical range.  Bijective for any grid size.  The scorers order their work
+// by it so that neighbouring work shares an XCD's L2, and the selectors order
+// their rows by it so that a row is selected on the XCD that scored it: with
+// few rows the scores are still in that L2 when the selector reads them.
+__device__ __forceinline__ uint32_t xcd_logical_id(uint32_t bid, uint32_t nblk) {
+    const uint32_t q = nblk / 8, r = nblk % 8;
+    const uint32_t x = bid % 8, idx = bid / 8;
+    return x * q + (x < r ? x : r) + idx;
+}
+
 // fp32 -> fp16 bits, round to nearest even.  v_cvt_f16_f32 rounds by the
 // MODE register, which is round-to-nearest-even for compute kernels, keeps
 // fp16 subnormals and overflows to infinity.  NaN is rewritten explicitly so

@@ -67,15 +67,6 @@ struct ScoreArgs {
     int32_t n_qgroups, n_splits, tiles_per_split, n_tiles;
 };
 
-// Logical workgroup id such that the workgroups the hardware places on one
-// XCD (consecutive ids modulo 8 land on consecutive XCDs) get a contiguous
-// logical range.  Bijective for any grid size.
-__device__ __forceinline__ uint32_t xcd_logical_id(uint32_t bid, uint32_t nblk) {
-    const uint32_t q = nblk / 8, r = nblk % 8;
-    const uint32_t x = bid % 8, idx = bid / 8;
-    return x * q + (x < r ? x : r) + idx;
-}
-
 // Cache policy of the score stores: non-temporal.  The scores are written
 // once and read back by the selector long after they would have left the
 // caches, so they stream to memory without displacing the queries and keys.

@@ -67,12 +67,6 @@ __device__ __forceinline__ float relu_bits(float x) {
     return __builtin_bit_cast(float, max(__builtin_bit_cast(int32_t, x), 0));
 }
 
-__device__ __forceinline__ uint32_t xcd_logical_id(uint32_t bid, uint32_t nblk) {
-    const uint32_t q = nblk / 8, r = nblk % 8;
-    const uint32_t x = bid % 8, idx = bid / 8;
-    return x * q + (x < r ? x : r) + idx;
-}
-
 __device__ __forceinline__ float h2f(uint32_t bits16) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
 }

@@ -202,7 +202,8 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     // addresses and buffer descriptor live in scalar registers
     const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
-    const int64_t R = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + w;
+    // rows in the scorers' XCD order: row R is read on the XCD that wrote it
+    const int64_t R = static_cast<int64_t>(xcd_logical_id(blockIdx.x, gridDim.x)) * (blockDim.x >> 6) + w;
     if (R >= a.total_rows) return;               // whole wave; no block barriers below
     int64_t grp = 0, t = R;
     if (a.rows_per_group != a.total_rows) {   // grouped rows (the phase's chunks)
@@ -477,7 +478,8 @@ __global__ __launch_bounds__(256) void topk_quad_kernel(TopkArgs a) {
     __shared__ uint64_t lists[4][64];
     const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
-    const int64_t R = blockIdx.x;
+    // rows in the scorers' XCD order: row R is read on the XCD that wrote it
+    const int64_t R = xcd_logical_id(blockIdx.x, gridDim.x);
     if (R >= a.total_rows) return;               // whole workgroup
     int64_t grp = 0, t = R;
     if (a.rows_per_group != a.total_rows) {
