@@ -100,7 +100,8 @@ def scorer_kernel(cfg):
         segs = min(-(-256 // base) if base < 256 else 1, max(n_tiles, 1))
         tps = -(-n_tiles // segs) if n_tiles else 0
         ch = 2 if tps >= 4 and tps % 2 == 0 else 1
-        return "score_small", f"score_small_kernel<{cfg.D},{np_},true,{ch}>"
+        stage = "true" if cfg.nq >= 4 * (16 // np_) else "false"   # fp32 queries staged in LDS
+        return "score_small", f"score_small_kernel<{cfg.D},{np_},true,{ch},{stage}>"
     np_ = min(4, (cfg.H + 1) // 2)
     return "score_full", f"score_full_kernel<{cfg.D},{np_},false,true,{tail},true>"
 

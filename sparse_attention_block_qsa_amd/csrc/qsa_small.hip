@@ -14,13 +14,14 @@
 //    pair.  A wave's whole A operand is KS fragments (32 VGPRs at D = 128).
 //  * The workgroup's four waves own four query groups (one each) and walk
 //    the same segment of the block axis: 32-block K tiles are staged once
-//    through LDS in fragment order (coalesced loads), two tiles per
-//    barrier, double-buffered, and read by the four waves.
+//    through LDS in fragment order (coalesced loads), one or two tiles per
+//    barrier, double-buffered, and read by the four waves.  fp32 queries of
+//    many rows go through LDS in fragment order as well, loaded coalesced.
 //  * Epilogue per tile: relu per head; v_permlane32_swap of the registers of
 //    queries q and q+1 brings the two heads of each pair into one lane; the
 //    pair sums are added in ascending pair order.  That is the head-sum
 //    order of the wide scorer, so both produce the same bits.
-//  * With fp32 queries (the select phase) the fragments are converted on
+//  * With fp32 queries (the select phase) the chunks are converted on
 //    load with the rounding of the conversion kernel, and the first segment
 //    of each query group writes the converted rows to the caller's fp16
 //    buffer when there is one: the phase needs no conversion launch.  With
@@ -71,7 +72,7 @@ __device__ __forceinline__ float h2f(uint32_t bits16) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
 }
 
-template <int D, int NP, bool SRC32, int CH>
+template <int D, int NP, bool SRC32, int CH, bool STAGE>
 __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
     constexpr int KS = D / 16;
     constexpr int QPG = 16 / NP;
@@ -81,10 +82,12 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
     static_assert(NP == 1 || NP == 2 || NP == 4 || NP == 8, "head pairs per row block");
     static_assert(TILE_U4 % 256 == 0 && (LOADS == 1 || LOADS == 2), "D must be 64 or 128");
     static_assert(CH == 1 || CH == 2, "tiles per staged chunk");
+    static_assert(!STAGE || SRC32, "only fp32 queries are staged through LDS");
 
-    // two chunks of K tiles shared by the four waves, and per wave the
-    // relu'd tail chains
+    // two chunks of K tiles shared by the four waves, the four waves' query
+    // fragments, and per wave the relu'd tail chains
     __shared__ uint4 kbuf[2][CH][TILE_U4];
+    __shared__ uint4 qfrag[STAGE ? kScoreWaves * KS * 64 : 1];
     __shared__ float red[kScoreWaves][QPG][2 * NP];
 
     const uint32_t L = xcd_logical_id(blockIdx.x, gridDim.x);
@@ -141,38 +144,101 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
     // latencies overlap
     if (tb < te) fetch(tb);   // uniform over the workgroup
 
-    // ---- A operand: all KS fragments' loads in flight together.  fp32
-    // queries are converted (f16x8) once they have landed, and the first
-    // segment of each query group writes the converted rows (real rows only)
-    // to the fp16 buffer when there is one.
     half8 qa[KS];
-    if constexpr (SRC32) {
-        float4 x0[KS], x1[KS];
+    if constexpr (STAGE) {
+        // ---- A operand, fp32 queries staged through LDS.  The workgroup's
+        // 4*QPG query slots x 2*NP head slots x D channels are walked in
+        // 8-element chunks, consecutive chunks of a (query, head) row on
+        // consecutive threads, so the loads are coalesced: each lane loading
+        // its own fragments touches 32 lines per load instruction, and at few
+        // rows those requests, not the bytes, set the time.  Each chunk is one
+        // lane's fragment of one K-step, converted (f16x8) and written to LDS
+        // in fragment order with the lane index XORed by the chunk's index in
+        // its row (K-step and half): the 16 chunks of a row land in 16
+        // different bank groups, and every wave still reads its A operand
+        // conflict-free.  The first segment of each query group also writes
+        // the converted rows to the fp16 buffer when there is one.  Chunks of
+        // rows past nq and of padded heads are not loaded; their fragments are
+        // zeroed when read.
+        constexpr int CPR = D / 8;                     // chunks per (query, head) row
+        constexpr int MAXJ = 4 * QPG * 2 * NP * CPR / 256;
+        static_assert(MAXJ * 256 == 4 * QPG * 2 * NP * CPR, "128 rows of chunks over 256 threads");
+        const int t0 = qg4 * kScoreWaves * QPG;
+        int64_t off[MAXJ];
+        bool ok[MAXJ];
+        int dst[MAXJ];
         #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            x0[s] = *reinterpret_cast<const float4 *>(a.q32 + a_off + 16 * s);
-            x1[s] = *reinterpret_cast<const float4 *>(a.q32 + a_off + 16 * s + 4);
+        for (int j = 0; j < MAXJ; ++j) {
+            const int ch = static_cast<int>(threadIdx.x) + 256 * j;
+            const int row = ch / CPR, d8 = ch % CPR;
+            const int qs = row / (2 * NP), h = row % (2 * NP);   // query slot, head
+            ok[j] = h < a.H && t0 + qs < a.nq;
+            off[j] = ok[j] ? static_cast<int64_t>(t0 + qs) * a.qts +
+                                 static_cast<int64_t>(g * a.H + h) * D + 8 * d8
+                           : 0;
+            // fragment slot: wave qs / QPG, K-step d8 / 2, lane of row
+            // (query qs % QPG, head h) and half d8 % 2, swizzled by d8
+            const int cc = (h >> 1) * QPG + qs % QPG;
+            const int ln = 8 * (cc >> 2) + 4 * (h & 1) + (cc & 3) + 32 * (d8 & 1);
+            dst[j] = ((qs / QPG) * KS + (d8 >> 1)) * 64 + (ln ^ (d8 & 15));
         }
-        uint4 hv[KS];
+        float4 x0[MAXJ], x1[MAXJ];
         #pragma unroll
-        for (int s = 0; s < KS; ++s) hv[s] = f16x8(x0[s], x1[s]);
+        for (int j = 0; j < MAXJ; ++j) {
+            x0[j] = *reinterpret_cast<const float4 *>(a.q32 + off[j]);
+            x1[j] = *reinterpret_cast<const float4 *>(a.q32 + off[j] + 4);
+        }
+        uint4 hv[MAXJ];
         #pragma unroll
-        for (int s = 0; s < KS; ++s) qa[s] = a_ok ? __builtin_bit_cast(half8, hv[s]) : half8{};
-        if (a.q16w && seg == 0 && a_ok) {
+        for (int j = 0; j < MAXJ; ++j) hv[j] = f16x8(x0[j], x1[j]);
+        if (a.q16w && seg == 0) {
             #pragma unroll
-            for (int s = 0; s < KS; ++s) *reinterpret_cast<uint4 *>(a.q16w + a_off + 16 * s) = hv[s];
+            for (int j = 0; j < MAXJ; ++j)
+                if (ok[j]) *reinterpret_cast<uint4 *>(a.q16w + off[j]) = hv[j];
         }
-    } else {
         #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const half8 v = *reinterpret_cast<const half8 *>(a.q16 + a_off + 16 * s);
-            qa[s] = a_ok ? v : half8{};
+        for (int j = 0; j < MAXJ; ++j)
+            if (ok[j]) qfrag[dst[j]] = hv[j];
+        if (tb < te) publish(0);   // uniform over the workgroup
+        __syncthreads();
+        #pragma unroll
+        for (int s = 0; s < KS; ++s)   // chunk index within the row: 2s + l/32
+            qa[s] = a_ok ? __builtin_bit_cast(half8, qfrag[(w * KS + s) * 64 + (l ^ ((2 * s + kc) & 15))])
+                         : half8{};
+    } else {
+        // ---- A operand loaded per lane (fp16 queries, or few rows such as
+        // one decode query per KV head, where staging would only add its LDS
+        // round trip).  All KS fragments' loads are in flight together; fp32
+        // queries are converted once they have landed, and the first segment
+        // writes the fp16 buffer if any.
+        if constexpr (SRC32) {
+            float4 x0[KS], x1[KS];
+            #pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                x0[s] = *reinterpret_cast<const float4 *>(a.q32 + a_off + 16 * s);
+                x1[s] = *reinterpret_cast<const float4 *>(a.q32 + a_off + 16 * s + 4);
+            }
+            uint4 hv[KS];
+            #pragma unroll
+            for (int s = 0; s < KS; ++s) hv[s] = f16x8(x0[s], x1[s]);
+            #pragma unroll
+            for (int s = 0; s < KS; ++s) qa[s] = a_ok ? __builtin_bit_cast(half8, hv[s]) : half8{};
+            if (a.q16w && seg == 0 && a_ok) {
+                #pragma unroll
+                for (int s = 0; s < KS; ++s) *reinterpret_cast<uint4 *>(a.q16w + a_off + 16 * s) = hv[s];
+            }
+        } else {
+            #pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const half8 v = *reinterpret_cast<const half8 *>(a.q16 + a_off + 16 * s);
+                qa[s] = a_ok ? v : half8{};
+            }
         }
+        if (tb < te) publish(0);   // uniform over the workgroup
+        __syncthreads();
     }
 
     if (tb < te) {   // uniform over the workgroup
-        publish(0);
-        __syncthreads();
         int buf = 0;
         for (int t0 = tb; t0 < te; t0 += CH) {
             const bool more = t0 + CH < te;   // uniform
@@ -271,26 +337,28 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
 
 typedef void (*small_fn)(SmallArgs);
 
-template <int D, bool SRC32, int CH>
+template <int D, bool SRC32, int CH, bool STAGE>
 small_fn pick_np(int np) {
     switch (np) {
-        case 1: return score_small_kernel<D, 1, SRC32, CH>;
-        case 2: return score_small_kernel<D, 2, SRC32, CH>;
-        case 4: return score_small_kernel<D, 4, SRC32, CH>;
-        case 8: return score_small_kernel<D, 8, SRC32, CH>;
+        case 1: return score_small_kernel<D, 1, SRC32, CH, STAGE>;
+        case 2: return score_small_kernel<D, 2, SRC32, CH, STAGE>;
+        case 4: return score_small_kernel<D, 4, SRC32, CH, STAGE>;
+        case 8: return score_small_kernel<D, 8, SRC32, CH, STAGE>;
     }
     return nullptr;
 }
 
-template <int D>
-small_fn pick_d(int np, bool src32, int ch) {
-    if (ch == 2) return src32 ? pick_np<D, true, 2>(np) : pick_np<D, false, 2>(np);
-    return src32 ? pick_np<D, true, 1>(np) : pick_np<D, false, 1>(np);
+// src: 0 fp16 queries, 1 fp32 loaded per lane, 2 fp32 staged through LDS
+template <int D, int CH>
+small_fn pick_src(int np, int src) {
+    if (src == 2) return pick_np<D, true, CH, true>(np);
+    if (src == 1) return pick_np<D, true, CH, false>(np);
+    return pick_np<D, false, CH, false>(np);
 }
 
-small_fn pick_small(int D, int np, bool src32, int ch) {
-    if (D == 128) return pick_d<128>(np, src32, ch);
-    if (D == 64) return pick_d<64>(np, src32, ch);
+small_fn pick_small(int D, int np, int src, int ch) {
+    if (D == 128) return ch == 2 ? pick_src<128, 2>(np, src) : pick_src<128, 1>(np, src);
+    if (D == 64) return ch == 2 ? pick_src<64, 2>(np, src) : pick_src<64, 1>(np, src);
     return nullptr;
 }
 
@@ -333,7 +401,13 @@ hipError_t launch_score_small(const ScoreGeom &geo, bool tail, hipStream_t s, co
     if (n_tiles > 0) segs = (n_tiles + tps - 1) / tps;
     const int64_t grid = base * segs;
     if (grid > 0x7fffffffLL || n_tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    small_fn fn = pick_small(geo.D, np, q32 != nullptr, tps >= 4 && tps % 2 == 0 ? 2 : 1);
+    // fp32 queries are staged through LDS when a workgroup can hold a full
+    // row group.  Interleaved phase medians at nq = 256: 128K keys 10.8 ->
+    // 10.0 us, 4K keys 6.9 -> 6.1 us; with one query per KV head staging
+    // only adds its LDS round trip (9.9 -> 10.2 us), and fp16 queries, half
+    // the bytes, lose too (the fp16-input scorer 5.2 -> 5.6 us).
+    const int src = q32 == nullptr ? 0 : geo.nq >= kScoreWaves * qpg ? 2 : 1;
+    small_fn fn = pick_small(geo.D, np, src, tps >= 4 && tps % 2 == 0 ? 2 : 1);
     if (!fn) return hipErrorInvalidValue;
     SmallArgs a{geo.q16, q32, q32 ? q16w : nullptr, geo.qts, geo.kblk, geo.khs, geo.scores,
                 geo.ld_s, geo.G, geo.nq, geo.H, geo.nf, tail ? 1 : 0,

@@ -423,6 +423,7 @@ PHASE_CONV = [
     (1, 33, 8, 128, 40, 64, 4, 8, 0),              # only a tail block
     (3, 129, 5, 128, 100 * 64 + 3, 64, 16, 0, 0),  # contiguous, odd H
     (1, 40, 8, 128, 10 * 64 + 7, 64, 8, 0, 1),     # contiguous, 4-byte aligned fp32
+    (2, 5, 8, 128, 10 * 64 + 7, 64, 8, 24, 0),     # too few rows to stage: per-lane loads
     # wide rows: two block splits (only the first writes the workspace),
     # padded rows, two head passes
     (4, 4096, 12, 64, 40 * 64 + 5, 64, 8, 24, 0),
