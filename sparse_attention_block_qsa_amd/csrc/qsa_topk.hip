@@ -369,21 +369,18 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     }
 }
 
-// The exact top-kk (kk <= 64) of `ncol` 64-wide columns of values held by one
-// wave (column jj of this wave is column col0 + jj of the row, block id
-// (col0 + jj)*64 + lane), returned as composites sorted descending over the
-// lanes (lane 0 largest, zero past the set).  The same steps as topk_kernel's
-// fast path (sampled threshold, candidates compacted into slot, bitonic sort)
-// with its exact bisection as the fallback; val(id) reads a value back by id.
-template <int NC, typename Val>
-__device__ __forceinline__ uint64_t wave_topk(const uint32_t (&xr)[NC], int col0, int kk, int nb,
-                                              int lane, uint64_t *slot, Val val) {
-    const uint64_t lt = (1ull << lane) - 1ull;
+// A threshold from the per-lane top two of NC columns held by one wave
+// (fp32 bits ordered as signed integers, exact for scores >= 0, merely a
+// heuristic otherwise): the kq-th largest of those 128 samples, to 16 leading
+// bits (bisection on the biased bits, two ballots per step), as biased bits.
+// Any threshold is correct for the callers, who check the count they get.
+template <int NC>
+__device__ __forceinline__ uint32_t sampled_threshold(const uint32_t (&xr)[NC], int kq) {
     int32_t m1 = INT32_MIN, m2 = INT32_MIN;
     #pragma unroll
     for (int j = 0; j < NC; ++j) {
         const int32_t x = static_cast<int32_t>(xr[j]);
-        m2 = max(min(m1, x), min(max(m1, x), m2));
+        m2 = max(min(m1, x), min(max(m1, x), m2));   // median of three: v_med3_i32
         m1 = max(m1, x);
     }
     const uint32_t s1 = static_cast<uint32_t>(m1) ^ 0x80000000u;
@@ -392,8 +389,23 @@ __device__ __forceinline__ uint64_t wave_topk(const uint32_t (&xr)[NC], int col0
     for (int bit = 31; bit >= 16; --bit) {
         const uint32_t cand = T | (1u << bit);
         const int c = __popcll(ballot(s1 >= cand)) + __popcll(ballot(s2 >= cand));
-        if (c >= kk) T = cand;
+        if (c >= kq) T = cand;
     }
+    return T;
+}
+
+// The exact top-kk (kk <= 64) of NC 64-wide columns of values held by one
+// wave (column jj of this wave is column col0 + jj of the row, block id
+// (col0 + jj)*64 + lane; ids at or past id_end are padding, NaN in xr), or
+// all of them when the wave holds fewer than kk, returned as composites
+// sorted descending over the lanes (lane 0 largest, zero past the set).  The same steps as topk_kernel's fast path (sampled
+// threshold, candidates compacted into slot, bitonic sort) with its exact
+// bisection as the fallback; val(id) reads a value back by id.
+template <int NC, typename Val>
+__device__ __forceinline__ uint64_t wave_topk(const uint32_t (&xr)[NC], int col0, int kk, int id_end,
+                                              int lane, uint64_t *slot, Val val) {
+    const uint64_t lt = (1ull << lane) - 1ull;
+    uint32_t T = sampled_threshold<NC>(xr, kk);
     const float th = __builtin_bit_cast(float, T ^ 0x80000000u);
     uint32_t mask = 0;
     #pragma unroll
@@ -435,7 +447,7 @@ __device__ __forceinline__ uint64_t wave_topk(const uint32_t (&xr)[NC], int col0
     for (int j = 0; j < NC; ++j) {
         const uint32_t kj = key(j);
         const int id = (col0 + j) * 64 + lane;
-        const bool eq = (kj == T) && (id < nb);
+        const bool eq = (kj == T) && (id < id_end);
         const uint64_t meq = ballot(eq);
         const bool tsel = eq && (__popcll(meq & lt) < need);
         const int ceq = __popcll(meq);
@@ -448,7 +460,9 @@ __device__ __forceinline__ uint64_t wave_topk(const uint32_t (&xr)[NC], int col0
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    return sort64_desc(lane < kk ? slot[lane] : 0ull, lane);
+    // base < kk when the wave holds fewer than kk of the row's values (a short
+    // or empty last wave): only the slots written are read
+    return sort64_desc(lane < base ? slot[lane] : 0ull, lane);
 }
 
 // Two composite lists, each sorted descending over the lanes: the 64 largest
@@ -467,15 +481,29 @@ __device__ __forceinline__ uint64_t merge64(uint64_t v, uint64_t u_rev, int lane
 }
 
 // Few rows of more than 512 blocks (latency-bound): one workgroup of four
-// waves per row.  Wave w takes columns [w*NC, (w+1)*NC) of the row and finds
-// their exact top-kk (wave_topk); the union of the four holds the row's
-// top-kk, and two levels of merge64 give it sorted.  Each wave's work is a
-// quarter of the one-wave kernel's load and candidate steps.
+// waves per row.  The row's ncol columns are shared out evenly, wave w
+// holding columns [w*ncol/4, (w+1)*ncol/4), at most NC of them: with the
+// values spread alike the four sampled thresholds below are alike too.
+//
+// Pooled path.  Wave w, holding nw of the row's nb values, samples a
+// threshold that at least ceil(kk*nw/nb) of its values reach.  These shares
+// sum to at least kk, so the smallest of the four thresholds is one that at
+// least kk values of the row reach; shares in proportion to the values keep
+// the pool near kk.  The waves compact the candidates x >= th into one pool
+// (offsets from an LDS counter), and if it holds kk..128 of them the row's
+// top-kk is among them: wave 0 sorts the pool.  One barrier more than the
+// per-wave selection, and no merges.
+//
+// Otherwise each wave finds the exact top-kk of its own columns (wave_topk);
+// the union of the four holds the row's top-kk, and two levels of merge64
+// give it sorted.
 template <int NC>
 __global__ __launch_bounds__(256) void topk_quad_kernel(TopkArgs a) {
     __shared__ uint32_t row[4 * NC * 64];        // the row's raw fp32 bits (pad past nb)
-    __shared__ uint64_t slot[4][128];
+    __shared__ uint64_t slot[4][128];            // per-wave slots; slot[0] is also the pool
     __shared__ uint64_t lists[4][64];
+    __shared__ uint32_t thr[4];
+    __shared__ int pool_n;
     const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
     // rows in the scorers' XCD order: row R is read on the XCD that wrote it
@@ -493,29 +521,80 @@ __global__ __launch_bounds__(256) void topk_quad_kernel(TopkArgs a) {
     const uint32_t kPad = 0xffffffffu;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float *>(srow), 0, nb * 4, 0x00020000 /* 32-bit elements, raw */);
-    const int col0 = w * NC;
+    const int ncol = (nb + 63) >> 6;
+    const int col0 = w * ncol / 4, ncw = (w + 1) * ncol / 4 - col0;   // this wave's columns
+    const int id_end = min(nb, (col0 + ncw) * 64);                    // ... and its ids
+    const int nw = max(id_end - col0 * 64, 0);                        // ... and its values
     uint32_t xr[NC];
     #pragma unroll
     for (int j = 0; j < NC; ++j) {
+        // All NC columns are loaded and stashed: a column past the share is
+        // the next wave's, which stashes the same bits, or lies past nb
+        // (pads, never read back).  Ownership is a per-lane test, so that
+        // no load or store sits under a branch that would serialise them.
         const int c = col0 + j;
         const uint32_t x = __builtin_amdgcn_raw_buffer_load_b32(rs, (c * 64 + lane) * 4, 0, 0);
-        xr[j] = lane < nb - 64 * c ? x : kPad;
-        row[c * 64 + lane] = xr[j];
+        const uint32_t xv = lane < nb - 64 * c ? x : kPad;
+        row[c * 64 + lane] = xv;
+        xr[j] = 64 * j + lane < nw ? xv : kPad;
     }
+    if (threadIdx.x == 0) pool_n = 0;
     uint64_t v = 0;
+    bool pooled = false;
     if (kk > 0) {   // uniform
-        v = wave_topk<NC>(xr, col0, kk, nb, lane, slot[w],
-                          [&](int id) { return __builtin_bit_cast(float, row[id]); });
-        lists[w][lane] = v;
+        // a share of kk proportional to the wave's values; the shares sum to >= kk
+        const uint32_t Tw = sampled_threshold<NC>(xr, (kk * nw + nb - 1) / nb);
+        if (lane == 0) thr[w] = Tw;
+        __syncthreads();   // also publishes the row stash and the zeroed counter
+        const uint32_t T = min(min(thr[0], thr[1]), min(thr[2], thr[3]));
+        const float th = __builtin_bit_cast(float, T ^ 0x80000000u);
+        uint32_t mask = 0;
+        #pragma unroll
+        for (int j = 0; j < NC; ++j)
+            mask |= static_cast<uint32_t>(__builtin_bit_cast(float, xr[j]) >= th) << j;
+        int cw = 0;
+        int off = wave_excl_scan(__popc(mask), lane, &cw);
+        int base = 0;
+        if (lane == 0 && cw > 0) base = atomicAdd(&pool_n, cw);
+        base = __builtin_amdgcn_readfirstlane(base);
+        if (base + cw <= 128) {   // uniform; a fuller pool is not used
+            off += base;
+            while (mask) {
+                const int j = __builtin_ctz(mask);
+                mask &= mask - 1;
+                const int id = (col0 + j) * 64 + lane;
+                slot[0][off++] = composite(order_key(__builtin_bit_cast(float, row[id])), id);
+            }
+        }
+        __syncthreads();
+        const int C = pool_n;   // uniform over the workgroup
+        pooled = C >= kk && C <= 128;
+        if (pooled) {
+            if (w != 0) return;
+            const uint64_t v0 = lane < C ? slot[0][lane] : 0ull;
+            if (C <= 64) {
+                v = sort64_desc(v0, lane);
+            } else {
+                const uint64_t v1 = lane + 64 < C ? slot[0][lane + 64] : 0ull;
+                v = top64_of_128(v0, v1, lane);
+            }
+        }
     }
-    __syncthreads();
-    if (kk > 0 && (w & 1) == 0) {   // waves 0, 2: merge with wave w + 1
-        v = merge64(v, lists[w + 1][63 - lane], lane);
-        lists[w][lane] = v;
+    if (!pooled) {   // uniform
+        if (kk > 0) {
+            v = wave_topk<NC>(xr, col0, kk, id_end, lane, slot[w],
+                              [&](int id) { return __builtin_bit_cast(float, row[id]); });
+            lists[w][lane] = v;
+        }
+        __syncthreads();
+        if (kk > 0 && (w & 1) == 0) {   // waves 0, 2: merge with wave w + 1
+            v = merge64(v, lists[w + 1][63 - lane], lane);
+            lists[w][lane] = v;
+        }
+        __syncthreads();
+        if (w != 0) return;
+        if (kk > 0) v = merge64(v, lists[2][63 - lane], lane);
     }
-    __syncthreads();
-    if (w != 0) return;
-    if (kk > 0) v = merge64(v, lists[2][63 - lane], lane);
     if (lane < a.k) {
         int32_t id = -1;
         float val = -__builtin_inff();

@@ -308,7 +308,8 @@ def test_ragged_geometry(geo):
 def topk_cases():
     rng = np.random.default_rng(42)
     cases = []
-    for nb in (1, 5, 63, 64, 65, 200, 2049, 4096, 5000):
+    # 520, 1100, 3000: few-row selector shapes whose last waves hold few or none of the values
+    for nb in (1, 5, 63, 64, 65, 200, 520, 1100, 2049, 3000, 4096, 5000):
         cases.append(("random", rng.standard_normal((13, nb)).astype(np.float32), nb))
     nb = 300
     cases.append(("all_equal", np.full((4, nb), 0.5, np.float32), nb))
@@ -338,6 +339,14 @@ def topk_cases():
         zz[r, pos[30:50]] = 0.0
         zz[r, pos[50:]] = -0.0
     cases.append(("signed_zero_threshold_500", zz, 500))
+    # 150 tied maxima per row: more candidates than the few-row selector's
+    # pooled path holds, so its per-wave selection and merges decide, ties
+    # spread over the four waves' columns
+    for nbt in (1100, 2049):
+        tt = rng.standard_normal((4, nbt)).astype(np.float32)
+        for r in range(4):
+            tt[r, rng.choice(nbt, 150, replace=False)] = 3.0
+        cases.append((f"tied_top_{nbt}", tt, nbt))
     cases.append(("all_negative_100", -rng.random((6, 100)).astype(np.float32) - 0.5, 100))
     cases.append(("all_negative_2049", -rng.random((4, 2049)).astype(np.float32), 2049))
     return cases
