@@ -39,6 +39,15 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
+// 2*mask + (x >= th) in two VALU ops: the compare writes VCC and the add
+// takes it as its carry (written as C, the compiler turns the add into ORs of
+// shifted select results, three to four ops).  NaN never compares >= .
+__device__ __forceinline__ uint32_t shift_in_ge(uint32_t mask, float x, float th) {
+    asm("v_cmp_le_f32 vcc, %2, %1\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc"
+        : "+v"(mask) : "v"(x), "v"(th) : "vcc");
+    return mask;
+}
+
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
     return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, false));
@@ -81,37 +90,45 @@ __device__ __forceinline__ uint32_t xor_lane(uint32_t v, int lane) {
     }
 }
 
-template <int M>
-__device__ __forceinline__ uint64_t xor_lane64(uint64_t v, int lane) {
-    const uint32_t lo = xor_lane<M>(static_cast<uint32_t>(v), lane);
-    const uint32_t hi = xor_lane<M>(static_cast<uint32_t>(v >> 32), lane);
-    return (static_cast<uint64_t>(hi) << 32) | lo;
+template <int M, typename T>
+__device__ __forceinline__ T xor_lane_t(T v, int lane) {
+    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit elements");
+    if constexpr (sizeof(T) == 4) {
+        return static_cast<T>(xor_lane<M>(static_cast<uint32_t>(v), lane));
+    } else {
+        const uint32_t lo = xor_lane<M>(static_cast<uint32_t>(v), lane);
+        const uint32_t hi = xor_lane<M>(static_cast<uint32_t>(v >> 32), lane);
+        return static_cast<T>((static_cast<uint64_t>(hi) << 32) | lo);
+    }
 }
 
 // Compare-exchange with the partner's value p: keep the larger or the smaller.
-__device__ __forceinline__ uint64_t cmpx(uint64_t v, uint64_t p, bool keep_max) {
+template <typename T>
+__device__ __forceinline__ T cmpx(T v, T p, bool keep_max) {
     return ((p > v) == keep_max) ? p : v;
 }
 
 // Bitonic networks in the uniform-direction (mirror) form: a merge of size s
 // first pairs element e with its mirror e ^ (s-1), then with e ^ (s/4), ...,
 // e ^ 1; the element of the pair with the clear bit keeps the larger value
-// (descending) or the smaller (ascending).  One composite per lane.
-template <int M, int B>
-__device__ __forceinline__ void step2(uint64_t &v0, uint64_t &v1, int lane) {
-    const uint64_t p0 = xor_lane64<M>(v0, lane);
-    const uint64_t p1 = xor_lane64<M>(v1, lane);
+// (descending) or the smaller (ascending).  One element per lane: a 64-bit
+// (key, ~id) composite, or a 32-bit word of the same order.
+template <int M, int B, typename T>
+__device__ __forceinline__ void step2(T &v0, T &v1, int lane) {
+    const T p0 = xor_lane_t<M>(v0, lane);
+    const T p1 = xor_lane_t<M>(v1, lane);
     const bool lower = (lane & B) == 0;
     v0 = cmpx(v0, p0, lower);    // descending
     v1 = cmpx(v1, p1, !lower);   // ascending
 }
-template <int M, int B>
-__device__ __forceinline__ void step1(uint64_t &v, int lane) {
-    v = cmpx(v, xor_lane64<M>(v, lane), (lane & B) == 0);
+template <int M, int B, typename T>
+__device__ __forceinline__ void step1(T &v, int lane) {
+    v = cmpx(v, xor_lane_t<M>(v, lane), (lane & B) == 0);
 }
 
 // Sorts v0 descending and v1 ascending over the 64 lanes.
-__device__ __forceinline__ void sort64_pair(uint64_t &v0, uint64_t &v1, int lane) {
+template <typename T>
+__device__ __forceinline__ void sort64_pair(T &v0, T &v1, int lane) {
     step2<1, 1>(v0, v1, lane);
     step2<3, 2>(v0, v1, lane);   step2<1, 1>(v0, v1, lane);
     step2<7, 4>(v0, v1, lane);   step2<2, 2>(v0, v1, lane);   step2<1, 1>(v0, v1, lane);
@@ -124,7 +141,8 @@ __device__ __forceinline__ void sort64_pair(uint64_t &v0, uint64_t &v1, int lane
 }
 
 // Sorts v descending over the 64 lanes (lane 0 largest).
-__device__ __forceinline__ uint64_t sort64_desc(uint64_t v, int lane) {
+template <typename T>
+__device__ __forceinline__ T sort64_desc(T v, int lane) {
     step1<1, 1>(v, lane);
     step1<3, 2>(v, lane);   step1<1, 1>(v, lane);
     step1<7, 4>(v, lane);   step1<2, 2>(v, lane);   step1<1, 1>(v, lane);
@@ -136,14 +154,17 @@ __device__ __forceinline__ uint64_t sort64_desc(uint64_t v, int lane) {
     return v;
 }
 
-// The 64 largest of 128 composites (two per lane), sorted descending: sort
+// The 64 largest of 128 elements (two per lane), sorted descending: sort
 // the slots in opposite directions, so that element i of the 128-sequence
 // meets element i + 64 in the same lane; the larger of each pair forms a
 // bitonic sequence holding the 64 largest, which a half-cleaner cascade
-// (partners lane ^ 32, ..., lane ^ 1) sorts.
-__device__ __forceinline__ uint64_t top64_of_128(uint64_t v0, uint64_t v1, int lane) {
+// (partners lane ^ 32, ..., lane ^ 1) sorts.  *rest receives the smaller of
+// each pair: the 64 elements left out.
+template <typename T>
+__device__ __forceinline__ T top64_of_128(T v0, T v1, int lane, T *rest = nullptr) {
     sort64_pair(v0, v1, lane);
-    uint64_t v = v0 > v1 ? v0 : v1;
+    T v = v0 > v1 ? v0 : v1;
+    if (rest) *rest = v0 > v1 ? v1 : v0;
     step1<32, 32>(v, lane);
     step1<16, 16>(v, lane);
     step1<8, 8>(v, lane);
@@ -155,6 +176,53 @@ __device__ __forceinline__ uint64_t top64_of_128(uint64_t v0, uint64_t v1, int l
 
 __device__ __forceinline__ uint64_t composite(uint32_t key, int id) {
     return (static_cast<uint64_t>(key) << 32) | (0xffffffffu - static_cast<uint32_t>(id));
+}
+
+// The candidates slot[0..C) (composites, C <= 128) sorted descending and cut
+// to 64: lane i returns the i-th largest (zero past C).
+//
+// With words set (a constant at every call), the network moves 32-bit words
+// where that is exact.  A candidate's word is its key's distance above kb (a
+// key no candidate is below) shifted left by 7, with 127 - (its slot) in the
+// low bits: words order as the keys do while every distance stays below
+// 2^25, and the low bits make them unique.  Equal keys come out in slot
+// order, which is not id order (slots are filled lane by lane), so a sorted
+// run of equal keys, or equal keys on both sides of the 64th place, sends the
+// candidates through the network again as composites.  A step of the network
+// moves one register instead of two and compares 32 bits instead of 64.
+// C = 128 takes the composites too: its last slot's word could be zero, the
+// value of an empty place.  That pays where many rows keep the VALU busy
+// (1.9 % per prefill phase of 65,536 rows of 2049 blocks); a launch of few
+// rows waits on the chain of steps instead, which the tie checks and the
+// second LDS read lengthen as much as the narrower network shortens it.
+__device__ __forceinline__ uint64_t sorted_top64(const uint64_t *slot, int C, uint32_t kb, int lane,
+                                                 bool words) {
+    if (words && C <= 127) {   // uniform
+        const uint32_t d0 = static_cast<uint32_t>((lane < C ? slot[lane] : 0ull) >> 32) - kb;
+        const uint32_t d1 = static_cast<uint32_t>((lane + 64 < C ? slot[lane + 64] : 0ull) >> 32) - kb;
+        const bool far = (lane < C && d0 >= (1u << 25)) || (lane + 64 < C && d1 >= (1u << 25));
+        if (ballot(far) == 0) {   // uniform
+            const uint32_t w0 = lane < C ? (d0 << 7) | static_cast<uint32_t>(127 - lane) : 0u;
+            const uint32_t w1 = lane + 64 < C ? (d1 << 7) | static_cast<uint32_t>(63 - lane) : 0u;
+            uint32_t u, rest = 0;   // rest: the words left out of the 64 (zero if empty)
+            if (C <= 64) u = sort64_desc(w0, lane);
+            else u = top64_of_128(w0, w1, lane, &rest);
+            const int n = C < 64 ? C : 64;
+            const uint32_t next = static_cast<uint32_t>(
+                __builtin_amdgcn_ds_bpermute((lane + 1) << 2, static_cast<int>(u)));
+            const uint32_t last = static_cast<uint32_t>(
+                __builtin_amdgcn_readlane(static_cast<int>(u), 63));
+            const bool tie = (lane + 1 < n && (u >> 7) == (next >> 7)) ||
+                             (rest != 0 && (rest >> 7) == (last >> 7));
+            if (ballot(tie) == 0) return lane < n ? slot[127 - (u & 127)] : 0ull;
+        }
+    }
+    // the second half is read only when there is one: a launch of few rows
+    // waits on every read
+    const uint64_t v0 = lane < C ? slot[lane] : 0ull;
+    if (C <= 64) return sort64_desc(v0, lane);
+    const uint64_t v1 = lane + 64 < C ? slot[lane + 64] : 0ull;
+    return top64_of_128(v0, v1, lane);
 }
 
 template <int CTRL, int ROW_MASK>
@@ -179,6 +247,19 @@ __device__ __forceinline__ int wave_excl_scan(int x, int lane, int *total) {
     return static_cast<int>(v) - x;
 }
 
+// The register-held row lengths, in 64-wide columns: a row of nj columns
+// takes the first case >= nj.  So the columns below the case before it are
+// always full, and only the ones above can hold padding.
+constexpr int kTopkCases[] = {1, 2, 4, 8, 16, 24, 32, 33, 40, 48, 64};
+constexpr int full_columns(int npl) {
+    int prev = 0;
+    for (int c : kTopkCases) {
+        if (c == npl) return prev;
+        prev = c;
+    }
+    return 0;
+}
+
 // NPL > 0: the row's values held in registers (row length <= 64*NPL).
 // NPL == 0: values re-read from memory in every pass (any row length).
 //
@@ -192,7 +273,13 @@ __device__ __forceinline__ int wave_excl_scan(int x, int lane, int *total) {
 // by bitonic networks.  Any other C takes the exact path: a 32-step
 // ballot bisection for the kk-th largest key over every value, then ties in
 // id order.
-template <int NPL>
+//
+// MANY: the launch of four rows per workgroup over many rows, bound by the
+// VALU's throughput; it takes the steps with fewer VALU ops even where they
+// lengthen a row's chain of dependent steps (the candidate mask, the sort of
+// 32-bit words).  Without it, a launch of few rows, each row's latency is
+// what counts.
+template <int NPL, bool MANY>
 __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     __shared__ uint64_t slot[4][128];   // one per wave of the workgroup (at most four)
     // the row's values, for the candidates' second look (lane l keeps its own
@@ -227,10 +314,11 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
         // branch), then the pad substituted past nb.
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<float *>(srow), 0, nb * 4, 0x00020000 /* 32-bit elements, raw */);
+        constexpr int kFull = full_columns(NPL);
         #pragma unroll
         for (int j = 0; j < NPL; ++j) {
             const uint32_t x = __builtin_amdgcn_raw_buffer_load_b32(rs, (j * 64 + lane) * 4, 0, 0);
-            xr[j] = lane < nb - 64 * j ? x : kPad;
+            xr[j] = j < kFull || lane < nb - 64 * j ? x : kPad;
         }
         #pragma unroll
         for (int j = 0; j < NPL; ++j) stash[w][j * 64 + lane] = xr[j];
@@ -269,13 +357,29 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
                 if (cnt >= kk) T = cand;
             }
             const float th = __builtin_bit_cast(float, T ^ 0x80000000u);
-            // 3. candidates x >= th as a per-lane bitmask over j
+            // 3. candidates x >= th as a per-lane bitmask over j.  Many rows:
+            //    shifted in from the highest column down, two VALU ops a
+            //    column but one chain of dependent ops; few rows, which wait
+            //    on that chain: the compiler's tree of selects and ORs.
             uint32_t mlo = 0, mhi = 0;
-            #pragma unroll
-            for (int j = 0; j < NPL; ++j) {
-                const bool c = __builtin_bit_cast(float, xr[j]) >= th;
-                if (j < 32) mlo |= static_cast<uint32_t>(c) << j;
-                else mhi |= static_cast<uint32_t>(c) << (j - 32);
+            if constexpr (MANY) {
+                #pragma unroll
+                for (int j = NPL - 1; j >= 0; --j) {
+                    const float x = __builtin_bit_cast(float, xr[j]);
+                    if (j < 32) mlo = shift_in_ge(mlo, x, th);
+                    else mhi = shift_in_ge(mhi, x, th);
+                }
+                // the masks' widths, which the compiler cannot see through
+                // the asm: with them it sizes the compaction loop below
+                if constexpr (NPL < 32) mlo &= (1u << NPL) - 1u;
+                if constexpr (NPL > 32 && NPL < 64) mhi &= (1u << (NPL - 32)) - 1u;
+            } else {
+                #pragma unroll
+                for (int j = 0; j < NPL; ++j) {
+                    const bool c = __builtin_bit_cast(float, xr[j]) >= th;
+                    if (j < 32) mlo |= static_cast<uint32_t>(c) << j;
+                    else mhi |= static_cast<uint32_t>(c) << (j - 32);
+                }
             }
             const int cnt = __popc(mlo) + __popc(mhi);
             int C = 0;
@@ -308,13 +412,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                const uint64_t v0 = lane < C ? slot[w][lane] : 0ull;
-                if (C <= 64) {
-                    v = sort64_desc(v0, lane);
-                } else {
-                    const uint64_t v1 = lane + 64 < C ? slot[w][lane + 64] : 0ull;
-                    v = top64_of_128(v0, v1, lane);
-                }
+                v = sorted_top64(slot[w], C, order_key(th), lane, MANY);
                 done = true;
             }
         }
@@ -423,10 +521,7 @@ __device__ __forceinline__ uint64_t wave_topk(const uint32_t (&xr)[NC], int col0
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const uint64_t v0 = lane < C ? slot[lane] : 0ull;
-        if (C <= 64) return sort64_desc(v0, lane);
-        const uint64_t v1 = lane + 64 < C ? slot[lane + 64] : 0ull;
-        return top64_of_128(v0, v1, lane);
+        return sorted_top64(slot, C, order_key(th), lane, false);
     }
     // exact path over the wave's columns
     auto key = [&](int j) -> uint32_t { return order_key(__builtin_bit_cast(float, xr[j])); };
@@ -571,13 +666,7 @@ __global__ __launch_bounds__(256) void topk_quad_kernel(TopkArgs a) {
         pooled = C >= kk && C <= 128;
         if (pooled) {
             if (w != 0) return;
-            const uint64_t v0 = lane < C ? slot[0][lane] : 0ull;
-            if (C <= 64) {
-                v = sort64_desc(v0, lane);
-            } else {
-                const uint64_t v1 = lane + 64 < C ? slot[0][lane + 64] : 0ull;
-                v = top64_of_128(v0, v1, lane);
-            }
+            v = sorted_top64(slot[0], C, order_key(th), lane, false);
         }
     }
     if (!pooled) {   // uniform
@@ -609,24 +698,29 @@ __global__ __launch_bounds__(256) void topk_quad_kernel(TopkArgs a) {
 
 typedef void (*topk_fn)(TopkArgs);
 
-topk_fn pick(int nb, int *npl_out) {
+// The first case of the table that holds nj columns (topk_kernel<0, .>, the
+// re-reading path, past the last).
+template <bool MANY, int I = 0>
+topk_fn pick_case(int nj, int *npl_out) {
+    constexpr int kN = sizeof(kTopkCases) / sizeof(kTopkCases[0]);
+    if constexpr (I < kN) {
+        constexpr int N = kTopkCases[I];
+        if (nj <= N) {
+            *npl_out = N;
+            return topk_kernel<N, MANY>;
+        }
+        return pick_case<MANY, I + 1>(nj, npl_out);
+    } else {
+        *npl_out = 0;
+        return topk_kernel<0, MANY>;
+    }
+}
+
+// many: the launch of many rows (four per workgroup), which the VALU's
+// throughput bounds rather than each row's chain of steps
+topk_fn pick(int nb, bool many, int *npl_out) {
     const int nj = (nb + 63) / 64;
-#define QSA_TOPK_CASE(N) \
-    if (nj <= N) { *npl_out = N; return topk_kernel<N>; }
-    QSA_TOPK_CASE(1)
-    QSA_TOPK_CASE(2)
-    QSA_TOPK_CASE(4)
-    QSA_TOPK_CASE(8)
-    QSA_TOPK_CASE(16)
-    QSA_TOPK_CASE(24)
-    QSA_TOPK_CASE(32)
-    QSA_TOPK_CASE(33)
-    QSA_TOPK_CASE(40)
-    QSA_TOPK_CASE(48)
-    QSA_TOPK_CASE(64)
-#undef QSA_TOPK_CASE
-    *npl_out = 0;
-    return topk_kernel<0>;
+    return many ? pick_case<true>(nj, npl_out) : pick_case<false>(nj, npl_out);
 }
 
 }  // namespace
@@ -656,7 +750,7 @@ hipError_t launch_topk(const TopkGeom &geo, hipStream_t s) {
                geo.rows_per_group, geo.src_group_rows, geo.dst_group_rows, geo.dst_row0,
                geo.nb, geo.k};
     int npl = 0;
-    topk_fn fn = pick(geo.nb, &npl);
+    topk_fn fn = pick(geo.nb, wpb == 4, &npl);
     void *args[] = {&a};
     return hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(static_cast<unsigned>(blocks)),
                            dim3(64 * wpb), args, 0, s);

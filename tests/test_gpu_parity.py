@@ -339,6 +339,21 @@ def topk_cases():
         zz[r, pos[30:50]] = 0.0
         zz[r, pos[50:]] = -0.0
     cases.append(("signed_zero_threshold_500", zz, 500))
+    # Pairs of equal values inside the top 64 and one straddling the 64th
+    # place, otherwise distinct values; and rows whose top values span many
+    # binades (a few huge values among normal ones): the selector's sort of
+    # 32-bit words must hand both kinds back to its sort of composites.
+    for nbt in (300, 2049):
+        pt = rng.standard_normal((6, nbt)).astype(np.float32)
+        for r in range(6):
+            order = np.argsort(-pt[r], kind="stable")
+            for rank in (3, 20, 63):
+                pt[r, order[rank + 1]] = pt[r, order[rank]]
+        cases.append((f"paired_ties_{nbt}", pt, nbt))
+        wr = rng.standard_normal((6, nbt)).astype(np.float32)
+        for r in range(6):
+            wr[r, rng.choice(nbt, 5, replace=False)] = np.float32(1e30) * rng.random(5).astype(np.float32)
+        cases.append((f"wide_range_{nbt}", wr, nbt))
     # 150 tied maxima per row: more candidates than the few-row selector's
     # pooled path holds, so its per-wave selection and merges decide, ties
     # spread over the four waves' columns
@@ -366,11 +381,12 @@ def test_topk_bit_exact(case, k):
     assert np.all(vals[~sel] == -np.inf)
 
 
-@pytest.mark.parametrize("case", [c for c in topk_cases() if c[2] > 512], ids=lambda c: c[0])
+@pytest.mark.parametrize("case", topk_cases(), ids=lambda c: f"{c[0]}_nb{c[2]}")
 def test_topk_many_rows_path_bit_exact(case):
     """The same rows repeated to 4096+ rows: the selector's many-rows launch
-    (four rows per workgroup instead of one): ids and values bit for bit
-    the oracle's top-k for k = 64 and k = 5."""
+    (four rows per workgroup instead of one, candidates sorted as 32-bit
+    words where exact): ids and values bit for bit the oracle's top-k for
+    k = 64 and k = 5."""
     _, s, nb = case
     reps = -(-4096 // s.shape[0])
     big = np.ascontiguousarray(np.tile(s, (reps, 1)))
