@@ -664,9 +664,20 @@ __global__ __launch_bounds__(256) void topk_quad_kernel(TopkArgs a) {
         __syncthreads();
         const int C = pool_n;   // uniform over the workgroup
         pooled = C >= kk && C <= 128;
-        if (pooled) {
-            if (w != 0) return;
-            v = sorted_top64(slot[0], C, order_key(th), lane, false);
+        if (pooled) {   // uniform over the workgroup
+            if (C > 64) {
+                // waves 0 and 1 sort the pool's two halves side by side and
+                // wave 0 merges them: one 64-wide sort and a merge on the
+                // row's path instead of the 128 -> 64 network on one wave
+                if (w == 1) lists[1][lane] = sort64_desc(lane + 64 < C ? slot[0][lane + 64] : 0ull, lane);
+                if (w == 0) v = sort64_desc(slot[0][lane], lane);
+                __syncthreads();   // every wave, so that no barrier counts on ended waves
+                if (w != 0) return;
+                v = merge64(v, lists[1][63 - lane], lane);
+            } else {
+                if (w != 0) return;
+                v = sort64_desc(lane < C ? slot[0][lane] : 0ull, lane);
+            }
         }
     }
     if (!pooled) {   // uniform
