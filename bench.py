@@ -53,13 +53,38 @@ def parse():
     return p.parse_args()
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments and trailing blanks: what compiles."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":                      # string or character literal
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = (line.rstrip() for line in "".join(out).split("\n"))
+    return "\n".join(line for line in lines if line)
+
+
 def source_digest() -> str:
-    """sha256 over the kernel sources, to tie stored counter figures to code."""
+    """sha256 over the kernel sources' code (comments left out), to tie
+    stored counter figures to the code they were taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_attention_block_qsa_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

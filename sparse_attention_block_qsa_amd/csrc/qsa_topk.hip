@@ -8,13 +8,18 @@
 // sign-magnitude flip.  Ids beyond the row also get key 0 and, having the
 // largest ids, rank after every real entry.
 //
-// One wave64 per row, the row's keys held in registers (NPL per lane, block
-// id = j*64 + lane), or re-read per pass when the row is longer than the
-// register budget.  Steps:
-// a sampled threshold filters the row down to <= 128 candidates, whose exact
-// composites are sorted by a bitonic network (see topk_kernel); rows the
-// filter cannot reduce take an exact ballot-bisection path.  LDS use is a
-// per-wave slot of 128 x 8 bytes, independent of the row length.
+// Every form takes the same steps: a sampled threshold filters the row down
+// to <= 128 candidates, whose exact composites are sorted by bitonic networks
+// over the wave's lanes; a row the filter cannot reduce takes an exact
+// ballot-bisection path.  The row's values are also stashed in LDS, so that a
+// candidate's value is read back by id.  Launch forms:
+//  * topk_kernel<NPL, MANY>: one wave64 per row, the row's values held in
+//    registers (NPL per lane, block id = j*64 + lane), or re-read per pass
+//    past the register budget (NPL = 0).  One row per workgroup for few rows;
+//    four per workgroup for many (MANY), where VALU throughput rather than a
+//    row's latency bounds the launch and the steps with fewer ops are taken.
+//  * topk_quad_kernel<NC>: few rows of more than 512 blocks, four waves per
+//    row, the waves' candidates pooled into one set.
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -586,8 +591,8 @@ __device__ __forceinline__ uint64_t merge64(uint64_t v, uint64_t u_rev, int lane
 // least kk values of the row reach; shares in proportion to the values keep
 // the pool near kk.  The waves compact the candidates x >= th into one pool
 // (offsets from an LDS counter), and if it holds kk..128 of them the row's
-// top-kk is among them: wave 0 sorts the pool.  One barrier more than the
-// per-wave selection, and no merges.
+// top-kk is among them: wave 0 sorts a pool of up to 64, and a fuller one is
+// sorted half by wave 0 and half by wave 1, then merged by wave 0.
 //
 // Otherwise each wave finds the exact top-kk of its own columns (wave_topk);
 // the union of the four holds the row's top-kk, and two levels of merge64
