@@ -339,6 +339,22 @@ def topk_cases():
         zz[r, pos[30:50]] = 0.0
         zz[r, pos[50:]] = -0.0
     cases.append(("signed_zero_threshold_500", zz, 500))
+    # the same special values in rows of more than 512 blocks: the four-wave
+    # few-row selector and, repeated, the 33-column many-rows one
+    s2 = rng.standard_normal((6, 2049)).astype(np.float32)
+    s2[rng.random((6, 2049)) < 0.1] = np.nan
+    s2[rng.random((6, 2049)) < 0.03] = np.inf
+    s2[rng.random((6, 2049)) < 0.03] = -np.inf
+    s2[0, :] = np.nan
+    s2[1, 40:] = np.nan   # fewer numbers than k: NaNs selected, in id order
+    cases.append(("nan_inf", s2, 2049))
+    z2 = -1.0 - rng.random((6, 1100)).astype(np.float32)
+    for r in range(6):
+        pos = rng.choice(1100, 70, replace=False)
+        z2[r, pos[:30]] = rng.random(30).astype(np.float32) + 1.0
+        z2[r, pos[30:50]] = 0.0
+        z2[r, pos[50:]] = -0.0
+    cases.append(("signed_zero_threshold_1100", z2, 1100))
     # Pairs of equal values inside the top 64 and one straddling the 64th
     # place, otherwise distinct values; and rows whose top values span many
     # binades (a few huge values among normal ones): the selector's sort of
