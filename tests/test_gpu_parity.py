@@ -415,6 +415,51 @@ def test_topk_many_rows_path_bit_exact(case):
                               big[np.nonzero(sel)[0], ids[sel]].view(np.uint32))
 
 
+def _random_topk_case(i):
+    """Case i of the seeded randomised selector sweep: a row length near one
+    of the selector's boundaries, few or many rows, any k, and one of five
+    value mixes (normal; quantised, many ties; NaN and infinities; a block
+    of tied maxima; a few huge values among normal ones)."""
+    rng = np.random.default_rng(7000 + i)
+    ranges = [(1, 80), (500, 600), (1000, 1200), (2000, 2200), (3000, 4100), (4097, 6000),
+              (60, 520), (2049, 2112)]
+    lo, hi = ranges[i % 8]
+    nb = int(rng.integers(lo, hi + 1))
+    many = i % 8 == 7   # the many-rows launch at the prefill chunk's row length
+    rows = 4096 + int(rng.integers(0, 64)) if many else int(rng.integers(1, 65))
+    k = int(rng.integers(1, 65))
+    mix = i % 5
+    s = rng.standard_normal((rows, nb)).astype(np.float32)
+    if mix == 1:
+        s = (rng.integers(0, int(rng.integers(5, 2000)), (rows, nb)) / 8.0).astype(np.float32)
+    elif mix == 2:
+        s[rng.random((rows, nb)) < 0.08] = np.nan
+        s[rng.random((rows, nb)) < 0.02] = np.inf
+        s[rng.random((rows, nb)) < 0.02] = -np.inf
+    elif mix == 3:
+        n_tied = int(rng.integers(1, min(nb, 200) + 1))
+        for r in range(rows):
+            s[r, rng.choice(nb, n_tied, replace=False)] = 4.0
+    elif mix == 4:
+        s[rng.random((rows, nb)) < 0.003] = np.float32(3e28)
+    return s, nb, k
+
+
+@pytest.mark.parametrize("i", range(48))
+def test_topk_randomised_shapes(i):
+    """Seeded random selector cases across the launch forms (one wave per
+    row, four rows per workgroup, four waves per row, the re-reading path):
+    ids and values bit for bit the oracle's top-k of the same fp32 rows."""
+    s, nb, k = _random_topk_case(i)
+    print(f"case {i}: rows {s.shape[0]}, nb {nb}, k {k}", flush=True)
+    ids, vals = run_topk_dev(s, nb, k)
+    want_ids, _ = oracle.topk(s.astype(np.float64), k)
+    assert np.array_equal(ids, want_ids), f"case {i}: rows {s.shape[0]}, nb {nb}, k {k}"
+    sel = ids >= 0
+    assert np.array_equal(vals[sel].view(np.uint32), s[np.nonzero(sel)[0], ids[sel]].view(np.uint32))
+    assert np.all(vals[~sel] == -np.inf)
+
+
 def test_topk_k_larger_than_nb_and_empty_rows():
     s = np.arange(10, dtype=np.float32)[None, :].repeat(3, 0)
     ids, vals = run_topk_dev(s, 10, 16)
