@@ -187,6 +187,71 @@ def test_decode_shapes_phase(shape):
     assert np.all(v[~sel] == -np.inf)
 
 
+def _random_phase_case(i):
+    """Case i of the seeded randomised phase sweep: KV heads, queries, heads,
+    head dim, block size, context length, k and a query chunk; every twelfth
+    case has enough query rows for the wide scorer."""
+    rng = np.random.default_rng(9000 + i)
+    if i % 12 == 11:
+        G, nq = 4, 4096 + int(rng.integers(0, 64))
+        H = int(rng.choice([4, 8, 12]))
+        D = 64 if H == 12 else 128
+        bs = 64
+        n_kv = int(rng.integers(1, 12)) * bs + int(rng.integers(0, bs))
+    else:
+        G = int(rng.choice([1, 2, 3, 4, 8]))
+        nq = int(rng.integers(1, 400))
+        H = int(rng.integers(1, 17))
+        D = int(rng.choice([64, 128]))
+        bs = int(rng.choice([8, 16, 32, 64, 128]))
+        n_kv = int(rng.integers(0, 3000))
+    k = int(rng.integers(1, 65))
+    q_chunk = 0 if i % 3 else int(rng.integers(1, nq + 1))
+    return G, nq, H, D, n_kv, bs, k, q_chunk
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_phase_randomised_geometry(i):
+    """Seeded random geometries through the whole phase with fp32 queries:
+    scores within the bound, the tail bit for bit the fixed-order model, ids
+    the top-k of the device scores and near-tie consistent with the oracle's,
+    values bit for bit; with a query chunk, the same bits as one pass."""
+    G, nq, H, D, n_kv, bs, k, q_chunk = _random_phase_case(i)
+    log(f"phase case {i}: G {G} nq {nq} H {H} D {D} n_kv {n_kv} bs {bs} k {k} q_chunk {q_chunk}")
+    cfg = qi.Config("rphase", G, nq, H, D, n_kv, bs, k, "normal", 9100 + i)
+    w = qi.make(cfg)
+    q = torch.from_numpy(w.q32).to(dev())
+    kb = k_dev(w.kblk)
+
+    def run(chunk):
+        ws = qsa.PhaseWorkspace(nq, G, H, D, n_kv, bs, k, dev(), with_vals=True)
+        ids, vals = qsa.select_phase(q, kb, n_kv, bs, k, ws, q_chunk=chunk)
+        torch.cuda.synchronize()
+        return ws, ids.reshape(cfg.rows, k).cpu().numpy(), vals.reshape(cfg.rows, k).cpu().numpy()
+
+    ws, got, v = run(q_chunk)
+    nb = cfg.nb
+    if nb == 0:
+        assert np.all(got == -1) and np.all(v == -np.inf)
+        return
+    s_gpu = ws.scores[:, :, :nb].reshape(cfg.rows, nb).cpu().numpy().astype(np.float64)
+    ref = oracle.scores(w.q16, w.kblk, nb)
+    check_bound(s_gpu, ref, "rphase")
+    if nb > cfg.nf:
+        model = oracle.block_model_f32(w.q16, w.kblk, cfg.nf)
+        assert np.array_equal(s_gpu[:, cfg.nf].astype(np.float32).view(np.uint32),
+                              model.view(np.uint32))
+    check_ids(got, s_gpu, ref, k, "rphase")
+    sel = got >= 0
+    assert np.array_equal(v[sel].view(np.uint32),
+                          s_gpu[np.nonzero(sel)[0], got[sel]].astype(np.float32).view(np.uint32))
+    assert np.all(v[~sel] == -np.inf)
+    if q_chunk:
+        ws1, got1, _ = run(0)
+        assert np.array_equal(got1, got)
+        assert torch.equal(ws1.scores[:, :, :nb].view(torch.int32), ws.scores[:, :, :nb].view(torch.int32))
+
+
 def test_tiny_nkv0_writes_nothing_and_selects_nothing():
     cfg = qi.TINY
     w = qi.make(cfg)
