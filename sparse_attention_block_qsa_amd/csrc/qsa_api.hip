@@ -186,9 +186,15 @@ qsa_status qsa_select_phase(const float *q32, uint16_t *q16, int64_t q_tok_strid
             if (e != hipSuccess) return QSA_ERR_HIP;
         }
         if (k > 0) {
-            // the scorer wrote this chunk's rows at g*n + t' (n = rows in the chunk)
-            TopkGeom tg{scores_ws, ld_s, ids, ld_ids, vals, G, n, n, nq, t0,
-                        static_cast<int32_t>(c.nb), k};
+            // the scorer wrote this chunk's rows at g*n + t' (n = rows in the
+            // chunk); in one pass over all rows that is the output's row
+            // order too, and the selector sees one flat group of rows
+            const int64_t rows = static_cast<int64_t>(G) * n;
+            TopkGeom tg = n == nq
+                ? TopkGeom{scores_ws, ld_s, ids, ld_ids, vals, 1, rows, rows, rows, 0,
+                           static_cast<int32_t>(c.nb), k}
+                : TopkGeom{scores_ws, ld_s, ids, ld_ids, vals, G, n, n, nq, t0,
+                           static_cast<int32_t>(c.nb), k};
             hipError_t e = qsa::launch_topk(tg, s);
             if (e != hipSuccess) return QSA_ERR_HIP;
         }

@@ -35,6 +35,14 @@ struct TopkArgs {
     int32_t nb, k;
 };
 
+// R / rows_per_group for a wave-uniform row R: a 32-bit division (a few
+// scalar ops) when the rows fit in 31 bits, else the 64-bit one (about 190).
+__device__ __forceinline__ int64_t row_group(int64_t R, int64_t rows_per_group, int64_t total_rows) {
+    if (total_rows <= 0x7fffffff)   // uniform
+        return static_cast<uint32_t>(R) / static_cast<uint32_t>(rows_per_group);
+    return R / rows_per_group;
+}
+
 __device__ __forceinline__ uint32_t order_key(float x) {
     uint32_t u = __builtin_bit_cast(uint32_t, x);
     if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;   // NaN: lowest
@@ -299,7 +307,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     if (R >= a.total_rows) return;               // whole wave; no block barriers below
     int64_t grp = 0, t = R;
     if (a.rows_per_group != a.total_rows) {   // grouped rows (the phase's chunks)
-        grp = R / a.rows_per_group;
+        grp = row_group(R, a.rows_per_group, a.total_rows);
         t = R - grp * a.rows_per_group;
     }
     const float *srow = a.scores + (grp * a.src_group_rows + t) * a.ld_s;
@@ -611,7 +619,7 @@ __global__ __launch_bounds__(256) void topk_quad_kernel(TopkArgs a) {
     if (R >= a.total_rows) return;               // whole workgroup
     int64_t grp = 0, t = R;
     if (a.rows_per_group != a.total_rows) {
-        grp = R / a.rows_per_group;
+        grp = row_group(R, a.rows_per_group, a.total_rows);
         t = R - grp * a.rows_per_group;
     }
     const float *srow = a.scores + (grp * a.src_group_rows + t) * a.ld_s;
