@@ -91,11 +91,12 @@ qsa_status qsa_convert_f32_f16(const float *src, uint16_t *dst, int64_t n, void 
  * qsa_block_scores -- step 2 of the phase: the score of every (g, t, b)
  * cell, b < nb = ceil(n_kv / bs).  Blocks b < nf = floor(n_kv / bs) go to the
  * MFMA full-block scorer; the partial block b = nf (present when n_kv % bs
- * != 0) goes to the separate tail kernel, whose fixed order (per head a
- * single-precision fused multiply-add chain over i ascending, relu, then the
- * head sum over h ascending) reproduces the same results bit for bit on
- * every run (Strata pull request #228, part 1, the paragraph naming the tail
- * kernel; Strata pull request #856, "What").
+ * != 0) is scored in a fixed order (per head a single-precision fused
+ * multiply-add chain over i ascending, relu, then the head sum over h
+ * ascending) that reproduces the same results bit for bit on every run
+ * (Strata pull request #228, part 1, the paragraph naming the tail kernel;
+ * Strata pull request #856, "What"): inside the full-block scorer's launch,
+ * or by a tail kernel of its own when there is no full block.
  *   q16        device fp16 bits, layout above; q_tok_stride >= G*H*D,
  *              q16 and q_tok_stride 16-byte aligned (q_tok_stride % 8 == 0)
  *   kblk       device fp16 bits [G][>= nb][D] at kblk_head_stride >= nb*D
