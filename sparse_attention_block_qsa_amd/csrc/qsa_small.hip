@@ -399,6 +399,11 @@ hipError_t launch_score_small(const ScoreGeom &geo, bool tail, hipStream_t s, co
     if (segs < 1) segs = 1;
     const int64_t tps = n_tiles > 0 ? (n_tiles + segs - 1) / segs : 0;
     if (n_tiles > 0) segs = (n_tiles + tps - 1) / tps;
+    // The partial last block gets a segment of its own, past the tile
+    // segments (its tile range is empty), so that its fixed-order chain runs
+    // beside the tiles instead of after the last segment's: the decode step's
+    // scorer 5.25 -> 3.9 us.  The last segment scores the tail either way.
+    if (tail && n_tiles > 0) segs += 1;
     const int64_t grid = base * segs;
     if (grid > 0x7fffffffLL || n_tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     // fp32 queries are staged through LDS when a workgroup can hold a full
