@@ -141,8 +141,19 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
             for (int j = 0; j < LOADS; ++j) kbuf[buf][i][threadIdx.x + 256 * j] = st[i][j];
     };
     // the first chunk's loads go out before the queries', so that the two
-    // latencies overlap
+    // latencies overlap; the tail segment's loads of the partial block's key
+    // likewise
     if (tb < te) fetch(tb);   // uniform over the workgroup
+    const bool tail_seg = a.tail && seg == a.n_segs - 1;   // uniform
+    uint4 kv[KS][2];
+    if (tail_seg) {
+        const uint16_t *kt = kg + a.nf * D;
+        #pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            kv[s][0] = *reinterpret_cast<const uint4 *>(kt + 16 * s);
+            kv[s][1] = *reinterpret_cast<const uint4 *>(kt + 16 * s + 8);
+        }
+    }
 
     half8 qa[KS];
     if constexpr (STAGE) {
@@ -294,14 +305,7 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
     // already in registers: v_permlane32_swap gives it the other half of
     // every 16-channel run (held by lane l + 32), so it walks channels
     // 16s .. 16s + 15 in ascending order.
-    if (a.tail && seg == a.n_segs - 1) {   // uniform over the workgroup
-        const uint16_t *kt = kg + a.nf * D;
-        uint4 kv[KS][2];
-        #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            kv[s][0] = *reinterpret_cast<const uint4 *>(kt + 16 * s);
-            kv[s][1] = *reinterpret_cast<const uint4 *>(kt + 16 * s + 8);
-        }
+    if (tail_seg) {   // uniform over the workgroup
         float acc = 0.0f;
         #pragma unroll
         for (int s = 0; s < KS; ++s) {
