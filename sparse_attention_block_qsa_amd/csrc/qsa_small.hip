@@ -27,7 +27,9 @@
 //    buffer when there is one: the phase needs no conversion launch.  With
 //    no full block (a tail only) this kernel serves any number of rows.
 //  * The partial last block (n_kv mod bs != 0) is scored by the last segment
-//    in the fixed fma order of the tail model, one lane per (query, head).
+//    in the fixed fma order of the tail model, one lane per (query, head);
+//    when there are full blocks that segment is one of its own, with no
+//    tiles, so that the chain runs beside the tiles.
 #include "qsa_internal.h"
 
 #pragma clang fp contract(off)
