@@ -45,6 +45,8 @@ def parse():
                    help="steps for the full-prefill chunk reported beside the workload (0: skip)")
     p.add_argument("--decode-steps", type=int, default=200,
                    help="steps for the decode step reported beside the workload (0: skip)")
+    p.add_argument("--sweep-steps", type=int, default=100,
+                   help="steps per point of the nq = 256 context sweep, 1K-128K keys (0: skip)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target wall time of the CPU-baseline sample")
@@ -394,6 +396,24 @@ def main():
         print(f"# decode: {dr['ms_per_step'] * 1e3:.2f} us/step, scorer {ds['scorer'] * 1e3:.2f} us",
               file=sys.stderr, flush=True)
 
+    # nq = 256 across context lengths 1K-128K keys, the headline's shape
+    # otherwise (k = 64: rows shorter than 64 blocks pad with -1)
+    sweep = None
+    if args.sweep_steps > 0 and cfg.name == qi.HEADLINE.name:
+        sweep = []
+        for n_kv in (1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072):
+            ws_ = qi.make(cfg, n_kv=n_kv)
+            r = measure(ws_.cfg, qsa, torch, args.sweep_steps, 10, w=ws_)
+            sweep.append({"n_kv": n_kv, "nb": ws_.cfg.nb, "k": ws_.cfg.k,
+                          "phase_us": r["ms_per_step"] * 1e3,
+                          "scorer_us": r["stages_ms"]["scorer"] * 1e3,
+                          "topk_us": r["stages_ms"]["topk"] * 1e3,
+                          "scorer_tflops": r["scorer_tflops"],
+                          "scorer_frac_of_peak": r["scorer_tflops"] / PEAK_FP16_TFLOPS})
+            print(f"# sweep n_kv {n_kv}: phase {sweep[-1]['phase_us']:.2f} us, scorer "
+                  f"{sweep[-1]['scorer_us']:.2f} us, topk {sweep[-1]['topk_us']:.2f} us",
+                  file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -433,6 +453,7 @@ def main():
         "cpu_baseline": cpu,
         "full_prefill": prefill,
         "decode": decode,
+        "context_sweep": sweep,
         "source_digest": source_digest(),
         "context": {"pages_rx7900xtx_gfx1100_scores_ms_128k": {"warp": 2.627, "wmma": 0.252},
                     "note": "other hardware; context only"},

@@ -753,12 +753,18 @@ hipError_t launch_topk(const TopkGeom &geo, hipStream_t s) {
     const int64_t total = geo.n_groups * geo.rows_per_group;
     if (total <= 0 || geo.k <= 0) return hipSuccess;
     const int ncol = (geo.nb + 63) / 64;
-    if (total < 4096 && ncol > 8 && ncol <= 64) {
-        // Few rows of more than 512 blocks: four waves per row.
+    // Few rows of more than 512 blocks, or of 129..512 blocks with k > 32:
+    // four waves per row.  The four waves pay for their barriers when the
+    // pool is likely to hold more than 64 candidates, whose sort they split:
+    // at nq = 256 and k = 64, 512 blocks 7.78 -> 7.48 us per phase and 256
+    // blocks 7.32 -> 7.23 us; at 512 blocks and k = 32 one wave per row stays
+    // ahead (7.13 against 7.20 us).
+    if (total < 4096 && ncol <= 64 && (ncol > 8 || (ncol > 2 && geo.k > 32))) {
         TopkArgs qa{geo.scores, geo.ld_s, geo.ids, geo.ld_ids, geo.vals, total,
                     geo.rows_per_group, geo.src_group_rows, geo.dst_group_rows, geo.dst_row0,
                     geo.nb, geo.k};
-        topk_fn fn = ncol <= 16 ? topk_quad_kernel<4> : ncol <= 32 ? topk_quad_kernel<8>
+        topk_fn fn = ncol <= 8 ? topk_quad_kernel<2> : ncol <= 16 ? topk_quad_kernel<4>
+                   : ncol <= 32 ? topk_quad_kernel<8>
                    : ncol <= 36 ? topk_quad_kernel<9> : ncol <= 48 ? topk_quad_kernel<12>
                                                        : topk_quad_kernel<16>;
         void *qargs[] = {&qa};
