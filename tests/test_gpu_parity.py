@@ -154,6 +154,7 @@ DECODE_SHAPES = [
     (2, 3, 16, 64, 5000, 16),      # H = 16: two queries x 16 heads per MFMA row block
     (4, 8, 4, 64, 3 * 64 + 63, 8), # H = 4, three full blocks and a 63-token tail
     (3, 2, 5, 128, 40, 4),         # a single partial block (no full block)
+    (8, 1, 8, 128, (1 << 20) + 41, 64),   # a 1M-token decode step: 16385 blocks, rows past 4096 blocks
 ]
 
 
@@ -478,6 +479,37 @@ def test_topk_many_rows_path_bit_exact(case):
         sel = ids >= 0
         assert np.array_equal(vals[sel].view(np.uint32),
                               big[np.nonzero(sel)[0], ids[sel]].view(np.uint32))
+
+
+def _long_topk_rows(nb, mix, rng):
+    if mix == "normal":
+        return rng.standard_normal((3, nb)).astype(np.float32)
+    if mix == "quantised":   # few levels: long runs of ties straddle the k-th place
+        return (rng.integers(0, 40, (3, nb)) / 4.0).astype(np.float32)
+    if mix == "special":
+        s = rng.standard_normal((3, nb)).astype(np.float32)
+        s[rng.random((3, nb)) < 0.05] = np.nan
+        s[rng.random((3, nb)) < 0.0002] = np.inf
+        s[rng.random((3, nb)) < 0.01] = -np.inf
+        return s
+    return np.full((3, nb), -1.25, np.float32)   # all equal: the first k ids
+
+
+@pytest.mark.parametrize("nb", [65536 + 37, 262144 + 3])
+@pytest.mark.parametrize("mix", ["normal", "quantised", "special", "equal"])
+def test_topk_long_rows(nb, mix):
+    """Rows far past the selector's register-resident lengths (64 K and
+    256 K blocks, ragged): ids and values bit for bit the oracle's top-k for
+    k = 64 and k = 1."""
+    rng = np.random.default_rng(nb + len(mix))
+    s = _long_topk_rows(nb, mix, rng)
+    log(f"long rows nb={nb} mix={mix}")
+    for k in (64, 1):
+        ids, vals = run_topk_dev(s, nb, k)
+        want_ids, _ = oracle.topk(s.astype(np.float64), k)
+        assert np.array_equal(ids, want_ids)
+        sel = ids >= 0
+        assert np.array_equal(vals[sel].view(np.uint32), s[np.nonzero(sel)[0], ids[sel]].view(np.uint32))
 
 
 def _random_topk_case(i):
