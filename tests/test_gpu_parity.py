@@ -813,6 +813,33 @@ def test_small_scorer_matches_wide_bitwise(H, D):
                        whole[:, t0:t0 + n].contiguous().view(torch.int32))
 
 
+# The wide scorer with several tiles per block split (4 KV heads x 4096
+# queries: two splits of ceil(T/2) and floor(T/2) tiles): splits of one tile,
+# shorter than the load distance; odd counts, the two-tile loop's remainder;
+# both head dims; H = 12, whose second, accumulating head pass keeps the
+# shorter load distance.
+WIDE_TILES = [(64, 2, 8), (64, 5, 8), (64, 12, 8), (128, 3, 8), (128, 7, 8), (128, 5, 12)]
+
+
+@pytest.mark.parametrize("D,n_tiles,H", WIDE_TILES, ids=lambda v: str(v))
+def test_wide_scorer_tile_counts(D, n_tiles, H):
+    """Wide-scorer bits equal the small scorer's on a slice of 100 queries,
+    tail block included, and that slice is within the bound of the oracle."""
+    G, nq, t0, n = 4, 4096, 777, 100
+    cfg = qi.Config("wide_tiles", G, nq, H, D, n_tiles * 32 * 64 + 9, 64, 4, "normal",
+                    1100 + 10 * n_tiles + D + H)
+    log(f"wide scorer D={D} tiles={n_tiles} H={H}")
+    w = qi.make(cfg)
+    kd = k_dev(w.kblk)
+    whole = qsa.block_scores(q_dev(w.q16), kd, cfg.n_kv, cfg.bs)
+    part = qsa.block_scores(q_dev(w.q16[t0:t0 + n]), kd, cfg.n_kv, cfg.bs)
+    torch.cuda.synchronize()
+    sl = whole[:, t0:t0 + n].contiguous()
+    assert torch.equal(part.contiguous().view(torch.int32), sl.view(torch.int32))
+    s_gpu = sl.reshape(G * n, cfg.nb).cpu().numpy().astype(np.float64)
+    check_bound(s_gpu, oracle.scores(w.q16[t0:t0 + n], w.kblk, cfg.nb), "wide tiles")
+
+
 # 256 queries of one KV head at H = 8 give 16 groups of four query groups,
 # so the block axis is cut into 16 segments of n_tiles/16 tiles: 2, 3, 4 and
 # 6 tiles per segment, K staged one tile per barrier (2, 3) or two (4, 6).
