@@ -26,6 +26,11 @@ LIB_PATH = os.path.join(HERE, "liboracle.so")
 BOUND_REL = 2.0 ** -9.5
 BOUND_ABS = 8.0 * 2.0 ** -24
 NEG_CONTROL = 2.5
+# Selection ids may differ from the oracle's only between blocks whose
+# score_ref gap is within this many bounds (the larger of the two cells'
+# B): the near-tie-gap guard of Strata pull request #856, "Arithmetic
+# contract and parity", read as "gap <= 2*B".
+NEAR_TIE_FACTOR = 2.0
 
 _lib = None
 
@@ -210,6 +215,14 @@ class SelectionResult:
     detail: str = ""
 
 
+def near_tie_limit(b_x: float, b_y: float) -> float:
+    """Largest score_ref gap by which a device selection may prefer block x
+    over block y: NEAR_TIE_FACTOR times the larger of the two bounds (either
+    cell's score may be off by its own B, so the guard must admit the wider
+    one)."""
+    return NEAR_TIE_FACTOR * max(b_x, b_y)
+
+
 def check_selection(ids_gpu: np.ndarray, ref: Scores, k: int) -> SelectionResult:
     """R6: the device ids against the oracle's own top-k of score_ref.  Per row
     the sets must match, except that every x in gpu\\oracle and y in
@@ -242,7 +255,7 @@ def check_selection(ids_gpu: np.ndarray, ref: Scores, k: int) -> SelectionResult
             for x in xs:
                 for y in ys:
                     gap = ref.score[r, y] - ref.score[r, x]
-                    lim = 2.0 * max(ref.B[r, x], ref.B[r, y])
+                    lim = near_tie_limit(float(ref.B[r, x]), float(ref.B[r, y]))
                     if gap > lim:
                         ok = False
                         detail = f"row {r}: swapped {x}<->{y} gap {gap} > {lim}"
@@ -252,9 +265,3 @@ def check_selection(ids_gpu: np.ndarray, ref: Scores, k: int) -> SelectionResult
                         worst = np.inf
     return SelectionResult(ok, rows_diff, ids_diff, ids_gpu.shape[0] * kk, worst, detail)
 
-
-def exact_selection(ids_gpu: np.ndarray, s_rows: np.ndarray, k: int) -> np.ndarray:
-    """R6 first part / R7: the oracle's top-k of the given score rows, to be
-    compared bit for bit with the device ids computed from the same rows."""
-    ids, _ = topk(np.asarray(s_rows, dtype=np.float64), k)
-    return ids

@@ -164,17 +164,24 @@ def select_topk(scores: torch.Tensor, nb: int, k: int, ids: torch.Tensor | None 
 
 
 class PhaseWorkspace:
-    """Device buffers of one select phase, allocated once and reused.  With
-    keep_q16 the phase also stores the fp16 conversion of fp32 queries in
-    q16 (one more write of the queries); without it q16 is None and the
-    scorers convert the queries in registers only."""
+    """Device buffers of one select phase, allocated once and reused for
+    phases of exactly this geometry (select_phase refuses any other).  With
+    keep_q16 the phase also stores the fp16 conversion of fp32 queries in q16
+    (one more write of the queries); without it q16 is None and the scorers
+    convert the queries in registers only.  With 0 < q_chunk < nq the score
+    workspace holds G*q_chunk rows and the phase walks the queries in chunks
+    of q_chunk."""
 
     def __init__(self, nq: int, G: int, H: int, D: int, n_kv: int, bs: int, k: int,
                  device="cuda", q_chunk: int = 0, with_vals: bool = False, ld_pad: int = 0,
                  keep_q16: bool = False):
+        if q_chunk < 0:
+            raise ValueError("q_chunk must be >= 0")
+        self.geometry = (nq, G, H, D, n_kv, bs, k)
         self.nb = n_blocks(n_kv, bs)
         qc = q_chunk if 0 < q_chunk < nq else nq
         self.q_chunk = q_chunk
+        self.chunk_rows = qc
         # Rows start on 128-byte boundaries: every 32-column tile store of the
         # scorer then fills whole cache lines.
         self.ld_s = -(-(max(self.nb, 1) + ld_pad) // 32) * 32
@@ -186,13 +193,14 @@ class PhaseWorkspace:
 
 
 def select_phase(q: torch.Tensor, kblk: torch.Tensor, n_kv: int, bs: int, k: int,
-                 ws: PhaseWorkspace | None = None, q_chunk: int = 0,
+                 ws: PhaseWorkspace | None = None, q_chunk: int | None = None,
                  stream: torch.cuda.Stream | None = None):
     """The whole phase: (fp32 -> fp16 conversion when q is float32), scores,
     top-k.  Returns ids [G, nq, k] (and vals when the workspace has them).
     fp32 queries are converted by the scorers as they load them; without a
     kept fp16 copy (ws.q16 is None) their rows must be 16-byte aligned, which
-    a contiguous tensor from the caching allocator always is."""
+    a contiguous tensor from the caching allocator always is.  q_chunk is the
+    workspace's when one is given (a different value is refused), else 0."""
     fp32 = q.dtype == torch.float32
     nq, G, H, D, qts = _check_q(q, torch.float32 if fp32 else torch.float16)
     if fp32 and not q.is_contiguous():
@@ -200,12 +208,19 @@ def select_phase(q: torch.Tensor, kblk: torch.Tensor, n_kv: int, bs: int, k: int
     nb = n_blocks(n_kv, bs)
     khs = _check_k(kblk, G, D, nb)
     if ws is None:
-        ws = PhaseWorkspace(nq, G, H, D, n_kv, bs, k, q.device, q_chunk)
+        ws = PhaseWorkspace(nq, G, H, D, n_kv, bs, k, q.device, q_chunk or 0)
+    else:
+        if ws.geometry != (nq, G, H, D, n_kv, bs, k):
+            raise ValueError(f"workspace built for (nq, G, H, D, n_kv, bs, k) = {ws.geometry}, "
+                             f"called with {(nq, G, H, D, n_kv, bs, k)}")
+        if q_chunk is not None and q_chunk != ws.q_chunk:
+            raise ValueError(f"q_chunk {q_chunk} differs from the workspace's {ws.q_chunk}")
     q16 = ws.q16 if fp32 else q
     if fp32 and q16 is not None and q16.stride(0) != qts:
         raise ValueError("workspace q16 layout does not match the queries")
     _check("qsa_select_phase",
            lib.qsa_select_phase(_ptr(q) if fp32 else None, _ptr(q16), qts, _ptr(kblk), khs,
-                                _ptr(ws.scores), ws.ld_s, _ptr(ws.ids), k, _ptr(ws.vals), G, nq,
-                                H, D, n_kv, bs, k, ws.q_chunk, _stream(stream)))
+                                _ptr(ws.scores), ws.ld_s, _ptr(ws.ids), ws.ids.stride(1),
+                                _ptr(ws.vals), G, nq, H, D, n_kv, bs, k, ws.q_chunk,
+                                _stream(stream)))
     return (ws.ids, ws.vals) if ws.vals is not None else ws.ids

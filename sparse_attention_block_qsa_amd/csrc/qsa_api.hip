@@ -1,9 +1,27 @@
 // qsa_api.hip -- the extern "C" boundary of libqsa.so (declared in qsa.h).
 // Validates every argument before any HIP call, sizes the launches, and
 // orchestrates the select phase on the caller's stream.  No allocation, no
-// state, no synchronisation.
+// state, no synchronisation.  This file holds host code only: the launchers
+// it calls live in the kernel files, so it also builds on its own, with
+// host sanitizers, against stand-in launchers (the CPU test suite does).
 #include "qsa.h"
 #include "qsa_internal.h"
+
+#include <string.h>
+
+namespace qsa {
+
+// Dispatch predicates (host only; declared in qsa_internal.h).
+bool small_rows(const ScoreGeom &geo) {
+    const int64_t wide_groups = (geo.nq + kGroupQueries - 1) / kGroupQueries;
+    return static_cast<int64_t>(geo.G) * wide_groups < 256;
+}
+
+bool src32_ok(const float *q32, int64_t qts) {
+    return reinterpret_cast<uintptr_t>(q32) % 16 == 0 && qts % 4 == 0;
+}
+
+}  // namespace qsa
 
 namespace {
 
@@ -94,7 +112,11 @@ extern "C" {
 int qsa_abi_version(void) { return QSA_ABI_VERSION; }
 
 const char *qsa_status_string(qsa_status s) {
-    switch (s) {
+    // A C caller may pass any int: read the bits rather than the enum value,
+    // which C++ only defines for the enumerators' range.
+    int v;
+    memcpy(&v, &s, sizeof v);
+    switch (v) {
         case QSA_OK: return "ok";
         case QSA_ERR_ARG: return "invalid argument (null pointer, negative size, stride or leading dimension too small)";
         case QSA_ERR_UNSUPPORTED: return "unsupported geometry (D not in {64,128}, H not in [1,16], k > 64, block size < 1, or misaligned pointer/stride)";

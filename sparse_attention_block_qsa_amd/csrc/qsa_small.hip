@@ -376,15 +376,6 @@ int small_pairs(int H) {
 
 }  // namespace
 
-bool small_rows(const ScoreGeom &geo) {
-    const int64_t wide_groups = (geo.nq + kGroupQueries - 1) / kGroupQueries;
-    return static_cast<int64_t>(geo.G) * wide_groups < 256;
-}
-
-bool src32_ok(const float *q32, int64_t qts) {
-    return reinterpret_cast<uintptr_t>(q32) % 16 == 0 && qts % 4 == 0;
-}
-
 hipError_t launch_score_small(const ScoreGeom &geo, bool tail, hipStream_t s, const float *q32,
                               uint16_t *q16w) {
     if (geo.nq <= 0 || geo.G <= 0 || (geo.nf <= 0 && !tail)) return hipSuccess;

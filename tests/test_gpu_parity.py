@@ -225,12 +225,13 @@ def test_phase_randomised_geometry(i):
     kb = k_dev(w.kblk)
 
     def run(chunk):
-        ws = qsa.PhaseWorkspace(nq, G, H, D, n_kv, bs, k, dev(), with_vals=True)
-        ids, vals = qsa.select_phase(q, kb, n_kv, bs, k, ws, q_chunk=chunk)
+        ws = qsa.PhaseWorkspace(nq, G, H, D, n_kv, bs, k, dev(), with_vals=True, q_chunk=chunk)
+        ids, vals = qsa.select_phase(q, kb, n_kv, bs, k, ws)
         torch.cuda.synchronize()
         return ws, ids.reshape(cfg.rows, k).cpu().numpy(), vals.reshape(cfg.rows, k).cpu().numpy()
 
-    ws, got, v = run(q_chunk)
+    # one pass over every query: all scores stay in the workspace
+    ws, got, v = run(0)
     nb = cfg.nb
     if nb == 0:
         assert np.all(got == -1) and np.all(v == -np.inf)
@@ -248,9 +249,19 @@ def test_phase_randomised_geometry(i):
                           s_gpu[np.nonzero(sel)[0], got[sel]].astype(np.float32).view(np.uint32))
     assert np.all(v[~sel] == -np.inf)
     if q_chunk:
-        ws1, got1, _ = run(0)
-        assert np.array_equal(got1, got)
-        assert torch.equal(ws1.scores[:, :, :nb].view(torch.int32), ws.scores[:, :, :nb].view(torch.int32))
+        # the host walks the queries in chunks of q_chunk through a workspace
+        # of G*qc rows: ids and values bit for bit those of one pass, and the
+        # workspace holds the last chunk's scores (query t0 + t' of KV head g
+        # at row g*n + t')
+        wsc, gotc, vc = run(q_chunk)
+        qc = wsc.chunk_rows
+        assert qc == min(q_chunk, nq) and wsc.scores.shape[1] == qc
+        assert np.array_equal(gotc, got)
+        assert np.array_equal(vc.view(np.uint32), v.view(np.uint32))
+        t0 = ((nq - 1) // qc) * qc
+        n = nq - t0
+        last = wsc.scores.reshape(-1, wsc.ld_s)[:G * n].reshape(G, n, wsc.ld_s)[:, :, :nb]
+        assert torch.equal(last.view(torch.int32), ws.scores[:, t0:, :nb].view(torch.int32))
 
 
 def test_tiny_nkv0_writes_nothing_and_selects_nothing():

@@ -156,15 +156,20 @@ def test_convert_known_values():
 # scores: exact brute force, library special case, closed forms, invariants
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("seed", range(12))
-def test_scores_vs_exact_bruteforce(seed):
+# Each pin below is a function of the scoring routine it checks, so that the
+# same pins can be run against deliberately broken scorers (planted mistakes
+# in test_planted_mistakes.py), which each must fail at least one of them.
+
+def pin_exact_bruteforce(scores_fn, seed: int) -> None:
     rng = np.random.default_rng(100 + seed)
     D = [1, 2, 3, 16, 64][seed % 5]
     G, nq, H, nb = int(rng.integers(1, 3)), int(rng.integers(1, 6)), int(rng.integers(1, 5)), \
         int(rng.integers(1, 6))
+    if seed % 4 == 3:   # several KV heads and query heads: layout mistakes show
+        G, H = 2, max(H, 2)
     q16 = random_f16(rng, (nq, G, H, D))
     kb = random_f16(rng, (G, nb, D))
-    ref = oracle.scores(q16, kb, nb)
+    ref = scores_fn(q16, kb, nb)
     ex, exS = exact_scores(q16, kb, nb)
     for r in range(G * nq):
         for b in range(nb):
@@ -176,24 +181,35 @@ def test_scores_vs_exact_bruteforce(seed):
             assert math.isclose(ref.B[r, b], want_B, rel_tol=1e-12, abs_tol=1e-300)
 
 
-def test_single_head_is_relu_matmul():
+@pytest.mark.parametrize("seed", range(12))
+def test_scores_vs_exact_bruteforce(seed):
+    pin_exact_bruteforce(oracle.scores, seed)
+
+
+def pin_single_head_matmul(scores_fn) -> None:
     """With H = 1 the score is relu(Q K^T): numpy float64 matmul."""
     rng = np.random.default_rng(3)
     nq, nb, D = 33, 47, 128
     q16 = qi.f64_to_f16_bits(rng.standard_normal((nq, 1, 1, D)) / math.sqrt(D))
     kb = qi.f64_to_f16_bits(rng.standard_normal((1, nb, D)) / math.sqrt(D))
-    ref = oracle.scores(q16, kb, nb)
+    ref = scores_fn(q16, kb, nb)
     Q = q16.view(np.float16).astype(np.float64).reshape(nq, D)
     K = kb.view(np.float16).astype(np.float64).reshape(nb, D)
     want = np.maximum(Q @ K.T, 0.0)
     assert np.all(np.abs(ref.score - want) <= D * 2.0 ** -52 * ref.S)
+    # S of one head is the matmul of the magnitudes
+    assert np.all(np.abs(ref.S - np.abs(Q) @ np.abs(K).T) <= D * 2.0 ** -52 * ref.S)
 
 
-def test_coded_fixture_closed_form():
+def test_single_head_is_relu_matmul():
+    pin_single_head_matmul(oracle.scores)
+
+
+def pin_coded_fixture(scores_fn) -> None:
     cfg = qi.CONFIGS["nq256_nkv32768"]
     small = qi.Config("coded_small", 2, 40, cfg.H, cfg.D, 64 * 37, 64, 8, "normal", 0)
     w = qi.coded_fixture(small)
-    ref = oracle.scores(w.q16, w.kblk, small.nb)
+    ref = scores_fn(w.q16, w.kblk, small.nb)
     ch, kint = w.extra["channel"], w.extra["kint"]
     want = np.zeros((small.G * small.nq, small.nb))
     for g in range(small.G):
@@ -205,10 +221,14 @@ def test_coded_fixture_closed_form():
         np.arange(small.nb)[None, :, None], np.tile(ch, (small.G, 1))[:, None, :]]).sum(axis=2))
 
 
-def test_integer_fixture_exact():
+def test_coded_fixture_closed_form():
+    pin_coded_fixture(oracle.scores)
+
+
+def pin_integer_fixture(scores_fn) -> None:
     cfg = qi.Config("int_small", 2, 19, 8, 128, 64 * 9 + 7, 64, 8, "normal", 0)
     w = qi.integer_fixture(cfg)
-    ref = oracle.scores(w.q16, w.kblk, cfg.nb)
+    ref = scores_fn(w.q16, w.kblk, cfg.nb)
     Q = w.q16.view(np.float16).astype(np.int64)
     K = w.kblk.view(np.float16).astype(np.int64)
     want = np.zeros((cfg.G * cfg.nq, cfg.nb), dtype=np.int64)
@@ -217,21 +237,32 @@ def test_integer_fixture_exact():
         want[g * cfg.nq:(g + 1) * cfg.nq] = np.maximum(d, 0).sum(axis=1)
     assert np.array_equal(ref.score, want.astype(np.float64))
     assert want.max() > 2048  # large enough that fp16 accumulation would fail
+    wantS = np.zeros_like(want)
+    for g in range(cfg.G):
+        wantS[g * cfg.nq:(g + 1) * cfg.nq] = np.einsum("thi,bi->tb", np.abs(Q[:, g]),
+                                                       np.abs(K[g, :cfg.nb]))
+    assert np.array_equal(ref.S, wantS.astype(np.float64))
+    assert np.allclose(ref.B, oracle.BOUND_REL * ref.S + oracle.BOUND_ABS * ref.score,
+                       rtol=1e-14, atol=0)
 
 
-def test_trivial_closed_forms():
+def test_integer_fixture_exact():
+    pin_integer_fixture(oracle.scores)
+
+
+def pin_trivial_closed_forms(scores_fn) -> None:
     rng = np.random.default_rng(9)
     nq, G, H, D, nb = 5, 2, 3, 64, 11
     kb = qi.f64_to_f16_bits(rng.standard_normal((G, nb, D)))
     zero_q = np.zeros((nq, G, H, D), np.uint16)
-    ref = oracle.scores(zero_q, kb, nb)
+    ref = scores_fn(zero_q, kb, nb)
     assert np.all(ref.score == 0) and np.all(ref.S == 0) and np.all(ref.B == 0)
     ids, _ = oracle.topk(ref.score, 4)
     assert np.array_equal(ids, np.tile(np.arange(4, dtype=np.int32), (G * nq, 1)))
     # all key rows equal -> equal scores -> ids 0..k-1
     q16 = qi.f64_to_f16_bits(rng.standard_normal((nq, G, H, D)))
     same = np.repeat(kb[:, :1, :], nb, axis=1)
-    ref = oracle.scores(q16, same, nb)
+    ref = scores_fn(q16, same, nb)
     assert np.all(ref.score == ref.score[:, :1])
     ids, _ = oracle.topk(ref.score, 4)
     assert np.array_equal(ids, np.tile(np.arange(4, dtype=np.int32), (G * nq, 1)))
@@ -241,34 +272,38 @@ def test_trivial_closed_forms():
     qp = qi.f64_to_f16_bits(np.abs(rng.standard_normal((nq, G, H, D))) + 1.0)
     kd[:, :7] = qi.f64_to_f16_bits(np.full((G, 7, D), -1.0))
     kd[:, 8:] = qi.f64_to_f16_bits(np.full((G, nb - 8, D), -1.0))
-    ref = oracle.scores(qp, kd, nb)
+    ref = scores_fn(qp, kd, nb)
     ids, _ = oracle.topk(ref.score, 1)
     assert np.all(ids[:, 0] == 7)
 
 
-def test_invariants():
+def test_trivial_closed_forms():
+    pin_trivial_closed_forms(oracle.scores)
+
+
+def pin_invariants(scores_fn) -> None:
     rng = np.random.default_rng(11)
     nq, G, H, D, nb = 7, 2, 4, 64, 13
     q16 = qi.f64_to_f16_bits(rng.standard_normal((nq, G, H, D)) * 0.3)
     kb = qi.f64_to_f16_bits(rng.standard_normal((G, nb, D)) * 0.3)
-    ref = oracle.scores(q16, kb, nb)
+    ref = scores_fn(q16, kb, nb)
     assert np.all(ref.score >= 0) and np.all(ref.score <= ref.S)
     # head permutation: same value up to float64 summation order
     perm = rng.permutation(H)
-    rp = oracle.scores(q16[:, :, perm], kb, nb)
+    rp = scores_fn(q16[:, :, perm], kb, nb)
     assert np.all(np.abs(rp.score - ref.score) <= 2.0 ** -45 * ref.S)
     # block permutation: each block is independent
     bp = rng.permutation(nb)
-    rb = oracle.scores(q16, kb[:, bp], nb)
+    rb = scores_fn(q16, kb[:, bp], nb)
     assert np.array_equal(rb.score, ref.score[:, bp])
     # scaling by 2^j scales scores by 2^(2j) exactly
     q2 = qi.f64_to_f16_bits(q16.view(np.float16).astype(np.float64) * 4.0)
     k2 = qi.f64_to_f16_bits(kb.view(np.float16).astype(np.float64) * 0.5)
-    r2 = oracle.scores(q2, k2, nb)
+    r2 = scores_fn(q2, k2, nb)
     assert np.array_equal(r2.score, ref.score * 2.0)
     # relu(x) - relu(-x) = x: score(Q,K) - score(Q,-K) = (sum_h q_h) . k
     kneg = kb ^ np.uint16(0x8000)
-    rn = oracle.scores(q16, kneg, nb)
+    rn = scores_fn(q16, kneg, nb)
     Qf = q16.view(np.float16).astype(np.float64)
     Kf = kb.view(np.float16).astype(np.float64)
     for g in range(G):
@@ -277,17 +312,25 @@ def test_invariants():
         assert np.all(np.abs(got - want) <= 2.0 ** -44 * ref.S[g * nq:(g + 1) * nq])
 
 
-def test_f32_queries_use_unrounded_values():
+def test_invariants():
+    pin_invariants(oracle.scores)
+
+
+def pin_f32_queries(scores_fn) -> None:
     """For fp32 queries the oracle uses the fp32 values themselves."""
     rng = np.random.default_rng(4)
     nq, G, H, D, nb = 3, 1, 2, 64, 5
     q32 = (rng.standard_normal((nq, G, H, D)) / 8).astype(np.float32)
     kb = qi.f64_to_f16_bits(rng.standard_normal((G, nb, D)) / 8)
-    ref = oracle.scores(q32, kb, nb)
+    ref = scores_fn(q32, kb, nb)
     Q = q32.astype(np.float64)
     K = kb.view(np.float16).astype(np.float64)
     want = np.maximum(np.einsum("thi,bi->thb", Q[:, 0], K[0]), 0).sum(axis=1)
     assert np.all(np.abs(ref.score - want) <= 2.0 ** -45 * ref.S)
+
+
+def test_f32_queries_use_unrounded_values():
+    pin_f32_queries(oracle.scores)
 
 
 # --------------------------------------------------------------------------
@@ -314,20 +357,24 @@ def load_hand_examples():
     return exs
 
 
-@pytest.mark.parametrize("ex", load_hand_examples(), ids=lambda e: e["name"])
-def test_hand_examples(ex):
+def pin_hand_example(scores_fn, ex) -> None:
     H, D, nq, nb, k = ex["H"], ex["D"], ex["nq"], ex["nb"], ex["k"]
     q = np.zeros((nq, 1, H, D))
     for (t, h), v in ex["q"].items():
         q[t, 0, h] = v
     kb = np.array([ex["kb"][b] for b in range(nb)])[None]
-    ref = oracle.scores(qi.f64_to_f16_bits(q), qi.f64_to_f16_bits(kb), nb)
+    ref = scores_fn(qi.f64_to_f16_bits(q), qi.f64_to_f16_bits(kb), nb)
     for t in range(nq):
         assert ref.score[t].tolist() == ex["score"][t]
         assert ref.S[t].tolist() == ex["S"][t]
     ids, _ = oracle.topk(ref.score, k)
     for t in range(nq):
         assert ids[t].tolist() == [int(x) for x in ex["topk"][t]]
+
+
+@pytest.mark.parametrize("ex", load_hand_examples(), ids=lambda e: e["name"])
+def test_hand_examples(ex):
+    pin_hand_example(oracle.scores, ex)
 
 
 def test_contract_constants_match_pages():
@@ -340,6 +387,8 @@ def test_contract_constants_match_pages():
     assert oracle.BOUND_REL == 2.0 ** vals["bound_rel_log2"]
     assert oracle.BOUND_ABS == vals["bound_abs_coeff"] * 2.0 ** vals["bound_abs_log2"]
     assert oracle.NEG_CONTROL == vals["negative_control_factor"]
+    assert oracle.NEAR_TIE_FACTOR == vals["near_tie_factor"]
+    assert oracle.near_tie_limit(1.0, 0.5) == vals["near_tie_factor"]
 
 
 # --------------------------------------------------------------------------
@@ -461,19 +510,92 @@ def test_selection_checker_near_ties():
     ref = oracle.scores(w.q16, w.kblk, w.cfg.nb)
     ids, _ = oracle.topk(ref.score, 4)
     assert oracle.check_selection(ids, ref, 4).ok
-    # swap the 4th choice for the 5th: allowed only if the gap is within 2B
-    ids5, _ = oracle.topk(ref.score, 5)
-    swapped = ids.copy()
-    swapped[:, 3] = ids5[:, 4]
-    res = oracle.check_selection(swapped, ref, 4)
-    gaps = ref.score[np.arange(ids.shape[0]), ids[:, 3]] - \
-        ref.score[np.arange(ids.shape[0]), ids5[:, 4]]
-    lim = 2 * np.maximum(ref.B[np.arange(ids.shape[0]), ids[:, 3]],
-                         ref.B[np.arange(ids.shape[0]), ids5[:, 4]])
-    assert res.ok == bool(np.all(gaps <= lim))
     bad = ids.copy()
     bad[0, 0] = bad[0, 1]  # duplicate id
     assert not oracle.check_selection(bad, ref, 4).ok
+    bad = ids.copy()
+    bad[1, 2] = w.cfg.nb   # id out of range
+    assert not oracle.check_selection(bad, ref, 4).ok
+
+
+def _one_row(score, B, ids, k):
+    """A single-row oracle.Scores with given score_ref and B, and the device
+    ids to judge."""
+    score = np.array([score], dtype=np.float64)
+    B = np.array([B], dtype=np.float64)
+    return (np.array([ids], dtype=np.int64), oracle.Scores(score, np.zeros_like(score), B,
+                                                           np.zeros(1, np.int64)), k)
+
+
+# Gaps just inside and just outside 2*max(B), exact binary fractions.
+_IN, _OUT = 127.0 / 64.0, 129.0 / 64.0   # 1.984..., 2.016... times max(B)
+
+
+def selection_pins():
+    """(name, ids, Scores, k, verdict) rows worked by hand from the near-tie
+    rule: the oracle's top-2 of score_ref is {0, 1}; the device picked
+    block 2 instead of block 1 (or agrees).  The swap is allowed iff
+    score_ref(1) - score_ref(2) <= 2 * max(B(1), B(2))."""
+    s = 10.0
+    return [
+        ("agree", *_one_row([20.0, s, s - 5.0, 0.0], [1, 1, 1, 1], [0, 1], 2), True),
+        ("agree_order_free", *_one_row([20.0, s, s - 5.0, 0.0], [1, 1, 1, 1], [1, 0], 2), True),
+        # equal bounds: just inside passes, just outside fails
+        ("inside_equal_B", *_one_row([20.0, s, s - _IN, 0.0], [1, 1, 1, 1], [0, 2], 2), True),
+        ("outside_equal_B", *_one_row([20.0, s, s - _OUT, 0.0], [1, 1, 1, 1], [0, 2], 2), False),
+        # unequal bounds: the larger one decides, whichever cell holds it
+        ("inside_max_at_x", *_one_row([20.0, s, s - _IN, 0.0], [1, 0.125, 1, 1], [0, 2], 2), True),
+        ("inside_max_at_y", *_one_row([20.0, s, s - _IN, 0.0], [1, 1, 0.125, 1], [0, 2], 2), True),
+        ("outside_max_at_x", *_one_row([20.0, s, s - _OUT, 0.0], [1, 0.125, 1, 1], [0, 2], 2),
+         False),
+        ("outside_max_at_y", *_one_row([20.0, s, s - _OUT, 0.0], [1, 1, 0.125, 1], [0, 2], 2),
+         False),
+        # the sum of the two bounds is wider than the rule: 2.016 < 2.25
+        ("outside_not_sum", *_one_row([20.0, s, s - _OUT, 0.0], [1, 1, 0.125, 1], [0, 2], 2),
+         False),
+        # exact cells (B == 0): an exact tie may go either way, any gap may not
+        ("exact_tie_either_way", *_one_row([20.0, s, s, 0.0], [0, 0, 0, 0], [0, 2], 2), True),
+        ("exact_gap_fails", *_one_row([20.0, s, s - 2.0 ** -40, 0.0], [0, 0, 0, 0], [0, 2], 2),
+         False),
+        # k > nb pads with -1; a real id in a pad slot fails
+        ("pads", *_one_row([1.0, 2.0], [0, 0], [1, 0, -1], 3), True),
+        ("pad_not_minus1", *_one_row([1.0, 2.0], [0, 0], [1, 0, 0], 3), False),
+        # two swaps in one row: each pair (x, y) is judged
+        ("two_swaps_inside", *_one_row([20.0, s, s, s - _IN, s - _IN], [1, 1, 1, 1, 1],
+                                       [0, 3, 4], 3), True),
+        ("two_swaps_one_outside", *_one_row([20.0, s, s, s - _IN, s - _OUT], [1, 1, 1, 1, 1],
+                                            [0, 3, 4], 3), False),
+    ]
+
+
+@pytest.mark.parametrize("pin", selection_pins(), ids=lambda p: p[0])
+def test_selection_checker_hand_rows(pin):
+    name, ids, ref, k, verdict = pin
+    res = oracle.check_selection(ids, ref, k)
+    assert res.ok == verdict, (name, res.detail)
+
+
+def selection_pins_hold() -> bool:
+    return all(oracle.check_selection(ids, ref, k).ok == verdict
+               for _, ids, ref, k, verdict in selection_pins())
+
+
+@pytest.mark.parametrize("mutant", [
+    ("factor_4", lambda bx, by: 4.0 * max(bx, by)),
+    ("factor_1", lambda bx, by: 1.0 * max(bx, by)),
+    ("min_of_bounds", lambda bx, by: 2.0 * min(bx, by)),
+    ("bound_of_x_only", lambda bx, by: 2.0 * bx),
+    ("bound_of_y_only", lambda bx, by: 2.0 * by),
+    ("sum_of_bounds", lambda bx, by: 2.0 * (bx + by)),
+    ("reject_every_swap", lambda bx, by: -1.0),
+    ("accept_every_swap", lambda bx, by: np.inf),
+], ids=lambda m: m[0])
+def test_selection_pins_catch_planted_checker_mistakes(mutant, monkeypatch):
+    """Each plausible mistake in the near-tie rule, planted into the checker,
+    makes at least one hand row come out wrong."""
+    assert selection_pins_hold()
+    monkeypatch.setattr(oracle, "near_tie_limit", mutant[1])
+    assert not selection_pins_hold(), mutant[0]
 
 
 # --------------------------------------------------------------------------
