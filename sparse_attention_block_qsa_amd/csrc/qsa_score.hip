@@ -71,6 +71,10 @@ struct ScoreArgs {
     int32_t n_qgroups, n_splits, tiles_per_split, n_tiles;
 };
 
+// s_waitcnt immediate for vmcnt(0) with the other counters left free
+// (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int kVmcnt0 = 0x0F70;
+
 // Cache policy of the score stores: non-temporal.  The scores are written
 // once and read back by the selector long after they would have left the
 // caches, so they stream to memory without displacing the queries and keys.
@@ -294,6 +298,13 @@ void score_full_kernel(ScoreArgs a) {
         }
     }
     __syncthreads();
+    // Every query fragment (and the prologue's K loads) has landed before the
+    // tile loop.  Without this wait the compiler's wait counting carries the
+    // query loads into the loop as possibly outstanding, and, because the
+    // vector-memory counter also counts stores in issue order, the waits it
+    // then places before the MFMAs of every tile (vmcnt(33) down to vmcnt(2))
+    // wait for the previous tile's score stores to be acknowledged.
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
 
     int slot = 0;   // ring slot of the current tile
     half8 kf0 = __builtin_bit_cast(half8, kbuf[0][l]);

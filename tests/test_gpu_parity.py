@@ -851,6 +851,52 @@ def test_wide_scorer_tile_counts(D, n_tiles, H):
     check_bound(s_gpu, oracle.scores(w.q16[t0:t0 + n], w.kblk, cfg.nb), "wide tiles")
 
 
+# More (KV head, query group) items than two workgroups per CU: the wide
+# scorer's grid runs in more than one round of workgroups (520 to 1536 items,
+# odd tile counts, one tile, partial query groups).
+MANY_ITEMS = [(8, 4100, 8, 128, 3), (16, 4096, 4, 64, 5), (17, 4000, 8, 128, 1),
+              (12, 8192, 2, 128, 2)]
+
+
+@pytest.mark.parametrize("G,nq,H,D,n_tiles", MANY_ITEMS, ids=lambda v: str(v))
+def test_wide_scorer_many_items(G, nq, H, D, n_tiles):
+    """The wide scorer over more work items than one round of workgroups:
+    the fp16-input scores and the phase's fp32-input scores are the same
+    bits, a slice of queries scored by the small scorer too, every tail cell
+    is the fixed-order model, the kept fp16 copy is exactly the oracle's
+    conversion, and the rows of every query group edge are within the bound
+    of the oracle."""
+    cfg = qi.Config("many_items", G, nq, H, D, n_tiles * 32 * 64 + 7, 64, 8, "normal",
+                    1300 + G + n_tiles + H)
+    log(f"wide scorer, many items: G={G} nq={nq} H={H} D={D} tiles={n_tiles}")
+    w = qi.make(cfg)
+    kd = k_dev(w.kblk)
+    nb = cfg.nb
+    whole = qsa.block_scores(q_dev(w.q16), kd, cfg.n_kv, cfg.bs)
+    t0, n = 1000, 70
+    part = qsa.block_scores(q_dev(w.q16[t0:t0 + n]), kd, cfg.n_kv, cfg.bs)
+    ws = qsa.PhaseWorkspace(cfg.nq, cfg.G, cfg.H, cfg.D, cfg.n_kv, cfg.bs, cfg.k, dev(),
+                            keep_q16=True)
+    ids = qsa.select_phase(torch.from_numpy(w.q32).to(dev()), kd, cfg.n_kv, cfg.bs, cfg.k, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(part.contiguous().view(torch.int32),
+                       whole[:, t0:t0 + n].contiguous().view(torch.int32))
+    assert torch.equal(ws.scores[:, :, :nb].contiguous().view(torch.int32),
+                       whole.contiguous().view(torch.int32))
+    assert np.array_equal(ws.q16.cpu().numpy().view(np.uint16), w.q16)
+    s_all = whole.reshape(cfg.rows, nb)
+    model = oracle.block_model_f32(w.q16, w.kblk, cfg.nf)
+    assert np.array_equal(s_all[:, cfg.nf].cpu().numpy().view(np.uint32), model.view(np.uint32))
+    edges = sorted({g * nq + t for g in range(G) for t in (0, 63, 64, 1023, 1024, nq - 65,
+                                                          nq - 64, nq - 1)})
+    rows = np.array(edges, dtype=np.int64)
+    s_gpu = s_all[torch.from_numpy(rows).to(dev())].cpu().numpy().astype(np.float64)
+    ref = oracle.scores(w.q16, w.kblk, nb, rows=rows)
+    check_bound(s_gpu, ref, "many items")
+    got = ids.reshape(cfg.rows, cfg.k)[torch.from_numpy(rows).to(dev())].cpu().numpy()
+    check_ids(got, s_gpu, ref, cfg.k, "many items")
+
+
 # 256 queries of one KV head at H = 8 give 16 groups of four query groups,
 # so the block axis is cut into 16 segments of n_tiles/16 tiles: 2, 3, 4 and
 # 6 tiles per segment, K staged one tile per barrier (2, 3) or two (4, 6).
