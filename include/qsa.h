@@ -26,8 +26,10 @@
  *    that owns `stream`).  fp16 data is passed as its raw bits (uint16_t).
  *  - Strides are in ELEMENTS of the pointed-to type.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
- *    enqueues work on it and returns; nothing is synchronised, allocated,
- *    or kept between calls.  Calls are thread-safe.
+ *    enqueues work on it and returns; nothing is synchronised or allocated,
+ *    and nothing is kept between calls except the fixed per-GPU scratch
+ *    array of qsa_select_phase_noalloc.  Calls are thread-safe (calls of
+ *    qsa_select_phase_noalloc that overlap on one GPU race on its array).
  *  - Refusal is clean: when a call returns anything but QSA_OK, nothing was
  *    launched and no output byte was written.  Errors that happen on the
  *    device after a successful launch surface at the caller's next
@@ -62,11 +64,16 @@ typedef enum qsa_status {
                                 {64, 128}, H outside [1, 16], k > 64, block size
                                 < 1, a pointer or stride not 16-byte aligned
                                 where the kernels load 16-byte vectors */
-    QSA_ERR_HIP = 3          /* the HIP runtime refused a launch */
+    QSA_ERR_HIP = 3,         /* the HIP runtime refused a launch */
+    QSA_ERR_TOO_LARGE = 4    /* qsa_select_phase_noalloc: the work does not fit
+                                the library's fixed scratch array */
 } qsa_status;
 
-#define QSA_ABI_VERSION 2
+#define QSA_ABI_VERSION 3
 #define QSA_MAX_K 64
+/* Size of the per-GPU device array qsa_select_phase_noalloc keeps its score
+ * workspace in (64 MiB). */
+#define QSA_NOALLOC_SCRATCH_BYTES (64ll << 20)
 
 /* Version of this ABI (QSA_ABI_VERSION of the header the library was built
  * with). */
@@ -162,6 +169,34 @@ qsa_status qsa_select_phase(const float *q32, uint16_t *q16, int64_t q_tok_strid
                             int32_t G, int32_t nq, int32_t H, int32_t D,
                             int64_t n_kv, int32_t bs, int32_t k, int64_t q_chunk,
                             void *stream);
+
+/*
+ * qsa_select_phase_noalloc -- qsa_select_phase for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It takes the same inputs and outputs
+ * (q32, q16, q_tok_stride, kblk, kblk_head_stride, ids, ld_ids, vals and the
+ * geometry, as qsa_select_phase) but no score workspace: the scores live in a
+ * device array of QSA_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * GPU it runs on, from the first call on that GPU until the process ends.
+ * Nothing else is allocated (no hipMalloc, hipFree or allocating library
+ * call).  The GPU is the current device, which must own `stream`.
+ *   q_chunk  queries per pass; 0 = as many as fit the array, i.e. the queries
+ *            are walked in chunks of floor(QSA_NOALLOC_SCRATCH_BYTES /
+ *            (4 * G * ld)) with ld = ceil(max(nb, 1) / 32) * 32 floats
+ *            (one pass when they all fit)
+ * Results are those of qsa_select_phase with the same q_chunk, bit for bit.
+ * Errors: as qsa_select_phase; QSA_ERR_TOO_LARGE (nothing launched) when one
+ * query's G score rows, or the q_chunk asked for, exceed the array.
+ * Calls on one GPU share the array: calls that overlap in time on one GPU
+ * (unordered streams) race and give undefined results; calls ordered on one
+ * stream are safe.  The array's contents after a call are unspecified.
+ */
+qsa_status qsa_select_phase_noalloc(const float *q32, uint16_t *q16, int64_t q_tok_stride,
+                                    const uint16_t *kblk, int64_t kblk_head_stride,
+                                    int32_t *ids, int64_t ld_ids, float *vals,
+                                    int32_t G, int32_t nq, int32_t H, int32_t D,
+                                    int64_t n_kv, int32_t bs, int32_t k, int64_t q_chunk,
+                                    void *stream);
 
 #ifdef __cplusplus
 }

@@ -21,11 +21,12 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqsa.so")
 
-QSA_OK, QSA_ERR_ARG, QSA_ERR_UNSUPPORTED, QSA_ERR_HIP = 0, 1, 2, 3
+QSA_OK, QSA_ERR_ARG, QSA_ERR_UNSUPPORTED, QSA_ERR_HIP, QSA_ERR_TOO_LARGE = 0, 1, 2, 3, 4
 MAX_K = 64
-ABI_VERSION = 2   # qsa.h QSA_ABI_VERSION this binding is written for
+NOALLOC_SCRATCH_BYTES = 64 << 20   # qsa.h QSA_NOALLOC_SCRATCH_BYTES
+ABI_VERSION = 3   # qsa.h QSA_ABI_VERSION this binding is written for
 EXPORTS = ("qsa_abi_version", "qsa_status_string", "qsa_convert_f32_f16", "qsa_block_scores",
-           "qsa_select_topk", "qsa_select_phase")
+           "qsa_select_topk", "qsa_select_phase", "qsa_select_phase_noalloc")
 
 
 class QSAError(RuntimeError):
@@ -51,6 +52,9 @@ def _load() -> ctypes.CDLL:
     L.qsa_select_phase.argtypes = [vp, vp, i64, vp, i64, vp, i64, vp, i64, vp, i32, i32, i32,
                                    i32, i64, i32, i32, i64, vp]
     L.qsa_select_phase.restype = ctypes.c_int
+    L.qsa_select_phase_noalloc.argtypes = [vp, vp, i64, vp, i64, vp, i64, vp, i32, i32, i32, i32,
+                                           i64, i32, i32, i64, vp]
+    L.qsa_select_phase_noalloc.restype = ctypes.c_int
     if L.qsa_abi_version() != ABI_VERSION:
         raise ImportError(f"{LIB_PATH}: ABI version {L.qsa_abi_version()}, this binding needs "
                           f"{ABI_VERSION}; rebuild with __graft_entry__.build()")
@@ -224,3 +228,31 @@ def select_phase(q: torch.Tensor, kblk: torch.Tensor, n_kv: int, bs: int, k: int
                                 _ptr(ws.vals), G, nq, H, D, n_kv, bs, k, ws.q_chunk,
                                 _stream(stream)))
     return (ws.ids, ws.vals) if ws.vals is not None else ws.ids
+
+
+def select_phase_noalloc(q: torch.Tensor, kblk: torch.Tensor, n_kv: int, bs: int, k: int,
+                         ids: torch.Tensor, vals: torch.Tensor | None = None, q_chunk: int = 0,
+                         q16: torch.Tensor | None = None,
+                         stream: torch.cuda.Stream | None = None):
+    """The whole phase with no device allocation: scores go to the library's
+    fixed per-GPU scratch array (NOALLOC_SCRATCH_BYTES), ids [G, nq, k] and
+    optional vals are the caller's.  q is float32 (with an optional fp16
+    buffer q16 that receives the converted queries) or float16."""
+    fp32 = q.dtype == torch.float32
+    nq, G, H, D, qts = _check_q(q, torch.float32 if fp32 else torch.float16)
+    nb = n_blocks(n_kv, bs)
+    khs = _check_k(kblk, G, D, nb)
+    if ids.dtype != torch.int32 or tuple(ids.shape) != (G, nq, k) or ids.stride(2) != 1 \
+            or ids.stride(0) != nq * ids.stride(1):
+        raise ValueError("ids must be int32 [G, nq, k] with rows at a common stride")
+    if vals is not None and (vals.dtype != torch.float32 or vals.shape != ids.shape
+                             or vals.stride() != ids.stride()):
+        raise ValueError("vals must be float32 with the layout of ids")
+    qsrc16 = q16 if fp32 else q
+    if fp32 and q16 is not None and (q16.dtype != torch.float16 or q16.stride(0) != qts):
+        raise ValueError("q16 must be float16 with the queries' layout")
+    _check("qsa_select_phase_noalloc",
+           lib.qsa_select_phase_noalloc(_ptr(q) if fp32 else None, _ptr(qsrc16), qts, _ptr(kblk),
+                                        khs, _ptr(ids), ids.stride(1), _ptr(vals), G, nq, H, D,
+                                        n_kv, bs, k, q_chunk, _stream(stream)))
+    return (ids, vals) if vals is not None else ids

@@ -121,6 +121,7 @@ const char *qsa_status_string(qsa_status s) {
         case QSA_ERR_ARG: return "invalid argument (null pointer, negative size, stride or leading dimension too small)";
         case QSA_ERR_UNSUPPORTED: return "unsupported geometry (D not in {64,128}, H not in [1,16], k > 64, block size < 1, or misaligned pointer/stride)";
         case QSA_ERR_HIP: return "HIP runtime error at launch";
+        case QSA_ERR_TOO_LARGE: return "the work does not fit the fixed scratch array of the no-allocation entry point (QSA_NOALLOC_SCRATCH_BYTES): pass a smaller q_chunk or use qsa_select_phase with a workspace";
     }
     return "unknown status";
 }

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qsa.h")
 LIB = os.path.join(ROOT, "sparse_attention_block_qsa_amd", "libqsa.so")
 
-OK, ARG, UNSUP, HIP = 0, 1, 2, 3
+OK, ARG, UNSUP, HIP, TOO_LARGE = 0, 1, 2, 3, 4
 A16 = 0x10000          # a fake, 16-byte aligned device address (never dereferenced)
 
 
@@ -39,6 +39,8 @@ def lib():
     L.qsa_convert_f32_f16.argtypes = [vp, vp, i64, vp]
     L.qsa_select_phase.argtypes = [vp, vp, i64, vp, i64, vp, i64, vp, i64, vp, i32, i32, i32,
                                    i32, i64, i32, i32, i64, vp]
+    L.qsa_select_phase_noalloc.argtypes = [vp, vp, i64, vp, i64, vp, i64, vp, i32, i32, i32,
+                                           i32, i64, i32, i32, i64, vp]
     L.qsa_status_string.argtypes = [ctypes.c_int]
     L.qsa_status_string.restype = ctypes.c_char_p
     return L
@@ -47,7 +49,7 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["qsa_abi_version", "qsa_status_string", "qsa_convert_f32_f16", "qsa_block_scores",
-         "qsa_select_topk", "qsa_select_phase"])
+         "qsa_select_topk", "qsa_select_phase", "qsa_select_phase_noalloc"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -59,7 +61,7 @@ def test_abi_version_and_status_strings(lib):
     hdr = open(HEADER).read()
     ver = int(re.search(r"#define QSA_ABI_VERSION (\d+)", hdr).group(1))
     assert lib.qsa_abi_version() == ver
-    for st in (OK, ARG, UNSUP, HIP, 99):
+    for st in (OK, ARG, UNSUP, HIP, TOO_LARGE, 99):
         assert lib.qsa_status_string(st)
 
 
@@ -148,3 +150,30 @@ def test_select_phase_refusals(lib, kw, want):
 def test_select_phase_empty_is_ok_without_launch(lib):
     assert phase_call(lib, nq=0) == OK
     assert phase_call(lib, G=0) == OK
+
+
+def noalloc_call(lib, **kw):
+    a = dict(q32=A16, q16=None, qts=8 * 128, kblk=A16, khs=64 * 128, ids=A16, ld_ids=16,
+             vals=None, G=1, nq=256, H=8, D=128, n_kv=4096, bs=64, k=16, q_chunk=0)
+    a.update(kw)
+    return lib.qsa_select_phase_noalloc(a["q32"], a["q16"], a["qts"], a["kblk"], a["khs"],
+                                        a["ids"], a["ld_ids"], a["vals"], a["G"], a["nq"],
+                                        a["H"], a["D"], a["n_kv"], a["bs"], a["k"],
+                                        a["q_chunk"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q_chunk=-1), ARG), (dict(G=-1), ARG), (dict(nq=-1), ARG), (dict(n_kv=-1), ARG),
+    (dict(bs=0), UNSUP),
+    # one query's score row (17M blocks of one token, 68 MB) exceeds the 64 MiB array
+    (dict(n_kv=17 << 20, bs=1, khs=(17 << 20) * 128), TOO_LARGE),
+    # four KV heads of 2049 blocks fit 2016 queries per pass, not 4096
+    (dict(G=4, qts=4 * 1024, n_kv=131077, khs=2049 * 128, nq=4096, q_chunk=4096), TOO_LARGE),
+])
+def test_select_phase_noalloc_refusals(lib, kw, want):
+    assert noalloc_call(lib, **kw) == want
+
+
+def test_select_phase_noalloc_empty_is_ok_without_launch(lib):
+    assert noalloc_call(lib, nq=0) == OK
+    assert noalloc_call(lib, G=0) == OK
