@@ -48,6 +48,8 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         L.oracle_abi_version.restype = ctypes.c_int
         L.oracle_max_threads.restype = ctypes.c_int
+        L.oracle_set_threads.argtypes = [ctypes.c_int]
+        L.oracle_set_threads.restype = None
         L.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
         L.oracle_f16_to_f64.restype = ctypes.c_double
         L.oracle_f32_to_f16_one.argtypes = [ctypes.c_float]
@@ -68,6 +70,11 @@ def lib():
 
 def max_threads() -> int:
     return lib().oracle_max_threads()
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's following parallel regions."""
+    lib().oracle_set_threads(int(n))
 
 
 def _p(a: np.ndarray | None):

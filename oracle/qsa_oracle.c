@@ -42,6 +42,14 @@ int oracle_abi_version(void) { return ORACLE_ABI; }
 /* Threads an OpenMP region of the oracle uses (for reporting). */
 int oracle_max_threads(void) { return omp_get_max_threads(); }
 
+/* Sets the threads of the following OpenMP regions (the benchmark's
+ * single-thread baseline); n < 1 is ignored. */
+void oracle_set_threads(int n)
+{
+    if (n >= 1)
+        omp_set_num_threads(n);
+}
+
 /* IEEE 754 binary16 -> exact double, from the format's definition:
  * sign s, 5-bit biased exponent e, 10-bit fraction m.
  *   e == 0        : (-1)^s * m * 2^-24            (zero and subnormals)

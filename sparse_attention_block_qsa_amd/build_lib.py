@@ -46,6 +46,21 @@ def _compile(src: str, extra: list[str], verbose: bool) -> str:
     return obj
 
 
+BENCH_SRC = os.path.join(HERE, "bench_kernels", "qsa_bench.hip")
+BENCH_LIB = os.path.join(HERE, "libqsa_bench.so")
+
+
+def build_bench(verbose: bool = False) -> str:
+    """libqsa_bench.so: the benchmark's measurement kernels (an MFMA loop and
+    a streaming read), kept out of libqsa.so."""
+    cmd = [HIPCC, *FLAGS, "-shared", "-o", BENCH_LIB + ".tmp", BENCH_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(BENCH_LIB + ".tmp", BENCH_LIB)
+    return BENCH_LIB
+
+
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     extra = list(extra or [])
@@ -56,6 +71,7 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(LIB + ".tmp", LIB)
+    build_bench(verbose)
     return LIB
 
 
