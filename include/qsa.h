@@ -69,8 +69,10 @@ typedef enum qsa_status {
                                 the library's fixed scratch array */
 } qsa_status;
 
-#define QSA_ABI_VERSION 3
+#define QSA_ABI_VERSION 4
 #define QSA_MAX_K 64
+/* Largest block size qsa_block_keys takes (its sums stay exact in float64). */
+#define QSA_BLOCK_KEYS_MAX_BS 8192
 /* Size of the per-GPU device array qsa_select_phase_noalloc keeps its score
  * workspace in (64 MiB). */
 #define QSA_NOALLOC_SCRATCH_BYTES (64ll << 20)
@@ -134,6 +136,31 @@ qsa_status qsa_block_scores(const uint16_t *q16, int64_t q_tok_stride,
 qsa_status qsa_select_topk(const float *scores, int64_t ld_s, int64_t rows, int32_t nb,
                            int32_t k, int32_t *ids, int64_t ld_ids, float *vals,
                            void *stream);
+
+/*
+ * qsa_block_keys -- the block keys the scorer reads, built from token keys:
+ * the step before the phase.  The pages index one key vector k_b per KV
+ * block (Strata pull request #228, part 1, score formula) but do not say how
+ * it is built; the reading taken is the mean of the block's token keys:
+ *   kblk[g][b][i] = fp16 nearest (ties to even) to
+ *                   (1/len_b) * sum_{t in block b} k_tok[t][g][i]
+ * with block b = tokens [b*bs, min((b+1)*bs, n_kv)) and len_b its length
+ * (the partial last block averages its own tokens).  The mean is exact
+ * before its one rounding, so the result does not depend on any summation
+ * order.
+ *   k_tok      device fp16 bits, token-major like a KV cache: element
+ *              (t, g, i) at k_tok[t * tok_stride + g * D + i];
+ *              tok_stride >= G*D; 16-byte aligned, tok_stride % 8 == 0;
+ *              values must be finite
+ *   kblk       device fp16 bits [G][>= nb][D] at kblk_head_stride >= nb*D
+ *              (16-byte aligned, kblk_head_stride % 8 == 0);
+ *              written: [g][0, nb)[0, D)
+ *   G >= 0, D in {64, 128}, n_kv >= 0, 1 <= bs <= QSA_BLOCK_KEYS_MAX_BS
+ * G == 0 or n_kv == 0: QSA_OK, nothing written.
+ */
+qsa_status qsa_block_keys(const uint16_t *k_tok, int64_t tok_stride, uint16_t *kblk,
+                          int64_t kblk_head_stride, int32_t G, int32_t D, int64_t n_kv,
+                          int32_t bs, void *stream);
 
 /*
  * qsa_select_phase -- the whole phase on one stream: convert (when q32 is

@@ -64,6 +64,10 @@ def lib():
         L.oracle_block_model_f32.restype = ctypes.c_int
         L.oracle_topk.argtypes = [_vp, _i64, _i64, _i64, _i32, _vp, _i64, _vp]
         L.oracle_topk.restype = ctypes.c_int
+        L.oracle_round_ratio_f16.argtypes = [_i64, _i64]
+        L.oracle_round_ratio_f16.restype = ctypes.c_uint16
+        L.oracle_block_keys.argtypes = [_vp, _i64, _i32, _i32, _i64, _i32, _vp, _i64]
+        L.oracle_block_keys.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -157,6 +161,26 @@ def topk(score_rows: np.ndarray, k: int) -> tuple[np.ndarray, np.ndarray]:
     rc = lib().oracle_topk(_p(s), nb, rows, nb, k, _p(ids), k, _p(vals))
     assert rc == 0
     return ids, vals
+
+
+def round_ratio_f16(num: int, den: int) -> int:
+    """fp16 bits nearest (ties to even) to num / den * 2^-24."""
+    return int(lib().oracle_round_ratio_f16(int(num), int(den)))
+
+
+def block_keys(k_tok: np.ndarray, n_kv: int, bs: int) -> np.ndarray:
+    """The block key of every (KV head, block): the mean of the block's token
+    keys rounded once to the nearest fp16 (the reading taken for k_b, which
+    the pages index but do not define).  k_tok is uint16 fp16 bits
+    [n_tok >= n_kv][G][D]; returns uint16 [G][nb][D]."""
+    k = np.ascontiguousarray(k_tok, dtype=np.uint16)
+    n_tok, G, D = k.shape
+    assert n_tok >= n_kv
+    nb = -(-n_kv // bs)
+    out = np.zeros((G, max(nb, 1), D), dtype=np.uint16)
+    rc = lib().oracle_block_keys(_p(k), G * D, G, D, n_kv, bs, _p(out), max(nb, 1) * D)
+    assert rc == 0
+    return out[:, :nb]
 
 
 # --------------------------------------------------------------------------

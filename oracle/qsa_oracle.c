@@ -260,3 +260,75 @@ int oracle_topk(const double *scores, int64_t ld, int64_t rows, int64_t nb, int3
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Block keys (the step before the phase).  The pages index one key vector
+ * k_b per KV block (PR #228 part 1, score formula) without saying how it is
+ * built from the block's token keys.  The reading taken: the mean of the
+ * block's token keys, per KV head and channel, rounded once to the nearest
+ * fp16 (ties to even): the partial last block averages its own tokens.
+ *
+ * Written from the definition with exact integer arithmetic: every fp16
+ * value is an integer m times 2^-24 (|m| < 2^40), so a block's sum is an
+ * exact integer N (|N| < 2^53 for up to 2^13 tokens) and its mean is the
+ * rational N / len.  The fp16 result is the value of the fp16 grid nearest
+ * to it, found by trying exponents from the largest down. */
+static int64_t oracle_f16_units(uint16_t h)   /* value * 2^24, finite input */
+{
+    int e = (h >> 10) & 0x1f;
+    int64_t m = h & 0x3ff;
+    int64_t v = (e == 0) ? m : ((1024 + m) << (e - 1));
+    return (h & 0x8000) ? -v : v;
+}
+
+/* nearest fp16 (ties to even) to num / den * 2^-24, den > 0 */
+uint16_t oracle_round_ratio_f16(int64_t num, int64_t den)
+{
+    uint16_t sign = num < 0 ? 0x8000u : 0;
+    unsigned __int128 a = (unsigned __int128)(num < 0 ? -num : num);
+    if (a == 0)
+        return 0;   /* an exact zero mean is +0 */
+    /* the fp16 binade [2^E, 2^(E+1)) holding the value, E in [-14, 15];
+     * below 2^-14 the grid is the subnormal one (spacing 2^-24) */
+    int E = 15;
+    while (E > -14 && a < ((unsigned __int128)den << (E + 24)))
+        --E;
+    int spacing_log2 = (E == -14 && a < ((unsigned __int128)den << 10)) ? 0 : E + 14;
+    unsigned __int128 unit = (unsigned __int128)den << spacing_log2;
+    unsigned __int128 q = a / unit, r = a % unit;
+    if (2 * r > unit || (2 * r == unit && (q & 1)))
+        ++q;
+    if (spacing_log2 == 0 && E == -14 && q <= 1024)   /* subnormal (1024 = 2^-14) */
+        return (uint16_t)(sign | (uint16_t)q);
+    if (q == 2048) {   /* rounded up into the next binade */
+        q = 1024;
+        ++E;
+    }
+    if (E > 15)
+        return (uint16_t)(sign | 0x7c00u);
+    return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)(q - 1024));
+}
+
+/* kblk[g*head_stride + b*D + i] = nearest fp16 to the mean of
+ * k_tok[t*tok_stride + g*D + i] over the tokens t of block b
+ * (t in [b*bs, min((b+1)*bs, n_kv))), for every g < G, b < nb, i < D. */
+int oracle_block_keys(const uint16_t *k_tok, int64_t tok_stride, int32_t G, int32_t D,
+                      int64_t n_kv, int32_t bs, uint16_t *kblk, int64_t head_stride)
+{
+    if (G < 0 || D < 1 || n_kv < 0 || bs < 1 || bs > 8192 || tok_stride < (int64_t)G * D ||
+        head_stride < ((n_kv + bs - 1) / bs) * D)
+        return 1;
+    int64_t nb = (n_kv + bs - 1) / bs;
+#pragma omp parallel for schedule(static)
+    for (int64_t gb = 0; gb < (int64_t)G * nb; ++gb) {
+        int64_t g = gb / nb, b = gb % nb;
+        int64_t t0 = b * bs, t1 = t0 + bs < n_kv ? t0 + bs : n_kv;
+        for (int32_t i = 0; i < D; ++i) {
+            int64_t sum = 0;
+            for (int64_t t = t0; t < t1; ++t)
+                sum += oracle_f16_units(k_tok[t * tok_stride + g * D + i]);
+            kblk[g * head_stride + b * D + i] = oracle_round_ratio_f16(sum, t1 - t0);
+        }
+    }
+    return 0;
+}

@@ -24,9 +24,10 @@ LIB_PATH = os.path.join(_HERE, "libqsa.so")
 QSA_OK, QSA_ERR_ARG, QSA_ERR_UNSUPPORTED, QSA_ERR_HIP, QSA_ERR_TOO_LARGE = 0, 1, 2, 3, 4
 MAX_K = 64
 NOALLOC_SCRATCH_BYTES = 64 << 20   # qsa.h QSA_NOALLOC_SCRATCH_BYTES
-ABI_VERSION = 3   # qsa.h QSA_ABI_VERSION this binding is written for
-EXPORTS = ("qsa_abi_version", "qsa_status_string", "qsa_convert_f32_f16", "qsa_block_scores",
-           "qsa_select_topk", "qsa_select_phase", "qsa_select_phase_noalloc")
+ABI_VERSION = 4   # qsa.h QSA_ABI_VERSION this binding is written for
+BLOCK_KEYS_MAX_BS = 8192   # qsa.h QSA_BLOCK_KEYS_MAX_BS
+EXPORTS = ("qsa_abi_version", "qsa_status_string", "qsa_convert_f32_f16", "qsa_block_keys",
+           "qsa_block_scores", "qsa_select_topk", "qsa_select_phase", "qsa_select_phase_noalloc")
 
 
 class QSAError(RuntimeError):
@@ -45,6 +46,8 @@ def _load() -> ctypes.CDLL:
     L.qsa_status_string.restype = ctypes.c_char_p
     L.qsa_convert_f32_f16.argtypes = [vp, vp, i64, vp]
     L.qsa_convert_f32_f16.restype = ctypes.c_int
+    L.qsa_block_keys.argtypes = [vp, i64, vp, i64, i32, i32, i64, i32, vp]
+    L.qsa_block_keys.restype = ctypes.c_int
     L.qsa_block_scores.argtypes = [vp, i64, vp, i64, vp, i64, i32, i32, i32, i32, i64, i32, vp]
     L.qsa_block_scores.restype = ctypes.c_int
     L.qsa_select_topk.argtypes = [vp, i64, i64, i32, i32, vp, i64, vp, vp]
@@ -123,6 +126,27 @@ def convert_f32_f16(src: torch.Tensor, out: torch.Tensor | None = None,
     _check("qsa_convert_f32_f16",
            lib.qsa_convert_f32_f16(_ptr(src), _ptr(out), src.numel(), _stream(stream)))
     return out
+
+
+def block_keys(k_tok: torch.Tensor, n_kv: int, bs: int, out: torch.Tensor | None = None,
+               stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """Block keys [G, nb, D] fp16 from token keys k_tok [>= n_kv, G, D] fp16
+    (token-major, the (G, D) dims contiguous): the mean of each block's
+    tokens rounded once to fp16 (a view of ``out`` when given)."""
+    if k_tok.dim() != 3 or k_tok.dtype != torch.float16 or not k_tok.is_cuda \
+            or k_tok.shape[0] < n_kv or k_tok.stride(2) != 1 or k_tok.stride(1) != k_tok.shape[2]:
+        raise ValueError("k_tok must be a float16 CUDA tensor [>= n_kv, G, D], (G, D) contiguous")
+    _, G, D = k_tok.shape
+    nb = n_blocks(n_kv, bs)
+    if out is None:
+        out = torch.empty((G, max(nb, 1), D), dtype=torch.float16, device=k_tok.device)
+    if out.dim() != 3 or out.dtype != torch.float16 or out.shape[0] != G or out.shape[1] < nb \
+            or out.shape[2] != D or out.stride(2) != 1 or out.stride(1) != D:
+        raise ValueError("out must be float16 [G, >= nb, D] with (nb, D) contiguous")
+    _check("qsa_block_keys",
+           lib.qsa_block_keys(_ptr(k_tok), k_tok.stride(0), _ptr(out), out.stride(0), G, D, n_kv,
+                              bs, _stream(stream)))
+    return out[:, :nb]
 
 
 def block_scores(q16: torch.Tensor, kblk: torch.Tensor, n_kv: int, bs: int,

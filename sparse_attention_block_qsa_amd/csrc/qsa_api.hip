@@ -154,6 +154,26 @@ qsa_status qsa_select_topk(const float *scores, int64_t ld_s, int64_t rows, int3
     return hip_status(qsa::launch_topk(geo, static_cast<hipStream_t>(stream)));
 }
 
+qsa_status qsa_block_keys(const uint16_t *k_tok, int64_t tok_stride, uint16_t *kblk,
+                          int64_t kblk_head_stride, int32_t G, int32_t D, int64_t n_kv,
+                          int32_t bs, void *stream) {
+    if (G < 0 || n_kv < 0 || tok_stride < 0 || kblk_head_stride < 0) return QSA_ERR_ARG;
+    if (bs < 1 || bs > QSA_BLOCK_KEYS_MAX_BS) return QSA_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return QSA_ERR_UNSUPPORTED;
+    if (G == 0 || n_kv == 0) return QSA_OK;
+    if (!k_tok || !kblk) return QSA_ERR_ARG;
+    const int64_t nb = n_kv / bs + (n_kv % bs != 0);
+    int64_t tmp;
+    if (tok_stride < static_cast<int64_t>(G) * D) return QSA_ERR_ARG;
+    if (!mad_ok(nb, D, 0, &tmp) || kblk_head_stride < tmp) return QSA_ERR_ARG;
+    if (!mad_ok(n_kv - 1, tok_stride, static_cast<int64_t>(G) * D, &tmp)) return QSA_ERR_ARG;
+    if (!mad_ok(static_cast<int64_t>(G) - 1, kblk_head_stride, nb * D, &tmp)) return QSA_ERR_ARG;
+    if (!aligned16(k_tok) || tok_stride % 8 != 0) return QSA_ERR_UNSUPPORTED;
+    if (!aligned16(kblk) || kblk_head_stride % 8 != 0) return QSA_ERR_UNSUPPORTED;
+    return hip_status(qsa::launch_block_keys(k_tok, tok_stride, kblk, kblk_head_stride, G, D, n_kv,
+                                             bs, static_cast<hipStream_t>(stream)));
+}
+
 qsa_status qsa_select_phase(const float *q32, uint16_t *q16, int64_t q_tok_stride,
                             const uint16_t *kblk, int64_t kblk_head_stride, float *scores_ws,
                             int64_t ld_s, int32_t *ids, int64_t ld_ids, float *vals, int32_t G,

@@ -114,6 +114,12 @@ hipError_t launch_topk(const TopkGeom &g, hipStream_t s);
 
 hipError_t launch_convert(const float *src, uint16_t *dst, int64_t n, hipStream_t s);
 
+// Block keys: kblk[g][b] = the fp16-rounded mean of the tokens of block b of
+// KV head g (qsa_blockkeys.hip).  D in {64, 128}, 1 <= bs <= 8192.
+hipError_t launch_block_keys(const uint16_t *k_tok, int64_t tok_stride, uint16_t *kblk,
+                             int64_t khs, int32_t G, int32_t D, int64_t n_kv, int32_t bs,
+                             hipStream_t s);
+
 // rows of row_len elements at a stride of stride elements (both arrays)
 hipError_t launch_convert_rows(const float *src, uint16_t *dst, int64_t rows, int64_t row_len,
                                int64_t stride, hipStream_t s);

@@ -330,7 +330,10 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
         constexpr int kFull = full_columns(NPL);
         #pragma unroll
         for (int j = 0; j < NPL; ++j) {
-            const uint32_t x = __builtin_amdgcn_raw_buffer_load_b32(rs, (j * 64 + lane) * 4, 0, 0);
+            // the column's byte offset is a constant added to the lane's: it
+            // folds into the instruction's immediate offset (no per-column
+            // address math on the VALU)
+            const uint32_t x = __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4 + j * 256, 0, 0);
             xr[j] = j < kFull || lane < nb - 64 * j ? x : kPad;
         }
         #pragma unroll
@@ -350,23 +353,49 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     bool done = false;
     if constexpr (NPL > 0) {
         if (kk > 0) {
-            // 1. per-lane top two of the fp32 bits as signed integers
-            int32_t m1 = INT32_MIN, m2 = INT32_MIN;
-            #pragma unroll
-            for (int j = 0; j < NPL; ++j) {
-                const int32_t x = static_cast<int32_t>(xr[j]);
-                m2 = max(min(m1, x), min(max(m1, x), m2));   // median of three: v_med3_i32
-                m1 = max(m1, x);
+            // 1. samples of the fp32 bits as signed integers.  Few rows: the
+            //    per-lane top two (two ops a column, a short chain).  Many
+            //    rows (VALU-bound) with at least nine columns: the maxima of
+            //    three column groups, about one op per three columns
+            //    (v_max3_i32).  Either way kk samples >= th are kk values >=
+            //    th.  On the prefill chunk's scores both give pools of about
+            //    74 candidates at 2049 blocks and k = 64 (a group of 11 of
+            //    2049 values reaches the 64th-largest of 192 group maxima
+            //    with probability 1/3, so p = 1 - (2/3)^(1/11) ~ 3.6 %).
+            constexpr bool kGroups = MANY && NPL >= 9;
+            uint32_t s1, s2, s3 = 0;
+            if constexpr (kGroups) {
+                constexpr int G1 = NPL / 3, G2 = 2 * NPL / 3;
+                int32_t g0 = INT32_MIN, g1 = INT32_MIN, g2 = INT32_MIN;
+                #pragma unroll
+                for (int j = 0; j < NPL; ++j) {
+                    const int32_t x = static_cast<int32_t>(xr[j]);
+                    if (j < G1) g0 = max(g0, x);
+                    else if (j < G2) g1 = max(g1, x);
+                    else g2 = max(g2, x);
+                }
+                s1 = static_cast<uint32_t>(g0) ^ 0x80000000u;
+                s2 = static_cast<uint32_t>(g1) ^ 0x80000000u;
+                s3 = static_cast<uint32_t>(g2) ^ 0x80000000u;
+            } else {
+                int32_t m1 = INT32_MIN, m2 = INT32_MIN;
+                #pragma unroll
+                for (int j = 0; j < NPL; ++j) {
+                    const int32_t x = static_cast<int32_t>(xr[j]);
+                    m2 = max(min(m1, x), min(max(m1, x), m2));   // median of three: v_med3_i32
+                    m1 = max(m1, x);
+                }
+                s1 = static_cast<uint32_t>(m1) ^ 0x80000000u;
+                s2 = static_cast<uint32_t>(m2) ^ 0x80000000u;
             }
-            // 2. th = the kk-th largest of the 128 samples, to 16 leading
-            //    bits (bisection on the biased bits, two ballots per step):
-            //    any th is correct, the low bits only tighten C slightly
-            const uint32_t s1 = static_cast<uint32_t>(m1) ^ 0x80000000u;
-            const uint32_t s2 = static_cast<uint32_t>(m2) ^ 0x80000000u;
+            // 2. th = the kk-th largest of the samples, to 16 leading bits
+            //    (bisection on the biased bits, a ballot per sample set and
+            //    step): any th is correct, the low bits only tighten C
             uint32_t T = 0;
             for (int bit = 31; bit >= 16; --bit) {
                 const uint32_t cand = T | (1u << bit);
-                const int cnt = __popcll(ballot(s1 >= cand)) + __popcll(ballot(s2 >= cand));
+                int cnt = __popcll(ballot(s1 >= cand)) + __popcll(ballot(s2 >= cand));
+                if constexpr (kGroups) cnt += __popcll(ballot(s3 >= cand));
                 if (cnt >= kk) T = cand;
             }
             const float th = __builtin_bit_cast(float, T ^ 0x80000000u);
@@ -641,7 +670,7 @@ __global__ __launch_bounds__(256) void topk_quad_kernel(TopkArgs a) {
         // (pads, never read back).  Ownership is a per-lane test, so that
         // no load or store sits under a branch that would serialise them.
         const int c = col0 + j;
-        const uint32_t x = __builtin_amdgcn_raw_buffer_load_b32(rs, (c * 64 + lane) * 4, 0, 0);
+        const uint32_t x = __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, c * 256, 0);
         const uint32_t xv = lane < nb - 64 * c ? x : kPad;
         row[c * 64 + lane] = xv;
         xr[j] = 64 * j + lane < nw ? xv : kPad;

@@ -22,7 +22,8 @@
 namespace {
 
 struct Launch {
-    char kind;   // 'f' full scorer, 's' small scorer, 't' tail, 'k' top-k, 'c' convert, 'r' rows
+    char kind;   // 'f' full scorer, 's' small scorer, 't' tail, 'k' top-k, 'c' convert, 'r' rows,
+                 // 'b' block keys
     int64_t a, b, c;
 };
 std::vector<Launch> g_launches;
@@ -51,6 +52,11 @@ hipError_t launch_topk(const TopkGeom &g, hipStream_t) {
 }
 hipError_t launch_convert(const float *, uint16_t *, int64_t n, hipStream_t) {
     g_launches.push_back({'c', n, 0, 0});
+    return hipSuccess;
+}
+hipError_t launch_block_keys(const uint16_t *, int64_t, uint16_t *, int64_t, int32_t G, int32_t D,
+                             int64_t n_kv, int32_t bs, hipStream_t) {
+    g_launches.push_back({'b', G * 1000 + D, n_kv, bs});
     return hipSuccess;
 }
 hipError_t launch_convert_rows(const float *, uint16_t *, int64_t rows, int64_t row_len,
@@ -216,6 +222,22 @@ int main() {
            [] { return qsa_select_topk(F32, 2048, 256, 2048, 0, nullptr, 0, nullptr, nullptr); }, 0);
     expect("topk nb=0 pads", QSA_OK,
            [] { return qsa_select_topk(nullptr, 0, 256, 0, 8, I32, 8, nullptr, nullptr); }, 1);
+
+    // ---- qsa_block_keys -----------------------------------------------------
+    expect("keys ok", QSA_OK,
+           [] { return qsa_block_keys(H16, 4 * 128, H16, 2049 * 128, 4, 128, 131077, 64, nullptr); }, 1);
+    CHECK(g_launches[0].kind == 'b' && g_launches[0].a == 4128 && g_launches[0].b == 131077,
+          "block keys of 4 KV heads, D = 128");
+    expect("keys bs>8192", QSA_ERR_UNSUPPORTED,
+           [] { return qsa_block_keys(H16, 512, H16, 128, 4, 128, 8193, 8193, nullptr); }, 0);
+    expect("keys D=32", QSA_ERR_UNSUPPORTED,
+           [] { return qsa_block_keys(H16, 512, H16, 2049 * 32, 4, 32, 131077, 64, nullptr); }, 0);
+    expect("keys khs small", QSA_ERR_ARG,
+           [] { return qsa_block_keys(H16, 512, H16, 2048 * 128, 4, 128, 131077, 64, nullptr); }, 0);
+    expect("keys misaligned", QSA_ERR_UNSUPPORTED,
+           [] { return qsa_block_keys(H16 + 1, 512, H16, 2049 * 128, 4, 128, 131077, 64, nullptr); }, 0);
+    expect("keys empty", QSA_OK,
+           [] { return qsa_block_keys(nullptr, 512, nullptr, 0, 4, 128, 0, 64, nullptr); }, 0);
 
     // ---- qsa_convert_f32_f16 -----------------------------------------------
     expect("convert ok", QSA_OK, [] { return qsa_convert_f32_f16(F32, H16, 1000, nullptr); }, 1);

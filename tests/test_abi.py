@@ -41,6 +41,7 @@ def lib():
                                    i32, i64, i32, i32, i64, vp]
     L.qsa_select_phase_noalloc.argtypes = [vp, vp, i64, vp, i64, vp, i64, vp, i32, i32, i32,
                                            i32, i64, i32, i32, i64, vp]
+    L.qsa_block_keys.argtypes = [vp, i64, vp, i64, i32, i32, i64, i32, vp]
     L.qsa_status_string.argtypes = [ctypes.c_int]
     L.qsa_status_string.restype = ctypes.c_char_p
     return L
@@ -48,8 +49,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
-        ["qsa_abi_version", "qsa_status_string", "qsa_convert_f32_f16", "qsa_block_scores",
-         "qsa_select_topk", "qsa_select_phase", "qsa_select_phase_noalloc"])
+        ["qsa_abi_version", "qsa_status_string", "qsa_convert_f32_f16", "qsa_block_keys",
+         "qsa_block_scores", "qsa_select_topk", "qsa_select_phase", "qsa_select_phase_noalloc"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -177,3 +178,26 @@ def test_select_phase_noalloc_refusals(lib, kw, want):
 def test_select_phase_noalloc_empty_is_ok_without_launch(lib):
     assert noalloc_call(lib, nq=0) == OK
     assert noalloc_call(lib, G=0) == OK
+
+
+def keys_call(lib, **kw):
+    a = dict(k=A16, ts=4 * 128, kb=A16, khs=2049 * 128, G=4, D=128, n_kv=131077, bs=64)
+    a.update(kw)
+    return lib.qsa_block_keys(a["k"], a["ts"], a["kb"], a["khs"], a["G"], a["D"], a["n_kv"],
+                              a["bs"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(G=-1), ARG), (dict(n_kv=-1), ARG), (dict(ts=-8), ARG), (dict(bs=0), UNSUP),
+    (dict(bs=8193), UNSUP), (dict(D=96), UNSUP), (dict(k=None), ARG), (dict(kb=None), ARG),
+    (dict(ts=4 * 128 - 8), ARG), (dict(khs=2048 * 128), ARG), (dict(k=A16 + 2), UNSUP),
+    (dict(ts=4 * 128 + 4), UNSUP), (dict(kb=A16 + 8), UNSUP), (dict(khs=2049 * 128 + 2), UNSUP),
+    (dict(ts=1 << 50), ARG),                  # token extent overflows int64
+])
+def test_block_keys_refusals(lib, kw, want):
+    assert keys_call(lib, **kw) == want
+
+
+@pytest.mark.parametrize("kw", [dict(G=0), dict(n_kv=0), dict(n_kv=0, k=None, kb=None)])
+def test_block_keys_empty_is_ok_without_launch(lib, kw):
+    assert keys_call(lib, **kw) == OK

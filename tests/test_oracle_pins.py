@@ -629,3 +629,105 @@ def test_config_shapes():
     assert w.q16.shape == (37, 1, 4, 64) and w.kblk.shape == (1, 16, 64)
     x8 = qi.scaled_by_8(qi.make("nq256_nkv4096"))
     assert np.abs(x8.q16.view(np.float16).astype(np.float64)).max() < 8188
+
+
+# --------------------------------------------------------------------------
+# block keys: the mean of a block's token keys, rounded once to fp16 (the
+# reading taken for k_b, which the pages index but never define)
+# --------------------------------------------------------------------------
+
+def f16_nearest_fraction(x: Fraction) -> int:
+    """fp16 bits of the value of the fp16 grid nearest to x, ties to the even
+    significand, from the format's definition (finite x, |x| < 65520):
+    binade [2^E, 2^(E+1)) has spacing 2^(E-10) for E >= -14, and below 2^-14
+    the spacing is 2^-24."""
+    sign = 0x8000 if x < 0 else 0
+    a = abs(x)
+    if a == 0:
+        return 0
+    E = 15
+    while E > -14 and a < Fraction(2) ** E:
+        E -= 1
+    spacing = Fraction(2) ** (E - 10)
+    q, r = divmod(a, spacing)
+    q = int(q)
+    if r * 2 > spacing or (r * 2 == spacing and q % 2 == 1):
+        q += 1
+    if q < 1024:                      # subnormal (E = -14, below 2^-14)
+        return sign | q
+    if q == 2048:
+        q, E = 1024, E + 1
+    if E > 15:
+        return sign | 0x7C00
+    return sign | ((E + 15) << 10) | (q - 1024)
+
+
+def test_round_ratio_vs_fractions():
+    rng = np.random.default_rng(77)
+    cases = [(1, 2), (3, 2), (5, 2), (-1, 2), (1 << 24, 3), (-(1 << 24), 3), (2047, 1),
+             (2049, 2), (2 ** 40 - 1, 1), (65504 << 24, 1), (1023 * 2 + 1, 2), (1 << 10, 1),
+             ((1 << 10) * 3 - 1, 3)]
+    for _ in range(3000):
+        den = int(rng.integers(1, 9000))
+        num = int(rng.integers(-(2 ** 40), 2 ** 40)) * int(rng.integers(1, den + 1)) // den
+        if rng.random() < 0.3:
+            num = int(rng.integers(-3000, 3000))          # subnormal range and ties
+        cases.append((num, den))
+    for num, den in cases:
+        want = f16_nearest_fraction(Fraction(num, den) / 2 ** 24)
+        assert oracle.round_ratio_f16(num, den) == want, (num, den, hex(want))
+
+
+def _keys_fraction(k_tok, n_kv, bs):
+    n, G, D = k_tok.shape
+    nb = -(-n_kv // bs)
+    vals = k_tok.view(np.float16).astype(np.float64)
+    out = np.zeros((G, nb, D), np.uint16)
+    for g in range(G):
+        for b in range(nb):
+            t0, t1 = b * bs, min((b + 1) * bs, n_kv)
+            for i in range(D):
+                s = sum((Fraction(float(v)) for v in vals[t0:t1, g, i]), Fraction(0))
+                out[g, b, i] = f16_nearest_fraction(s / (t1 - t0))
+    return out
+
+
+@pytest.mark.parametrize("n_kv,bs,G,D", [(13, 3, 2, 5), (40, 7, 1, 8), (64 * 3 + 5, 64, 2, 4),
+                                         (1, 64, 1, 3), (0, 64, 2, 4)])
+def test_block_keys_vs_fractions(n_kv, bs, G, D):
+    rng = np.random.default_rng(1000 + n_kv + bs)
+    k_tok = random_f16(rng, (max(n_kv, 1), G, D))
+    got = oracle.block_keys(k_tok, n_kv, bs)
+    assert np.array_equal(got, _keys_fraction(k_tok, n_kv, bs))
+
+
+def test_block_keys_dyadic_blocks_vs_numpy():
+    """Full blocks of 64 tokens: the sum of 64 fp16 values and its division
+    by 64 are exact in float64, so numpy's float64 -> float16 conversion
+    (correctly rounded) gives the fp16 mean."""
+    rng = np.random.default_rng(31)
+    n_kv, bs, G, D = 64 * 20, 64, 3, 128
+    k_tok = qi.f64_to_f16_bits(rng.standard_normal((n_kv, G, D)) / math.sqrt(D))
+    got = oracle.block_keys(k_tok, n_kv, bs)
+    vals = k_tok.view(np.float16).astype(np.float64).reshape(n_kv // bs, bs, G, D)
+    want = (vals.sum(axis=1) / bs).astype(np.float16).view(np.uint16).transpose(1, 0, 2)
+    assert np.array_equal(got, want)
+
+
+def test_block_keys_closed_forms():
+    rng = np.random.default_rng(32)
+    G, D, bs, nb = 2, 16, 8, 5
+    # a block of one repeated key averages to that key; the partial last
+    # block (3 tokens) to its own tokens' mean, not divided by bs
+    key = random_f16(rng, (G, nb, D), special_frac=0.0)
+    k_tok = np.repeat(key, bs, axis=1).transpose(1, 0, 2)[: (nb - 1) * bs + 3].copy()
+    got = oracle.block_keys(k_tok, (nb - 1) * bs + 3, bs)
+    assert np.array_equal(got, key)
+    # integers: mean of 1..8 = 4.5; of (2, 4, 9) = 5; a zero mean is +0
+    ints = np.zeros((11, 1, 2))
+    ints[:8, 0, 0] = np.arange(1, 9)
+    ints[8:, 0, 0] = [2, 4, 9]
+    ints[:, 0, 1] = [1, -1] * 5 + [0]
+    got = oracle.block_keys(qi.f64_to_f16_bits(ints), 11, 8)
+    assert got[0, :, 0].view(np.float16).tolist() == [4.5, 5.0]
+    assert got[0, :, 1].tolist() == [0, 0]
