@@ -69,7 +69,7 @@ typedef enum qsa_status {
                                 the library's fixed scratch array */
 } qsa_status;
 
-#define QSA_ABI_VERSION 4
+#define QSA_ABI_VERSION 5
 #define QSA_MAX_K 64
 /* Largest block size qsa_block_keys takes (its sums stay exact in float64). */
 #define QSA_BLOCK_KEYS_MAX_BS 8192
@@ -161,6 +161,36 @@ qsa_status qsa_select_topk(const float *scores, int64_t ld_s, int64_t rows, int3
 qsa_status qsa_block_keys(const uint16_t *k_tok, int64_t tok_stride, uint16_t *kblk,
                           int64_t kblk_head_stride, int32_t G, int32_t D, int64_t n_kv,
                           int32_t bs, void *stream);
+
+/*
+ * qsa_sparse_attention -- attention over the selected blocks: the step after
+ * the phase.  The pages stop at the selection (Strata pull request #228,
+ * part 1: the phase keeps each query's top-k blocks); the reading taken for
+ * the step that consumes it is plain softmax attention of every query head
+ * over the tokens of the blocks its (KV head, query) row selected:
+ *   s_j = scale * sum_i q[t][g][h][i] * k[j][g][i],   scale = fp32(1/sqrt(D))
+ *   out[t][g][h][:] = sum_j exp(s_j - max_j s_j) v[j][g][:] / sum_j exp(s_j - max_j s_j)
+ * over every token j of every block b = ids[g*nq + t][slot], slot < k,
+ * tokens [b*bs, min((b+1)*bs, n_kv)); ids outside [0, nb) are empty slots;
+ * a row with no token gives 0.  fp16 inputs, fp32 arithmetic and output.
+ * ids must not repeat a block within a row (each listed block counts once
+ * per listing).
+ *   q16        device fp16 bits, layout of qsa_block_scores' q16 (2-byte aligned)
+ *   k_tok, v_tok  device fp16 bits, token-major: element (j, g, i) at
+ *              [j * kv_tok_stride + g * D + i]; kv_tok_stride >= G*D,
+ *              16-byte aligned, kv_tok_stride % 8 == 0 (unused when n_kv == 0)
+ *   ids        device int32 [G*nq][ld_ids], ld_ids >= k (the selector's ids)
+ *   out        device fp32, element (t, g, h, i) at
+ *              [t * out_tok_stride + (g*H + h) * D + i], out_tok_stride >= G*H*D;
+ *              written: exactly those G*H*D elements of each of the nq rows
+ *   G, nq >= 0; H in [1, 16]; D in {64, 128}; n_kv >= 0; bs >= 1; 0 <= k <= 64
+ * nq == 0 or G == 0: QSA_OK, nothing written.
+ */
+qsa_status qsa_sparse_attention(const uint16_t *q16, int64_t q_tok_stride, const uint16_t *k_tok,
+                                const uint16_t *v_tok, int64_t kv_tok_stride, const int32_t *ids,
+                                int64_t ld_ids, float *out, int64_t out_tok_stride, int32_t G,
+                                int32_t nq, int32_t H, int32_t D, int64_t n_kv, int32_t bs,
+                                int32_t k, void *stream);
 
 /*
  * qsa_select_phase -- the whole phase on one stream: convert (when q32 is

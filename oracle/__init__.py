@@ -68,6 +68,9 @@ def lib():
         L.oracle_round_ratio_f16.restype = ctypes.c_uint16
         L.oracle_block_keys.argtypes = [_vp, _i64, _i32, _i32, _i64, _i32, _vp, _i64]
         L.oracle_block_keys.restype = ctypes.c_int
+        L.oracle_attention.argtypes = [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _i32, _i32, _i32,
+                                       _i32, _i64, _i32, _i32, _vp, _vp]
+        L.oracle_attention.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -181,6 +184,37 @@ def block_keys(k_tok: np.ndarray, n_kv: int, bs: int) -> np.ndarray:
     rc = lib().oracle_block_keys(_p(k), G * D, G, D, n_kv, bs, _p(out), max(nb, 1) * D)
     assert rc == 0
     return out[:, :nb]
+
+
+def attention(q16: np.ndarray, k_tok: np.ndarray, v_tok: np.ndarray, ids: np.ndarray,
+              n_kv: int, bs: int) -> tuple[np.ndarray, np.ndarray]:
+    """Softmax attention of every query head over the tokens of the blocks
+    its (KV head, query) row selected (the reading taken for the step after
+    the selection), in float64, and the bound B of a fp32 device result.
+    q16 uint16 [nq][G][H][D]; k_tok, v_tok uint16 [>= n_kv][G][D]; ids
+    int32 [G][nq][k] (negative = empty slot).  Returns (out, B), float64
+    [nq][G][H][D]."""
+    q = np.ascontiguousarray(q16, dtype=np.uint16)
+    nq, G, H, D = q.shape
+    kt = np.ascontiguousarray(k_tok, dtype=np.uint16)
+    vt = np.ascontiguousarray(v_tok, dtype=np.uint16)
+    assert kt.shape == vt.shape and kt.shape[1:] == (G, D) and kt.shape[0] >= n_kv
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    assert ids.shape[:2] == (G, nq)
+    k = ids.shape[2]
+    out = np.empty((nq, G, H, D))
+    B = np.empty((nq, G, H, D))
+    rc = lib().oracle_attention(_p(q), G * H * D, _p(kt), _p(vt), G * D, _p(ids), k, G, nq, H, D,
+                                n_kv, bs, k, _p(out), _p(B))
+    assert rc == 0
+    return out, B
+
+
+def check_attention(o_dev: np.ndarray, ref: np.ndarray, B: np.ndarray) -> CheckResult:
+    """Every output element within its bound (elements with B = 0 exactly)."""
+    return check_scores(np.asarray(o_dev, dtype=np.float64).reshape(-1, ref.shape[-1]),
+                        Scores(ref.reshape(-1, ref.shape[-1]), np.zeros(1), B.reshape(-1, ref.shape[-1]),
+                               np.zeros(1, np.int64)))
 
 
 # --------------------------------------------------------------------------

@@ -332,3 +332,114 @@ int oracle_block_keys(const uint16_t *k_tok, int64_t tok_stride, int32_t G, int3
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Attention over the selected blocks (the step after the phase).  The pages
+ * stop at the selection; the reading taken for the step that consumes it is
+ * plain softmax attention of every query head over the tokens of the blocks
+ * its (KV head, query) row selected:
+ *   s_j   = scale * sum_i q[t][g][h][i] * k[j][g][i],  scale = fp32(1/sqrt(D))
+ *   out   = sum_j exp(s_j - max s) v[j][g][:] / sum_j exp(s_j - max s)
+ * over every token j of every listed block (ids < 0 are empty slots; a row
+ * with no token gives 0).  Computed in float64 in plain order.
+ *
+ * Bound of a device result computed in fp32 with fp16 inputs (per output
+ * element, float64), for a device that sums each logit's D exact products
+ * in one fp32 chain, scales once, takes exp in fp32, and sums P*V and P per
+ * chunk of at most 64 tokens before adding the chunk into a running sum
+ * rescaled when the maximum grows:
+ *   delta = max_j ( scale*D*u*sum_i|q_i k_ji| + 2u*|s_j| + 4u*(1 + |s_j - max s|) )
+ *   E     = 2*delta + (2*(64 + C) + 16*C + 32)*u,   C = number of 64-token chunks
+ *   B     = E * (sum_j p_j |v_j| / sum_j p_j) + 2u*|out|,   u = 2^-24
+ * (logit errors move each weight by at most delta relatively, in the
+ * numerator and the denominator; each fp32 sum is a chain of at most
+ * 64 + C additions; each rescale and exp costs a few more roundings). */
+int oracle_attention(const uint16_t *q16, int64_t q_tok_stride, const uint16_t *k_tok,
+                     const uint16_t *v_tok, int64_t kv_tok_stride, const int32_t *ids,
+                     int64_t ld_ids, int32_t G, int32_t nq, int32_t H, int32_t D,
+                     int64_t n_kv, int32_t bs, int32_t k, double *out, double *bound)
+{
+    if (G < 0 || nq < 0 || H < 1 || D < 1 || n_kv < 0 || bs < 1 || k < 0 || ld_ids < k)
+        return 1;
+    const float scale_f = (float)(1.0 / sqrt((double)D));
+    const double scale = (double)scale_f;
+    const double u = ldexp(1.0, -24);
+    const int64_t nb = (n_kv + bs - 1) / bs;
+#pragma omp parallel
+    {
+        int64_t cap = (int64_t)k * bs;
+        int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)(cap > 0 ? cap : 1));
+        double *s = (double *)malloc(sizeof(double) * (size_t)(cap > 0 ? cap : 1));
+        double *sabs = (double *)malloc(sizeof(double) * (size_t)(cap > 0 ? cap : 1));
+        double *kv = (double *)malloc(sizeof(double) * (size_t)D);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < (int64_t)G * nq; ++r) {
+            const int64_t g = r / nq, t = r % nq;
+            /* the tokens of the listed blocks, block by block */
+            int64_t L = 0, chunks = 0;
+            for (int32_t slot = 0; slot < k; ++slot) {
+                int32_t b = ids[r * ld_ids + slot];
+                if (b < 0 || b >= nb)
+                    continue;
+                int64_t t0 = (int64_t)b * bs, t1 = t0 + bs < n_kv ? t0 + bs : n_kv;
+                chunks += (t1 - t0 + 63) / 64;
+                for (int64_t j = t0; j < t1; ++j)
+                    tok[L++] = j;
+            }
+            for (int32_t h = 0; h < H; ++h) {
+                const uint16_t *qh = q16 + t * q_tok_stride + ((int64_t)g * H + h) * D;
+                double *o = out + ((t * G + g) * H + h) * (int64_t)D;
+                double *bo = bound + ((t * G + g) * H + h) * (int64_t)D;
+                if (L == 0) {
+                    for (int32_t i = 0; i < D; ++i)
+                        o[i] = bo[i] = 0.0;
+                    continue;
+                }
+                double m = -INFINITY;
+                for (int64_t a = 0; a < L; ++a) {
+                    const uint16_t *kj = k_tok + tok[a] * kv_tok_stride + g * D;
+                    double d = 0.0, da = 0.0;
+                    for (int32_t i = 0; i < D; ++i) {
+                        double p = oracle_f16_to_f64(qh[i]) * oracle_f16_to_f64(kj[i]);
+                        d += p;
+                        da += fabs(p);
+                    }
+                    s[a] = scale * d;
+                    sabs[a] = scale * da;
+                    if (s[a] > m)
+                        m = s[a];
+                }
+                double den = 0.0, delta = 0.0;
+                for (int64_t a = 0; a < L; ++a) {
+                    /* sabs already holds scale * sum_i |q_i k_ji| */
+                    double e = sabs[a] * D * u + 2.0 * u * fabs(s[a]) + 4.0 * u * (1.0 + fabs(s[a] - m));
+                    if (e > delta)
+                        delta = e;
+                    s[a] = exp(s[a] - m);   /* weight p_a, reusing the logit slot */
+                    den += s[a];
+                }
+                const double E = 2.0 * delta + (2.0 * (64.0 + (double)chunks) + 16.0 * (double)chunks + 32.0) * u;
+                for (int32_t i = 0; i < D; ++i)
+                    o[i] = bo[i] = 0.0;
+                for (int64_t a = 0; a < L; ++a) {
+                    const uint16_t *vj = v_tok + tok[a] * kv_tok_stride + g * D;
+                    for (int32_t i = 0; i < D; ++i)
+                        kv[i] = oracle_f16_to_f64(vj[i]);
+                    for (int32_t i = 0; i < D; ++i) {
+                        o[i] += s[a] * kv[i];
+                        bo[i] += s[a] * fabs(kv[i]);
+                    }
+                }
+                for (int32_t i = 0; i < D; ++i) {
+                    o[i] /= den;
+                    bo[i] = E * (bo[i] / den) + 2.0 * u * fabs(o[i]);
+                }
+            }
+        }
+        free(tok);
+        free(s);
+        free(sabs);
+        free(kv);
+    }
+    return 0;
+}

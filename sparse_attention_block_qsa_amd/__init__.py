@@ -24,10 +24,11 @@ LIB_PATH = os.path.join(_HERE, "libqsa.so")
 QSA_OK, QSA_ERR_ARG, QSA_ERR_UNSUPPORTED, QSA_ERR_HIP, QSA_ERR_TOO_LARGE = 0, 1, 2, 3, 4
 MAX_K = 64
 NOALLOC_SCRATCH_BYTES = 64 << 20   # qsa.h QSA_NOALLOC_SCRATCH_BYTES
-ABI_VERSION = 4   # qsa.h QSA_ABI_VERSION this binding is written for
+ABI_VERSION = 5   # qsa.h QSA_ABI_VERSION this binding is written for
 BLOCK_KEYS_MAX_BS = 8192   # qsa.h QSA_BLOCK_KEYS_MAX_BS
 EXPORTS = ("qsa_abi_version", "qsa_status_string", "qsa_convert_f32_f16", "qsa_block_keys",
-           "qsa_block_scores", "qsa_select_topk", "qsa_select_phase", "qsa_select_phase_noalloc")
+           "qsa_block_scores", "qsa_select_topk", "qsa_select_phase", "qsa_select_phase_noalloc",
+           "qsa_sparse_attention")
 
 
 class QSAError(RuntimeError):
@@ -48,6 +49,9 @@ def _load() -> ctypes.CDLL:
     L.qsa_convert_f32_f16.restype = ctypes.c_int
     L.qsa_block_keys.argtypes = [vp, i64, vp, i64, i32, i32, i64, i32, vp]
     L.qsa_block_keys.restype = ctypes.c_int
+    L.qsa_sparse_attention.argtypes = [vp, i64, vp, vp, i64, vp, i64, vp, i64, i32, i32, i32, i32,
+                                       i64, i32, i32, vp]
+    L.qsa_sparse_attention.restype = ctypes.c_int
     L.qsa_block_scores.argtypes = [vp, i64, vp, i64, vp, i64, i32, i32, i32, i32, i64, i32, vp]
     L.qsa_block_scores.restype = ctypes.c_int
     L.qsa_select_topk.argtypes = [vp, i64, i64, i32, i32, vp, i64, vp, vp]
@@ -280,3 +284,33 @@ def select_phase_noalloc(q: torch.Tensor, kblk: torch.Tensor, n_kv: int, bs: int
                                         khs, _ptr(ids), ids.stride(1), _ptr(vals), G, nq, H, D,
                                         n_kv, bs, k, q_chunk, _stream(stream)))
     return (ids, vals) if vals is not None else ids
+
+
+def sparse_attention(q16: torch.Tensor, k_tok: torch.Tensor, v_tok: torch.Tensor,
+                     ids: torch.Tensor, n_kv: int, bs: int, out: torch.Tensor | None = None,
+                     stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """Attention of every query head over the tokens of its row's selected
+    blocks: q16 [nq, G, H, D] fp16, k_tok / v_tok [>= n_kv, G, D] fp16
+    (token-major), ids [G, nq, k] int32 (the selector's ids, -1 = empty).
+    Returns out [nq, G, H, D] float32."""
+    nq, G, H, D, qts = _check_q(q16, torch.float16)
+    for name, kv in (("k_tok", k_tok), ("v_tok", v_tok)):
+        if kv.dim() != 3 or kv.dtype != torch.float16 or not kv.is_cuda or kv.shape[0] < n_kv \
+                or tuple(kv.shape[1:]) != (G, D) or kv.stride(2) != 1 or kv.stride(1) != D:
+            raise ValueError(f"{name} must be float16 [>= n_kv, G, D] with (G, D) contiguous")
+    if k_tok.stride(0) != v_tok.stride(0):
+        raise ValueError("k_tok and v_tok must share their token stride")
+    if ids.dim() != 3 or ids.dtype != torch.int32 or tuple(ids.shape[:2]) != (G, nq) \
+            or ids.stride(2) != 1 or (nq > 1 and ids.stride(0) != nq * ids.stride(1)):
+        raise ValueError("ids must be int32 [G, nq, k] with rows at a common stride")
+    k = ids.shape[2]
+    if out is None:
+        out = torch.empty((nq, G, H, D), dtype=torch.float32, device=q16.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (nq, G, H, D) or out.stride(3) != 1 \
+            or out.stride(2) != D or out.stride(1) != H * D:
+        raise ValueError("out must be float32 [nq, G, H, D] with (G, H, D) contiguous")
+    _check("qsa_sparse_attention",
+           lib.qsa_sparse_attention(_ptr(q16), qts, _ptr(k_tok), _ptr(v_tok), k_tok.stride(0),
+                                    _ptr(ids), ids.stride(1), _ptr(out), out.stride(0), G, nq, H,
+                                    D, n_kv, bs, k, _stream(stream)))
+    return out

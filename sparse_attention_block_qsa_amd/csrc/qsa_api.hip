@@ -174,6 +174,41 @@ qsa_status qsa_block_keys(const uint16_t *k_tok, int64_t tok_stride, uint16_t *k
                                              bs, static_cast<hipStream_t>(stream)));
 }
 
+qsa_status qsa_sparse_attention(const uint16_t *q16, int64_t q_tok_stride, const uint16_t *k_tok,
+                                const uint16_t *v_tok, int64_t kv_tok_stride, const int32_t *ids,
+                                int64_t ld_ids, float *out, int64_t out_tok_stride, int32_t G,
+                                int32_t nq, int32_t H, int32_t D, int64_t n_kv, int32_t bs,
+                                int32_t k, void *stream) {
+    if (G < 0 || nq < 0 || n_kv < 0 || k < 0 || q_tok_stride < 0 || kv_tok_stride < 0 ||
+        ld_ids < 0 || out_tok_stride < 0)
+        return QSA_ERR_ARG;
+    if (bs < 1) return QSA_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return QSA_ERR_UNSUPPORTED;
+    if (H < 1 || H > 16) return QSA_ERR_UNSUPPORTED;
+    if (k > QSA_MAX_K) return QSA_ERR_UNSUPPORTED;
+    if (G == 0 || nq == 0) return QSA_OK;
+    if (!q16 || !out || (k > 0 && !ids)) return QSA_ERR_ARG;
+    if (n_kv > 0 && (!k_tok || !v_tok)) return QSA_ERR_ARG;
+    const int64_t row = static_cast<int64_t>(G) * H * D;
+    if (q_tok_stride < row || out_tok_stride < row) return QSA_ERR_ARG;
+    if (ld_ids < k) return QSA_ERR_ARG;
+    int64_t tmp;
+    if (!mad_ok(static_cast<int64_t>(nq) - 1, q_tok_stride, row, &tmp)) return QSA_ERR_ARG;
+    if (!mad_ok(static_cast<int64_t>(nq) - 1, out_tok_stride, row, &tmp)) return QSA_ERR_ARG;
+    if (!mad_ok(static_cast<int64_t>(G) * nq - 1, ld_ids, k, &tmp)) return QSA_ERR_ARG;
+    if (n_kv > 0) {
+        if (kv_tok_stride < static_cast<int64_t>(G) * D) return QSA_ERR_ARG;
+        if (!mad_ok(n_kv - 1, kv_tok_stride, static_cast<int64_t>(G) * D, &tmp)) return QSA_ERR_ARG;
+        if (!aligned16(k_tok) || !aligned16(v_tok) || kv_tok_stride % 8 != 0)
+            return QSA_ERR_UNSUPPORTED;
+    }
+    if (reinterpret_cast<uintptr_t>(q16) % 2 != 0 || !aligned4(out) || (ids && !aligned4(ids)))
+        return QSA_ERR_UNSUPPORTED;
+    return hip_status(qsa::launch_attention(q16, q_tok_stride, k_tok, v_tok, kv_tok_stride, ids,
+                                            ld_ids, out, out_tok_stride, G, nq, H, D, n_kv, bs, k,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 qsa_status qsa_select_phase(const float *q32, uint16_t *q16, int64_t q_tok_stride,
                             const uint16_t *kblk, int64_t kblk_head_stride, float *scores_ws,
                             int64_t ld_s, int32_t *ids, int64_t ld_ids, float *vals, int32_t G,

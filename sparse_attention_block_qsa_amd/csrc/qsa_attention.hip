@@ -1,0 +1,254 @@
+// qsa_attention.hip -- attention over the selected blocks: the step after
+// the select phase.
+//
+// The pages stop at the selection (Strata pull request #228, part 1: the
+// phase keeps, per query, the blocks whose score ranks in the top k).  The
+// reading taken for the step that consumes it is plain softmax attention of
+// every query head over the tokens of the blocks its (KV head, query) row
+// selected:
+//   s_j = scale * sum_i q[t][g][h][i] * k[j][g][i],   scale = fp32(1/sqrt(D))
+//   out[t][g][h][:] = sum_j exp(s_j - max) v[j][g][:] / sum_j exp(s_j - max)
+// with fp16 queries, keys and values and fp32 arithmetic.
+//
+// Mapping (decode and few-query shapes, where a row's tokens are gathered
+// from the KV cache): one workgroup of 8 waves per (KV head, query) row.  The
+// row's selected blocks are cut into chunks of at most 64 tokens; wave w
+// takes chunks w, w + 8, ...  Within a chunk lane l owns token l:
+//   * its key row is loaded into registers (16-byte loads) and its logit for
+//     every head is one fp32 fused multiply-add chain over the channels
+//     (fp16 key x fp32 query, exact products), the queries read from LDS as
+//     broadcasts;
+//   * each head's chunk maximum and sum come from wave reductions; the
+//     wave's running maximum, denominator and output are rescaled when the
+//     maximum grows (online softmax);
+//   * for the weighted sum lane l owns output channels, reads each token's
+//     weights from LDS (broadcast) and its value row with coalesced loads,
+//     and adds the chunk's sum into the running output.
+// The 8 waves' partial results are merged through LDS at the end.  Every sum
+// is a chain of at most 64 + (chunks) terms, which the oracle's bound
+// assumes.
+#include "qsa_internal.h"
+
+#include <math.h>
+
+namespace qsa {
+namespace {
+
+constexpr int kAttnWaves = 8;
+constexpr int kChunk = 64;
+
+struct AttnArgs {
+    const uint16_t *q16;
+    int64_t qts;
+    const uint16_t *k_tok, *v_tok;
+    int64_t kvts;
+    const int32_t *ids;
+    int64_t ld_ids;
+    float *out;
+    int64_t ots;
+    int32_t G, nq, H;
+    int64_t n_kv, nb;
+    int32_t bs, k;
+    float scale;
+};
+
+__device__ __forceinline__ float wave_max(float x) {
+    #pragma unroll
+    for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+    #pragma unroll
+    for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
+    return x;
+}
+
+__device__ __forceinline__ float f16_to_f32(uint32_t bits) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+}
+
+// HM: heads per row rounded up to a power of two (1, 2, 4, 8, 16).  Heads
+// past H carry zero queries: their logits and sums are computed and never
+// stored, so every per-head loop is unrolled without branches and the
+// per-head state stays in registers.
+template <int D, int HM>
+__global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(AttnArgs a) {
+    constexpr int CPL = D / 64;   // output channels per lane (1 or 2)
+    __shared__ float4 qs[HM][D / 4];
+    __shared__ float ps[kAttnWaves][kChunk][HM];          // this chunk's weights
+    __shared__ float red_m[kAttnWaves][HM], red_l[kAttnWaves][HM];
+    __shared__ float red_o[kAttnWaves][HM][D];
+
+    const int H = a.H;
+    const int64_t row = blockIdx.x;                 // r = g * nq + t
+    const int64_t g = row / a.nq, t = row % a.nq;
+    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+
+    // queries of this row, fp16 -> fp32, into LDS (zero past H)
+    for (int e = threadIdx.x; e < HM * D; e += 64 * kAttnWaves) {
+        const int h = e / D, i = e % D;
+        reinterpret_cast<float *>(&qs[h][0])[i] =
+            h < H ? f16_to_f32(a.q16[t * a.qts + (g * H + h) * D + i]) : 0.0f;
+    }
+    __syncthreads();
+
+    float m[HM], l[HM], acc[HM][CPL];
+    #pragma unroll
+    for (int h = 0; h < HM; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.0f;
+        #pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[h][c] = 0.0f;
+    }
+
+    const uint16_t *kg = a.k_tok + g * D;
+    const uint16_t *vg = a.v_tok + g * D;
+    int chunk = 0;   // index of the chunk over the row's selected blocks
+    for (int slot = 0; slot < a.k; ++slot) {
+        const int b = a.ids[row * a.ld_ids + slot];   // uniform
+        if (b < 0 || b >= a.nb) continue;
+        const int64_t tb = static_cast<int64_t>(b) * a.bs;
+        const int64_t te = min(tb + a.bs, a.n_kv);
+        for (int64_t c0 = tb; c0 < te; c0 += kChunk, ++chunk) {
+            if (chunk % kAttnWaves != w) continue;
+            const int n = static_cast<int>(min(static_cast<int64_t>(kChunk), te - c0));
+            // 1. logits of this lane's token (c0 + lane) for every head: one
+            //    fp32 fma chain per head over the channels in ascending order
+            const bool valid = lane < n;
+            const uint4 *krow = reinterpret_cast<const uint4 *>(kg + (c0 + (valid ? lane : 0)) * a.kvts);
+            float s[HM];
+            #pragma unroll
+            for (int h = 0; h < HM; ++h) s[h] = 0.0f;
+            uint4 kr[D / 8];   // the whole key row in flight at once
+            #pragma unroll
+            for (int u = 0; u < D / 8; ++u) kr[u] = krow[u];
+            #pragma unroll
+            for (int u = 0; u < D / 8; ++u) {
+                // keep each step's query reads in its step: hoisted, the
+                // reads of every step would need HM*D registers
+                __builtin_amdgcn_sched_barrier(0);
+                const uint4 kq = kr[u];
+                const uint32_t kw[4] = {kq.x, kq.y, kq.z, kq.w};
+                float kf[8];
+                #pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    kf[2 * e] = f16_to_f32(kw[e] & 0xffffu);
+                    kf[2 * e + 1] = f16_to_f32(kw[e] >> 16);
+                }
+                #pragma unroll
+                for (int h = 0; h < HM; ++h) {
+                    const float4 q0 = qs[h][2 * u], q1 = qs[h][2 * u + 1];
+                    s[h] = __builtin_fmaf(kf[0], q0.x, s[h]);
+                    s[h] = __builtin_fmaf(kf[1], q0.y, s[h]);
+                    s[h] = __builtin_fmaf(kf[2], q0.z, s[h]);
+                    s[h] = __builtin_fmaf(kf[3], q0.w, s[h]);
+                    s[h] = __builtin_fmaf(kf[4], q1.x, s[h]);
+                    s[h] = __builtin_fmaf(kf[5], q1.y, s[h]);
+                    s[h] = __builtin_fmaf(kf[6], q1.z, s[h]);
+                    s[h] = __builtin_fmaf(kf[7], q1.w, s[h]);
+                }
+            }
+            // 2. weights and the running state of every head
+            #pragma unroll
+            for (int h = 0; h < HM; ++h) {
+                const float x = valid ? s[h] * a.scale : -INFINITY;
+                const float mn = fmaxf(m[h], wave_max(x));
+                const float p = valid ? expf(x - mn) : 0.0f;
+                const float alpha = expf(m[h] - mn);   // 0 on the first chunk (m = -inf)
+                l[h] = l[h] * alpha + wave_sum(p);
+                m[h] = mn;
+                ps[w][lane][h] = p;
+                #pragma unroll
+                for (int c = 0; c < CPL; ++c) acc[h][c] *= alpha;
+            }
+            // 3. this chunk's weighted values (lane l owns channels CPL*l..),
+            //    added into the running output
+            float cs[HM][CPL];
+            #pragma unroll
+            for (int h = 0; h < HM; ++h) {
+                #pragma unroll
+                for (int c = 0; c < CPL; ++c) cs[h][c] = 0.0f;
+            }
+            for (int j = 0; j < n; ++j) {
+                const uint16_t *vrow = vg + (c0 + j) * a.kvts + CPL * lane;
+                float v[CPL];
+                if constexpr (CPL == 2) {
+                    const uint32_t vw = *reinterpret_cast<const uint32_t *>(vrow);
+                    v[0] = f16_to_f32(vw & 0xffffu);
+                    v[1] = f16_to_f32(vw >> 16);
+                } else {
+                    v[0] = f16_to_f32(*vrow);
+                }
+                #pragma unroll
+                for (int h = 0; h < HM; ++h) {
+                    const float p = ps[w][j][h];
+                    #pragma unroll
+                    for (int c = 0; c < CPL; ++c) cs[h][c] = __builtin_fmaf(p, v[c], cs[h][c]);
+                }
+            }
+            #pragma unroll
+            for (int h = 0; h < HM; ++h) {
+                #pragma unroll
+                for (int c = 0; c < CPL; ++c) acc[h][c] += cs[h][c];
+            }
+        }
+    }
+
+    // 4. merge the waves' partial results
+    #pragma unroll
+    for (int h = 0; h < HM; ++h) {
+        if (lane == 0) {
+            red_m[w][h] = m[h];
+            red_l[w][h] = l[h];
+        }
+        #pragma unroll
+        for (int c = 0; c < CPL; ++c) red_o[w][h][CPL * lane + c] = acc[h][c];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < H * D; e += 64 * kAttnWaves) {
+        const int h = e / D, i = e % D;
+        float M = -INFINITY;
+        #pragma unroll
+        for (int v = 0; v < kAttnWaves; ++v) M = fmaxf(M, red_m[v][h]);
+        float num = 0.0f, den = 0.0f;
+        if (M != -INFINITY) {
+            #pragma unroll
+            for (int v = 0; v < kAttnWaves; ++v) {
+                const float f = red_m[v][h] == -INFINITY ? 0.0f : expf(red_m[v][h] - M);
+                num = __builtin_fmaf(red_o[v][h][i], f, num);
+                den = __builtin_fmaf(red_l[v][h], f, den);
+            }
+        }
+        a.out[t * a.ots + (g * H + h) * D + i] = den > 0.0f ? num / den : 0.0f;
+    }
+}
+
+template <int D>
+void (*pick_attention(int H))(AttnArgs) {
+    if (H <= 1) return attention_kernel<D, 1>;
+    if (H <= 2) return attention_kernel<D, 2>;
+    if (H <= 4) return attention_kernel<D, 4>;
+    if (H <= 8) return attention_kernel<D, 8>;
+    return attention_kernel<D, 16>;
+}
+
+}  // namespace
+
+hipError_t launch_attention(const uint16_t *q16, int64_t qts, const uint16_t *k_tok,
+                            const uint16_t *v_tok, int64_t kvts, const int32_t *ids, int64_t ld_ids,
+                            float *out, int64_t ots, int32_t G, int32_t nq, int32_t H, int32_t D,
+                            int64_t n_kv, int32_t bs, int32_t k, hipStream_t s) {
+    const int64_t rows = static_cast<int64_t>(G) * nq;
+    if (rows <= 0) return hipSuccess;
+    if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    AttnArgs a{q16, qts, k_tok, v_tok, kvts, ids, ld_ids, out, ots, G, nq, H,
+               n_kv, n_kv / bs + (n_kv % bs != 0), bs, k,
+               static_cast<float>(1.0 / sqrt(static_cast<double>(D)))};
+    void (*fn)(AttnArgs) = D == 128 ? pick_attention<128>(H) : pick_attention<64>(H);
+    hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(rows)), dim3(64 * kAttnWaves), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace qsa

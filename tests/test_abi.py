@@ -42,6 +42,8 @@ def lib():
     L.qsa_select_phase_noalloc.argtypes = [vp, vp, i64, vp, i64, vp, i64, vp, i32, i32, i32,
                                            i32, i64, i32, i32, i64, vp]
     L.qsa_block_keys.argtypes = [vp, i64, vp, i64, i32, i32, i64, i32, vp]
+    L.qsa_sparse_attention.argtypes = [vp, i64, vp, vp, i64, vp, i64, vp, i64, i32, i32, i32,
+                                       i32, i64, i32, i32, vp]
     L.qsa_status_string.argtypes = [ctypes.c_int]
     L.qsa_status_string.restype = ctypes.c_char_p
     return L
@@ -50,7 +52,8 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["qsa_abi_version", "qsa_status_string", "qsa_convert_f32_f16", "qsa_block_keys",
-         "qsa_block_scores", "qsa_select_topk", "qsa_select_phase", "qsa_select_phase_noalloc"])
+         "qsa_block_scores", "qsa_select_topk", "qsa_select_phase", "qsa_select_phase_noalloc",
+         "qsa_sparse_attention"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -201,3 +204,31 @@ def test_block_keys_refusals(lib, kw, want):
 @pytest.mark.parametrize("kw", [dict(G=0), dict(n_kv=0), dict(n_kv=0, k=None, kb=None)])
 def test_block_keys_empty_is_ok_without_launch(lib, kw):
     assert keys_call(lib, **kw) == OK
+
+
+def attn_call(lib, **kw):
+    a = dict(q=A16, qts=8 * 128, k=A16, v=A16, kvts=128, ids=A16, ld=64, out=A16, ots=8 * 128,
+             G=1, nq=256, H=8, D=128, n_kv=131072, bs=64, kk=64)
+    a.update(kw)
+    return lib.qsa_sparse_attention(a["q"], a["qts"], a["k"], a["v"], a["kvts"], a["ids"], a["ld"],
+                                    a["out"], a["ots"], a["G"], a["nq"], a["H"], a["D"],
+                                    a["n_kv"], a["bs"], a["kk"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(G=-1), ARG), (dict(nq=-1), ARG), (dict(n_kv=-1), ARG), (dict(kk=-1), ARG),
+    (dict(bs=0), UNSUP), (dict(D=96), UNSUP), (dict(H=0), UNSUP), (dict(H=17), UNSUP),
+    (dict(kk=65, ld=65), UNSUP), (dict(q=None), ARG), (dict(out=None), ARG), (dict(ids=None), ARG),
+    (dict(k=None), ARG), (dict(v=None), ARG), (dict(qts=8 * 128 - 1), ARG),
+    (dict(ots=8 * 128 - 1), ARG), (dict(ld=63), ARG), (dict(kvts=127), ARG),
+    (dict(k=A16 + 2), UNSUP), (dict(v=A16 + 8), UNSUP), (dict(kvts=132), UNSUP),
+    (dict(q=A16 + 1), UNSUP), (dict(out=A16 + 2), UNSUP), (dict(ids=A16 + 2), UNSUP),
+    (dict(ots=1 << 60), ARG),
+])
+def test_sparse_attention_refusals(lib, kw, want):
+    assert attn_call(lib, **kw) == want
+
+
+def test_sparse_attention_empty_is_ok_without_launch(lib):
+    assert attn_call(lib, nq=0) == OK
+    assert attn_call(lib, G=0) == OK

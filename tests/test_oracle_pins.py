@@ -731,3 +731,132 @@ def test_block_keys_closed_forms():
     got = oracle.block_keys(qi.f64_to_f16_bits(ints), 11, 8)
     assert got[0, :, 0].view(np.float16).tolist() == [4.5, 5.0]
     assert got[0, :, 1].tolist() == [0, 0]
+
+
+# --------------------------------------------------------------------------
+# attention over the selected blocks (the step after the selection)
+# --------------------------------------------------------------------------
+
+def _attn_case(seed, nq=5, G=2, H=3, D=64, n_kv=64 * 6 + 9, bs=64, k=4, scale_v=1.0):
+    rng = np.random.default_rng(seed)
+    q16 = qi.f64_to_f16_bits(rng.standard_normal((nq, G, H, D)) * 0.5)
+    kt = qi.f64_to_f16_bits(rng.standard_normal((n_kv, G, D)) * 0.5)
+    vt = qi.f64_to_f16_bits(rng.standard_normal((n_kv, G, D)) * scale_v)
+    nb = -(-n_kv // bs)
+    ids = np.full((G, nq, k), -1, np.int32)
+    for g in range(G):
+        for t in range(nq):
+            sel = rng.permutation(nb)[:min(k, nb)]
+            ids[g, t, :sel.size] = sel
+            if t == 1:
+                ids[g, t, 1] = -1           # an empty slot in the middle
+    return q16, kt, vt, ids, n_kv, bs
+
+
+def _numpy_attention(q16, kt, vt, ids, n_kv, bs):
+    """Dense float64 attention with numpy over an explicit token list."""
+    nq, G, H, D = q16.shape
+    Q = q16.view(np.float16).astype(np.float64)
+    K = kt.view(np.float16).astype(np.float64)
+    V = vt.view(np.float16).astype(np.float64)
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    out = np.zeros((nq, G, H, D))
+    for g in range(G):
+        for t in range(nq):
+            toks = [j for b in ids[g, t] if b >= 0 for j in range(b * bs, min((b + 1) * bs, n_kv))]
+            if not toks:
+                continue
+            s = Q[t, g] @ K[toks, g].T * scale          # [H, L]
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            out[t, g] = (p @ V[toks, g]) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+def test_attention_vs_numpy_dense():
+    case = _attn_case(41)
+    out, B = oracle.attention(*case)
+    want = _numpy_attention(*case)
+    assert np.allclose(out, want, rtol=1e-12, atol=1e-14)
+    assert np.all(B > 0)
+
+
+def test_attention_closed_forms():
+    q16, kt, vt, ids, n_kv, bs = _attn_case(42)
+    # one selected token (a one-token tail block): the output is that value row
+    n1 = 64 * 3 + 1
+    one = np.full_like(ids, -1)
+    one[:, :, 0] = 3                      # the tail block holds only token 192
+    out, _ = oracle.attention(q16, kt[:n1], vt[:n1], one, n1, bs)
+    V = vt.view(np.float16).astype(np.float64)
+    for g in range(ids.shape[0]):
+        assert np.array_equal(out[:, g], np.broadcast_to(V[192, g], out[:, g].shape))
+    # zero queries: equal weights, the output is the mean of the selected values
+    out, _ = oracle.attention(np.zeros_like(q16), kt, vt, ids, n_kv, bs)
+    for g in range(ids.shape[0]):
+        for t in range(q16.shape[0]):
+            toks = [j for b in ids[g, t] if b >= 0 for j in range(b * bs, min((b + 1) * bs, n_kv))]
+            assert np.allclose(out[t, g], V[toks, g].mean(axis=0), rtol=1e-12, atol=1e-15)
+    # no selected block: zeros
+    out, B = oracle.attention(q16, kt, vt, np.full_like(ids, -1), n_kv, bs)
+    assert np.all(out == 0) and np.all(B == 0)
+
+
+def test_attention_invariants():
+    q16, kt, vt, ids, n_kv, bs = _attn_case(43)
+    out, _ = oracle.attention(q16, kt, vt, ids, n_kv, bs)
+    # the order of the selected ids does not matter
+    perm = ids[:, :, ::-1].copy()
+    outp, _ = oracle.attention(q16, kt, vt, perm, n_kv, bs)
+    assert np.allclose(outp, out, rtol=1e-13, atol=1e-15)
+    # values x2 -> output x2 exactly (every operation scales exactly)
+    v2 = qi.f64_to_f16_bits(vt.view(np.float16).astype(np.float64) * 2)
+    out2, _ = oracle.attention(q16, kt, v2, ids, n_kv, bs)
+    assert np.array_equal(out2, out * 2)
+
+
+def _fp32_device_model(q16, kt, vt, ids, n_kv, bs, no_rescale=False, drop_last=False,
+                       scale_1_over_d=False):
+    """The device's algorithm in numpy float32: per row and head, chunks of
+    up to 64 tokens in id order, a running maximum, chunk sums of P*V and P
+    added into rescaled running sums."""
+    nq, G, H, D = q16.shape
+    Q = q16.view(np.float16).astype(np.float32)
+    K = kt.view(np.float16).astype(np.float32)
+    V = vt.view(np.float16).astype(np.float32)
+    scale = np.float32(1.0 / D if scale_1_over_d else 1.0 / math.sqrt(D))
+    out = np.zeros((nq, G, H, D), np.float32)
+    for g in range(G):
+        for t in range(nq):
+            toks = [j for b in ids[g, t] if b >= 0 for j in range(b * bs, min((b + 1) * bs, n_kv))]
+            if drop_last:
+                toks = toks[:-1]
+            if not toks:
+                continue
+            m = np.full(H, -np.inf, np.float32)
+            acc = np.zeros((H, D), np.float32)
+            den = np.zeros(H, np.float32)
+            for c0 in range(0, len(toks), 64):
+                ch = toks[c0:c0 + 64]
+                s = np.einsum("hi,ji->hj", Q[t, g], K[ch, g]).astype(np.float32) * scale
+                mn = np.maximum(m, s.max(axis=1))
+                a = np.exp((m - mn).astype(np.float32)).astype(np.float32)
+                p = np.exp((s - mn[:, None]).astype(np.float32)).astype(np.float32)
+                if no_rescale:   # the running sums kept at the old maximum's scale
+                    a = np.ones_like(a)
+                acc = acc * a[:, None] + (p @ V[ch, g]).astype(np.float32)
+                den = den * a + p.sum(axis=1, dtype=np.float32)
+                m = mn
+            out[t, g] = acc / den[:, None]
+    return out
+
+
+def test_attention_bound_admits_fp32_model_and_rejects_mistakes():
+    case = _attn_case(44, nq=4, G=2, H=4, D=128, n_kv=64 * 40 + 17, k=24)
+    ref, B = oracle.attention(*case)
+    good = _fp32_device_model(*case)
+    res = oracle.check_attention(good, ref, B)
+    assert res.ok, str(res)
+    for kw in (dict(no_rescale=True), dict(drop_last=True), dict(scale_1_over_d=True)):
+        bad = _fp32_device_model(*case, **kw)
+        assert not oracle.check_attention(bad, ref, B).ok, kw
+    assert not oracle.check_attention(ref + 2.5 * B, ref, B).ok
