@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 METRIC = "QSA select ms + scorer TFLOP/s (fraction of FP16 MFMA peak), nq=256 @128K"
 PEAK_FP16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense fp16 FLOP/clk/CU (published 2.5 PF)
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_TFLOPS = 157.3       # dense fp32 vector (published)
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -49,6 +50,8 @@ def parse():
                    help="steps per point of the nq = 256 context sweep, 1K-128K keys (0: skip)")
     p.add_argument("--config-steps", type=int, default=100,
                    help="steps for each of the other nq = 256 / tiny configurations (0: skip)")
+    p.add_argument("--beside-steps", type=int, default=50,
+                   help="launches per timing of block-key construction and attention (0: skip)")
     p.add_argument("--no-peaks", action="store_true",
                    help="skip the measured MFMA and HBM-read ceilings")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -457,6 +460,76 @@ def measure(cfg, qsa, torch, steps, warmup, w=None, calls_100=False):
     }
 
 
+def _time_launches(torch, fn, n) -> float:
+    """ms per launch of a graph of n back-to-back launches (after 3 eager)."""
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    g = graph_of(torch, fn, n)
+    ms = time_graph(torch, g, n)
+    del g
+    return ms
+
+
+def measure_beside(qsa, torch, n, peaks) -> dict:
+    """The block keys of the full-prefill chunk built from token keys
+    (HBM-bound: 2*D bytes per token and KV head read, 2*D per block written)
+    and attention over the selection phase's ids at nq = 256 with 128K keys
+    and at the decode step (per row k*bs tokens gathered: 4*D bytes of keys
+    and values per token and KV head; 4*D FLOP per token and query head)."""
+    import numpy as np
+    import qsa_inputs as qi
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(9)
+    out = {}
+    pc = qi.PREFILL
+    kt = torch.from_numpy(qi.f64_to_f16_bits(rng.standard_normal((pc.n_kv, pc.G, pc.D))
+                                             / np.sqrt(pc.D)).view(np.float16)).to(dev)
+    kb = torch.empty((pc.G, pc.nb, pc.D), dtype=torch.float16, device=dev)
+    qsa.block_keys(kt, pc.n_kv, pc.bs, out=kb)
+    L = qsa.lib
+    args = (qsa._ptr(kt), kt.stride(0), qsa._ptr(kb), kb.stride(0), pc.G, pc.D, pc.n_kv, pc.bs)
+    ms = _time_launches(torch, lambda: L.qsa_block_keys(*args, qsa._stream(None)), n)
+    nbytes = 2.0 * pc.D * pc.G * (pc.n_kv + pc.nb)
+    out["block_keys"] = {"workload": pc.name, "us": ms * 1e3, "bytes": nbytes,
+                         "gbs": nbytes / (ms * 1e-3) / 1e9,
+                         "frac_of_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "frac_of_measured_read": (nbytes / (ms * 1e-3) / 1e9 / peaks["hbm_read_gbs"]
+                                                   if peaks else None)}
+    del kt, kb
+    out["attention"] = {}
+    for cfg in (qi.HEADLINE, qi.DECODE):
+        w = qi.make(cfg)
+        q16 = torch.from_numpy(w.q16.view(np.float16)).to(dev)
+        kv = [torch.from_numpy(qi.f64_to_f16_bits(rng.standard_normal((cfg.n_kv, cfg.G, cfg.D)))
+                               .view(np.float16)).to(dev) for _ in range(2)]
+        ws = qsa.PhaseWorkspace(cfg.nq, cfg.G, cfg.H, cfg.D, cfg.n_kv, cfg.bs, cfg.k, dev)
+        ids = qsa.select_phase(torch.from_numpy(w.q32).to(dev),
+                               torch.from_numpy(w.kblk.view(np.float16)).to(dev), cfg.n_kv, cfg.bs,
+                               cfg.k, ws)
+        o = qsa.sparse_attention(q16, kv[0], kv[1], ids, cfg.n_kv, cfg.bs, ws=None)
+        aws = qsa.attention_workspace(cfg.G, cfg.nq, cfg.H, cfg.D, cfg.bs, cfg.k, dev)
+        torch.cuda.synchronize()
+        ids_np = ids.cpu().numpy()
+        nb = cfg.nb
+        toks = sum(min(cfg.bs, cfg.n_kv - int(b) * cfg.bs) for b in ids_np.ravel() if 0 <= b < nb)
+        a = (qsa._ptr(q16), cfg.G * cfg.H * cfg.D, qsa._ptr(kv[0]), qsa._ptr(kv[1]), cfg.G * cfg.D,
+             qsa._ptr(ids), cfg.k, qsa._ptr(o), cfg.G * cfg.H * cfg.D, cfg.G, cfg.nq, cfg.H, cfg.D,
+             cfg.n_kv, cfg.bs, cfg.k, qsa._ptr(aws), 0 if aws is None else aws.numel())
+        ms = _time_launches(torch, lambda: L.qsa_sparse_attention(*a, qsa._stream(None)), n)
+        flop = 4.0 * toks * cfg.H * cfg.D
+        gathered = 4.0 * toks * cfg.D
+        out["attention"][cfg.name] = {
+            "us": ms * 1e3, "tokens_attended": toks, "flop": flop,
+            "tflops": flop / (ms * 1e-3) / 1e12,
+            "frac_of_fp32_vector_peak": flop / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
+            "gathered_bytes": gathered, "gathered_gbs": gathered / (ms * 1e-3) / 1e9,
+            "workgroups_per_row": (aws.numel() // (cfg.rows * cfg.H * (2 + cfg.D))
+                                   if aws is not None else 1)}
+        del q16, kv, ws, ids, o, aws
+    return out
+
+
 def config_summary(cfg, r) -> dict:
     """One workload reported the way the headline is."""
     st, al = r["stages_ms"], r["entry_points_ms"]
@@ -677,6 +750,16 @@ def main():
                   f"{sweep[-1]['scorer_us']:.2f} us, topk {sweep[-1]['topk_us']:.2f} us",
                   file=sys.stderr, flush=True)
 
+    # the steps beside the phase: block keys built from token keys (the step
+    # before) and attention over the selected blocks (the step after)
+    beside = None
+    if args.beside_steps > 0:
+        beside = measure_beside(qsa, torch, args.beside_steps, peaks)
+        print(f"# block keys {beside['block_keys']['us']:.1f} us "
+              f"({beside['block_keys']['gbs']:.0f} GB/s); attention "
+              + ", ".join(f"{k} {v['us']:.1f} us" for k, v in beside["attention"].items()),
+              file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -727,6 +810,7 @@ def main():
         "full_prefill": prefill,
         "decode": decode,
         "context_sweep": sweep,
+        "beside_the_phase": beside,
         "source_digest": source_digest(),
         "context": {"pages_rx7900xtx_gfx1100_scores_ms_128k": {"warp": 2.627, "wmma": 0.252},
                     "note": "other hardware; context only"},

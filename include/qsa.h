@@ -183,14 +183,26 @@ qsa_status qsa_block_keys(const uint16_t *k_tok, int64_t tok_stride, uint16_t *k
  *   out        device fp32, element (t, g, h, i) at
  *              [t * out_tok_stride + (g*H + h) * D + i], out_tok_stride >= G*H*D;
  *              written: exactly those G*H*D elements of each of the nq rows
+ *   ws         device fp32 workspace of ws_floats floats, or NULL.  With
+ *              few rows (a decode step) each row is split over several
+ *              workgroups whose partial results a second launch merges, if
+ *              ws holds qsa_sparse_attention_ws_floats() floats (a smaller ws
+ *              splits less; NULL: one workgroup per row).  Contents on
+ *              return are unspecified; must not overlap the other buffers.
  *   G, nq >= 0; H in [1, 16]; D in {64, 128}; n_kv >= 0; bs >= 1; 0 <= k <= 64
- * nq == 0 or G == 0: QSA_OK, nothing written.
+ * nq == 0 or G == 0: QSA_OK, nothing written.  The results do not depend on
+ * ws beyond fp32 rounding (the order of the partial sums).
  */
 qsa_status qsa_sparse_attention(const uint16_t *q16, int64_t q_tok_stride, const uint16_t *k_tok,
                                 const uint16_t *v_tok, int64_t kv_tok_stride, const int32_t *ids,
                                 int64_t ld_ids, float *out, int64_t out_tok_stride, int32_t G,
                                 int32_t nq, int32_t H, int32_t D, int64_t n_kv, int32_t bs,
-                                int32_t k, void *stream);
+                                int32_t k, float *ws, int64_t ws_floats, void *stream);
+
+/* Floats of workspace qsa_sparse_attention splits its rows with for this
+ * geometry (0: it would not split them). */
+int64_t qsa_sparse_attention_ws_floats(int32_t G, int32_t nq, int32_t H, int32_t D, int32_t bs,
+                                       int32_t k);
 
 /*
  * qsa_select_phase -- the whole phase on one stream: convert (when q32 is

@@ -28,7 +28,7 @@ ABI_VERSION = 5   # qsa.h QSA_ABI_VERSION this binding is written for
 BLOCK_KEYS_MAX_BS = 8192   # qsa.h QSA_BLOCK_KEYS_MAX_BS
 EXPORTS = ("qsa_abi_version", "qsa_status_string", "qsa_convert_f32_f16", "qsa_block_keys",
            "qsa_block_scores", "qsa_select_topk", "qsa_select_phase", "qsa_select_phase_noalloc",
-           "qsa_sparse_attention")
+           "qsa_sparse_attention", "qsa_sparse_attention_ws_floats")
 
 
 class QSAError(RuntimeError):
@@ -50,8 +50,10 @@ def _load() -> ctypes.CDLL:
     L.qsa_block_keys.argtypes = [vp, i64, vp, i64, i32, i32, i64, i32, vp]
     L.qsa_block_keys.restype = ctypes.c_int
     L.qsa_sparse_attention.argtypes = [vp, i64, vp, vp, i64, vp, i64, vp, i64, i32, i32, i32, i32,
-                                       i64, i32, i32, vp]
+                                       i64, i32, i32, vp, i64, vp]
     L.qsa_sparse_attention.restype = ctypes.c_int
+    L.qsa_sparse_attention_ws_floats.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.qsa_sparse_attention_ws_floats.restype = ctypes.c_int64
     L.qsa_block_scores.argtypes = [vp, i64, vp, i64, vp, i64, i32, i32, i32, i32, i64, i32, vp]
     L.qsa_block_scores.restype = ctypes.c_int
     L.qsa_select_topk.argtypes = [vp, i64, i64, i32, i32, vp, i64, vp, vp]
@@ -286,13 +288,23 @@ def select_phase_noalloc(q: torch.Tensor, kblk: torch.Tensor, n_kv: int, bs: int
     return (ids, vals) if vals is not None else ids
 
 
+def attention_workspace(G: int, nq: int, H: int, D: int, bs: int, k: int,
+                        device="cuda") -> torch.Tensor | None:
+    """The workspace that lets sparse_attention split few rows over several
+    workgroups (None when it would not split them)."""
+    n = lib.qsa_sparse_attention_ws_floats(G, nq, H, D, bs, k)
+    return torch.empty(n, dtype=torch.float32, device=device) if n > 0 else None
+
+
 def sparse_attention(q16: torch.Tensor, k_tok: torch.Tensor, v_tok: torch.Tensor,
                      ids: torch.Tensor, n_kv: int, bs: int, out: torch.Tensor | None = None,
+                     ws: torch.Tensor | None | bool = True,
                      stream: torch.cuda.Stream | None = None) -> torch.Tensor:
     """Attention of every query head over the tokens of its row's selected
     blocks: q16 [nq, G, H, D] fp16, k_tok / v_tok [>= n_kv, G, D] fp16
     (token-major), ids [G, nq, k] int32 (the selector's ids, -1 = empty).
-    Returns out [nq, G, H, D] float32."""
+    ws: a workspace tensor, None (no row splitting) or True (allocate the
+    one attention_workspace gives).  Returns out [nq, G, H, D] float32."""
     nq, G, H, D, qts = _check_q(q16, torch.float16)
     for name, kv in (("k_tok", k_tok), ("v_tok", v_tok)):
         if kv.dim() != 3 or kv.dtype != torch.float16 or not kv.is_cuda or kv.shape[0] < n_kv \
@@ -309,8 +321,13 @@ def sparse_attention(q16: torch.Tensor, k_tok: torch.Tensor, v_tok: torch.Tensor
     if out.dtype != torch.float32 or tuple(out.shape) != (nq, G, H, D) or out.stride(3) != 1 \
             or out.stride(2) != D or out.stride(1) != H * D:
         raise ValueError("out must be float32 [nq, G, H, D] with (G, H, D) contiguous")
+    if ws is True:
+        ws = attention_workspace(G, nq, H, D, bs, k, q16.device)
+    if ws is not None and (ws.dtype != torch.float32 or not ws.is_contiguous()):
+        raise ValueError("ws must be a contiguous float32 tensor")
     _check("qsa_sparse_attention",
            lib.qsa_sparse_attention(_ptr(q16), qts, _ptr(k_tok), _ptr(v_tok), k_tok.stride(0),
                                     _ptr(ids), ids.stride(1), _ptr(out), out.stride(0), G, nq, H,
-                                    D, n_kv, bs, k, _stream(stream)))
+                                    D, n_kv, bs, k, _ptr(ws), 0 if ws is None else ws.numel(),
+                                    _stream(stream)))
     return out

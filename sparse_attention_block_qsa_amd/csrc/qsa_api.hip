@@ -21,6 +21,18 @@ bool src32_ok(const float *q32, int64_t qts) {
     return reinterpret_cast<uintptr_t>(q32) % 16 == 0 && qts % 4 == 0;
 }
 
+// Workgroups per (KV head, query) row of the attention when a workspace is
+// given: enough for about four workgroups per CU over all rows, but no more
+// than give each of a workgroup's 8 waves one 64-token chunk, and at most 64.
+int64_t attention_splits(int64_t rows, int32_t bs, int32_t k) {
+    const int64_t chunks = static_cast<int64_t>(k) * ((static_cast<int64_t>(bs) + 63) / 64);
+    int64_t sp = (1024 + rows - 1) / rows;
+    const int64_t by_chunks = (chunks + 7) / 8;
+    if (sp > by_chunks) sp = by_chunks;
+    if (sp > 64) sp = 64;
+    return sp < 1 ? 1 : sp;
+}
+
 }  // namespace qsa
 
 namespace {
@@ -174,13 +186,23 @@ qsa_status qsa_block_keys(const uint16_t *k_tok, int64_t tok_stride, uint16_t *k
                                              bs, static_cast<hipStream_t>(stream)));
 }
 
+int64_t qsa_sparse_attention_ws_floats(int32_t G, int32_t nq, int32_t H, int32_t D, int32_t bs,
+                                       int32_t k) {
+    if (G <= 0 || nq <= 0 || H < 1 || H > 16 || (D != 64 && D != 128) || bs < 1 || k < 1 ||
+        k > QSA_MAX_K)
+        return 0;
+    const int64_t rows = static_cast<int64_t>(G) * nq;
+    const int64_t sp = qsa::attention_splits(rows, bs, k);
+    return sp > 1 ? sp * rows * H * (2 + D) : 0;
+}
+
 qsa_status qsa_sparse_attention(const uint16_t *q16, int64_t q_tok_stride, const uint16_t *k_tok,
                                 const uint16_t *v_tok, int64_t kv_tok_stride, const int32_t *ids,
                                 int64_t ld_ids, float *out, int64_t out_tok_stride, int32_t G,
                                 int32_t nq, int32_t H, int32_t D, int64_t n_kv, int32_t bs,
-                                int32_t k, void *stream) {
+                                int32_t k, float *ws, int64_t ws_floats, void *stream) {
     if (G < 0 || nq < 0 || n_kv < 0 || k < 0 || q_tok_stride < 0 || kv_tok_stride < 0 ||
-        ld_ids < 0 || out_tok_stride < 0)
+        ld_ids < 0 || out_tok_stride < 0 || ws_floats < 0)
         return QSA_ERR_ARG;
     if (bs < 1) return QSA_ERR_UNSUPPORTED;
     if (D != 64 && D != 128) return QSA_ERR_UNSUPPORTED;
@@ -202,10 +224,12 @@ qsa_status qsa_sparse_attention(const uint16_t *q16, int64_t q_tok_stride, const
         if (!aligned16(k_tok) || !aligned16(v_tok) || kv_tok_stride % 8 != 0)
             return QSA_ERR_UNSUPPORTED;
     }
-    if (reinterpret_cast<uintptr_t>(q16) % 2 != 0 || !aligned4(out) || (ids && !aligned4(ids)))
+    if (reinterpret_cast<uintptr_t>(q16) % 2 != 0 || !aligned4(out) || (ids && !aligned4(ids)) ||
+        (ws && !aligned4(ws)))
         return QSA_ERR_UNSUPPORTED;
     return hip_status(qsa::launch_attention(q16, q_tok_stride, k_tok, v_tok, kv_tok_stride, ids,
                                             ld_ids, out, out_tok_stride, G, nq, H, D, n_kv, bs, k,
+                                            ws, ws ? ws_floats : 0,
                                             static_cast<hipStream_t>(stream)));
 }
 

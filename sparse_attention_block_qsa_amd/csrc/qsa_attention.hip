@@ -24,9 +24,11 @@
 //   * for the weighted sum lane l owns output channels, reads each token's
 //     weights from LDS (broadcast) and its value row with coalesced loads,
 //     and adds the chunk's sum into the running output.
-// The 8 waves' partial results are merged through LDS at the end.  Every sum
-// is a chain of at most 64 + (chunks) terms, which the oracle's bound
-// assumes.
+// The 8 waves' partial results are merged through LDS at the end.  With a
+// workspace and few rows (decode), a row is split over several workgroups
+// (chunks dealt round-robin to all their waves) whose partial results a
+// second kernel merges.  Every sum is a chain of at most 64 + (chunks)
+// terms, which the oracle's bound assumes.
 #include "qsa_internal.h"
 
 #include <math.h>
@@ -50,6 +52,8 @@ struct AttnArgs {
     int64_t n_kv, nb;
     int32_t bs, k;
     float scale;
+    int32_t splits;   // workgroups per row; > 1: partial results go to ws
+    float *ws;        // [row][split][H][2 + D]: maximum, denominator, numerator
 };
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -81,7 +85,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(AttnArgs a) 
     __shared__ float red_o[kAttnWaves][HM][D];
 
     const int H = a.H;
-    const int64_t row = blockIdx.x;                 // r = g * nq + t
+    const int64_t row = blockIdx.x / a.splits;      // r = g * nq + t
+    const int split = static_cast<int>(blockIdx.x % a.splits);
     const int64_t g = row / a.nq, t = row % a.nq;
     const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
@@ -112,7 +117,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(AttnArgs a) 
         const int64_t tb = static_cast<int64_t>(b) * a.bs;
         const int64_t te = min(tb + a.bs, a.n_kv);
         for (int64_t c0 = tb; c0 < te; c0 += kChunk, ++chunk) {
-            if (chunk % kAttnWaves != w) continue;
+            if (chunk % (kAttnWaves * a.splits) != split * kAttnWaves + w) continue;
             const int n = static_cast<int>(min(static_cast<int64_t>(kChunk), te - c0));
             // 1. logits of this lane's token (c0 + lane) for every head: one
             //    fp32 fma chain per head over the channels in ascending order
@@ -171,21 +176,30 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(AttnArgs a) 
                 #pragma unroll
                 for (int c = 0; c < CPL; ++c) cs[h][c] = 0.0f;
             }
-            for (int j = 0; j < n; ++j) {
-                const uint16_t *vrow = vg + (c0 + j) * a.kvts + CPL * lane;
-                float v[CPL];
-                if constexpr (CPL == 2) {
-                    const uint32_t vw = *reinterpret_cast<const uint32_t *>(vrow);
-                    v[0] = f16_to_f32(vw & 0xffffu);
-                    v[1] = f16_to_f32(vw >> 16);
-                } else {
-                    v[0] = f16_to_f32(*vrow);
+            // value rows in batches of 16 tokens, every load of a batch in
+            // flight before its adds (token j's weights are ps[w][j][*]);
+            // rows past the chunk read the chunk's first token, weight 0
+            for (int j0 = 0; j0 < n; j0 += 16) {
+                uint32_t vw[16];
+                #pragma unroll
+                for (int jj = 0; jj < 16; ++jj) {
+                    const int j = j0 + jj < n ? j0 + jj : 0;
+                    const uint16_t *vrow = vg + (c0 + j) * a.kvts + CPL * lane;
+                    if constexpr (CPL == 2) vw[jj] = *reinterpret_cast<const uint32_t *>(vrow);
+                    else vw[jj] = *vrow;
                 }
                 #pragma unroll
-                for (int h = 0; h < HM; ++h) {
-                    const float p = ps[w][j][h];
+                for (int jj = 0; jj < 16; ++jj) {
+                    if (j0 + jj >= n) break;   // uniform
+                    float v[CPL];
+                    v[0] = f16_to_f32(vw[jj] & 0xffffu);
+                    if constexpr (CPL == 2) v[1] = f16_to_f32(vw[jj] >> 16);
                     #pragma unroll
-                    for (int c = 0; c < CPL; ++c) cs[h][c] = __builtin_fmaf(p, v[c], cs[h][c]);
+                    for (int h = 0; h < HM; ++h) {
+                        const float p = ps[w][j0 + jj][h];
+                        #pragma unroll
+                        for (int c = 0; c < CPL; ++c) cs[h][c] = __builtin_fmaf(p, v[c], cs[h][c]);
+                    }
                 }
             }
             #pragma unroll
@@ -221,6 +235,39 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(AttnArgs a) 
                 den = __builtin_fmaf(red_l[v][h], f, den);
             }
         }
+        if (a.splits == 1) {
+            a.out[t * a.ots + (g * H + h) * D + i] = den > 0.0f ? num / den : 0.0f;
+        } else {
+            float *part = a.ws + (static_cast<int64_t>(blockIdx.x) * H + h) * (2 + D);
+            if (i == 0) {
+                part[0] = M;
+                part[1] = den;
+            }
+            part[2 + i] = num;
+        }
+    }
+}
+
+// Rows split over several workgroups: combine their partial results.
+template <int D>
+__global__ __launch_bounds__(256) void attention_merge_kernel(AttnArgs a) {
+    const int H = a.H;
+    const int64_t row = blockIdx.x;
+    const int64_t g = row / a.nq, t = row % a.nq;
+    const float *base = a.ws + row * a.splits * H * (2 + D);
+    for (int e = threadIdx.x; e < H * D; e += 256) {
+        const int h = e / D, i = e % D;
+        float M = -INFINITY;
+        for (int sp = 0; sp < a.splits; ++sp) M = fmaxf(M, base[(sp * H + h) * (2 + D)]);
+        float num = 0.0f, den = 0.0f;
+        if (M != -INFINITY) {
+            for (int sp = 0; sp < a.splits; ++sp) {
+                const float *part = base + (sp * H + h) * (2 + D);
+                const float f = part[0] == -INFINITY ? 0.0f : expf(part[0] - M);
+                num = __builtin_fmaf(part[2 + i], f, num);
+                den = __builtin_fmaf(part[1], f, den);
+            }
+        }
         a.out[t * a.ots + (g * H + h) * D + i] = den > 0.0f ? num / den : 0.0f;
     }
 }
@@ -239,15 +286,27 @@ void (*pick_attention(int H))(AttnArgs) {
 hipError_t launch_attention(const uint16_t *q16, int64_t qts, const uint16_t *k_tok,
                             const uint16_t *v_tok, int64_t kvts, const int32_t *ids, int64_t ld_ids,
                             float *out, int64_t ots, int32_t G, int32_t nq, int32_t H, int32_t D,
-                            int64_t n_kv, int32_t bs, int32_t k, hipStream_t s) {
+                            int64_t n_kv, int32_t bs, int32_t k, float *ws, int64_t ws_floats,
+                            hipStream_t s) {
     const int64_t rows = static_cast<int64_t>(G) * nq;
     if (rows <= 0) return hipSuccess;
-    if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    int64_t sp = ws ? attention_splits(rows, bs, k) : 1;
+    const int64_t per_split = rows * H * (2 + D);
+    if (sp > 1 && sp * per_split > ws_floats) sp = ws_floats / per_split;
+    if (sp < 2) sp = 1;
+    if (rows * sp > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     AttnArgs a{q16, qts, k_tok, v_tok, kvts, ids, ld_ids, out, ots, G, nq, H,
                n_kv, n_kv / bs + (n_kv % bs != 0), bs, k,
-               static_cast<float>(1.0 / sqrt(static_cast<double>(D)))};
+               static_cast<float>(1.0 / sqrt(static_cast<double>(D))),
+               static_cast<int32_t>(sp), ws};
     void (*fn)(AttnArgs) = D == 128 ? pick_attention<128>(H) : pick_attention<64>(H);
-    hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(rows)), dim3(64 * kAttnWaves), 0, s, a);
+    hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(rows * sp)), dim3(64 * kAttnWaves), 0, s, a);
+    if (sp > 1) {
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        void (*mf)(AttnArgs) = D == 128 ? attention_merge_kernel<128> : attention_merge_kernel<64>;
+        hipLaunchKernelGGL(mf, dim3(static_cast<unsigned>(rows)), dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 

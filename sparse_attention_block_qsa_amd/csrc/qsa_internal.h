@@ -122,10 +122,16 @@ hipError_t launch_block_keys(const uint16_t *k_tok, int64_t tok_stride, uint16_t
 
 // Attention of every query head over the tokens of its row's selected
 // blocks (qsa_attention.hip).  D in {64, 128}, H in [1, 16].
+// With ws (ws_floats floats), few rows are split over several workgroups
+// whose partial results a second launch merges.
 hipError_t launch_attention(const uint16_t *q16, int64_t qts, const uint16_t *k_tok,
                             const uint16_t *v_tok, int64_t kvts, const int32_t *ids, int64_t ld_ids,
                             float *out, int64_t ots, int32_t G, int32_t nq, int32_t H, int32_t D,
-                            int64_t n_kv, int32_t bs, int32_t k, hipStream_t s);
+                            int64_t n_kv, int32_t bs, int32_t k, float *ws, int64_t ws_floats,
+                            hipStream_t s);
+
+// Workgroups per row the attention uses when a workspace allows.
+int64_t attention_splits(int64_t rows, int32_t bs, int32_t k);
 
 // rows of row_len elements at a stride of stride elements (both arrays)
 hipError_t launch_convert_rows(const float *src, uint16_t *dst, int64_t rows, int64_t row_len,

@@ -61,7 +61,8 @@ hipError_t launch_block_keys(const uint16_t *, int64_t, uint16_t *, int64_t, int
 }
 hipError_t launch_attention(const uint16_t *, int64_t, const uint16_t *, const uint16_t *, int64_t,
                             const int32_t *, int64_t, float *, int64_t, int32_t G, int32_t nq,
-                            int32_t H, int32_t D, int64_t n_kv, int32_t bs, int32_t k, hipStream_t) {
+                            int32_t H, int32_t D, int64_t n_kv, int32_t bs, int32_t k, float *,
+                            int64_t, hipStream_t) {
     g_launches.push_back({'a', static_cast<int64_t>(G) * nq, n_kv, H * 1000 + D + k * 100000 + bs * 0});
     return hipSuccess;
 }
@@ -248,25 +249,25 @@ int main() {
     // ---- qsa_sparse_attention -----------------------------------------------
     expect("attention ok", QSA_OK, [] {
         return qsa_sparse_attention(H16, 1024, H16, H16, 128, I32, 64, F32, 1024, 1, 256, 8, 128,
-                                    131072, 64, 64, nullptr);
+                                    131072, 64, 64, nullptr, 0, nullptr);
     }, 1);
     CHECK(g_launches[0].kind == 'a' && g_launches[0].a == 256 && g_launches[0].b == 131072,
           "attention over 256 rows");
     expect("attention n_kv=0 still writes zeros", QSA_OK, [] {
         return qsa_sparse_attention(H16, 1024, nullptr, nullptr, 0, I32, 64, F32, 1024, 1, 256, 8,
-                                    128, 0, 64, 64, nullptr);
+                                    128, 0, 64, 64, nullptr, 0, nullptr);
     }, 1);
     expect("attention H=17", QSA_ERR_UNSUPPORTED, [] {
         return qsa_sparse_attention(H16, 17 * 128, H16, H16, 128, I32, 64, F32, 17 * 128, 1, 256,
-                                    17, 128, 131072, 64, 64, nullptr);
+                                    17, 128, 131072, 64, 64, nullptr, 0, nullptr);
     }, 0);
     expect("attention kv misaligned", QSA_ERR_UNSUPPORTED, [] {
         return qsa_sparse_attention(H16, 1024, H16 + 4, H16, 128, I32, 64, F32, 1024, 1, 256, 8,
-                                    128, 131072, 64, 64, nullptr);
+                                    128, 131072, 64, 64, nullptr, 0, nullptr);
     }, 0);
     expect("attention nq=0", QSA_OK, [] {
         return qsa_sparse_attention(nullptr, 0, nullptr, nullptr, 0, nullptr, 0, nullptr, 0, 1, 0,
-                                    8, 128, 0, 64, 64, nullptr);
+                                    8, 128, 0, 64, 64, nullptr, 0, nullptr);
     }, 0);
 
     // ---- qsa_convert_f32_f16 -----------------------------------------------

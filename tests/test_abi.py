@@ -43,7 +43,9 @@ def lib():
                                            i32, i64, i32, i32, i64, vp]
     L.qsa_block_keys.argtypes = [vp, i64, vp, i64, i32, i32, i64, i32, vp]
     L.qsa_sparse_attention.argtypes = [vp, i64, vp, vp, i64, vp, i64, vp, i64, i32, i32, i32,
-                                       i32, i64, i32, i32, vp]
+                                       i32, i64, i32, i32, vp, i64, vp]
+    L.qsa_sparse_attention_ws_floats.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.qsa_sparse_attention_ws_floats.restype = ctypes.c_int64
     L.qsa_status_string.argtypes = [ctypes.c_int]
     L.qsa_status_string.restype = ctypes.c_char_p
     return L
@@ -53,7 +55,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["qsa_abi_version", "qsa_status_string", "qsa_convert_f32_f16", "qsa_block_keys",
          "qsa_block_scores", "qsa_select_topk", "qsa_select_phase", "qsa_select_phase_noalloc",
-         "qsa_sparse_attention"])
+         "qsa_sparse_attention", "qsa_sparse_attention_ws_floats"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -208,11 +210,11 @@ def test_block_keys_empty_is_ok_without_launch(lib, kw):
 
 def attn_call(lib, **kw):
     a = dict(q=A16, qts=8 * 128, k=A16, v=A16, kvts=128, ids=A16, ld=64, out=A16, ots=8 * 128,
-             G=1, nq=256, H=8, D=128, n_kv=131072, bs=64, kk=64)
+             G=1, nq=256, H=8, D=128, n_kv=131072, bs=64, kk=64, ws=None, wsf=0)
     a.update(kw)
     return lib.qsa_sparse_attention(a["q"], a["qts"], a["k"], a["v"], a["kvts"], a["ids"], a["ld"],
                                     a["out"], a["ots"], a["G"], a["nq"], a["H"], a["D"],
-                                    a["n_kv"], a["bs"], a["kk"], None)
+                                    a["n_kv"], a["bs"], a["kk"], a["ws"], a["wsf"], None)
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -223,7 +225,7 @@ def attn_call(lib, **kw):
     (dict(ots=8 * 128 - 1), ARG), (dict(ld=63), ARG), (dict(kvts=127), ARG),
     (dict(k=A16 + 2), UNSUP), (dict(v=A16 + 8), UNSUP), (dict(kvts=132), UNSUP),
     (dict(q=A16 + 1), UNSUP), (dict(out=A16 + 2), UNSUP), (dict(ids=A16 + 2), UNSUP),
-    (dict(ots=1 << 60), ARG),
+    (dict(ots=1 << 60), ARG), (dict(wsf=-1), ARG), (dict(ws=A16 + 2, wsf=100), UNSUP),
 ])
 def test_sparse_attention_refusals(lib, kw, want):
     assert attn_call(lib, **kw) == want
@@ -232,3 +234,14 @@ def test_sparse_attention_refusals(lib, kw, want):
 def test_sparse_attention_empty_is_ok_without_launch(lib):
     assert attn_call(lib, nq=0) == OK
     assert attn_call(lib, G=0) == OK
+
+
+def test_sparse_attention_workspace_size(lib):
+    f = lib.qsa_sparse_attention_ws_floats
+    # a decode step: 8 rows of 64 chunks split 8 ways (one chunk per wave)
+    assert f(8, 1, 8, 128, 64, 64) == 8 * 8 * 8 * 130
+    # the nq = 256 headline: 4 workgroups per row
+    assert f(1, 256, 8, 128, 64, 64) == 4 * 256 * 8 * 130
+    # enough rows to fill the chip alone: no split, no workspace
+    assert f(4, 16384, 8, 128, 64, 64) == 0
+    assert f(0, 1, 8, 128, 64, 64) == 0 and f(1, 1, 17, 128, 64, 64) == 0

@@ -32,7 +32,7 @@ def _kv(rng, n_kv, G, D, scale=1.0):
     return k, v
 
 
-def _run(q16, kt, vt, ids, n_kv, bs, tok_pad=0):
+def _run(q16, kt, vt, ids, n_kv, bs, tok_pad=0, split=True):
     nq, G, H, D = q16.shape
     row = G * H * D + tok_pad
     out = guarded((nq, row), torch.float32)
@@ -41,9 +41,11 @@ def _run(q16, kt, vt, ids, n_kv, bs, tok_pad=0):
     vd = torch.from_numpy(vt.view(np.float16)).to(dev())
     idd = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).to(dev())
     view = out.view.as_strided((nq, G, H, D), (row, H * D, D, 1))
+    ws = qsa.attention_workspace(G, nq, H, D, bs, ids.shape[2], dev()) if split else None
     st = qsa.lib.qsa_sparse_attention(qsa._ptr(qd), G * H * D, qsa._ptr(kd), qsa._ptr(vd), G * D,
                                       qsa._ptr(idd), ids.shape[2], qsa._ptr(view), row, G, nq, H,
-                                      D, n_kv, bs, ids.shape[2], qsa._stream(None))
+                                      D, n_kv, bs, ids.shape[2], qsa._ptr(ws),
+                                      0 if ws is None else ws.numel(), qsa._stream(None))
     assert st == qsa.QSA_OK, qsa.status_string(st)
     torch.cuda.synchronize()
     mask = np.zeros((nq, row), dtype=bool)
@@ -94,10 +96,11 @@ def test_attention_random_ids_within_bound(case):
                 ids[g, t, 0] = nb - 1              # the partial last block
     if nq > 4:
         ids[:, 4] = -1                             # rows with no token at all
-    o = _run(q16, kt, vt, ids, n_kv, bs, tok_pad=8)
-    if nq > 4:
-        assert np.all(o[4] == 0)
-    _check(o, q16, kt, vt, ids, n_kv, bs, name)
+    for split in (True, False):   # rows over several workgroups, or one each
+        o = _run(q16, kt, vt, ids, n_kv, bs, tok_pad=8, split=split)
+        if nq > 4:
+            assert np.all(o[4] == 0)
+        _check(o, q16, kt, vt, ids, n_kv, bs, f"{name} split={split}")
 
 
 def test_attention_nkv0_gives_zeros():
