@@ -173,13 +173,13 @@ class Phase:
         self._conv = (L.qsa_convert_f32_f16, (P(self.q32), P(self.q16), self.n_q))
         self._score16 = (L.qsa_block_scores, (P(self.q16), qts, P(self.kb), self.kb.stride(0),
                                               P(ws.scores), ws.ld_s, c.G, c.nq, c.H, c.D,
-                                              c.n_kv, c.bs))
+                                              c.n_kv, c.bs, 0))
         self._topk = (L.qsa_select_topk, (P(ws.scores), ws.ld_s, c.rows, c.nb, c.k, P(ws.ids),
                                           c.k, None))
         phase = (P(self.q32), None, qts, P(self.kb), self.kb.stride(0), P(ws.scores), ws.ld_s,
                  P(ws.ids), c.k, None, c.G, c.nq, c.H, c.D, c.n_kv, c.bs)
-        self._phase = (L.qsa_select_phase, phase + (c.k, 0))
-        self._score = (L.qsa_select_phase, phase + (0, 0))   # k = 0: the scorer launch only
+        self._phase = (L.qsa_select_phase, phase + (c.k, 0, 0))
+        self._score = (L.qsa_select_phase, phase + (0, 0, 0))   # k = 0: the scorer launch only
 
     def _call(self, fa):
         fn, args = fa

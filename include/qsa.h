@@ -69,7 +69,7 @@ typedef enum qsa_status {
                                 the library's fixed scratch array */
 } qsa_status;
 
-#define QSA_ABI_VERSION 5
+#define QSA_ABI_VERSION 6
 #define QSA_MAX_K 64
 /* Largest block size qsa_block_keys takes (its sums stay exact in float64). */
 #define QSA_BLOCK_KEYS_MAX_BS 8192
@@ -96,6 +96,14 @@ const char *qsa_status_string(qsa_status s);
  */
 qsa_status qsa_convert_f32_f16(const float *src, uint16_t *dst, int64_t n, void *stream);
 
+/* The forced-tail rule of the scorer (Strata pull request #856, "What": the
+ * tail block keeps the +1e9 rule of the shared tail kernel).  Reading taken:
+ * the partial last block's score, once its head sum is done, gets 1e9 added
+ * in single precision, s = fl32(s + 1e9f), so that the block holding the
+ * newest tokens ranks first in every row's selection whatever its keys
+ * score.  It applies only when that block exists (n_kv % bs != 0). */
+#define QSA_FORCE_TAIL 1u
+
 /*
  * qsa_block_scores -- step 2 of the phase: the score of every (g, t, b)
  * cell, b < nb = ceil(n_kv / bs).  Blocks b < nf = floor(n_kv / bs) go to the
@@ -112,13 +120,14 @@ qsa_status qsa_convert_f32_f16(const float *src, uint16_t *dst, int64_t n, void 
  *              (16-byte aligned, kblk_head_stride % 8 == 0)
  *   scores     device fp32 [G*nq][ld_s], ld_s >= nb; written: [r][0, nb)
  *   G, nq >= 0; H in [1, 16]; D in {64, 128}; n_kv >= 0; bs >= 1
+ *   flags      0, or QSA_FORCE_TAIL; any other bit: QSA_ERR_ARG
  * n_kv == 0 (nb == 0), nq == 0 or G == 0: QSA_OK, nothing written.
  */
 qsa_status qsa_block_scores(const uint16_t *q16, int64_t q_tok_stride,
                             const uint16_t *kblk, int64_t kblk_head_stride,
                             float *scores, int64_t ld_s,
                             int32_t G, int32_t nq, int32_t H, int32_t D,
-                            int64_t n_kv, int32_t bs, void *stream);
+                            int64_t n_kv, int32_t bs, uint32_t flags, void *stream);
 
 /*
  * qsa_select_topk -- step 3 of the phase ("selection/topk", Strata pull
@@ -227,6 +236,7 @@ int64_t qsa_sparse_attention_ws_floats(int32_t G, int32_t nq, int32_t H, int32_t
  *             at query t0, row g*n + t' holds the scores of query t0 + t'
  *             (after the call: those of the last chunk)
  *   ids, vals as qsa_select_topk with rows = G*nq (vals may be NULL)
+ *   flags     as qsa_block_scores (QSA_FORCE_TAIL)
  *   other arguments as qsa_block_scores / qsa_select_topk.
  * Workspaces must not overlap the inputs or outputs.  Errors as the three
  * stage entry points; the whole call is validated before the first launch.
@@ -237,14 +247,14 @@ qsa_status qsa_select_phase(const float *q32, uint16_t *q16, int64_t q_tok_strid
                             int32_t *ids, int64_t ld_ids, float *vals,
                             int32_t G, int32_t nq, int32_t H, int32_t D,
                             int64_t n_kv, int32_t bs, int32_t k, int64_t q_chunk,
-                            void *stream);
+                            uint32_t flags, void *stream);
 
 /*
  * qsa_select_phase_noalloc -- qsa_select_phase for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc.  It takes the same inputs and outputs
- * (q32, q16, q_tok_stride, kblk, kblk_head_stride, ids, ld_ids, vals and the
- * geometry, as qsa_select_phase) but no score workspace: the scores live in a
+ * (q32, q16, q_tok_stride, kblk, kblk_head_stride, ids, ld_ids, vals, flags
+ * and the geometry, as qsa_select_phase) but no score workspace: the scores live in a
  * device array of QSA_NOALLOC_SCRATCH_BYTES that the library holds on each
  * GPU it runs on, from the first call on that GPU until the process ends.
  * Nothing else is allocated (no hipMalloc, hipFree or allocating library
@@ -265,7 +275,7 @@ qsa_status qsa_select_phase_noalloc(const float *q32, uint16_t *q16, int64_t q_t
                                     int32_t *ids, int64_t ld_ids, float *vals,
                                     int32_t G, int32_t nq, int32_t H, int32_t D,
                                     int64_t n_kv, int32_t bs, int32_t k, int64_t q_chunk,
-                                    void *stream);
+                                    uint32_t flags, void *stream);
 
 #ifdef __cplusplus
 }

@@ -136,8 +136,9 @@ def scores(q: np.ndarray, kblk: np.ndarray, nb: int, rows: np.ndarray | None = N
 
 
 def block_model_f32(q16: np.ndarray, kblk: np.ndarray, b: int,
-                    rows: np.ndarray | None = None) -> np.ndarray:
-    """R2: fixed-order fp32 scores of block b for each requested row."""
+                    rows: np.ndarray | None = None, force_tail: bool = False) -> np.ndarray:
+    """R2: fixed-order fp32 scores of block b for each requested row.  With
+    force_tail the forced-tail rule follows the head sum: s = fl32(s + 1e9)."""
     q16 = np.ascontiguousarray(q16, dtype=np.uint16)
     nq, G, H, D = q16.shape
     kblk = np.ascontiguousarray(kblk, dtype=np.uint16)
@@ -148,7 +149,34 @@ def block_model_f32(q16: np.ndarray, kblk: np.ndarray, b: int,
     rc = lib().oracle_block_model_f32(_p(q16), G * H * D, _p(kblk), kblk.shape[1] * D, G, nq, H,
                                       D, b, _p(rows), rows.size, _p(out))
     assert rc == 0
+    if force_tail:
+        out = (out + np.float32(FORCE_TAIL_ADD)).astype(np.float32)   # one IEEE fp32 addition
     return out
+
+
+# The forced-tail rule.  Strata pull request #856 ("What") says the WMMA arm
+# keeps the shared tail kernel's "+1e9 dead-tail rule" exactly, without
+# defining it.  Reading taken: the partial last block (present when n_kv % bs
+# != 0) gets 1e9 added to its score after the head sum, so that the block
+# holding the newest tokens ranks first in every row's selection whatever its
+# keys score.
+FORCE_TAIL_ADD = 1e9
+
+
+def force_tail(ref: Scores, n_kv: int, bs: int) -> Scores:
+    """R1 followed by the forced-tail rule: the partial block's exact score
+    plus 1e9 (float64), and that cell's bound recomputed from the contract
+    for the new score, 2^-9.5*S + 8*2^-24*|score|.  Its second term grows by
+    8*2^-24*1e9 (about 477), which covers the device's one fp32 rounding of
+    s + 1e9 (at most half an ulp: 32 below 2^30, 64 below 2^31).  Without a
+    partial block the scores are returned unchanged."""
+    nf, nb = n_kv // bs, -(-n_kv // bs)
+    if nb == nf:
+        return ref
+    score, B = ref.score.copy(), ref.B.copy()
+    score[:, nf] = score[:, nf] + FORCE_TAIL_ADD
+    B[:, nf] = 2.0 ** -9.5 * ref.S[:, nf] + 8.0 * 2.0 ** -24 * np.abs(score[:, nf])
+    return Scores(score, ref.S, B, ref.rows)
 
 
 def topk(score_rows: np.ndarray, k: int) -> tuple[np.ndarray, np.ndarray]:

@@ -24,8 +24,9 @@ LIB_PATH = os.path.join(_HERE, "libqsa.so")
 QSA_OK, QSA_ERR_ARG, QSA_ERR_UNSUPPORTED, QSA_ERR_HIP, QSA_ERR_TOO_LARGE = 0, 1, 2, 3, 4
 MAX_K = 64
 NOALLOC_SCRATCH_BYTES = 64 << 20   # qsa.h QSA_NOALLOC_SCRATCH_BYTES
-ABI_VERSION = 5   # qsa.h QSA_ABI_VERSION this binding is written for
+ABI_VERSION = 6   # qsa.h QSA_ABI_VERSION this binding is written for
 BLOCK_KEYS_MAX_BS = 8192   # qsa.h QSA_BLOCK_KEYS_MAX_BS
+FORCE_TAIL = 1   # qsa.h QSA_FORCE_TAIL
 EXPORTS = ("qsa_abi_version", "qsa_status_string", "qsa_convert_f32_f16", "qsa_block_keys",
            "qsa_block_scores", "qsa_select_topk", "qsa_select_phase", "qsa_select_phase_noalloc",
            "qsa_sparse_attention", "qsa_sparse_attention_ws_floats")
@@ -41,7 +42,7 @@ def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
     L = ctypes.CDLL(LIB_PATH)
-    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    vp, i64, i32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
     L.qsa_abi_version.restype = ctypes.c_int
     L.qsa_status_string.argtypes = [ctypes.c_int]
     L.qsa_status_string.restype = ctypes.c_char_p
@@ -54,15 +55,16 @@ def _load() -> ctypes.CDLL:
     L.qsa_sparse_attention.restype = ctypes.c_int
     L.qsa_sparse_attention_ws_floats.argtypes = [i32, i32, i32, i32, i32, i32]
     L.qsa_sparse_attention_ws_floats.restype = ctypes.c_int64
-    L.qsa_block_scores.argtypes = [vp, i64, vp, i64, vp, i64, i32, i32, i32, i32, i64, i32, vp]
+    L.qsa_block_scores.argtypes = [vp, i64, vp, i64, vp, i64, i32, i32, i32, i32, i64, i32, u32,
+                                   vp]
     L.qsa_block_scores.restype = ctypes.c_int
     L.qsa_select_topk.argtypes = [vp, i64, i64, i32, i32, vp, i64, vp, vp]
     L.qsa_select_topk.restype = ctypes.c_int
     L.qsa_select_phase.argtypes = [vp, vp, i64, vp, i64, vp, i64, vp, i64, vp, i32, i32, i32,
-                                   i32, i64, i32, i32, i64, vp]
+                                   i32, i64, i32, i32, i64, u32, vp]
     L.qsa_select_phase.restype = ctypes.c_int
     L.qsa_select_phase_noalloc.argtypes = [vp, vp, i64, vp, i64, vp, i64, vp, i32, i32, i32, i32,
-                                           i64, i32, i32, i64, vp]
+                                           i64, i32, i32, i64, u32, vp]
     L.qsa_select_phase_noalloc.restype = ctypes.c_int
     if L.qsa_abi_version() != ABI_VERSION:
         raise ImportError(f"{LIB_PATH}: ABI version {L.qsa_abi_version()}, this binding needs "
@@ -156,10 +158,11 @@ def block_keys(k_tok: torch.Tensor, n_kv: int, bs: int, out: torch.Tensor | None
 
 
 def block_scores(q16: torch.Tensor, kblk: torch.Tensor, n_kv: int, bs: int,
-                 out: torch.Tensor | None = None,
+                 out: torch.Tensor | None = None, force_tail: bool = False,
                  stream: torch.cuda.Stream | None = None) -> torch.Tensor:
     """Scores [G, nq, nb] (a view of ``out`` when given, whose last dim may be
-    longer than nb: only [..., :nb] is written)."""
+    longer than nb: only [..., :nb] is written).  force_tail: the partial
+    last block's score gets 1e9 added (FORCE_TAIL)."""
     nq, G, H, D, qts = _check_q(q16, torch.float16)
     nb = n_blocks(n_kv, bs)
     khs = _check_k(kblk, G, D, nb)
@@ -168,7 +171,7 @@ def block_scores(q16: torch.Tensor, kblk: torch.Tensor, n_kv: int, bs: int,
     ld_s = _scores_view(out, G, nq, nb)
     _check("qsa_block_scores",
            lib.qsa_block_scores(_ptr(q16), qts, _ptr(kblk), khs, _ptr(out), ld_s, G, nq, H, D,
-                                n_kv, bs, _stream(stream)))
+                                n_kv, bs, FORCE_TAIL if force_tail else 0, _stream(stream)))
     return out[..., :nb]
 
 
@@ -228,7 +231,7 @@ class PhaseWorkspace:
 
 def select_phase(q: torch.Tensor, kblk: torch.Tensor, n_kv: int, bs: int, k: int,
                  ws: PhaseWorkspace | None = None, q_chunk: int | None = None,
-                 stream: torch.cuda.Stream | None = None):
+                 force_tail: bool = False, stream: torch.cuda.Stream | None = None):
     """The whole phase: (fp32 -> fp16 conversion when q is float32), scores,
     top-k.  Returns ids [G, nq, k] (and vals when the workspace has them).
     fp32 queries are converted by the scorers as they load them; without a
@@ -256,13 +259,13 @@ def select_phase(q: torch.Tensor, kblk: torch.Tensor, n_kv: int, bs: int, k: int
            lib.qsa_select_phase(_ptr(q) if fp32 else None, _ptr(q16), qts, _ptr(kblk), khs,
                                 _ptr(ws.scores), ws.ld_s, _ptr(ws.ids), ws.ids.stride(1),
                                 _ptr(ws.vals), G, nq, H, D, n_kv, bs, k, ws.q_chunk,
-                                _stream(stream)))
+                                FORCE_TAIL if force_tail else 0, _stream(stream)))
     return (ws.ids, ws.vals) if ws.vals is not None else ws.ids
 
 
 def select_phase_noalloc(q: torch.Tensor, kblk: torch.Tensor, n_kv: int, bs: int, k: int,
                          ids: torch.Tensor, vals: torch.Tensor | None = None, q_chunk: int = 0,
-                         q16: torch.Tensor | None = None,
+                         q16: torch.Tensor | None = None, force_tail: bool = False,
                          stream: torch.cuda.Stream | None = None):
     """The whole phase with no device allocation: scores go to the library's
     fixed per-GPU scratch array (NOALLOC_SCRATCH_BYTES), ids [G, nq, k] and
@@ -284,7 +287,8 @@ def select_phase_noalloc(q: torch.Tensor, kblk: torch.Tensor, n_kv: int, bs: int
     _check("qsa_select_phase_noalloc",
            lib.qsa_select_phase_noalloc(_ptr(q) if fp32 else None, _ptr(qsrc16), qts, _ptr(kblk),
                                         khs, _ptr(ids), ids.stride(1), _ptr(vals), G, nq, H, D,
-                                        n_kv, bs, k, q_chunk, _stream(stream)))
+                                        n_kv, bs, k, q_chunk, FORCE_TAIL if force_tail else 0,
+                                        _stream(stream)))
     return (ids, vals) if vals is not None else ids
 
 

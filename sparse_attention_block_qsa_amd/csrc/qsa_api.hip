@@ -103,6 +103,9 @@ qsa_status check_topk_args(const float *scores, int64_t ld_s, int64_t rows, int3
 
 qsa_status hip_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_HIP; }
 
+// What the tail scorers add to the partial block's head sum.
+float tail_addend(uint32_t flags) { return (flags & QSA_FORCE_TAIL) ? 1e9f : 0.0f; }
+
 // Scores of every block (full blocks and the tail).  With q32 the queries
 // are read as fp32 and converted on load (src32_ok holds), their fp16 bits
 // written to q16w when it is set; with no full block the small scorer then
@@ -149,12 +152,14 @@ qsa_status qsa_convert_f32_f16(const float *src, uint16_t *dst, int64_t n, void 
 qsa_status qsa_block_scores(const uint16_t *q16, int64_t q_tok_stride, const uint16_t *kblk,
                             int64_t kblk_head_stride, float *scores, int64_t ld_s, int32_t G,
                             int32_t nq, int32_t H, int32_t D, int64_t n_kv, int32_t bs,
-                            void *stream) {
+                            uint32_t flags, void *stream) {
+    if (flags & ~QSA_FORCE_TAIL) return QSA_ERR_ARG;
     ScoreCheck c;
     qsa_status st = check_scores_args(q16, q_tok_stride, kblk, kblk_head_stride, scores, ld_s, G,
                                       nq, H, D, n_kv, bs, &c);
     if (st != QSA_OK || G == 0 || nq == 0 || c.nb == 0) return st;
-    ScoreGeom geo{q16, q_tok_stride, kblk, kblk_head_stride, scores, ld_s, G, nq, H, D, c.nf};
+    ScoreGeom geo{q16, q_tok_stride, kblk, kblk_head_stride, scores, ld_s, G, nq, H, D, c.nf,
+                  tail_addend(flags)};
     return hip_status(run_scores(geo, c, static_cast<hipStream_t>(stream)));
 }
 
@@ -237,8 +242,8 @@ qsa_status qsa_select_phase(const float *q32, uint16_t *q16, int64_t q_tok_strid
                             const uint16_t *kblk, int64_t kblk_head_stride, float *scores_ws,
                             int64_t ld_s, int32_t *ids, int64_t ld_ids, float *vals, int32_t G,
                             int32_t nq, int32_t H, int32_t D, int64_t n_kv, int32_t bs, int32_t k,
-                            int64_t q_chunk, void *stream) {
-    if (q_chunk < 0) return QSA_ERR_ARG;
+                            int64_t q_chunk, uint32_t flags, void *stream) {
+    if (q_chunk < 0 || (flags & ~QSA_FORCE_TAIL)) return QSA_ERR_ARG;
     const int64_t qc = (q_chunk > 0 && q_chunk < nq) ? q_chunk : nq;
     ScoreCheck c;
     // scores are validated for the chunk-sized workspace; the query source
@@ -271,7 +276,7 @@ qsa_status qsa_select_phase(const float *q32, uint16_t *q16, int64_t q_tok_strid
         const int64_t qoff = t0 * q_tok_stride;
         uint16_t *q16c = q16 ? q16 + qoff : nullptr;   // may be null when nb == 0
         ScoreGeom geo{q16c, q_tok_stride, kblk, kblk_head_stride, scores_ws, ld_s, G, n, H, D,
-                      c.nf};
+                      c.nf, tail_addend(flags)};
         // With 16-byte aligned fp32 queries the scorer reads them itself,
         // converts them on load and writes this chunk's rows of the fp16
         // buffer (if any), so the conversion needs no launch of its own;

@@ -66,6 +66,9 @@ struct ScoreGeom {
     int64_t ld_s;
     int32_t G, nq, H, D;
     int64_t nf;           // full blocks
+    // Added to the partial last block's score after its head sum (fp32):
+    // 1e9 under the forced-tail rule, else 0 (then nothing is added).
+    float tail_add;
 };
 
 // Full-block MFMA scorer over blocks [0, nf).  Many query rows: one kernel

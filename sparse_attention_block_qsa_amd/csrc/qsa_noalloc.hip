@@ -55,8 +55,9 @@ qsa_status qsa_select_phase_noalloc(const float *q32, uint16_t *q16, int64_t q_t
                                     const uint16_t *kblk, int64_t kblk_head_stride,
                                     int32_t *ids, int64_t ld_ids, float *vals, int32_t G,
                                     int32_t nq, int32_t H, int32_t D, int64_t n_kv, int32_t bs,
-                                    int32_t k, int64_t q_chunk, void *stream) {
-    if (G < 0 || nq < 0 || n_kv < 0 || q_chunk < 0) return QSA_ERR_ARG;
+                                    int32_t k, int64_t q_chunk, uint32_t flags, void *stream) {
+    if (G < 0 || nq < 0 || n_kv < 0 || q_chunk < 0 || (flags & ~QSA_FORCE_TAIL))
+        return QSA_ERR_ARG;
     if (bs < 1) return QSA_ERR_UNSUPPORTED;
     // Rows of the workspace: nb scores rounded up to 32 floats, so that every
     // row starts on a 128-byte line.
@@ -65,7 +66,7 @@ qsa_status qsa_select_phase_noalloc(const float *q32, uint16_t *q16, int64_t q_t
     if (G == 0 || nq == 0) {
         // nothing to score or select; the phase itself checks the rest
         return qsa_select_phase(q32, q16, q_tok_stride, kblk, kblk_head_stride, nullptr, ld_s,
-                                ids, ld_ids, vals, G, nq, H, D, n_kv, bs, k, 0, stream);
+                                ids, ld_ids, vals, G, nq, H, D, n_kv, bs, k, 0, flags, stream);
     }
     if (ld_s > kScratchBytes / 4 / G) return QSA_ERR_TOO_LARGE;   // not even one query fits
     const int64_t fit = kScratchBytes / (4 * G * ld_s);           // queries per pass
@@ -77,7 +78,7 @@ qsa_status qsa_select_phase_noalloc(const float *q32, uint16_t *q16, int64_t q_t
     if (!ws) return QSA_ERR_HIP;
     return qsa_select_phase(q32, q16, q_tok_stride, kblk, kblk_head_stride,
                             static_cast<float *>(ws), ld_s, ids, ld_ids, vals, G, nq, H, D, n_kv,
-                            bs, k, qc < nq ? qc : 0, stream);
+                            bs, k, qc < nq ? qc : 0, flags, stream);
 }
 
 }  // extern "C"

@@ -69,6 +69,8 @@ struct ScoreArgs {
     int32_t accumulate;    // 1: continue the head sum already in scores
     int64_t nf;
     int32_t n_qgroups, n_splits, tiles_per_split, n_tiles;
+    float tail_add;        // added to the partial block's score when nonzero
+                           // (last head pass only)
 };
 
 // s_waitcnt immediate for vmcnt(0) with the other counters left free
@@ -466,6 +468,7 @@ void score_full_kernel(ScoreArgs a) {
                     for (int j = 0; j < 4; ++j)
                         if (4 * c + j < a.nh) sum = sum + red[64 * c + 16 * j + l];
                 }
+                if (a.tail_add != 0.0f) sum = sum + a.tail_add;   // forced-tail rule
                 *cell = sum;
             }
         }
@@ -543,7 +546,8 @@ hipError_t launch_score_full(const ScoreGeom &geo, bool tail, hipStream_t s, con
         ScoreArgs a{geo.q16, q32, q32 ? q16w : nullptr, geo.qts, geo.kblk, geo.khs, geo.scores, geo.ld_s,
                     geo.G, geo.nq, geo.H, h0, nh, h0 > 0 ? 1 : 0, geo.nf,
                     static_cast<int32_t>(n_qgroups), static_cast<int32_t>(splits),
-                    static_cast<int32_t>(tps), static_cast<int32_t>(n_tiles)};
+                    static_cast<int32_t>(tps), static_cast<int32_t>(n_tiles),
+                    h0 + nh == geo.H ? geo.tail_add : 0.0f};
         void *args[] = {&a};
         hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(fn),
                                        dim3(static_cast<unsigned>(grid)), dim3(256), args, 0, s);

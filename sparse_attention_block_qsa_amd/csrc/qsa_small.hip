@@ -64,6 +64,7 @@ struct SmallArgs {
     int32_t tail;          // block nf is a partial block
     int32_t n_qgroups;     // groups of four query groups (one per wave)
     int32_t n_segs, tiles_per_seg, n_tiles;
+    float tail_add;        // added to the partial block's score when nonzero
 };
 
 __device__ __forceinline__ float relu_bits(float x) {
@@ -335,6 +336,7 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
             if (t < a.nq) {
                 float sum = 0.0f;
                 for (int h = 0; h < a.H; ++h) sum = sum + red[w][l][h];
+                if (a.tail_add != 0.0f) sum = sum + a.tail_add;   // forced-tail rule
                 sbase[static_cast<int64_t>(t) * a.ld_s + a.nf] = sum;
             }
         }
@@ -414,7 +416,7 @@ hipError_t launch_score_small(const ScoreGeom &geo, bool tail, hipStream_t s, co
     SmallArgs a{geo.q16, q32, q32 ? q16w : nullptr, geo.qts, geo.kblk, geo.khs, geo.scores,
                 geo.ld_s, geo.G, geo.nq, geo.H, geo.nf, tail ? 1 : 0,
                 static_cast<int32_t>(n_qg4), static_cast<int32_t>(segs),
-                static_cast<int32_t>(tps), static_cast<int32_t>(n_tiles)};
+                static_cast<int32_t>(tps), static_cast<int32_t>(n_tiles), geo.tail_add};
     void *args[] = {&a};
     return hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(static_cast<unsigned>(grid)),
                            dim3(256), args, 0, s);

@@ -7,6 +7,9 @@
 //   acc_h = +0;  for i ascending: acc_h = fma(k[i], q_h[i], acc_h)   (fp32)
 //   r_h   = acc_h > 0 ? acc_h : +0
 //   s     = +0;  for h ascending: s = s + r_h
+//   s     = s + 1e9 under the forced-tail rule (Strata pull request #856,
+//           "What": the tail keeps its +1e9 rule), which puts the block
+//           holding the newest tokens first in every row's selection
 // One lane runs one (query, head) chain.  The queries are read once,
 // coalesced, and staged through LDS so that every lane walks its own row; a
 // second LDS pass sums the heads of each query in order.  HBM-bound: it
@@ -28,6 +31,7 @@ struct TailArgs {
     int32_t G, nq;
     int64_t b_tail;
     int64_t n_items;   // ceil(nq / R) * G
+    float tail_add;    // added after the head sum when nonzero
 };
 
 // One wave per workgroup: R = 64 / H query rows of one KV head, one lane per
@@ -118,6 +122,7 @@ __global__ __launch_bounds__(64) void tail_kernel(TailArgs a) {
                 float s = 0.0f;
                 #pragma unroll
                 for (int h = 0; h < H; ++h) s = s + red[lane * H + h];
+                if (a.tail_add != 0.0f) s = s + a.tail_add;
                 a.scores[(static_cast<int64_t>(g) * a.nq + t) * a.ld_s + a.b_tail] = s;
             }
         }
@@ -153,7 +158,8 @@ hipError_t launch_tail(const ScoreGeom &geo, int64_t b_tail, hipStream_t s) {
     const int64_t gx = items < kTailGrid ? items : kTailGrid;
     tail_fn fn = geo.D == 64 ? pick_h<64>(geo.H) : pick_h<128>(geo.H);
     if (!fn) return hipErrorInvalidValue;
-    TailArgs a{geo.q16, geo.qts, geo.kblk, geo.khs, geo.scores, geo.ld_s, geo.G, geo.nq, b_tail, items};
+    TailArgs a{geo.q16, geo.qts, geo.kblk, geo.khs, geo.scores, geo.ld_s, geo.G, geo.nq, b_tail, items,
+                geo.tail_add};
     void *args[] = {&a};
     return hipLaunchKernel(reinterpret_cast<const void *>(fn),
                            dim3(static_cast<unsigned>(gx)), dim3(64),

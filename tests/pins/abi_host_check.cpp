@@ -34,16 +34,17 @@ namespace qsa {
 hipError_t launch_score_full(const ScoreGeom &g, bool tail, hipStream_t, const float *q32,
                              uint16_t *) {
     // the real launcher hands few rows to the small scorer: bit 4 records it
-    g_launches.push_back({'f', g.nq, g.nf, (tail ? 1 : 0) + (q32 ? 2 : 0) + (small_rows(g) ? 4 : 0)});
+    g_launches.push_back({'f', g.nq, g.nf, (tail ? 1 : 0) + (q32 ? 2 : 0) + (small_rows(g) ? 4 : 0) +
+                                              (g.tail_add == 1e9f ? 8 : 0)});
     return hipSuccess;
 }
 hipError_t launch_score_small(const ScoreGeom &g, bool tail, hipStream_t, const float *q32,
                               uint16_t *) {
-    g_launches.push_back({'s', g.nq, g.nf, (tail ? 1 : 0) + (q32 ? 2 : 0)});
+    g_launches.push_back({'s', g.nq, g.nf, (tail ? 1 : 0) + (q32 ? 2 : 0) + (g.tail_add == 1e9f ? 8 : 0)});
     return hipSuccess;
 }
 hipError_t launch_tail(const ScoreGeom &g, int64_t b, hipStream_t) {
-    g_launches.push_back({'t', g.nq, b, 0});
+    g_launches.push_back({'t', g.nq, b, g.tail_add == 1e9f ? 8 : 0});
     return hipSuccess;
 }
 hipError_t launch_topk(const TopkGeom &g, hipStream_t) {
@@ -98,8 +99,10 @@ struct SArgs {
     int32_t G = 1, nq = 256, H = 8, D = 128;
     int64_t n_kv = 4096;
     int32_t bs = 64;
+    uint32_t flags = 0;
     qsa_status call() const {
-        return qsa_block_scores(q16, qts, kblk, khs, scores, ld_s, G, nq, H, D, n_kv, bs, nullptr);
+        return qsa_block_scores(q16, qts, kblk, khs, scores, ld_s, G, nq, H, D, n_kv, bs, flags,
+                                nullptr);
     }
 };
 
@@ -118,9 +121,10 @@ struct PArgs {
     int64_t n_kv = 4096;
     int32_t bs = 64, k = 16;
     int64_t q_chunk = 0;
+    uint32_t flags = 0;
     qsa_status call() const {
         return qsa_select_phase(q32, q16, qts, kblk, khs, ws, ld_s, ids, ld_ids, vals, G, nq, H, D,
-                                n_kv, bs, k, q_chunk, nullptr);
+                                n_kv, bs, k, q_chunk, flags, nullptr);
     }
 };
 
@@ -158,7 +162,15 @@ int main() {
         t.qts = 4 * 8 * 128;
         t.ld_s = 1;
         expect("tail only, many rows", QSA_OK, [&] { return t.call(); }, 1);
-        CHECK(g_launches[0].kind == 't' && g_launches[0].b == 0, "standalone tail of block 0");
+        CHECK(g_launches[0].kind == 't' && g_launches[0].b == 0 && g_launches[0].c == 0,
+              "standalone tail of block 0, nothing added");
+        t.flags = QSA_FORCE_TAIL;
+        expect("tail only, forced", QSA_OK, [&] { return t.call(); }, 1);
+        CHECK(g_launches[0].kind == 't' && g_launches[0].c == 8, "the tail kernel adds 1e9");
+        w.flags = QSA_FORCE_TAIL;
+        expect("prefill scores, forced tail", QSA_OK, [&] { return w.call(); }, 1);
+        CHECK(g_launches[0].kind == 'f' && g_launches[0].c == (1 | 8),
+              "the wide scorer's tail adds 1e9");
     }
     struct SCase {
         const char *name;
@@ -167,6 +179,8 @@ int main() {
     };
     const SCase scases[] = {
         {"D=96", [](SArgs &a) { a.D = 96; }, QSA_ERR_UNSUPPORTED},
+        {"flags=2", [](SArgs &a) { a.flags = 2; }, QSA_ERR_ARG},
+        {"flags=~0", [](SArgs &a) { a.flags = ~0u; }, QSA_ERR_ARG},
         {"H=0", [](SArgs &a) { a.H = 0; }, QSA_ERR_UNSUPPORTED},
         {"H=17", [](SArgs &a) { a.H = 17; }, QSA_ERR_UNSUPPORTED},
         {"bs=0", [](SArgs &a) { a.bs = 0; }, QSA_ERR_UNSUPPORTED},
@@ -285,8 +299,15 @@ int main() {
         a.q16 = nullptr;   // 16-byte aligned fp32 rows: converted by the scorer on load
         expect("phase fused", QSA_OK, [&] { return a.call(); }, 2);
         CHECK(g_launches[0].kind == 'f' && (g_launches[0].c & 2) && g_launches[1].kind == 'k' &&
-                  g_launches[1].a == 256,
+                  g_launches[1].a == 256 && !(g_launches[0].c & 8),
               "fused phase: scorer with fp32 queries, then one flat selector launch");
+        a.flags = QSA_FORCE_TAIL;
+        a.n_kv = 4096 + 7;   // 64 full blocks and a 7-token tail
+        a.khs = 65 * 128;
+        a.ld_s = 65;
+        expect("phase forced tail", QSA_OK, [&] { return a.call(); }, 2);
+        CHECK(g_launches[0].kind == 'f' && (g_launches[0].c & 1) && (g_launches[0].c & 8),
+              "forced tail: the phase's scorer adds 1e9 to the partial block");
         PArgs b;
         b.q32 = reinterpret_cast<float *>(uintptr_t(0x20004));   // 4-byte aligned only
         expect("phase separate conversion", QSA_OK, [&] { return b.call(); }, 3);
@@ -322,6 +343,7 @@ int main() {
     };
     const PCase pcases[] = {
         {"q_chunk<0", [](PArgs &a) { a.q_chunk = -1; }, QSA_ERR_ARG},
+        {"flags=4", [](PArgs &a) { a.flags = 4; }, QSA_ERR_ARG},
         {"k>64", [](PArgs &a) { a.k = 65; a.ld_ids = 65; }, QSA_ERR_UNSUPPORTED},
         {"D=80", [](PArgs &a) { a.D = 80; }, QSA_ERR_UNSUPPORTED},
         {"ids null", [](PArgs &a) { a.ids = nullptr; }, QSA_ERR_ARG},

@@ -33,14 +33,15 @@ def lib():
         spec.loader.exec_module(build_lib)
         build_lib.build()
     L = ctypes.CDLL(LIB)
-    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
-    L.qsa_block_scores.argtypes = [vp, i64, vp, i64, vp, i64, i32, i32, i32, i32, i64, i32, vp]
+    vp, i64, i32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
+    L.qsa_block_scores.argtypes = [vp, i64, vp, i64, vp, i64, i32, i32, i32, i32, i64, i32, u32,
+                                   vp]
     L.qsa_select_topk.argtypes = [vp, i64, i64, i32, i32, vp, i64, vp, vp]
     L.qsa_convert_f32_f16.argtypes = [vp, vp, i64, vp]
     L.qsa_select_phase.argtypes = [vp, vp, i64, vp, i64, vp, i64, vp, i64, vp, i32, i32, i32,
-                                   i32, i64, i32, i32, i64, vp]
+                                   i32, i64, i32, i32, i64, u32, vp]
     L.qsa_select_phase_noalloc.argtypes = [vp, vp, i64, vp, i64, vp, i64, vp, i32, i32, i32,
-                                           i32, i64, i32, i32, i64, vp]
+                                           i32, i64, i32, i32, i64, u32, vp]
     L.qsa_block_keys.argtypes = [vp, i64, vp, i64, i32, i32, i64, i32, vp]
     L.qsa_sparse_attention.argtypes = [vp, i64, vp, vp, i64, vp, i64, vp, i64, i32, i32, i32,
                                        i32, i64, i32, i32, vp, i64, vp]
@@ -79,10 +80,11 @@ def test_python_binding_exports_match_header():
 
 def scores_call(lib, **kw):
     a = dict(q16=A16, qts=8 * 128, kblk=A16, khs=64 * 128, scores=A16, ld_s=64, G=1, nq=256,
-             H=8, D=128, n_kv=4096, bs=64)
+             H=8, D=128, n_kv=4096, bs=64, flags=0)
     a.update(kw)
     return lib.qsa_block_scores(a["q16"], a["qts"], a["kblk"], a["khs"], a["scores"], a["ld_s"],
-                                a["G"], a["nq"], a["H"], a["D"], a["n_kv"], a["bs"], None)
+                                a["G"], a["nq"], a["H"], a["D"], a["n_kv"], a["bs"], a["flags"],
+                                None)
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -93,6 +95,8 @@ def scores_call(lib, **kw):
     (dict(q16=A16 + 2), UNSUP), (dict(qts=8 * 128 + 4), UNSUP), (dict(kblk=A16 + 8), UNSUP),
     (dict(khs=64 * 128 + 2), UNSUP), (dict(scores=A16 + 2), UNSUP),
     (dict(ld_s=1 << 62, nq=8), ARG),          # row extent overflows int64
+    (dict(flags=2), ARG), (dict(flags=0xFFFFFFFF), ARG),   # only QSA_FORCE_TAIL is defined
+    (dict(flags=3, n_kv=0), ARG),             # refused before the empty early return
 ])
 def test_block_scores_refusals(lib, kw, want):
     assert scores_call(lib, **kw) == want
@@ -135,11 +139,13 @@ def test_convert_refusals(lib):
 
 def phase_call(lib, **kw):
     a = dict(q32=A16, q16=A16, qts=8 * 128, kblk=A16, khs=64 * 128, ws=A16, ld_s=64, ids=A16,
-             ld_ids=16, vals=None, G=1, nq=256, H=8, D=128, n_kv=4096, bs=64, k=16, q_chunk=0)
+             ld_ids=16, vals=None, G=1, nq=256, H=8, D=128, n_kv=4096, bs=64, k=16, q_chunk=0,
+             flags=0)
     a.update(kw)
     return lib.qsa_select_phase(a["q32"], a["q16"], a["qts"], a["kblk"], a["khs"], a["ws"],
                                 a["ld_s"], a["ids"], a["ld_ids"], a["vals"], a["G"], a["nq"],
-                                a["H"], a["D"], a["n_kv"], a["bs"], a["k"], a["q_chunk"], None)
+                                a["H"], a["D"], a["n_kv"], a["bs"], a["k"], a["q_chunk"],
+                                a["flags"], None)
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -148,6 +154,7 @@ def phase_call(lib, **kw):
     (dict(ld_s=10), ARG), (dict(q32=A16 + 2), UNSUP), (dict(H=20), UNSUP),
     # no fp16 buffer: the fp32 rows must be 16-byte aligned
     (dict(q16=None, q32=A16 + 4), UNSUP), (dict(q16=None, qts=8 * 128 + 2), UNSUP),
+    (dict(flags=2), ARG), (dict(flags=1 << 31), ARG),
 ])
 def test_select_phase_refusals(lib, kw, want):
     assert phase_call(lib, **kw) == want
@@ -160,17 +167,17 @@ def test_select_phase_empty_is_ok_without_launch(lib):
 
 def noalloc_call(lib, **kw):
     a = dict(q32=A16, q16=None, qts=8 * 128, kblk=A16, khs=64 * 128, ids=A16, ld_ids=16,
-             vals=None, G=1, nq=256, H=8, D=128, n_kv=4096, bs=64, k=16, q_chunk=0)
+             vals=None, G=1, nq=256, H=8, D=128, n_kv=4096, bs=64, k=16, q_chunk=0, flags=0)
     a.update(kw)
     return lib.qsa_select_phase_noalloc(a["q32"], a["q16"], a["qts"], a["kblk"], a["khs"],
                                         a["ids"], a["ld_ids"], a["vals"], a["G"], a["nq"],
                                         a["H"], a["D"], a["n_kv"], a["bs"], a["k"],
-                                        a["q_chunk"], None)
+                                        a["q_chunk"], a["flags"], None)
 
 
 @pytest.mark.parametrize("kw,want", [
     (dict(q_chunk=-1), ARG), (dict(G=-1), ARG), (dict(nq=-1), ARG), (dict(n_kv=-1), ARG),
-    (dict(bs=0), UNSUP),
+    (dict(bs=0), UNSUP), (dict(flags=2), ARG),
     # one query's score row (17M blocks of one token, 68 MB) exceeds the 64 MiB array
     (dict(n_kv=17 << 20, bs=1, khs=(17 << 20) * 128), TOO_LARGE),
     # four KV heads of 2049 blocks fit 2016 queries per pass, not 4096

@@ -655,7 +655,7 @@ def test_phase_conversion_paths(case):
     st = qsa.lib.qsa_select_phase(
         ctypes.c_void_p(q32_rows.data_ptr()), ctypes.c_void_p(q16_view.data_ptr()), row,
         ctypes.c_void_p(kd.data_ptr()), kd.stride(0), ctypes.c_void_p(scores.data_ptr()), ld,
-        ctypes.c_void_p(ids.data_ptr()), k, None, G, nq, H, D, n_kv, bs, k, 0, None)
+        ctypes.c_void_p(ids.data_ptr()), k, None, G, nq, H, D, n_kv, bs, k, 0, 0, None)
     torch.cuda.synchronize()
     assert st == 0, qsa.status_string(st)
     flat = q16_flat.cpu().numpy()
@@ -679,7 +679,7 @@ def test_phase_conversion_paths(case):
     st = qsa.lib.qsa_select_phase(
         ctypes.c_void_p(q32_rows.data_ptr()), None, row,
         ctypes.c_void_p(kd.data_ptr()), kd.stride(0), ctypes.c_void_p(scores2.data_ptr()), ld,
-        ctypes.c_void_p(ids2.data_ptr()), k, None, G, nq, H, D, n_kv, bs, k, 0, None)
+        ctypes.c_void_p(ids2.data_ptr()), k, None, G, nq, H, D, n_kv, bs, k, 0, 0, None)
     torch.cuda.synchronize()
     if off % 4 != 0:
         assert st == qsa.QSA_ERR_UNSUPPORTED, qsa.status_string(st)
@@ -728,7 +728,8 @@ def test_phase_converts_special_values(G, nq, off):
     st = qsa.lib.qsa_select_phase(
         ctypes.c_void_p(qd.data_ptr()), ctypes.c_void_p(ws.q16.data_ptr()), row,
         ctypes.c_void_p(kd.data_ptr()), kd.stride(0), ctypes.c_void_p(ws.scores.data_ptr()),
-        ws.ld_s, ctypes.c_void_p(ws.ids.data_ptr()), k, None, G, nq, H, D, n_kv, 64, k, 0, None)
+        ws.ld_s, ctypes.c_void_p(ws.ids.data_ptr()), k, None, G, nq, H, D, n_kv, 64, k, 0, 0,
+        None)
     torch.cuda.synchronize()
     assert st == 0, qsa.status_string(st)
     got16 = ws.q16.cpu().numpy().view(np.uint16)
@@ -975,3 +976,54 @@ def test_wide_rows_use_global_store_path():
     check_bound(s_gpu.astype(np.float64), ref, "wide rows")
     del out
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# the forced-tail rule (QSA_FORCE_TAIL): 1e9 added to the partial block's
+# score after its head sum, on every path that scores that block
+# ---------------------------------------------------------------------------
+
+FORCED = [
+    # G, nq, H, D, n_kv, bs: path
+    (1, 37, 4, 64, 1000, 64),          # small scorer, tail segment
+    (8, 1, 8, 128, 131109, 64),        # the decode step: small scorer, one query per KV head
+    (4, 4096, 8, 128, 40 * 64 + 5, 64),    # wide scorer, tail in the same launch
+    (2, 8192, 12, 64, 20 * 64 + 9, 64),    # wide scorer, two head passes (the rule on the last)
+    (4, 4200, 8, 128, 40, 64),         # only a tail block: the standalone tail kernel
+    (1, 50, 16, 128, 18 * 64, 64),     # no partial block: the flag changes nothing
+]
+
+
+@pytest.mark.parametrize("geo", FORCED, ids=lambda g: "G{}_nq{}_H{}_D{}_nkv{}".format(*g[:5]))
+def test_force_tail_scores_and_selection(geo):
+    G, nq, H, D, n_kv, bs = geo
+    k = 16
+    cfg = qi.Config("forced", G, nq, H, D, n_kv, bs, k, "normal", 900 + nq)
+    w = qi.make(cfg)
+    log(f"forced tail {geo}")
+    qd, kd = q_dev(w.q16), k_dev(w.kblk)
+    s0 = qsa.block_scores(qd, kd, n_kv, bs).cpu().numpy().reshape(G * nq, cfg.nb)
+    s1 = qsa.block_scores(qd, kd, n_kv, bs, force_tail=True).cpu().numpy().reshape(G * nq, cfg.nb)
+    torch.cuda.synchronize()
+    nf = cfg.nf
+    # the full blocks are untouched by the flag, bit for bit
+    assert np.array_equal(s0[:, :nf].view(np.uint32), s1[:, :nf].view(np.uint32))
+    if cfg.nb == nf:
+        assert np.array_equal(s0.view(np.uint32), s1.view(np.uint32))
+        return
+    # the tail bit for bit the fixed-order model with the rule, and within the
+    # rule's bound of the exact forced score
+    model = oracle.block_model_f32(w.q16, w.kblk, nf, force_tail=True)
+    assert np.array_equal(s1[:, nf].view(np.uint32), model.view(np.uint32))
+    rows = np.arange(min(G * nq, 512), dtype=np.int64) * max(1, (G * nq) // 512)
+    rows = np.unique(np.minimum(rows, G * nq - 1))
+    ref = oracle.force_tail(oracle.scores(w.q16, w.kblk, cfg.nb, rows=rows), n_kv, bs)
+    check_bound(s1[rows].astype(np.float64), ref, "forced")
+    # the phase with the rule selects the tail first in every row
+    ws = qsa.PhaseWorkspace(nq, G, H, D, n_kv, bs, k, dev())
+    ids = qsa.select_phase(torch.from_numpy(w.q32).to(dev()), kd, n_kv, bs, k, ws,
+                           force_tail=True).cpu().numpy().reshape(G * nq, k)
+    sc = ws.scores[:, :, :cfg.nb].cpu().numpy().reshape(G * nq, cfg.nb)
+    assert np.array_equal(sc.view(np.uint32), s1.view(np.uint32))
+    assert np.all(ids[:, 0] == nf)
+    check_ids(ids[rows], sc[rows].astype(np.float64), ref, k, "forced phase")

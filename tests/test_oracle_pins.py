@@ -860,3 +860,93 @@ def test_attention_bound_admits_fp32_model_and_rejects_mistakes():
         bad = _fp32_device_model(*case, **kw)
         assert not oracle.check_attention(bad, ref, B).ok, kw
     assert not oracle.check_attention(ref + 2.5 * B, ref, B).ok
+
+
+# ---------------------------------------------------------------------------
+# The forced-tail rule (reading taken of the "+1e9 dead-tail rule", Strata
+# pull request #856, "What": the partial last block gets 1e9 added to its
+# score after the head sum).  Pinned by closed forms of fp32 and float64
+# addition, by the ranking it must produce, and by the bound staying valid for
+# the one extra fp32 rounding a device makes.
+# ---------------------------------------------------------------------------
+
+def pin_force_tail(force_fn, model_fn) -> None:
+    cfg = qi.TINY                       # 15 full blocks and a 40-token tail block
+    w = qi.make(cfg, with_q32=False)
+    ref = oracle.scores(w.q16, w.kblk, cfg.nb)
+    fr = force_fn(ref, cfg.n_kv, cfg.bs)
+    nf = cfg.nf
+    # only the tail column moves, by 1e9 (f64: the scores are far below 2^29,
+    # so s + 1e9 is exact to 2^-23 and equal to the sum of the two)
+    assert np.array_equal(fr.score[:, :nf], ref.score[:, :nf])
+    assert np.array_equal(fr.S, ref.S)
+    assert np.array_equal(fr.B[:, :nf], ref.B[:, :nf])
+    d = fr.score[:, nf] - ref.score[:, nf]
+    assert np.all(np.abs(d - 1e9) <= 2.0 ** -22), d
+    # the tail ranks first in every row, the other k - 1 slots as before
+    ids_f = oracle.topk(fr.score, cfg.k)[0]
+    ids_0 = oracle.topk(ref.score[:, :nf], cfg.k - 1)[0]
+    assert np.all(ids_f[:, 0] == nf)
+    assert np.array_equal(ids_f[:, 1:], ids_0)
+    # the fixed-order fp32 model with the rule: fp32 spacing at 1e9 is 64 and
+    # 1e9 is exact in fp32, so fl32(s + 1e9) = 1e9 + 64 * rne(s / 64) while s
+    # stays far below 2^30 - 1e9
+    m0 = model_fn(w.q16, w.kblk, nf, force_tail=False).astype(np.float64)
+    m1 = model_fn(w.q16, w.kblk, nf, force_tail=True).astype(np.float64)
+    assert np.all(m0 < 1e6)
+    assert np.array_equal(m1, 1e9 + 64.0 * np.round(m0 / 64.0))
+    # and it lies within the rule's bound of the exact forced score
+    s_dev = ref.score.copy()
+    s_dev[:, nf] = m1
+    assert oracle.check_scores(s_dev, fr).ok
+    # no partial block (the full blocks alone, n_kv = nf * bs): nothing changes
+    r2 = oracle.Scores(ref.score[:, :nf], ref.S[:, :nf], ref.B[:, :nf], ref.rows)
+    f2 = force_fn(r2, nf * cfg.bs, cfg.bs)
+    assert np.array_equal(f2.score, r2.score) and np.array_equal(f2.B, r2.B)
+
+
+def test_force_tail_rule():
+    pin_force_tail(oracle.force_tail, oracle.block_model_f32)
+
+
+def test_force_tail_bound_covers_fp32_rounding():
+    """For any exact score s >= 0 of fp32 magnitude and any device value x
+    within the unforced bound B0 of s, fl32(x + 1e9) is within the forced
+    bound of s + 1e9: the rule's term 8*2^-24*1e9 (about 477) exceeds half
+    the fp32 spacing at and above 1e9 (32 or 64) with room to spare."""
+    rng = np.random.default_rng(11)
+    s = np.concatenate([rng.random(20000) * 10.0 ** rng.integers(-3, 8, 20000),
+                        [0.0, 31.9, 32.0, 32.1, 95.99, 96.0, 7.3e7]])
+    S = s * (1.0 + rng.random(s.size) * 5.0)
+    B0 = 2.0 ** -9.5 * S + 8.0 * 2.0 ** -24 * s
+    x = (s + (rng.random(s.size) * 2.0 - 1.0) * B0).astype(np.float32)   # a device score
+    forced = (x + np.float32(1e9)).astype(np.float64)
+    exact = s + 1e9
+    B1 = 2.0 ** -9.5 * S + 8.0 * 2.0 ** -24 * exact
+    assert np.all(np.abs(forced - exact) <= B1)
+
+
+@pytest.mark.parametrize("mutant", ["wrong_column", "bound_not_recomputed", "add_1e8",
+                                    "model_adds_twice"])
+def test_force_tail_pins_catch_planted_mistakes(mutant):
+    def bad_force(ref, n_kv, bs):
+        nf, nb = n_kv // bs, -(-n_kv // bs)
+        if nb == nf:
+            return ref
+        col = nf - 1 if mutant == "wrong_column" else nf
+        add = 1e8 if mutant == "add_1e8" else 1e9
+        score, B = ref.score.copy(), ref.B.copy()
+        score[:, col] += add
+        if mutant != "bound_not_recomputed":
+            B[:, col] = 2.0 ** -9.5 * ref.S[:, col] + 8.0 * 2.0 ** -24 * np.abs(score[:, col])
+        return oracle.Scores(score, ref.S, B, ref.rows)
+
+    def bad_model(q16, kblk, b, rows=None, force_tail=False):
+        out = oracle.block_model_f32(q16, kblk, b, rows, force_tail)
+        if force_tail and mutant == "model_adds_twice":
+            out = (out + np.float32(1e9)).astype(np.float32)
+        return out
+
+    with pytest.raises(AssertionError):
+        pin_force_tail(bad_force if mutant != "model_adds_twice" else oracle.force_tail,
+                       bad_model)

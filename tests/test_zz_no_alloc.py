@@ -30,7 +30,7 @@ def _noalloc(q32, kd, cfg, ids, vals, q_chunk=0):
     return qsa.lib.qsa_select_phase_noalloc(
         ctypes.c_void_p(q32.data_ptr()), None, qts, ctypes.c_void_p(kd.data_ptr()), kd.stride(0),
         ctypes.c_void_p(ids.data_ptr()), cfg.k, ctypes.c_void_p(vals.data_ptr()), cfg.G, cfg.nq,
-        cfg.H, cfg.D, cfg.n_kv, cfg.bs, cfg.k, q_chunk,
+        cfg.H, cfg.D, cfg.n_kv, cfg.bs, cfg.k, q_chunk, 0,
         ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
 
 
