@@ -86,12 +86,23 @@ def _code_only(text: str) -> str:
     return "\n".join(line for line in lines if line)
 
 
-def source_digest() -> str:
+# The source files of each profiled kernel: the kernel and its launcher, and
+# the shared header.  A stored counter figure stays valid while these are
+# unchanged, whatever happens in the other kernels' files.
+KERNEL_FILES = {
+    "score_small": ("qsa_small.hip", "qsa_internal.h"),
+    "score_full": ("qsa_score.hip", "qsa_internal.h"),
+    "topk": ("qsa_topk.hip", "qsa_topk_row.h", "qsa_internal.h"),
+}
+
+
+def source_digest(files=None) -> str:
     """sha256 over the kernel sources' code (comments left out), to tie
-    stored counter figures to the code they were taken on."""
+    stored counter figures to the code they were taken on: the named files
+    of the csrc directory, or all of them."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_attention_block_qsa_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(files if files is not None else os.listdir(csrc)):
         with open(os.path.join(csrc, name), encoding="utf-8") as f:
             h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
@@ -109,7 +120,7 @@ def read_traffic(kernel: str, workload: str):
         if "=" in line:
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_digest") != source_digest():
+    if kv.get("source_digest") != source_digest(KERNEL_FILES.get(kernel)):
         return None
     try:
         return float(kv["bytes_per_launch"])
@@ -180,6 +191,9 @@ class Phase:
                  P(ws.ids), c.k, None, c.G, c.nq, c.H, c.D, c.n_kv, c.bs)
         self._phase = (L.qsa_select_phase, phase + (c.k, 0, 0))
         self._score = (L.qsa_select_phase, phase + (0, 0, 0))   # k = 0: the scorer launch only
+        # the phase with the selection inside the scorer's launch where the
+        # fused scorer serves the shape (QSA_FUSED_SELECT = 2)
+        self._phase_fused = (L.qsa_select_phase, phase + (c.k, 0, qsa.FUSED_SELECT))
 
     def _call(self, fa):
         fn, args = fa
@@ -201,6 +215,9 @@ class Phase:
 
     def step(self):
         self._call(self._phase)
+
+    def step_fused(self):
+        self._call(self._phase_fused)
 
 
 def graph_of(torch, fn, n):
@@ -435,12 +452,16 @@ def measure(cfg, qsa, torch, steps, warmup, w=None, calls_100=False):
 
     stages, alone = {}, {}
     for d, name, fn in ((stages, "scorer", ph.score), (stages, "topk", ph.topk),
-                        (alone, "convert", ph.convert), (alone, "block_scores_f16", ph.score16)):
+                        (alone, "convert", ph.convert), (alone, "block_scores_f16", ph.score16),
+                        (alone, "phase_fused_select", ph.step_fused)):
         g = graph_of(torch, fn, steps)
         d[name] = time_graph(torch, g, steps)
         del g
+    # the fused form's results are the separate selector's, bit for bit
+    fused_same = bool(torch.equal(eager_ids, ph.ws.ids))
     med9 = {name: median_of_9(torch, fn) for name, fn in
-            (("phase", ph.step), ("scorer", ph.score), ("block_scores_f16", ph.score16))}
+            (("phase", ph.step), ("scorer", ph.score), ("block_scores_f16", ph.score16),
+             ("phase_fused_select", ph.step_fused))}
     c100 = ({name: single_call_stats(torch, fn) for name, fn in
              (("phase", ph.step), ("scorer", ph.score), ("block_scores_f16", ph.score16))}
             if calls_100 else None)
@@ -452,6 +473,7 @@ def measure(cfg, qsa, torch, steps, warmup, w=None, calls_100=False):
         "ms_per_step": ms_step,
         "wall_s": wall,
         "graph_replay_matches_eager": same,
+        "fused_select_matches": fused_same,
         "stages_ms": stages,
         "entry_points_ms": alone,
         "scorer_tflops": flop / (stages["scorer"] * 1e-3) / 1e12,
@@ -695,6 +717,11 @@ def main():
             "scorer_frac_of_measured_peak":
                 (pr["scorer_tflops"] / peaks["mfma_f16_random_tflops"] if peaks else None),
             "graph_replay_matches_eager": pr["graph_replay_matches_eager"],
+            # the phase with the selection fused into the scorer's launch
+            # (QSA_FUSED_SELECT), same ids bit for bit
+            "phase_fused_select_ms": pe["phase_fused_select"],
+            "phase_fused_select_median_of_9_ms": pr["median_of_9_ms"]["phase_fused_select"],
+            "fused_select_matches": pr["fused_select_matches"],
             # single launches timed by the pages' protocol (3 warmups, median of 9)
             "median_of_9_ms": pr["median_of_9_ms"],
             "scorer_frac_of_peak_median_of_9":
@@ -707,8 +734,10 @@ def main():
               f"TFLOP/s; median of 9 single launches: phase "
               f"{pr['median_of_9_ms']['phase'] * 1e3:.1f} us, scorer "
               f"{pr['median_of_9_ms']['scorer'] * 1e3:.1f} us, fp16-input scorer "
-              f"{pr['median_of_9_ms']['block_scores_f16'] * 1e3:.1f} us", file=sys.stderr,
-              flush=True)
+              f"{pr['median_of_9_ms']['block_scores_f16'] * 1e3:.1f} us; fused-select phase "
+              f"{pe['phase_fused_select'] * 1e3:.1f} us (graph), "
+              f"{pr['median_of_9_ms']['phase_fused_select'] * 1e3:.1f} us (median of 9), same ids "
+              f"{pr['fused_select_matches']}", file=sys.stderr, flush=True)
 
     decode = None
     if args.decode_steps > 0 and cfg.name != qi.DECODE.name:
@@ -812,6 +841,7 @@ def main():
         "context_sweep": sweep,
         "beside_the_phase": beside,
         "source_digest": source_digest(),
+        "kernel_digests": {k: source_digest(f) for k, f in KERNEL_FILES.items()},
         "context": {"pages_rx7900xtx_gfx1100_scores_ms_128k": {"warp": 2.627, "wmma": 0.252},
                     "note": "other hardware; context only"},
     }

@@ -104,6 +104,15 @@ qsa_status qsa_convert_f32_f16(const float *src, uint16_t *dst, int64_t n, void 
  * score.  It applies only when that block exists (n_kv % bs != 0). */
 #define QSA_FORCE_TAIL 1u
 
+/* qsa_select_phase / qsa_select_phase_noalloc: select inside the scorer's
+ * launch where the fused scorer serves the shape (many query rows, so that
+ * each workgroup scores every block of its 64 queries; H <= 8; 513-1024 or
+ * 2049-2112 blocks); other shapes take the separate selector launch.  The
+ * ids, values and scores are the same bits either way: the fused scorer
+ * writes the scores, then each wave selects its own rows with the
+ * selector's row code.  Not accepted by qsa_block_scores. */
+#define QSA_FUSED_SELECT 2u
+
 /*
  * qsa_block_scores -- step 2 of the phase: the score of every (g, t, b)
  * cell, b < nb = ceil(n_kv / bs).  Blocks b < nf = floor(n_kv / bs) go to the
@@ -236,7 +245,7 @@ int64_t qsa_sparse_attention_ws_floats(int32_t G, int32_t nq, int32_t H, int32_t
  *             at query t0, row g*n + t' holds the scores of query t0 + t'
  *             (after the call: those of the last chunk)
  *   ids, vals as qsa_select_topk with rows = G*nq (vals may be NULL)
- *   flags     as qsa_block_scores (QSA_FORCE_TAIL)
+ *   flags     QSA_FORCE_TAIL (as qsa_block_scores), QSA_FUSED_SELECT, or 0
  *   other arguments as qsa_block_scores / qsa_select_topk.
  * Workspaces must not overlap the inputs or outputs.  Errors as the three
  * stage entry points; the whole call is validated before the first launch.

@@ -27,6 +27,7 @@ NOALLOC_SCRATCH_BYTES = 64 << 20   # qsa.h QSA_NOALLOC_SCRATCH_BYTES
 ABI_VERSION = 6   # qsa.h QSA_ABI_VERSION this binding is written for
 BLOCK_KEYS_MAX_BS = 8192   # qsa.h QSA_BLOCK_KEYS_MAX_BS
 FORCE_TAIL = 1   # qsa.h QSA_FORCE_TAIL
+FUSED_SELECT = 2   # qsa.h QSA_FUSED_SELECT
 EXPORTS = ("qsa_abi_version", "qsa_status_string", "qsa_convert_f32_f16", "qsa_block_keys",
            "qsa_block_scores", "qsa_select_topk", "qsa_select_phase", "qsa_select_phase_noalloc",
            "qsa_sparse_attention", "qsa_sparse_attention_ws_floats")
@@ -231,13 +232,17 @@ class PhaseWorkspace:
 
 def select_phase(q: torch.Tensor, kblk: torch.Tensor, n_kv: int, bs: int, k: int,
                  ws: PhaseWorkspace | None = None, q_chunk: int | None = None,
-                 force_tail: bool = False, stream: torch.cuda.Stream | None = None):
+                 force_tail: bool = False, fused_select: bool = False,
+                 stream: torch.cuda.Stream | None = None):
     """The whole phase: (fp32 -> fp16 conversion when q is float32), scores,
     top-k.  Returns ids [G, nq, k] (and vals when the workspace has them).
     fp32 queries are converted by the scorers as they load them; without a
     kept fp16 copy (ws.q16 is None) their rows must be 16-byte aligned, which
     a contiguous tensor from the caching allocator always is.  q_chunk is the
-    workspace's when one is given (a different value is refused), else 0."""
+    workspace's when one is given (a different value is refused), else 0.
+    force_tail: the forced-tail rule (FORCE_TAIL); fused_select: select inside
+    the scorer's launch where the fused scorer serves the shape (FUSED_SELECT),
+    with the same results."""
     fp32 = q.dtype == torch.float32
     nq, G, H, D, qts = _check_q(q, torch.float32 if fp32 else torch.float16)
     if fp32 and not q.is_contiguous():
@@ -259,7 +264,8 @@ def select_phase(q: torch.Tensor, kblk: torch.Tensor, n_kv: int, bs: int, k: int
            lib.qsa_select_phase(_ptr(q) if fp32 else None, _ptr(q16), qts, _ptr(kblk), khs,
                                 _ptr(ws.scores), ws.ld_s, _ptr(ws.ids), ws.ids.stride(1),
                                 _ptr(ws.vals), G, nq, H, D, n_kv, bs, k, ws.q_chunk,
-                                FORCE_TAIL if force_tail else 0, _stream(stream)))
+                                (FORCE_TAIL if force_tail else 0) |
+                                (FUSED_SELECT if fused_select else 0), _stream(stream)))
     return (ws.ids, ws.vals) if ws.vals is not None else ws.ids
 
 

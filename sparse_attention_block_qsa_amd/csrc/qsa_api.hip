@@ -112,9 +112,11 @@ float tail_addend(uint32_t flags) { return (flags & QSA_FORCE_TAIL) ? 1e9f : 0.0
 // scores the tail whatever the number of rows, since the standalone tail
 // kernel reads fp16 queries only.
 hipError_t run_scores(const ScoreGeom &geo, const ScoreCheck &c, hipStream_t s,
-                      const float *q32 = nullptr, uint16_t *q16w = nullptr) {
+                      const float *q32 = nullptr, uint16_t *q16w = nullptr,
+                      const qsa::FusedSelect *fs = nullptr, bool *selected = nullptr) {
     const bool tail = c.nb > c.nf;
-    if (c.nf > 0) return qsa::launch_score_full(geo, tail, s, q32, q16w);
+    if (selected) *selected = false;
+    if (c.nf > 0) return qsa::launch_score_full(geo, tail, s, q32, q16w, fs, selected);
     if (!tail) return hipSuccess;
     if (q32 || qsa::small_rows(geo)) return qsa::launch_score_small(geo, true, s, q32, q16w);
     return qsa::launch_tail(geo, c.nf, s);
@@ -243,7 +245,7 @@ qsa_status qsa_select_phase(const float *q32, uint16_t *q16, int64_t q_tok_strid
                             int64_t ld_s, int32_t *ids, int64_t ld_ids, float *vals, int32_t G,
                             int32_t nq, int32_t H, int32_t D, int64_t n_kv, int32_t bs, int32_t k,
                             int64_t q_chunk, uint32_t flags, void *stream) {
-    if (q_chunk < 0 || (flags & ~QSA_FORCE_TAIL)) return QSA_ERR_ARG;
+    if (q_chunk < 0 || (flags & ~(QSA_FORCE_TAIL | QSA_FUSED_SELECT))) return QSA_ERR_ARG;
     const int64_t qc = (q_chunk > 0 && q_chunk < nq) ? q_chunk : nq;
     ScoreCheck c;
     // scores are validated for the chunk-sized workspace; the query source
@@ -288,11 +290,17 @@ qsa_status qsa_select_phase(const float *q32, uint16_t *q16, int64_t q_tok_strid
                                                     static_cast<int64_t>(G) * H * D, q_tok_stride, s);
             if (e != hipSuccess) return QSA_ERR_HIP;
         }
+        // with QSA_FUSED_SELECT the shapes the fused scorer serves are
+        // selected inside the scorer's launch
+        const qsa::FusedSelect fsel{ids, ld_ids, vals, k, nq, t0};
+        const qsa::FusedSelect *fs = (flags & QSA_FUSED_SELECT) && k > 0 ? &fsel : nullptr;
+        bool selected = false;
         if (c.nb > 0) {
-            hipError_t e = fused ? run_scores(geo, c, s, q32 + qoff, q16c) : run_scores(geo, c, s);
+            hipError_t e = fused ? run_scores(geo, c, s, q32 + qoff, q16c, fs, &selected)
+                                 : run_scores(geo, c, s, nullptr, nullptr, fs, &selected);
             if (e != hipSuccess) return QSA_ERR_HIP;
         }
-        if (k > 0) {
+        if (k > 0 && !selected) {
             // the scorer wrote this chunk's rows at g*n + t' (n = rows in the
             // chunk); in one pass over all rows that is the output's row
             // order too, and the selector sees one flat group of rows

@@ -78,8 +78,24 @@ struct ScoreGeom {
 // read as fp32 in the layout of g.q16, converted on load (f16_rne bits), and
 // their fp16 bits written to q16w when it is set: the G*H*D elements of every
 // token row, nothing between rows.
+// Where a scorer that also selects (the fused form) writes the top-k of
+// score row g*nq + t: ids[(g*dst_group_rows + dst_row0 + t)*ld_ids + j],
+// j < k, and vals likewise when set.
+struct FusedSelect {
+    int32_t *ids;
+    int64_t ld_ids;
+    float *vals;
+    int32_t k;
+    int64_t dst_group_rows, dst_row0;
+};
+
+// With fs set, shapes the fused form serves (one workgroup per query group
+// over all blocks, one head pass, 513-1024 or 2049-2112 blocks) are scored
+// and selected in the one launch, and *selected is set; otherwise the
+// selection is left to the caller.
 hipError_t launch_score_full(const ScoreGeom &g, bool tail, hipStream_t s,
-                             const float *q32 = nullptr, uint16_t *q16w = nullptr);
+                             const float *q32 = nullptr, uint16_t *q16w = nullptr,
+                             const FusedSelect *fs = nullptr, bool *selected = nullptr);
 
 // Few query rows (fewer than 256 groups of 64 over the KV heads): the
 // scorer of qsa_small.hip, latency-bound shapes.

@@ -56,7 +56,8 @@ qsa_status qsa_select_phase_noalloc(const float *q32, uint16_t *q16, int64_t q_t
                                     int32_t *ids, int64_t ld_ids, float *vals, int32_t G,
                                     int32_t nq, int32_t H, int32_t D, int64_t n_kv, int32_t bs,
                                     int32_t k, int64_t q_chunk, uint32_t flags, void *stream) {
-    if (G < 0 || nq < 0 || n_kv < 0 || q_chunk < 0 || (flags & ~QSA_FORCE_TAIL))
+    if (G < 0 || nq < 0 || n_kv < 0 || q_chunk < 0 ||
+        (flags & ~(QSA_FORCE_TAIL | QSA_FUSED_SELECT)))
         return QSA_ERR_ARG;
     if (bs < 1) return QSA_ERR_UNSUPPORTED;
     // Rows of the workspace: nb scores rounded up to 32 floats, so that every

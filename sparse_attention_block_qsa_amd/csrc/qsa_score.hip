@@ -47,7 +47,14 @@
 //  * Grid: (KV head, 64-query group, block split), with logical ids laid out
 //    so that each XCD (blockIdx % 8) takes a contiguous range: the splits of
 //    one query group and the query groups of one KV head share that XCD's L2.
+//  * Fused selection (SEL > 0, one split per query group): after its last
+//    tile and the partial block, each wave selects the top-k of its own 16
+//    query rows, whose scores (every block, tail included) only it wrote,
+//    with the one-wave row selection of the top-k selector
+//    (qsa_topk_row.h), so the phase needs no selector launch.  The scores
+//    are still written; the selection re-reads them.
 #include "qsa_internal.h"
+#include "qsa_topk_row.h"
 
 namespace qsa {
 namespace {
@@ -71,6 +78,13 @@ struct ScoreArgs {
     int32_t n_qgroups, n_splits, tiles_per_split, n_tiles;
     float tail_add;        // added to the partial block's score when nonzero
                            // (last head pass only)
+    // fused selection (SEL > 0): ids / vals of row g*nq + t go to
+    // ids[(g*dst_group_rows + dst_row0 + t)*ld_ids + 0 .. k)
+    int32_t *ids;
+    int64_t ld_ids;
+    float *vals;
+    int32_t k, nb;
+    int64_t dst_group_rows, dst_row0;
 };
 
 // s_waitcnt immediate for vmcnt(0) with the other counters left free
@@ -89,7 +103,7 @@ __device__ __forceinline__ float relu_bits(float x) {
     return __builtin_bit_cast(float, max(__builtin_bit_cast(int32_t, x), 0));
 }
 
-template <int D, int NP, bool ACCUM, bool BUF, bool TAIL, bool SRC32>
+template <int D, int NP, bool ACCUM, bool BUF, bool TAIL, bool SRC32, int SEL = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void score_full_kernel(ScoreArgs a) {
     constexpr int KS = D / 16;              // MFMA K-steps per head
@@ -113,6 +127,10 @@ void score_full_kernel(ScoreArgs a) {
     constexpr int NS = DIST + 1;   // ring slots
     __shared__ uint4 kbuf[NS][TILE_U4];
     __shared__ uint4 ktail[TAIL ? CHUNKS : 1];   // the partial block's key
+    // fused selection: per wave 128 candidate composites and the row's values
+    __shared__ uint64_t sel_slot[SEL > 0 ? kScoreWaves : 1][SEL > 0 ? 128 : 1];
+    __shared__ uint32_t sel_stash[SEL > 0 ? kScoreWaves : 1][SEL > 0 ? 64 * SEL : 1];
+    static_assert(SEL == 0 || (!ACCUM && BUF), "fused selection: one head pass, buffer stores");
 
     const uint32_t L = xcd_logical_id(blockIdx.x, gridDim.x);
     const int split = static_cast<int>(L % a.n_splits);
@@ -473,6 +491,33 @@ void score_full_kernel(ScoreArgs a) {
             }
         }
     }
+
+    if constexpr (SEL > 0) {
+        // The wave's score stores (its 16 rows, every block) before its own
+        // loads of them: the stores were made by other lanes of this wave.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        const int wu = __builtin_amdgcn_readfirstlane(w);
+        const int nrows = min(kWaveQueries, a.nq - t_base);   // uniform
+        auto row = [&](int i) { return srow_base + static_cast<int64_t>(t_base + i) * a.ld_s; };
+        auto select = [&](int i, const uint32_t (&x)[SEL]) __attribute__((always_inline)) {
+            const int64_t drow = static_cast<int64_t>(g) * a.dst_group_rows + a.dst_row0 + t_base + i;
+            topk_row_select<SEL, true>(row(i), a.nb, a.k, x, a.ids + drow * a.ld_ids,
+                                       a.vals ? a.vals + drow * a.ld_ids : nullptr, sel_slot[wu],
+                                       sel_stash[wu], l);
+        };
+        // two register sets: the next row's loads are in flight while the
+        // current row is selected
+        uint32_t xa[SEL], xb[SEL];
+        if (nrows > 0) topk_row_load<SEL>(row(0), a.nb, l, xa);
+        for (int i = 0; i < nrows; i += 2) {
+            if (i + 1 < nrows) topk_row_load<SEL>(row(i + 1), a.nb, l, xb);
+            select(i, xa);
+            if (i + 1 >= nrows) break;
+            if (i + 2 < nrows) topk_row_load<SEL>(row(i + 2), a.nb, l, xa);
+            select(i + 1, xb);
+        }
+    }
 }
 
 typedef void (*score_fn)(ScoreArgs);
@@ -505,6 +550,40 @@ score_fn pick(int D, int np, bool accum, bool buf, bool tail, bool src32) {
     return nullptr;
 }
 
+// The fused-selection instances: one head pass (np <= 4), buffer stores, and
+// rows whose 64-wide column count takes the selector's 16- or 33-column case
+// (9-16 columns: 513-1024 blocks; 33 columns: 2049-2112 blocks).
+template <int D, bool TAIL, bool SRC32, int SEL>
+score_fn pick_sel_np(int np) {
+    switch (np) {
+        case 1: return score_full_kernel<D, 1, false, true, TAIL, SRC32, SEL>;
+        case 2: return score_full_kernel<D, 2, false, true, TAIL, SRC32, SEL>;
+        case 3: return score_full_kernel<D, 3, false, true, TAIL, SRC32, SEL>;
+        case 4: return score_full_kernel<D, 4, false, true, TAIL, SRC32, SEL>;
+    }
+    return nullptr;
+}
+
+template <int D, int SEL>
+score_fn pick_sel_ts(int np, bool tail, bool src32) {
+    if (tail) return src32 ? pick_sel_np<D, true, true, SEL>(np) : pick_sel_np<D, true, false, SEL>(np);
+    return src32 ? pick_sel_np<D, false, true, SEL>(np) : pick_sel_np<D, false, false, SEL>(np);
+}
+
+// Columns of the fused selection for nb blocks (0: no fused form).
+int sel_columns(int64_t nb) {
+    const int64_t nj = (nb + 63) / 64;
+    if (nj > 8 && nj <= 16) return 16;
+    if (nj == 33) return 33;
+    return 0;
+}
+
+score_fn pick_sel(int D, int np, bool tail, bool src32, int sel) {
+    if (D == 128) return sel == 16 ? pick_sel_ts<128, 16>(np, tail, src32) : pick_sel_ts<128, 33>(np, tail, src32);
+    if (D == 64) return sel == 16 ? pick_sel_ts<64, 16>(np, tail, src32) : pick_sel_ts<64, 33>(np, tail, src32);
+    return nullptr;
+}
+
 // Splits of the block axis so that base * splits workgroups reach target
 // (at most one split per tile); returns the splits and the tiles per split.
 void split_blocks(int64_t base, int64_t n_tiles, int64_t target, int64_t *splits, int64_t *tps) {
@@ -521,7 +600,8 @@ void split_blocks(int64_t base, int64_t n_tiles, int64_t target, int64_t *splits
 }  // namespace
 
 hipError_t launch_score_full(const ScoreGeom &geo, bool tail, hipStream_t s, const float *q32,
-                             uint16_t *q16w) {
+                             uint16_t *q16w, const FusedSelect *fs, bool *selected) {
+    if (selected) *selected = false;
     if (geo.nf <= 0 || geo.nq <= 0 || geo.G <= 0) return hipSuccess;
     if (small_rows(geo)) return launch_score_small(geo, tail, s, q32, q16w);
     const int hpp = kHeadsPerPass;
@@ -538,6 +618,25 @@ hipError_t launch_score_full(const ScoreGeom &geo, bool tail, hipStream_t s, con
     const int64_t grid = base * splits;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
 
+    // fused selection: each workgroup scores every block of its query group
+    const int64_t nb = geo.nf + (tail ? 1 : 0);
+    const int sel = fs && fs->k > 0 ? sel_columns(nb) : 0;
+    if (sel > 0 && splits == 1 && geo.H <= hpp && buf) {
+        const int np = (geo.H + 1) / 2;
+        score_fn fn = pick_sel(geo.D, np, tail, q32 != nullptr, sel);
+        if (!fn) return hipErrorInvalidValue;
+        ScoreArgs a{geo.q16, q32, q32 ? q16w : nullptr, geo.qts, geo.kblk, geo.khs, geo.scores,
+                    geo.ld_s, geo.G, geo.nq, geo.H, 0, geo.H, 0, geo.nf,
+                    static_cast<int32_t>(n_qgroups), 1, static_cast<int32_t>(tps),
+                    static_cast<int32_t>(n_tiles), geo.tail_add, fs->ids, fs->ld_ids, fs->vals,
+                    fs->k, static_cast<int32_t>(nb), fs->dst_group_rows, fs->dst_row0};
+        void *args[] = {&a};
+        hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(fn),
+                                       dim3(static_cast<unsigned>(grid)), dim3(256), args, 0, s);
+        if (e == hipSuccess && selected) *selected = true;
+        return e;
+    }
+
     for (int h0 = 0; h0 < geo.H; h0 += hpp) {
         const int nh = (geo.H - h0 < hpp) ? geo.H - h0 : hpp;
         const int np = (nh + 1) / 2;
@@ -547,7 +646,7 @@ hipError_t launch_score_full(const ScoreGeom &geo, bool tail, hipStream_t s, con
                     geo.G, geo.nq, geo.H, h0, nh, h0 > 0 ? 1 : 0, geo.nf,
                     static_cast<int32_t>(n_qgroups), static_cast<int32_t>(splits),
                     static_cast<int32_t>(tps), static_cast<int32_t>(n_tiles),
-                    h0 + nh == geo.H ? geo.tail_add : 0.0f};
+                    h0 + nh == geo.H ? geo.tail_add : 0.0f, nullptr, 0, nullptr, 0, 0, 0, 0};
         void *args[] = {&a};
         hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(fn),
                                        dim3(static_cast<unsigned>(grid)), dim3(256), args, 0, s);

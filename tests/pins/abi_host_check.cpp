@@ -32,10 +32,18 @@ std::vector<Launch> g_launches;
 
 namespace qsa {
 hipError_t launch_score_full(const ScoreGeom &g, bool tail, hipStream_t, const float *q32,
-                             uint16_t *) {
+                             uint16_t *, const FusedSelect *fs, bool *selected) {
     // the real launcher hands few rows to the small scorer: bit 4 records it
     g_launches.push_back({'f', g.nq, g.nf, (tail ? 1 : 0) + (q32 ? 2 : 0) + (small_rows(g) ? 4 : 0) +
                                               (g.tail_add == 1e9f ? 8 : 0)});
+    // a fused selection request: 'F' records where the ids go; this stand-in
+    // takes it for 4096 or more query rows per pass (the real launcher
+    // decides by shape)
+    if (selected) *selected = false;
+    if (fs) {
+        g_launches.push_back({'F', fs->dst_group_rows, fs->dst_row0, fs->k});
+        if (selected) *selected = g.nq >= 4096;
+    }
     return hipSuccess;
 }
 hipError_t launch_score_small(const ScoreGeom &g, bool tail, hipStream_t, const float *q32,
@@ -308,6 +316,23 @@ int main() {
         expect("phase forced tail", QSA_OK, [&] { return a.call(); }, 2);
         CHECK(g_launches[0].kind == 'f' && (g_launches[0].c & 1) && (g_launches[0].c & 8),
               "forced tail: the phase's scorer adds 1e9 to the partial block");
+        a.flags = QSA_FUSED_SELECT;
+        expect("phase fused select, not taken", QSA_OK, [&] { return a.call(); }, 3);
+        CHECK(g_launches[1].kind == 'F' && g_launches[1].a == 256 && g_launches[1].b == 0 &&
+                  g_launches[1].c == 16 && g_launches[2].kind == 'k',
+              "a fused request the scorer declines is followed by the selector launch");
+        PArgs f;
+        f.q16 = nullptr;
+        f.flags = QSA_FUSED_SELECT;
+        f.G = 2;
+        f.nq = 8192;
+        f.qts = 2 * 8 * 128;
+        f.q_chunk = 4096;
+        expect("phase fused select, chunks", QSA_OK, [&] { return f.call(); }, 4);
+        CHECK(g_launches[0].kind == 'f' && g_launches[1].kind == 'F' && g_launches[1].a == 8192 &&
+                  g_launches[1].b == 0 && g_launches[2].kind == 'f' && g_launches[3].kind == 'F' &&
+                  g_launches[3].b == 4096,
+              "fused chunks: the ids of chunk j go to query rows 4096*j onwards, no selector launch");
         PArgs b;
         b.q32 = reinterpret_cast<float *>(uintptr_t(0x20004));   // 4-byte aligned only
         expect("phase separate conversion", QSA_OK, [&] { return b.call(); }, 3);

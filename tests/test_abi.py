@@ -154,7 +154,7 @@ def phase_call(lib, **kw):
     (dict(ld_s=10), ARG), (dict(q32=A16 + 2), UNSUP), (dict(H=20), UNSUP),
     # no fp16 buffer: the fp32 rows must be 16-byte aligned
     (dict(q16=None, q32=A16 + 4), UNSUP), (dict(q16=None, qts=8 * 128 + 2), UNSUP),
-    (dict(flags=2), ARG), (dict(flags=1 << 31), ARG),
+    (dict(flags=4), ARG), (dict(flags=1 << 31), ARG),   # QSA_FORCE_TAIL | QSA_FUSED_SELECT only
 ])
 def test_select_phase_refusals(lib, kw, want):
     assert phase_call(lib, **kw) == want
@@ -177,7 +177,7 @@ def noalloc_call(lib, **kw):
 
 @pytest.mark.parametrize("kw,want", [
     (dict(q_chunk=-1), ARG), (dict(G=-1), ARG), (dict(nq=-1), ARG), (dict(n_kv=-1), ARG),
-    (dict(bs=0), UNSUP), (dict(flags=2), ARG),
+    (dict(bs=0), UNSUP), (dict(flags=4), ARG),
     # one query's score row (17M blocks of one token, 68 MB) exceeds the 64 MiB array
     (dict(n_kv=17 << 20, bs=1, khs=(17 << 20) * 128), TOO_LARGE),
     # four KV heads of 2049 blocks fit 2016 queries per pass, not 4096

@@ -33,7 +33,7 @@ def test_code_only_keeps_every_token_of_code():
     assert bench._code_only(src) == "x = y / z;\nw = *p;"
 
 
-def _digest_of(tmp_path, files):
+def _digest_of(tmp_path, files, only=None):
     csrc = tmp_path / "sparse_attention_block_qsa_amd" / "csrc"
     csrc.mkdir(parents=True, exist_ok=True)
     for name in os.listdir(csrc):
@@ -43,7 +43,7 @@ def _digest_of(tmp_path, files):
     old = bench.ROOT
     try:
         bench.ROOT = str(tmp_path)
-        return bench.source_digest()
+        return bench.source_digest(only)
     finally:
         bench.ROOT = old
 
@@ -53,6 +53,16 @@ def test_source_digest_ignores_comments_and_follows_code(tmp_path):
     assert _digest_of(tmp_path, {"k.hip": "// why\nint f() { return 1; }  // one\n\n"}) == base
     assert _digest_of(tmp_path, {"k.hip": "int f() { return 2; }\n"}) != base
     assert _digest_of(tmp_path, {"k2.hip": "int f() { return 1; }\n"}) != base
+
+
+def test_kernel_digest_follows_only_its_own_files(tmp_path):
+    a = {"a.hip": "int f() { return 1; }\n", "b.hip": "int g() { return 1; }\n"}
+    base = _digest_of(tmp_path, a, only=("a.hip",))
+    assert _digest_of(tmp_path, {**a, "b.hip": "int g() { return 2; }\n"}, only=("a.hip",)) == base
+    assert _digest_of(tmp_path, {**a, "a.hip": "int f() { return 2; }\n"}, only=("a.hip",)) != base
+    for files in bench.KERNEL_FILES.values():   # every listed file exists
+        for name in files:
+            assert os.path.exists(os.path.join(ROOT, "sparse_attention_block_qsa_amd", "csrc", name))
 
 
 def test_read_traffic_needs_the_current_digest(tmp_path, monkeypatch):
