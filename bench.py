@@ -93,6 +93,7 @@ KERNEL_FILES = {
     "score_small": ("qsa_small.hip", "qsa_internal.h"),
     "score_full": ("qsa_score.hip", "qsa_internal.h"),
     "topk": ("qsa_topk.hip", "qsa_topk_row.h", "qsa_internal.h"),
+    "score_decode": ("qsa_decode.hip", "qsa_internal.h"),
 }
 
 
@@ -130,13 +131,17 @@ def read_traffic(kernel: str, workload: str):
 
 def scorer_kernel(cfg):
     """The scorer kernel the phase runs for this workload (fp32 queries,
-    converted on load): the small scorer when the KV heads x groups of 64
-    queries number fewer than 256, else the wide one (head passes of up to
-    eight heads); the tail block, when there is one, is scored inside the
-    same launch.  Returns the profile key and the kernel's name."""
+    converted on load): the decode scorer when one MFMA row block holds
+    every query of a KV head (16 / head pairs), else the small scorer when
+    the KV heads x groups of 64 queries number fewer than 256, else the wide
+    one (head passes of up to eight heads); the tail block, when there is
+    one, is scored inside the same launch.  Returns the profile key and the
+    kernel's name."""
     tail = "true" if cfg.n_kv % cfg.bs else "false"
+    np_ = 1 if cfg.H <= 2 else 2 if cfg.H <= 4 else 4 if cfg.H <= 8 else 8
+    if cfg.nf > 0 and cfg.nq <= 16 // np_:
+        return "score_decode", f"score_decode_kernel<{cfg.D},{np_},true>"
     if cfg.G * -(-cfg.nq // 64) < 256:
-        np_ = 1 if cfg.H <= 2 else 2 if cfg.H <= 4 else 4 if cfg.H <= 8 else 8
         # K tiles per staged chunk: 2 when a block segment holds an even
         # number of at least four tiles (segments give about 256 workgroups,
         # at least one tile each)
@@ -421,6 +426,15 @@ def measured_peaks(torch, power=None) -> dict | None:
     res["hbm_read_gbs"] = nbytes / (ts[len(ts) // 2] * 1e-3) / 1e9
     res["hbm_read_bytes"] = nbytes
     del src
+    # the fixed cost of a launch: an empty kernel, timed like the stages (a
+    # graph of back-to-back launches), with one workgroup and with the decode
+    # scorer's grid (8 KV heads x 65 single-wave workgroups)
+    L.qsa_bench_empty.argtypes = [c_int, c_int, vp]
+    res["empty_launch_us"] = {}
+    for grid, block in ((1, 64), (520, 64), (1024, 256)):
+        fn = lambda: L.qsa_bench_empty(grid, block, ctypes.c_void_p(
+            torch.cuda.current_stream().cuda_stream))
+        res["empty_launch_us"][f"grid{grid}x{block}"] = _time_launches(torch, fn, 200) * 1e3
     return res
 
 
@@ -651,8 +665,8 @@ def main():
     peaks = measured_peaks(torch, power) if not args.no_peaks else None
     if peaks:
         print(f"# measured: mfma f16 {peaks['mfma_f16_random_tflops']:.0f} TFLOP/s random operands, "
-              f"{peaks['mfma_f16_zero_tflops']:.0f} zeros; HBM read {peaks['hbm_read_gbs']:.0f} GB/s",
-              file=sys.stderr, flush=True)
+              f"{peaks['mfma_f16_zero_tflops']:.0f} zeros; HBM read {peaks['hbm_read_gbs']:.0f} GB/s; "
+              f"empty launch {peaks['empty_launch_us']} us", file=sys.stderr, flush=True)
     roofline = {"bound": "mfma", "kernel": kernel_desc,
                 "achieved": achieved, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_FP16_TFLOPS,
@@ -756,6 +770,10 @@ def main():
             "scorer_bytes": sbytes,
             "scorer_gbs": sbytes / (ds["scorer"] * 1e-3) / 1e9,
             "scorer_frac_of_hbm": sbytes / (ds["scorer"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            # an empty kernel of the scorer's grid, timed the same way: the
+            # part of the scorer's time no kernel can avoid
+            "empty_launch_us_same_grid": (peaks["empty_launch_us"]["grid520x64"]
+                                          if peaks else None),
             "graph_replay_matches_eager": dr["graph_replay_matches_eager"],
         }
         print(f"# decode: {dr['ms_per_step'] * 1e3:.2f} us/step, scorer {ds['scorer'] * 1e3:.2f} us",

@@ -64,6 +64,10 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4 *src, int64_t n, 
     out[tid] = x;
 }
 
+// Does nothing: its launches measure the fixed cost of a launch, the floor
+// under every latency-bound kernel.
+__global__ void empty_kernel() {}
+
 }  // namespace
 
 extern "C" {
@@ -88,6 +92,13 @@ int qsa_bench_read(const void *src, int64_t n, uint32_t *out, int grid, void *st
     if (!src || !out || n < 1 || grid < 1) return hipErrorInvalidValue;
     hipLaunchKernelGGL(read_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
                        static_cast<const u32x4 *>(src), n, out);
+    return hipGetLastError();
+}
+
+// grid workgroups of block threads of a kernel with no work.
+int qsa_bench_empty(int grid, int block, void *stream) {
+    if (grid < 1 || block < 1 || block > 1024) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(empty_kernel, dim3(grid), dim3(block), 0, static_cast<hipStream_t>(stream));
     return hipGetLastError();
 }
 

@@ -21,8 +21,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libqsa.so")
 OBJDIR = os.path.join(ROOT, "_build", "qsa")
-SOURCES = ["qsa_api.hip", "qsa_attention.hip", "qsa_blockkeys.hip", "qsa_convert.hip", "qsa_noalloc.hip", "qsa_score.hip", "qsa_small.hip",
-           "qsa_tail.hip", "qsa_topk.hip"]
+SOURCES = ["qsa_api.hip", "qsa_attention.hip", "qsa_blockkeys.hip", "qsa_convert.hip",
+           "qsa_decode.hip", "qsa_noalloc.hip", "qsa_score.hip", "qsa_small.hip", "qsa_tail.hip",
+           "qsa_topk.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -112,6 +112,14 @@ bool src32_ok(const float *q32, int64_t qts);
 hipError_t launch_score_small(const ScoreGeom &g, bool tail, hipStream_t s,
                               const float *q32 = nullptr, uint16_t *q16w = nullptr);
 
+// Decode steps: at most one MFMA row block of queries per KV head (nq <=
+// 16 / head pairs) and at least one full block.  The decode scorer of
+// qsa_decode.hip: one wave per 32-block tile, operands straight from memory,
+// the same bits as the small scorer; with tail the partial block nf too.
+bool decode_rows(const ScoreGeom &g);
+hipError_t launch_score_decode(const ScoreGeom &g, bool tail, hipStream_t s,
+                               const float *q32 = nullptr, uint16_t *q16w = nullptr);
+
 // Fixed-order scorer of the single block b_tail, standalone (used when there
 // is no full block to share the query reads with).
 hipError_t launch_tail(const ScoreGeom &g, int64_t b_tail, hipStream_t s);

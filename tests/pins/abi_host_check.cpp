@@ -22,8 +22,8 @@
 namespace {
 
 struct Launch {
-    char kind;   // 'f' full scorer, 's' small scorer, 't' tail, 'k' top-k, 'c' convert, 'r' rows,
-                 // 'b' block keys, 'a' attention
+    char kind;   // 'f' full scorer, 's' small scorer, 'd' decode scorer, 't' tail, 'k' top-k,
+                 // 'c' convert, 'r' rows, 'b' block keys, 'a' attention, 'F' fused selection
     int64_t a, b, c;
 };
 std::vector<Launch> g_launches;
@@ -44,6 +44,16 @@ hipError_t launch_score_full(const ScoreGeom &g, bool tail, hipStream_t, const f
         g_launches.push_back({'F', fs->dst_group_rows, fs->dst_row0, fs->k});
         if (selected) *selected = g.nq >= 4096;
     }
+    return hipSuccess;
+}
+bool decode_rows(const ScoreGeom &g) {   // the rule of qsa_decode.hip
+    const int np = (g.H + 1) / 2;
+    const int pairs = np <= 1 ? 1 : np <= 2 ? 2 : np <= 4 ? 4 : 8;
+    return g.nq > 0 && g.nq <= 16 / pairs && g.nf > 0;
+}
+hipError_t launch_score_decode(const ScoreGeom &g, bool tail, hipStream_t, const float *q32,
+                               uint16_t *) {
+    g_launches.push_back({'d', g.nq, g.nf, (tail ? 1 : 0) + (q32 ? 2 : 0) + (g.tail_add == 1e9f ? 8 : 0)});
     return hipSuccess;
 }
 hipError_t launch_score_small(const ScoreGeom &g, bool tail, hipStream_t, const float *q32,
@@ -169,6 +179,20 @@ int main() {
         t.nq = 16384;
         t.qts = 4 * 8 * 128;
         t.ld_s = 1;
+        SArgs d = a;   // a decode step: one query of each of 8 KV heads, 2048 blocks + a tail
+        d.G = 8;
+        d.nq = 1;
+        d.qts = 8 * 8 * 128;
+        d.n_kv = 131109;
+        d.khs = 2049 * 128;
+        d.ld_s = 2049;
+        d.flags = QSA_FORCE_TAIL;
+        expect("decode scores", QSA_OK, [&] { return d.call(); }, 1);
+        CHECK(g_launches[0].kind == 'd' && g_launches[0].b == 2048 && g_launches[0].c == (1 | 8),
+              "a decode step takes the decode scorer, tail and forced rule included");
+        d.nq = 5;   // past one row block of 4 queries at H = 8
+        expect("five queries per KV head", QSA_OK, [&] { return d.call(); }, 1);
+        CHECK(g_launches[0].kind == 'f' && (g_launches[0].c & 4), "five queries take the small scorer");
         expect("tail only, many rows", QSA_OK, [&] { return t.call(); }, 1);
         CHECK(g_launches[0].kind == 't' && g_launches[0].b == 0 && g_launches[0].c == 0,
               "standalone tail of block 0, nothing added");

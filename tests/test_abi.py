@@ -247,8 +247,10 @@ def test_sparse_attention_workspace_size(lib):
     f = lib.qsa_sparse_attention_ws_floats
     # a decode step: 8 rows of 64 chunks split 8 ways (one chunk per wave)
     assert f(8, 1, 8, 128, 64, 64) == 8 * 8 * 8 * 130
-    # the nq = 256 headline: 4 workgroups per row
-    assert f(1, 256, 8, 128, 64, 64) == 4 * 256 * 8 * 130
+    # 256 rows fill the CUs alone: no split
+    assert f(1, 256, 8, 128, 64, 64) == 0
+    # 64 rows: four workgroups each
+    assert f(1, 64, 8, 128, 64, 64) == 4 * 64 * 8 * 130
     # enough rows to fill the chip alone: no split, no workspace
     assert f(4, 16384, 8, 128, 64, 64) == 0
     assert f(0, 1, 8, 128, 64, 64) == 0 and f(1, 1, 17, 128, 64, 64) == 0

@@ -1027,3 +1027,46 @@ def test_force_tail_scores_and_selection(geo):
     assert np.array_equal(sc.view(np.uint32), s1.view(np.uint32))
     assert np.all(ids[:, 0] == nf)
     check_ids(ids[rows], sc[rows].astype(np.float64), ref, k, "forced phase")
+
+
+# ---------------------------------------------------------------------------
+# the decode scorer (one MFMA row block of queries per KV head) against the
+# small scorer: a query's scores depend on that query alone, so the decode
+# rows must equal the same queries' rows scored among many (small scorer),
+# bit for bit, and the oracle's bound
+# ---------------------------------------------------------------------------
+
+DECODE_VS_SMALL = [
+    # G, nq (decode), H, D, n_kv
+    (8, 1, 8, 128, 131109),     # the decode step
+    (8, 4, 8, 128, 4096 + 3),   # a full row block of 4 queries x 8 heads
+    (2, 8, 4, 64, 33 * 64),     # 8 queries x 4 heads, no tail
+    (3, 2, 12, 128, 95 * 64 + 1),   # 2 queries x 16 head slots (H = 12)
+    (1, 16, 1, 64, 40 * 64 + 7),    # 16 queries x one head
+    (4, 3, 5, 128, 31),         # no full block: the small scorer's tail-only path
+]
+
+
+@pytest.mark.parametrize("geo", DECODE_VS_SMALL, ids=lambda g: "G{}_nq{}_H{}_D{}_nkv{}".format(*g))
+def test_decode_scorer_matches_small_bitwise(geo):
+    G, nq, H, D, n_kv = geo
+    big = 80   # 80 queries per KV head: the small scorer
+    cfg = qi.Config("dec", G, big, H, D, n_kv, 64, 8, "normal", 7700 + nq + H)
+    w = qi.make(cfg)
+    log(f"decode vs small {geo}")
+    q_all = torch.from_numpy(w.q32).to(dev())
+    kd = k_dev(w.kblk)
+    ws_big = qsa.PhaseWorkspace(big, G, H, D, n_kv, 64, 8, dev())
+    qsa.select_phase(q_all, kd, n_kv, 64, 8, ws_big)
+    ws_dec = qsa.PhaseWorkspace(nq, G, H, D, n_kv, 64, 8, dev(), keep_q16=True)
+    qsa.select_phase(q_all[:nq].contiguous(), kd, n_kv, 64, 8, ws_dec)
+    torch.cuda.synchronize()
+    nb = cfg.nb
+    a = ws_big.scores[:, :nq, :nb].cpu().numpy()
+    b = ws_dec.scores[:, :, :nb].cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), "decode rows differ from the small scorer's"
+    assert np.array_equal(ws_big.ids[:, :nq].cpu().numpy(), ws_dec.ids.cpu().numpy())
+    # the fp16 queries the decode scorer wrote are the conversion's
+    assert np.array_equal(ws_dec.q16.cpu().numpy().view(np.uint16), w.q16[:nq])
+    ref = oracle.scores(w.q16[:nq], w.kblk, nb)
+    check_bound(b.reshape(G * nq, nb).astype(np.float64), ref, "decode")
