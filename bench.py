@@ -770,6 +770,7 @@ def main():
             "scorer_bytes": sbytes,
             "scorer_gbs": sbytes / (ds["scorer"] * 1e-3) / 1e9,
             "scorer_frac_of_hbm": sbytes / (ds["scorer"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "scorer_traffic_bytes": read_traffic(scorer_kernel(dc)[0], dc.name),
             # an empty kernel of the scorer's grid, timed the same way: the
             # part of the scorer's time no kernel can avoid
             "empty_launch_us_same_grid": (peaks["empty_launch_us"]["grid520x64"]
