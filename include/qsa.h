@@ -104,6 +104,10 @@ qsa_status qsa_convert_f32_f16(const float *src, uint16_t *dst, int64_t n, void 
  * score.  It applies only when that block exists (n_kv % bs != 0). */
 #define QSA_FORCE_TAIL 1u
 
+/* Largest token stride (elements) of qsa_sparse_attention's K and V caches:
+ * 64 rows of it are addressed with 32-bit byte offsets. */
+#define QSA_ATTENTION_MAX_KV_STRIDE (16ll << 20)
+
 /* qsa_select_phase / qsa_select_phase_noalloc: select inside the scorer's
  * launch where the fused scorer serves the shape (many query rows, so that
  * each workgroup scores every block of its 64 queries; H <= 8; 513-1024 or
@@ -196,7 +200,8 @@ qsa_status qsa_block_keys(const uint16_t *k_tok, int64_t tok_stride, uint16_t *k
  *   q16        device fp16 bits, layout of qsa_block_scores' q16 (2-byte aligned)
  *   k_tok, v_tok  device fp16 bits, token-major: element (j, g, i) at
  *              [j * kv_tok_stride + g * D + i]; kv_tok_stride >= G*D,
- *              16-byte aligned, kv_tok_stride % 8 == 0 (unused when n_kv == 0)
+ *              16-byte aligned, kv_tok_stride % 8 == 0, kv_tok_stride <=
+ *              QSA_ATTENTION_MAX_KV_STRIDE (unused when n_kv == 0)
  *   ids        device int32 [G*nq][ld_ids], ld_ids >= k (the selector's ids)
  *   out        device fp32, element (t, g, h, i) at
  *              [t * out_tok_stride + (g*H + h) * D + i], out_tok_stride >= G*H*D;

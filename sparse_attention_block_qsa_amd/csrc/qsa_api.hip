@@ -234,6 +234,8 @@ qsa_status qsa_sparse_attention(const uint16_t *q16, int64_t q_tok_stride, const
         if (!mad_ok(n_kv - 1, kv_tok_stride, static_cast<int64_t>(G) * D, &tmp)) return QSA_ERR_ARG;
         if (!aligned16(k_tok) || !aligned16(v_tok) || kv_tok_stride % 8 != 0)
             return QSA_ERR_UNSUPPORTED;
+        // a chunk's 64 value rows are addressed with 32-bit byte offsets
+        if (kv_tok_stride > QSA_ATTENTION_MAX_KV_STRIDE) return QSA_ERR_UNSUPPORTED;
     }
     if (reinterpret_cast<uintptr_t>(q16) % 2 != 0 || !aligned4(out) || (ids && !aligned4(ids)) ||
         (ws && !aligned4(ws)))

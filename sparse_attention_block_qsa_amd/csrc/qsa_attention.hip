@@ -79,6 +79,9 @@ __device__ __forceinline__ float f16_to_f32(uint32_t bits) {
 template <int D, int HM>
 __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(AttnArgs a) {
     constexpr int CPL = D / 64;   // output channels per lane (1 or 2)
+    // value rows loaded at once: the whole chunk, issued with its keys, or
+    // (16 heads: the per-head state needs the registers) batches of 16
+    constexpr int VB = HM <= 8 ? kChunk : 16;
     __shared__ float4 qs[HM][D / 4];
     __shared__ float ps[kAttnWaves][kChunk][HM];          // this chunk's weights
     __shared__ float red_m[kAttnWaves][HM], red_l[kAttnWaves][HM];
@@ -119,16 +122,44 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(AttnArgs a) 
         for (int64_t c0 = tb; c0 < te; c0 += kChunk, ++chunk) {
             if (chunk % (kAttnWaves * a.splits) != split * kAttnWaves + w) continue;
             const int n = static_cast<int>(min(static_cast<int64_t>(kChunk), te - c0));
-            // 1. logits of this lane's token (c0 + lane) for every head: one
-            //    fp32 fma chain per head over the channels in ascending order
+            // 1. the chunk's loads, in flight together: the key row of this
+            //    lane's token (c0 + lane) and, with VB = 64, every token's
+            //    values for this lane's channels (rows past the chunk read
+            //    its last token; their weights are 0 and their values are
+            //    zeroed before use).  The values are not needed until the
+            //    weights are known, so their latency hides behind the logits.
             const bool valid = lane < n;
             const uint4 *krow = reinterpret_cast<const uint4 *>(kg + (c0 + (valid ? lane : 0)) * a.kvts);
+            uint4 kr[D / 8];   // the whole key row
+            #pragma unroll
+            for (int u = 0; u < D / 8; ++u) kr[u] = krow[u];
+            uint32_t vw[VB];
+            // raw buffer loads over the chunk's value rows: one lane offset
+            // (its channels) and a scalar row offset per load, so the loads
+            // need no per-row vector address registers
+            const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t *>(vg + c0 * a.kvts), 0, 0x7fffffff, 0x00020000);
+            const int vlane = CPL * 2 * lane;
+            const int rowb = static_cast<int>(a.kvts * 2);
+            auto vload = [&](int j) -> uint32_t {
+                const int r = j < n ? j : n - 1;   // rows past the chunk repeat its last
+                if constexpr (CPL == 2)
+                    return __builtin_amdgcn_raw_buffer_load_b32(vrs, vlane, r * rowb, 0);
+                else
+                    return __builtin_amdgcn_raw_buffer_load_b16(vrs, vlane, r * rowb, 0);
+            };
+            if constexpr (VB == kChunk) {
+                #pragma unroll
+                for (int j = 0; j < kChunk; ++j) vw[j] = vload(j);
+                // keep the loads here: sunk towards their use they would
+                // wait out their latency after the softmax
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // 2. logits of this lane's token for every head: one fp32 fma
+            //    chain per head over the channels in ascending order
             float s[HM];
             #pragma unroll
             for (int h = 0; h < HM; ++h) s[h] = 0.0f;
-            uint4 kr[D / 8];   // the whole key row in flight at once
-            #pragma unroll
-            for (int u = 0; u < D / 8; ++u) kr[u] = krow[u];
             #pragma unroll
             for (int u = 0; u < D / 8; ++u) {
                 // keep each step's query reads in its step: hoisted, the
@@ -155,7 +186,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(AttnArgs a) 
                     s[h] = __builtin_fmaf(kf[7], q1.w, s[h]);
                 }
             }
-            // 2. weights and the running state of every head
+            // 3. weights and the running state of every head
             #pragma unroll
             for (int h = 0; h < HM; ++h) {
                 const float x = valid ? s[h] * a.scale : -INFINITY;
@@ -168,38 +199,39 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(AttnArgs a) 
                 #pragma unroll
                 for (int c = 0; c < CPL; ++c) acc[h][c] *= alpha;
             }
-            // 3. this chunk's weighted values (lane l owns channels CPL*l..),
-            //    added into the running output
+            // 4. this chunk's weighted values (lane l owns channels CPL*l..),
+            //    added into the running output; token j's weights are
+            //    ps[w][j][*], 0 past the chunk
             float cs[HM][CPL];
             #pragma unroll
             for (int h = 0; h < HM; ++h) {
                 #pragma unroll
                 for (int c = 0; c < CPL; ++c) cs[h][c] = 0.0f;
             }
-            // value rows in batches of 16 tokens, every load of a batch in
-            // flight before its adds (token j's weights are ps[w][j][*]);
-            // rows past the chunk read the chunk's first token, weight 0
-            for (int j0 = 0; j0 < n; j0 += 16) {
-                uint32_t vw[16];
+            auto pv = [&](int j, uint32_t bits) __attribute__((always_inline)) {
+                float v[CPL];
+                v[0] = f16_to_f32(bits & 0xffffu);
+                if constexpr (CPL == 2) v[1] = f16_to_f32(bits >> 16);
                 #pragma unroll
-                for (int jj = 0; jj < 16; ++jj) {
-                    const int j = j0 + jj < n ? j0 + jj : 0;
-                    const uint16_t *vrow = vg + (c0 + j) * a.kvts + CPL * lane;
-                    if constexpr (CPL == 2) vw[jj] = *reinterpret_cast<const uint32_t *>(vrow);
-                    else vw[jj] = *vrow;
-                }
+                for (int c = 0; c < CPL; ++c) v[c] = j < n ? v[c] : 0.0f;   // no 0 * inf
                 #pragma unroll
-                for (int jj = 0; jj < 16; ++jj) {
-                    if (j0 + jj >= n) break;   // uniform
-                    float v[CPL];
-                    v[0] = f16_to_f32(vw[jj] & 0xffffu);
-                    if constexpr (CPL == 2) v[1] = f16_to_f32(vw[jj] >> 16);
+                for (int h = 0; h < HM; ++h) {
+                    const float p = ps[w][j][h];
                     #pragma unroll
-                    for (int h = 0; h < HM; ++h) {
-                        const float p = ps[w][j0 + jj][h];
-                        #pragma unroll
-                        for (int c = 0; c < CPL; ++c) cs[h][c] = __builtin_fmaf(p, v[c], cs[h][c]);
-                    }
+                    for (int c = 0; c < CPL; ++c) cs[h][c] = __builtin_fmaf(p, v[c], cs[h][c]);
+                }
+            };
+            if constexpr (VB == kChunk) {
+                #pragma unroll
+                for (int j = 0; j < kChunk; ++j) pv(j, vw[j]);
+            } else {
+                // many heads: value rows in batches of VB, every load of a
+                // batch in flight before its adds
+                for (int j0 = 0; j0 < n; j0 += VB) {
+                    #pragma unroll
+                    for (int jj = 0; jj < VB; ++jj) vw[jj] = vload(j0 + jj);
+                    #pragma unroll
+                    for (int jj = 0; jj < VB; ++jj) pv(j0 + jj, vw[jj]);
                 }
             }
             #pragma unroll

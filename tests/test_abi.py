@@ -233,6 +233,8 @@ def attn_call(lib, **kw):
     (dict(k=A16 + 2), UNSUP), (dict(v=A16 + 8), UNSUP), (dict(kvts=132), UNSUP),
     (dict(q=A16 + 1), UNSUP), (dict(out=A16 + 2), UNSUP), (dict(ids=A16 + 2), UNSUP),
     (dict(ots=1 << 60), ARG), (dict(wsf=-1), ARG), (dict(ws=A16 + 2, wsf=100), UNSUP),
+    # past QSA_ATTENTION_MAX_KV_STRIDE (64 value rows addressed with 32-bit offsets)
+    (dict(kvts=(16 << 20) + 8, n_kv=4), UNSUP),
 ])
 def test_sparse_attention_refusals(lib, kw, want):
     assert attn_call(lib, **kw) == want
