@@ -10,20 +10,21 @@
 //   out[t][g][h][:] = sum_j exp(s_j - max) v[j][g][:] / sum_j exp(s_j - max)
 // with fp16 queries, keys and values and fp32 arithmetic.
 //
-// Mapping (decode and few-query shapes, where a row's tokens are gathered
-// from the KV cache): one workgroup of 8 waves per (KV head, query) row.  The
-// row's selected blocks are cut into chunks of at most 64 tokens; wave w
-// takes chunks w, w + 8, ...  Within a chunk lane l owns token l:
-//   * its key row is loaded into registers (16-byte loads) and its logit for
-//     every head is one fp32 fused multiply-add chain over the channels
-//     (fp16 key x fp32 query, exact products), the queries read from LDS as
-//     broadcasts;
-//   * each head's chunk maximum and sum come from wave reductions; the
-//     wave's running maximum, denominator and output are rescaled when the
-//     maximum grows (online softmax);
-//   * for the weighted sum lane l owns output channels, reads each token's
-//     weights from LDS (broadcast) and its value row with coalesced loads,
-//     and adds the chunk's sum into the running output.
+// Mapping: one workgroup of 8 waves per (KV head, query) row.  The row's
+// selected blocks are cut into chunks of at most 64 tokens; wave w takes
+// chunks w, w + 8, ...  Per chunk:
+//   * the logits of every head are two MFMA chains (v_mfma_f32_32x32x16_f16,
+//     A = 32 tokens' keys loaded straight into fragment layout, B = the
+//     row's queries, transposed, from LDS): fp16 products are exact and the
+//     sums fp32; lane l receives head l%32's logits of 32 tokens;
+//   * head h's chunk maximum and weight sum take the lane's 32 tokens and
+//     its partner's (lane l ^ 32); the running maximum, denominator and
+//     output are rescaled when the maximum grows (online softmax); the
+//     weights go to LDS;
+//   * for the weighted sum lane l owns output channels D/64*l .., reads each
+//     token's weights from LDS (broadcast) and its value rows, loaded with
+//     the keys at the chunk's start so that their latency hides behind the
+//     logits, and adds the chunk's sum into the running output.
 // The 8 waves' partial results are merged through LDS at the end.  With a
 // workspace and few rows (decode), a row is split over several workgroups
 // (chunks dealt round-robin to all their waves) whose partial results a
@@ -56,20 +57,18 @@ struct AttnArgs {
     float *ws;        // [row][split][H][2 + D]: maximum, denominator, numerator
 };
 
-__device__ __forceinline__ float wave_max(float x) {
-    #pragma unroll
-    for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
-    return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-    #pragma unroll
-    for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
-    return x;
-}
-
 __device__ __forceinline__ float f16_to_f32(uint32_t bits) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+}
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// The value of the lane 32 away (lanes 0-31 <-> 32-63).
+__device__ __forceinline__ float swap32(float v, int lane) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, static_cast<uint32_t>((lane & 32) ? r[0] : r[1]));
 }
 
 // HM: heads per row rounded up to a power of two (1, 2, 4, 8, 16).  Heads
@@ -79,10 +78,11 @@ __device__ __forceinline__ float f16_to_f32(uint32_t bits) {
 template <int D, int HM>
 __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(AttnArgs a) {
     constexpr int CPL = D / 64;   // output channels per lane (1 or 2)
+    constexpr int KS = D / 16;    // K-steps of v_mfma_f32_32x32x16_f16
     // value rows loaded at once: the whole chunk, issued with its keys, or
     // (16 heads: the per-head state needs the registers) batches of 16
     constexpr int VB = HM <= 8 ? kChunk : 16;
-    __shared__ float4 qs[HM][D / 4];
+    __shared__ uint4 qh[HM][D / 8];                       // the row's queries, fp16 bits
     __shared__ float ps[kAttnWaves][kChunk][HM];          // this chunk's weights
     __shared__ float red_m[kAttnWaves][HM], red_l[kAttnWaves][HM];
     __shared__ float red_o[kAttnWaves][HM][D];
@@ -94,19 +94,32 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(AttnArgs a) 
     const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
 
-    // queries of this row, fp16 -> fp32, into LDS (zero past H)
+    // queries of this row, fp16 bits, into LDS (zero past H)
+    uint16_t *qh16 = reinterpret_cast<uint16_t *>(&qh[0][0]);
     for (int e = threadIdx.x; e < HM * D; e += 64 * kAttnWaves) {
         const int h = e / D, i = e % D;
-        reinterpret_cast<float *>(&qs[h][0])[i] =
-            h < H ? f16_to_f32(a.q16[t * a.qts + (g * H + h) * D + i]) : 0.0f;
+        qh16[e] = h < H ? a.q16[t * a.qts + (g * H + h) * D + i] : static_cast<uint16_t>(0);
     }
     __syncthreads();
 
-    float m[HM], l[HM], acc[HM][CPL];
+    // The logits of a 32-token tile for every head are one MFMA chain:
+    // A = the tile's keys (token l%32, channels 16s + 8*(l/32) .. +7 in lane
+    // l), B = the queries transposed (head l%32, the same channels), so lane
+    // l receives head l%32's logits of tokens 8*(r/4) + 4*(l/32) + r%4,
+    // r = 0..15.  fp16 products are exact and the sums fp32.
+    const int hq = lane & 31, kc = lane >> 5;
+    half8 qb[KS];
+    #pragma unroll
+    for (int s = 0; s < KS; ++s)
+        qb[s] = hq < HM ? __builtin_bit_cast(half8, qh[hq][2 * s + kc]) : half8{};
+
+    // running maximum and denominator of head hq (lanes hq and hq + 32 hold
+    // the same), and the running output of every head for this lane's
+    // channels CPL*lane ..
+    float mh = -INFINITY, lh = 0.0f;
+    float acc[HM][CPL];
     #pragma unroll
     for (int h = 0; h < HM; ++h) {
-        m[h] = -INFINITY;
-        l[h] = 0.0f;
         #pragma unroll
         for (int c = 0; c < CPL; ++c) acc[h][c] = 0.0f;
     }
@@ -122,17 +135,21 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(AttnArgs a) 
         for (int64_t c0 = tb; c0 < te; c0 += kChunk, ++chunk) {
             if (chunk % (kAttnWaves * a.splits) != split * kAttnWaves + w) continue;
             const int n = static_cast<int>(min(static_cast<int64_t>(kChunk), te - c0));
-            // 1. the chunk's loads, in flight together: the key row of this
-            //    lane's token (c0 + lane) and, with VB = 64, every token's
-            //    values for this lane's channels (rows past the chunk read
-            //    its last token; their weights are 0 and their values are
+            // 1. the chunk's loads, in flight together: the key fragments of
+            //    its two 32-token tiles (tokens past the chunk read its first
+            //    one; their logits are masked) and, with VB = 64, every
+            //    token's values for this lane's channels (rows past the chunk
+            //    repeat its last; their weights are 0 and their values are
             //    zeroed before use).  The values are not needed until the
             //    weights are known, so their latency hides behind the logits.
-            const bool valid = lane < n;
-            const uint4 *krow = reinterpret_cast<const uint4 *>(kg + (c0 + (valid ? lane : 0)) * a.kvts);
-            uint4 kr[D / 8];   // the whole key row
+            uint4 ka[2][KS];
             #pragma unroll
-            for (int u = 0; u < D / 8; ++u) kr[u] = krow[u];
+            for (int mt = 0; mt < 2; ++mt) {
+                const int tk = 32 * mt + hq;
+                const uint16_t *kp = kg + (c0 + (tk < n ? tk : 0)) * a.kvts + 8 * kc;
+                #pragma unroll
+                for (int s = 0; s < KS; ++s) ka[mt][s] = *reinterpret_cast<const uint4 *>(kp + 16 * s);
+            }
             uint32_t vw[VB];
             // raw buffer loads over the chunk's value rows: one lane offset
             // (its channels) and a scalar row offset per load, so the loads
@@ -155,49 +172,53 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(AttnArgs a) 
                 // wait out their latency after the softmax
                 __builtin_amdgcn_sched_barrier(0);
             }
-            // 2. logits of this lane's token for every head: one fp32 fma
-            //    chain per head over the channels in ascending order
-            float s[HM];
+            // 2. logits: two 32x32 tiles (tokens x heads)
+            floatx16 sa[2];
             #pragma unroll
-            for (int h = 0; h < HM; ++h) s[h] = 0.0f;
+            for (int mt = 0; mt < 2; ++mt) {
+                #pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    sa[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        __builtin_bit_cast(half8, ka[mt][s]), qb[s], s == 0 ? floatx16{} : sa[mt],
+                        0, 0, 0);
+            }
+            // 3. weights of head hq and its running state: the chunk's
+            //    maximum over the lane's 32 tokens and its partner's, the
+            //    weights, their sum; the weights go to LDS for the values
+            float cmax = -INFINITY;
             #pragma unroll
-            for (int u = 0; u < D / 8; ++u) {
-                // keep each step's query reads in its step: hoisted, the
-                // reads of every step would need HM*D registers
-                __builtin_amdgcn_sched_barrier(0);
-                const uint4 kq = kr[u];
-                const uint32_t kw[4] = {kq.x, kq.y, kq.z, kq.w};
-                float kf[8];
+            for (int mt = 0; mt < 2; ++mt) {
                 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    kf[2 * e] = f16_to_f32(kw[e] & 0xffffu);
-                    kf[2 * e + 1] = f16_to_f32(kw[e] >> 16);
-                }
-                #pragma unroll
-                for (int h = 0; h < HM; ++h) {
-                    const float4 q0 = qs[h][2 * u], q1 = qs[h][2 * u + 1];
-                    s[h] = __builtin_fmaf(kf[0], q0.x, s[h]);
-                    s[h] = __builtin_fmaf(kf[1], q0.y, s[h]);
-                    s[h] = __builtin_fmaf(kf[2], q0.z, s[h]);
-                    s[h] = __builtin_fmaf(kf[3], q0.w, s[h]);
-                    s[h] = __builtin_fmaf(kf[4], q1.x, s[h]);
-                    s[h] = __builtin_fmaf(kf[5], q1.y, s[h]);
-                    s[h] = __builtin_fmaf(kf[6], q1.z, s[h]);
-                    s[h] = __builtin_fmaf(kf[7], q1.w, s[h]);
+                for (int r = 0; r < 16; ++r) {
+                    const int tk = 32 * mt + 8 * (r >> 2) + 4 * kc + (r & 3);
+                    sa[mt][r] = tk < n ? sa[mt][r] * a.scale : -INFINITY;
+                    cmax = fmaxf(cmax, sa[mt][r]);
                 }
             }
-            // 3. weights and the running state of every head
+            cmax = fmaxf(cmax, swap32(cmax, lane));
+            const float mn = fmaxf(mh, cmax);
+            float csum = 0.0f;
+            #pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                #pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int tk = 32 * mt + 8 * (r >> 2) + 4 * kc + (r & 3);
+                    const float p = tk < n ? expf(sa[mt][r] - mn) : 0.0f;
+                    csum += p;
+                    if (hq < HM) ps[w][tk][hq] = p;
+                }
+            }
+            csum += swap32(csum, lane);
+            const float alpha = expf(mh - mn);   // 0 on the first chunk (mh = -inf)
+            lh = lh * alpha + csum;
+            mh = mn;
+            // every head's rescale for the output channels this lane owns
             #pragma unroll
             for (int h = 0; h < HM; ++h) {
-                const float x = valid ? s[h] * a.scale : -INFINITY;
-                const float mn = fmaxf(m[h], wave_max(x));
-                const float p = valid ? expf(x - mn) : 0.0f;
-                const float alpha = expf(m[h] - mn);   // 0 on the first chunk (m = -inf)
-                l[h] = l[h] * alpha + wave_sum(p);
-                m[h] = mn;
-                ps[w][lane][h] = p;
+                const float ah = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), h));
                 #pragma unroll
-                for (int c = 0; c < CPL; ++c) acc[h][c] *= alpha;
+                for (int c = 0; c < CPL; ++c) acc[h][c] *= ah;
             }
             // 4. this chunk's weighted values (lane l owns channels CPL*l..),
             //    added into the running output; token j's weights are
@@ -242,13 +263,13 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(AttnArgs a) 
         }
     }
 
-    // 4. merge the waves' partial results
+    // 5. merge the waves' partial results
+    if (lane < HM) {
+        red_m[w][lane] = mh;
+        red_l[w][lane] = lh;
+    }
     #pragma unroll
     for (int h = 0; h < HM; ++h) {
-        if (lane == 0) {
-            red_m[w][h] = m[h];
-            red_l[w][h] = l[h];
-        }
         #pragma unroll
         for (int c = 0; c < CPL; ++c) red_o[w][h][CPL * lane + c] = acc[h][c];
     }
