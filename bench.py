@@ -468,6 +468,9 @@ def measure(cfg, qsa, torch, steps, warmup, w=None, calls_100=False):
     for d, name, fn in ((stages, "scorer", ph.score), (stages, "topk", ph.topk),
                         (alone, "convert", ph.convert), (alone, "block_scores_f16", ph.score16),
                         (alone, "phase_fused_select", ph.step_fused)):
+        if cfg.nb == 0 and name in ("scorer", "block_scores_f16"):
+            d[name] = 0.0   # nothing to score: the call launches nothing
+            continue
         g = graph_of(torch, fn, steps)
         d[name] = time_graph(torch, g, steps)
         del g
