@@ -493,8 +493,9 @@ def measure(cfg, qsa, torch, steps, warmup, w=None, calls_100=False):
         "fused_select_matches": fused_same,
         "stages_ms": stages,
         "entry_points_ms": alone,
-        "scorer_tflops": flop / (stages["scorer"] * 1e-3) / 1e12,
-        "block_scores_f16_tflops": flop / (alone["block_scores_f16"] * 1e-3) / 1e12,
+        "scorer_tflops": flop / (stages["scorer"] * 1e-3) / 1e12 if stages["scorer"] > 0 else 0.0,
+        "block_scores_f16_tflops": (flop / (alone["block_scores_f16"] * 1e-3) / 1e12
+                                    if alone["block_scores_f16"] > 0 else 0.0),
         "flop": flop,
     }
 
