@@ -126,14 +126,24 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(AttnArgs a) 
 
     const uint16_t *kg = a.k_tok + g * D;
     const uint16_t *vg = a.v_tok + g * D;
-    int chunk = 0;   // index of the chunk over the row's selected blocks
+    // the row's ids, one per lane (k <= 64), read once: slot s's id is lane
+    // s's, broadcast by v_readlane, instead of a dependent scalar load per
+    // slot on the way to each chunk
+    const int idv = lane < a.k ? a.ids[row * a.ld_ids + lane] : -1;
+    // chunks over the row's selected blocks are dealt round-robin to the
+    // kAttnWaves * splits waves of the row; phase counts the chunk index
+    // modulo that (no division per chunk)
+    const int period = kAttnWaves * a.splits, mine = split * kAttnWaves + w;
+    int phase = 0;
     for (int slot = 0; slot < a.k; ++slot) {
-        const int b = a.ids[row * a.ld_ids + slot];   // uniform
+        const int b = __builtin_amdgcn_readlane(idv, slot);   // uniform
         if (b < 0 || b >= a.nb) continue;
         const int64_t tb = static_cast<int64_t>(b) * a.bs;
         const int64_t te = min(tb + a.bs, a.n_kv);
-        for (int64_t c0 = tb; c0 < te; c0 += kChunk, ++chunk) {
-            if (chunk % (kAttnWaves * a.splits) != split * kAttnWaves + w) continue;
+        for (int64_t c0 = tb; c0 < te; c0 += kChunk) {
+            const bool own = phase == mine;
+            phase = phase + 1 == period ? 0 : phase + 1;
+            if (!own) continue;
             const int n = static_cast<int>(min(static_cast<int64_t>(kChunk), te - c0));
             // 1. the chunk's loads, in flight together: the key fragments of
             //    its two 32-token tiles (tokens past the chunk read its first
@@ -301,28 +311,55 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(AttnArgs a) 
     }
 }
 
-// Rows split over several workgroups: combine their partial results.
+// Rows split over several workgroups: combine their partial results.  One
+// thread per output element (head h, channel i), rows of H*D elements over
+// as many 256-thread workgroups as they need; the splits' maxima, then their
+// denominators and numerators, are loaded eight splits at a time, all eight
+// in flight together (a merge of up to 8 splits is two memory round trips).
+constexpr int kMergeBatch = 8;
+
 template <int D>
 __global__ __launch_bounds__(256) void attention_merge_kernel(AttnArgs a) {
     const int H = a.H;
-    const int64_t row = blockIdx.x;
+    const int per_row = (H * D + 255) / 256;
+    const int64_t row = blockIdx.x / per_row;
+    const int e = static_cast<int>(blockIdx.x % per_row) * 256 + static_cast<int>(threadIdx.x);
+    if (e >= H * D) return;
+    const int h = e / D, i = e % D;
     const int64_t g = row / a.nq, t = row % a.nq;
-    const float *base = a.ws + row * a.splits * H * (2 + D);
-    for (int e = threadIdx.x; e < H * D; e += 256) {
-        const int h = e / D, i = e % D;
-        float M = -INFINITY;
-        for (int sp = 0; sp < a.splits; ++sp) M = fmaxf(M, base[(sp * H + h) * (2 + D)]);
-        float num = 0.0f, den = 0.0f;
-        if (M != -INFINITY) {
-            for (int sp = 0; sp < a.splits; ++sp) {
-                const float *part = base + (sp * H + h) * (2 + D);
-                const float f = part[0] == -INFINITY ? 0.0f : expf(part[0] - M);
-                num = __builtin_fmaf(part[2 + i], f, num);
-                den = __builtin_fmaf(part[1], f, den);
+    const int64_t sstride = static_cast<int64_t>(H) * (2 + D);   // floats between splits
+    const float *base = a.ws + row * a.splits * sstride + static_cast<int64_t>(h) * (2 + D);
+    float M = -INFINITY;
+    for (int sp0 = 0; sp0 < a.splits; sp0 += kMergeBatch) {
+        float mv[kMergeBatch];
+        #pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u)
+            mv[u] = sp0 + u < a.splits ? base[(sp0 + u) * sstride] : -INFINITY;
+        #pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) M = fmaxf(M, mv[u]);
+    }
+    float num = 0.0f, den = 0.0f;
+    if (M != -INFINITY) {
+        for (int sp0 = 0; sp0 < a.splits; sp0 += kMergeBatch) {
+            float mv[kMergeBatch], lv[kMergeBatch], ov[kMergeBatch];
+            #pragma unroll
+            for (int u = 0; u < kMergeBatch; ++u) {
+                const bool in = sp0 + u < a.splits;
+                const float *part = base + (in ? sp0 + u : 0) * sstride;
+                mv[u] = in ? part[0] : -INFINITY;
+                lv[u] = part[1];
+                ov[u] = part[2 + i];
+            }
+            #pragma unroll
+            for (int u = 0; u < kMergeBatch; ++u) {
+                // splits with no chunk hold -inf and add nothing
+                const float f = mv[u] == -INFINITY ? 0.0f : expf(mv[u] - M);
+                num = __builtin_fmaf(ov[u], f, num);
+                den = __builtin_fmaf(lv[u], f, den);
             }
         }
-        a.out[t * a.ots + (g * H + h) * D + i] = den > 0.0f ? num / den : 0.0f;
     }
+    a.out[t * a.ots + (g * H + h) * D + i] = den > 0.0f ? num / den : 0.0f;
 }
 
 template <int D>
@@ -358,7 +395,9 @@ hipError_t launch_attention(const uint16_t *q16, int64_t qts, const uint16_t *k_
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         void (*mf)(AttnArgs) = D == 128 ? attention_merge_kernel<128> : attention_merge_kernel<64>;
-        hipLaunchKernelGGL(mf, dim3(static_cast<unsigned>(rows)), dim3(256), 0, s, a);
+        const int64_t per_row = (static_cast<int64_t>(H) * D + 255) / 256;
+        if (rows * per_row > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(mf, dim3(static_cast<unsigned>(rows * per_row)), dim3(256), 0, s, a);
     }
     return hipGetLastError();
 }
