@@ -59,6 +59,9 @@ def parse():
                    help="target wall time of the CPU-baseline sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 256 MiB device copy (for counter calibration)")
+    p.add_argument("--fused-sweep", action="store_true",
+                   help="also time the phase with and without the fused selection at 4 KV heads "
+                        "x 16384 queries over 516, 1024 and 2049 blocks")
     return p.parse_args()
 
 
@@ -500,6 +503,42 @@ def measure(cfg, qsa, torch, steps, warmup, w=None, calls_100=False):
     }
 
 
+def fused_sweep(qsa, torch) -> dict:
+    """The phase with the selection in the scorer's launch (QSA_FUSED_SELECT)
+    against the two launches, at the prefill chunk's shape over the block
+    counts the fused form serves: per point the median of three interleaved
+    rounds, each a graph of 5 phases; the ids are compared bit for bit."""
+    import numpy as np
+    import qsa_inputs as qi
+    dev = torch.device("cuda:0")
+    out = []
+    for n_kv in (33000, 65536, 131077):
+        cfg = qi.Config("fused_sweep", 4, 16384, 8, 128, n_kv, 64, 64, "normal", 5)
+        w = qi.make(cfg)
+        q = torch.from_numpy(w.q32).to(dev)
+        kb = torch.from_numpy(w.kblk.view(np.float16)).to(dev)
+        ws = qsa.PhaseWorkspace(cfg.nq, cfg.G, cfg.H, cfg.D, cfg.n_kv, cfg.bs, cfg.k, dev)
+        times, ids = {False: [], True: []}, {}
+        for _ in range(3):
+            for fused in (False, True):
+                fn = lambda: qsa.select_phase(q, kb, n_kv, cfg.bs, cfg.k, ws, fused_select=fused)
+                for _ in range(2):
+                    fn()
+                torch.cuda.synchronize()
+                ids[fused] = ws.ids.clone()
+                g = graph_of(torch, fn, 5)
+                times[fused].append(time_graph(torch, g, 5))
+                del g
+        out.append({"n_kv": n_kv, "nb": cfg.nb, "two_launches_us": sorted(times[False])[1] * 1e3,
+                    "fused_us": sorted(times[True])[1] * 1e3,
+                    "same_ids": bool(torch.equal(ids[False], ids[True]))})
+        print(f"# fused sweep nb {cfg.nb}: two launches {out[-1]['two_launches_us']:.1f} us, "
+              f"fused {out[-1]['fused_us']:.1f} us, same ids {out[-1]['same_ids']}",
+              file=sys.stderr, flush=True)
+        del q, kb, ws, w
+    return {"workload": "4 KV heads x 16384 queries, H 8, D 128, bs 64, k 64", "points": out}
+
+
 def _time_launches(torch, fn, n) -> float:
     """ms per launch of a graph of n back-to-back launches (after 3 eager)."""
     for _ in range(3):
@@ -819,6 +858,8 @@ def main():
                            single_thread_cfgs=[qi.CONFIGS[n] for n in
                                                ("nq256_nkv4096", "nq256_nkv32768", "nq256_nkv131072")])
 
+    sweep_fused = fused_sweep(qsa, torch) if args.fused_sweep else None
+
     if args.copy_calibration:
         src = torch.empty(64 << 20, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -863,6 +904,7 @@ def main():
         "decode": decode,
         "context_sweep": sweep,
         "beside_the_phase": beside,
+        "fused_select_sweep": sweep_fused,
         "source_digest": source_digest(),
         "kernel_digests": {k: source_digest(f) for k, f in KERNEL_FILES.items()},
         "context": {"pages_rx7900xtx_gfx1100_scores_ms_128k": {"warp": 2.627, "wmma": 0.252},
