@@ -18,7 +18,8 @@
 // (16-byte chunks); lane l takes chunk l % (D/8) of every (64/(D/8))-th
 // token, issues all its 16-byte loads of the block before it adds, and
 // accumulates its 8 channels in float64.  The lanes that share a chunk are
-// then added with lane swaps, and the first D/8 lanes round and store.
+// then added with lane swaps, and each of them rounds and stores its share
+// of the chunk's 8 channels.
 // HBM-bound: 2*D bytes read per token and head, 2*D written per block.
 #include "qsa_internal.h"
 
@@ -43,7 +44,11 @@ __device__ uint32_t round_ratio_f16(int64_t num, int64_t den) {
     int E = fl - 24 < -14 ? -14 : fl - 24;
     const int s = E + 14;                  // log2 of the spacing, in units of 2^-24
     const uint64_t unit = d << s;          // < 2^13 * 2^29
-    uint64_t q = a / unit;
+    // q = floor(a / (d * 2^s)) = floor(floor(a / 2^s) / d).  The quotient is
+    // below 2^11 (a grid point below 2^(E+1)), so a >> s < 2^11 * d <= 2^24:
+    // a 32-bit division instead of a 64-bit one
+    const uint32_t x = static_cast<uint32_t>(a >> s);
+    uint64_t q = x / static_cast<uint32_t>(d);
     const uint64_t r = a - q * unit;
     if (2 * r > unit || (2 * r == unit && (q & 1))) ++q;
     if (q < 1024) return sign | static_cast<uint32_t>(q);   // subnormal
@@ -96,21 +101,30 @@ __global__ __launch_bounds__(256) void block_keys_kernel(const uint16_t *__restr
             }
         }
     }
-    // add the TPL lanes that hold the same chunk (exact in any order)
+    // add the TPL lanes that hold the same chunk (exact in any order); the
+    // butterfly leaves the chunk's sums in each of its TPL lanes
     #pragma unroll
     for (int m = LPT; m < 64; m <<= 1) {
         #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], m);
     }
-    if (r == 0) {
-        uint32_t h[8];
+    // the TPL lanes of a chunk share its 8 roundings: lane r rounds channels
+    // CPL*r ... CPL*r + CPL - 1 of the chunk
+    constexpr int CPL = 8 / TPL;
+    uint32_t h[CPL];
+    #pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        double v = acc[j];
         #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            h[e] = round_ratio_f16(static_cast<int64_t>(acc[e] * 16777216.0), len);
-        *reinterpret_cast<uint4 *>(kblk + g * khs + b * D + 8 * c) =
-            make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                       h[6] | (h[7] << 16));
+        for (int e = CPL + j; e < 8; e += CPL)
+            if (r == e / CPL) v = acc[e];
+        h[j] = round_ratio_f16(static_cast<int64_t>(v * 16777216.0), len);
     }
+    uint16_t *dst = kblk + g * khs + b * D + 8 * c + CPL * r;
+    if constexpr (CPL == 2)
+        *reinterpret_cast<uint32_t *>(dst) = h[0] | (h[1] << 16);
+    else
+        *dst = static_cast<uint16_t>(h[0]);
 }
 
 }  // namespace
