@@ -683,8 +683,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
-              "the select phase is per-GPU work with no collective; see the sharding note in "
-              "DESIGN.md", file=sys.stderr)
+              "the select phase is per-GPU work with no collective (each GPU runs it over the "
+              "KV heads or the block range it holds)", file=sys.stderr)
         sys.exit(2)
     import torch
 
