@@ -12,11 +12,15 @@
 //    is also the output register of that (query, head pair) in the 32x32
 //    accumulator, the half (lanes 0-31 / 32-63) picking the head of the
 //    pair.  A wave's whole A operand is KS fragments (32 VGPRs at D = 128).
-//  * The workgroup's four waves own four query groups (one each) and walk
-//    the same segment of the block axis: 32-block K tiles are staged once
-//    through LDS in fragment order (coalesced loads), one or two tiles per
-//    barrier, double-buffered, and read by the four waves.  fp32 queries of
-//    many rows go through LDS in fragment order as well, loaded coalesced.
+//  * The workgroup's waves own four query groups and walk the same segment
+//    of the block axis: 32-block K tiles are staged once through LDS in
+//    fragment order (coalesced loads), double-buffered, and read by every
+//    wave.  With four waves each owns one query group and scores every tile
+//    of a staged chunk (one or two tiles); with eight, waves w and w + 4 own
+//    the same query group and split each chunk's tiles (the first half, then
+//    the second): a wave's serial work halves and two waves share each SIMD,
+//    so one's loads and epilogue overlap the other's.  fp32 queries of many
+//    rows go through LDS in fragment order as well, loaded coalesced.
 //  * Epilogue per tile: relu per head; v_permlane32_swap of the registers of
 //    queries q and q+1 brings the two heads of each pair into one lane; the
 //    pair sums are added in ascending pair order.  That is the head-sum
@@ -40,15 +44,13 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-// K tiles staged per barrier (CH = 1 or 2, 8 or 16 KiB at D = 128),
-// double-buffered: at 8 MFMAs per tile, one tile's work is far shorter than a
-// load's latency.  The host takes CH = 2 when a segment holds an even number
-// of at least four tiles, else 1 (a chunk of 2 over an odd count stages a
-// tile that is not scored).  Measured on the phase at nq = 256: 4 tiles per
-// segment (128K keys) 11.8 us with CH = 2, 12.2 us with 1, 12.0 us with 4;
-// 1 tile per segment (32K keys) 8.25 us with CH = 1, 8.5 us with 2; 2 tiles
-// per segment (the decode step, 8 KV heads) 9.9 us with CH = 1, 10.05 us
-// with 2.
+// K tiles staged per barrier and wave half (CH = 1 or 2, 8 or 16 KiB at D =
+// 128), double-buffered: at 8 MFMAs per tile, one tile's work is far shorter
+// than a load's latency.  With eight waves a chunk is 2*CH tiles (a chunk
+// over a shorter remainder stages tiles that are not scored).  Interleaved
+// medians of the phase scorer at nq = 256, eight waves: 8 tiles per segment
+// (256K keys) 6.49 us with CH = 2, 6.81 us with 1; 4 tiles (128K keys) 4.88
+// and 4.84 us.
 
 struct SmallArgs {
     const uint16_t *q16;   // query source when q32 is null
@@ -75,21 +77,25 @@ __device__ __forceinline__ float h2f(uint32_t bits16) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
 }
 
-template <int D, int NP, bool SRC32, int CH, bool STAGE>
-__global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
+template <int D, int NP, bool SRC32, int CH, bool STAGE, int NW>
+__global__ __launch_bounds__(64 * NW) void score_small_kernel(SmallArgs a) {
     constexpr int KS = D / 16;
     constexpr int QPG = 16 / NP;
     constexpr int CHUNKS = D / 8;                  // 16-byte chunks per block row
     constexpr int TILE_U4 = CHUNKS * kTileBlocks;
-    constexpr int LOADS = TILE_U4 / 256;           // staging loads per thread per tile
+    constexpr int HALVES = NW / kScoreWaves;       // waves per query group
+    constexpr int NT = 64 * NW;                    // threads
+    constexpr int CT = HALVES * CH;                // tiles per staged chunk
+    constexpr int SLOADS = CT * TILE_U4 / NT;      // staging loads per thread per chunk
     static_assert(NP == 1 || NP == 2 || NP == 4 || NP == 8, "head pairs per row block");
-    static_assert(TILE_U4 % 256 == 0 && (LOADS == 1 || LOADS == 2), "D must be 64 or 128");
-    static_assert(CH == 1 || CH == 2, "tiles per staged chunk");
-    static_assert(!STAGE || SRC32, "only fp32 queries are staged through LDS");
+    static_assert(TILE_U4 == 256 || TILE_U4 == 512, "D must be 64 or 128");
+    static_assert(NW == 4 || NW == 8, "four query groups, one or two waves each");
+    static_assert(CH == 1 || CH == 2, "tiles per staged chunk and wave half");
+    static_assert(SLOADS * NT == CT * TILE_U4 && SLOADS >= 1, "whole loads per thread");
 
-    // two chunks of K tiles shared by the four waves, the four waves' query
-    // fragments, and per wave the relu'd tail chains
-    __shared__ uint4 kbuf[2][CH][TILE_U4];
+    // two chunks of K tiles shared by the waves, the four query groups'
+    // fragments, and per query group the relu'd tail chains
+    __shared__ uint4 kbuf[2][CT * TILE_U4];
     __shared__ uint4 qfrag[STAGE ? kScoreWaves * KS * 64 : 1];
     __shared__ float red[kScoreWaves][QPG][2 * NP];
 
@@ -98,7 +104,9 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
     const uint32_t rest = L / a.n_segs;
     const int qg4 = static_cast<int>(rest % a.n_qgroups);   // groups of four query groups
     const int g = static_cast<int>(rest / a.n_qgroups);
-    const int w = threadIdx.x >> 6;
+    const int wv = threadIdx.x >> 6;
+    const int w = wv % kScoreWaves;                          // query group slot
+    const int hf = wv / kScoreWaves;                         // tile half
     const int l = threadIdx.x & 63;
     const int qg = qg4 * kScoreWaves + w;                    // this wave's query group
 
@@ -117,31 +125,29 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
     const uint16_t *kg = a.kblk + static_cast<int64_t>(g) * a.khs;
     float *sbase = a.scores + static_cast<int64_t>(g) * a.nq * a.ld_s;
 
-    // K staging in chunks of CH tiles, double-buffered: the loads of
+    // K staging in chunks of CT tiles, double-buffered: the loads of
     // chunk c+1 are in flight while chunk c is scored, one barrier per chunk.
-    // LDS index u = threadIdx.x + 256*j of a tile is chunk-major (u = chunk*32
-    // + block), the B-fragment order: lane l of K-step s reads u = 64*s + l.
-    // Blocks past nf, and tiles past the segment, feed output columns that
-    // are never stored: their indices are clamped.
+    // A chunk's LDS index U = threadIdx.x + NT*j is tile-major (U = tile *
+    // TILE_U4 + u), and within a tile u is chunk-major (u = chunk*32 + block),
+    // the B-fragment order: lane l of K-step s reads u = 64*s + l.  Blocks
+    // past nf, and tiles past the segment, feed output columns that are never
+    // stored: their indices are clamped.
     const int64_t last = a.nf - 1;
-    auto kload = [&](int tile, int j) {
-        const int u = static_cast<int>(threadIdx.x) + 256 * j;
-        const int64_t b = min(static_cast<int64_t>(min(tile, te - 1)) * kTileBlocks +
+    auto kload = [&](int t0, int j) {
+        const int U = static_cast<int>(threadIdx.x) + NT * j;
+        const int u = U % TILE_U4;
+        const int64_t b = min(static_cast<int64_t>(min(t0 + U / TILE_U4, te - 1)) * kTileBlocks +
                                   (u % kTileBlocks), last);
         return *reinterpret_cast<const uint4 *>(kg + b * D + 8 * (u / kTileBlocks));
     };
-    uint4 st[CH][LOADS];
+    uint4 st[SLOADS];
     auto fetch = [&](int t0) {
         #pragma unroll
-        for (int i = 0; i < CH; ++i)
-            #pragma unroll
-            for (int j = 0; j < LOADS; ++j) st[i][j] = kload(t0 + i, j);
+        for (int j = 0; j < SLOADS; ++j) st[j] = kload(t0, j);
     };
     auto publish = [&](int buf) {
         #pragma unroll
-        for (int i = 0; i < CH; ++i)
-            #pragma unroll
-            for (int j = 0; j < LOADS; ++j) kbuf[buf][i][threadIdx.x + 256 * j] = st[i][j];
+        for (int j = 0; j < SLOADS; ++j) kbuf[buf][threadIdx.x + NT * j] = st[j];
     };
     // the first chunk's loads go out before the queries', so that the two
     // latencies overlap; the tail segment's loads of the partial block's key
@@ -149,7 +155,7 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
     if (tb < te) fetch(tb);   // uniform over the workgroup
     const bool tail_seg = a.tail && seg == a.n_segs - 1;   // uniform
     uint4 kv[KS][2];
-    if (tail_seg) {
+    if (tail_seg && hf == 0) {
         const uint16_t *kt = kg + a.nf * D;
         #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -160,13 +166,14 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
 
     half8 qa[KS];
     if constexpr (STAGE) {
-        // ---- A operand, fp32 queries staged through LDS.  The workgroup's
+        // ---- A operand staged through LDS.  The workgroup's
         // 4*QPG query slots x 2*NP head slots x D channels are walked in
         // 8-element chunks, consecutive chunks of a (query, head) row on
         // consecutive threads, so the loads are coalesced: each lane loading
         // its own fragments touches 32 lines per load instruction, and at few
         // rows those requests, not the bytes, set the time.  Each chunk is one
-        // lane's fragment of one K-step, converted (f16x8) and written to LDS
+        // lane's fragment of one K-step, converted (f16x8) when the queries
+        // are fp32, and written to LDS
         // in fragment order with the lane index XORed by the chunk's index in
         // its row (K-step and half): the 16 chunks of a row land in 16
         // different bank groups, and every wave still reads its A operand
@@ -175,15 +182,15 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
         // rows past nq and of padded heads are not loaded; their fragments are
         // zeroed when read.
         constexpr int CPR = D / 8;                     // chunks per (query, head) row
-        constexpr int MAXJ = 4 * QPG * 2 * NP * CPR / 256;
-        static_assert(MAXJ * 256 == 4 * QPG * 2 * NP * CPR, "128 rows of chunks over 256 threads");
+        constexpr int MAXJ = 4 * QPG * 2 * NP * CPR / NT;
+        static_assert(MAXJ * NT == 4 * QPG * 2 * NP * CPR, "128 rows of chunks over the threads");
         const int t0 = qg4 * kScoreWaves * QPG;
         int64_t off[MAXJ];
         bool ok[MAXJ];
         int dst[MAXJ];
         #pragma unroll
         for (int j = 0; j < MAXJ; ++j) {
-            const int ch = static_cast<int>(threadIdx.x) + 256 * j;
+            const int ch = static_cast<int>(threadIdx.x) + NT * j;
             const int row = ch / CPR, d8 = ch % CPR;
             const int qs = row / (2 * NP), h = row % (2 * NP);   // query slot, head
             ok[j] = h < a.H && t0 + qs < a.nq;
@@ -196,16 +203,21 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
             const int ln = 8 * (cc >> 2) + 4 * (h & 1) + (cc & 3) + 32 * (d8 & 1);
             dst[j] = ((qs / QPG) * KS + (d8 >> 1)) * 64 + (ln ^ (d8 & 15));
         }
-        float4 x0[MAXJ], x1[MAXJ];
-        #pragma unroll
-        for (int j = 0; j < MAXJ; ++j) {
-            x0[j] = *reinterpret_cast<const float4 *>(a.q32 + off[j]);
-            x1[j] = *reinterpret_cast<const float4 *>(a.q32 + off[j] + 4);
-        }
         uint4 hv[MAXJ];
-        #pragma unroll
-        for (int j = 0; j < MAXJ; ++j) hv[j] = f16x8(x0[j], x1[j]);
-        if (a.q16w && seg == 0) {
+        if constexpr (SRC32) {
+            float4 x0[MAXJ], x1[MAXJ];
+            #pragma unroll
+            for (int j = 0; j < MAXJ; ++j) {
+                x0[j] = *reinterpret_cast<const float4 *>(a.q32 + off[j]);
+                x1[j] = *reinterpret_cast<const float4 *>(a.q32 + off[j] + 4);
+            }
+            #pragma unroll
+            for (int j = 0; j < MAXJ; ++j) hv[j] = f16x8(x0[j], x1[j]);
+        } else {
+            #pragma unroll
+            for (int j = 0; j < MAXJ; ++j) hv[j] = *reinterpret_cast<const uint4 *>(a.q16 + off[j]);
+        }
+        if (SRC32 && a.q16w && seg == 0) {
             #pragma unroll
             for (int j = 0; j < MAXJ; ++j)
                 if (ok[j]) *reinterpret_cast<uint4 *>(a.q16w + off[j]) = hv[j];
@@ -237,7 +249,7 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
             for (int s = 0; s < KS; ++s) hv[s] = f16x8(x0[s], x1[s]);
             #pragma unroll
             for (int s = 0; s < KS; ++s) qa[s] = a_ok ? __builtin_bit_cast(half8, hv[s]) : half8{};
-            if (a.q16w && seg == 0 && a_ok) {
+            if (a.q16w && seg == 0 && hf == 0 && a_ok) {
                 #pragma unroll
                 for (int s = 0; s < KS; ++s) *reinterpret_cast<uint4 *>(a.q16w + a_off + 16 * s) = hv[s];
             }
@@ -254,12 +266,12 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
 
     if (tb < te) {   // uniform over the workgroup
         int buf = 0;
-        for (int t0 = tb; t0 < te; t0 += CH) {
-            const bool more = t0 + CH < te;   // uniform
-            if (more) fetch(t0 + CH);
-            for (int i = 0; i < CH && t0 + i < te; ++i) {
+        for (int t0 = tb; t0 < te; t0 += CT) {
+            const bool more = t0 + CT < te;   // uniform
+            if (more) fetch(t0 + CT);
+            for (int i = hf * CH; i < hf * CH + CH && t0 + i < te; ++i) {   // uniform per wave
                 const int tile = t0 + i;
-                const uint4 *kcur = &kbuf[buf][i][l];
+                const uint4 *kcur = &kbuf[buf][i * TILE_U4 + l];
                 floatx16 acc = {};
                 #pragma unroll
                 for (int s = 0; s < KS; ++s)
@@ -308,7 +320,10 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
     // already in registers: v_permlane32_swap gives it the other half of
     // every 16-channel run (held by lane l + 32), so it walks channels
     // 16s .. 16s + 15 in ascending order.
+    // With eight waves the first half runs the chains; the second only joins
+    // the barrier.
     if (tail_seg) {   // uniform over the workgroup
+      if (hf == 0) {
         float acc = 0.0f;
         #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -330,8 +345,9 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
         }
         const float r = (l < 32 && a_ok && acc > 0.0f) ? acc : 0.0f;
         if (l < 32) red[w][q_in][h_in] = r;   // padded heads and rows hold +0
+      }
         __syncthreads();
-        if (l < QPG) {
+        if (hf == 0 && l < QPG) {
             const int t = qg * QPG + l;
             if (t < a.nq) {
                 float sum = 0.0f;
@@ -345,28 +361,42 @@ __global__ __launch_bounds__(256) void score_small_kernel(SmallArgs a) {
 
 typedef void (*small_fn)(SmallArgs);
 
-template <int D, bool SRC32, int CH, bool STAGE>
+template <int D, bool SRC32, int CH, bool STAGE, int NW>
 small_fn pick_np(int np) {
     switch (np) {
-        case 1: return score_small_kernel<D, 1, SRC32, CH, STAGE>;
-        case 2: return score_small_kernel<D, 2, SRC32, CH, STAGE>;
-        case 4: return score_small_kernel<D, 4, SRC32, CH, STAGE>;
-        case 8: return score_small_kernel<D, 8, SRC32, CH, STAGE>;
+        case 1: return score_small_kernel<D, 1, SRC32, CH, STAGE, NW>;
+        case 2: return score_small_kernel<D, 2, SRC32, CH, STAGE, NW>;
+        case 4: return score_small_kernel<D, 4, SRC32, CH, STAGE, NW>;
+        case 8: return score_small_kernel<D, 8, SRC32, CH, STAGE, NW>;
     }
     return nullptr;
 }
 
-// src: 0 fp16 queries, 1 fp32 loaded per lane, 2 fp32 staged through LDS
-template <int D, int CH>
+// src: 0 fp16 queries loaded per lane, 1 fp32 loaded per lane, 2 fp32 staged
+// through LDS, 3 fp16 staged through LDS.  Eight waves serve only staged
+// queries, and fp16 queries are staged only with eight.
+template <int D, int CH, int NW>
 small_fn pick_src(int np, int src) {
-    if (src == 2) return pick_np<D, true, CH, true>(np);
-    if (src == 1) return pick_np<D, true, CH, false>(np);
-    return pick_np<D, false, CH, false>(np);
+    if constexpr (NW == 8) {
+        if (src == 3) return pick_np<D, false, CH, true, 8>(np);
+        if (src == 2) return pick_np<D, true, CH, true, 8>(np);
+    } else {
+        if (src == 2) return pick_np<D, true, CH, true, 4>(np);
+        if (src == 1) return pick_np<D, true, CH, false, 4>(np);
+        if (src == 0) return pick_np<D, false, CH, false, 4>(np);
+    }
+    return nullptr;
 }
 
-small_fn pick_small(int D, int np, int src, int ch) {
-    if (D == 128) return ch == 2 ? pick_src<128, 2>(np, src) : pick_src<128, 1>(np, src);
-    if (D == 64) return ch == 2 ? pick_src<64, 2>(np, src) : pick_src<64, 1>(np, src);
+template <int D>
+small_fn pick_ch(int np, int src, int ch, int nw) {
+    if (nw == 8) return ch == 2 ? pick_src<D, 2, 8>(np, src) : pick_src<D, 1, 8>(np, src);
+    return ch == 2 ? pick_src<D, 2, 4>(np, src) : pick_src<D, 1, 4>(np, src);
+}
+
+small_fn pick_small(int D, int np, int src, int ch, int nw) {
+    if (D == 128) return pick_ch<128>(np, src, ch, nw);
+    if (D == 64) return pick_ch<64>(np, src, ch, nw);
     return nullptr;
 }
 
@@ -408,10 +438,24 @@ hipError_t launch_score_small(const ScoreGeom &geo, bool tail, hipStream_t s, co
     // fp32 queries are staged through LDS when a workgroup can hold a full
     // row group.  Interleaved phase medians at nq = 256: 128K keys 10.8 ->
     // 10.0 us, 4K keys 6.9 -> 6.1 us; with one query per KV head staging
-    // only adds its LDS round trip (9.9 -> 10.2 us), and fp16 queries, half
-    // the bytes, lose too (the fp16-input scorer 5.2 -> 5.6 us).
-    const int src = q32 == nullptr ? 0 : geo.nq >= kScoreWaves * qpg ? 2 : 1;
-    small_fn fn = pick_small(geo.D, np, src, tps >= 4 && tps % 2 == 0 ? 2 : 1);
+    // only adds its LDS round trip (9.9 -> 10.2 us).  Eight waves when the
+    // rows fill the workgroup and a segment holds at least two tiles, so that
+    // both wave halves have work: interleaved medians at nq = 256, four ->
+    // eight waves, phase scorer 5.45 -> 4.91 us at 128K keys, 4.49 -> 3.88 at
+    // 64K, 7.87 -> 6.58 at 256K.  fp16 queries are staged only with eight
+    // waves, which share the staging: 5.21 -> 4.78 us at 128K (per-lane loads
+    // with four waves -> staged with eight), 4.11 -> 3.79 at 64K, 7.62 ->
+    // 6.53 at 256K; with four waves staging them loses (3.44 -> 4.07 us at
+    // 32K keys, one tile per segment).
+    const bool rows_fill = geo.nq >= kScoreWaves * qpg;
+    const int nw = rows_fill && tps >= 2 ? 8 : 4;
+    const int src = q32 == nullptr ? (nw == 8 ? 3 : 0) : rows_fill ? 2 : 1;
+    // A staged chunk is CH tiles per wave half: with eight waves CH = 2 when
+    // the segment is a whole number of 4-tile chunks; with four, when it
+    // holds an even number of at least four tiles (2 tiles per segment, the
+    // decode step's shape: 9.9 us with CH = 1, 10.05 us with 2).
+    const int ch = nw == 8 ? (tps % 4 == 0 ? 2 : 1) : (tps >= 4 && tps % 2 == 0 ? 2 : 1);
+    small_fn fn = pick_small(geo.D, np, src, ch, nw);
     if (!fn) return hipErrorInvalidValue;
     SmallArgs a{geo.q16, q32, q32 ? q16w : nullptr, geo.qts, geo.kblk, geo.khs, geo.scores,
                 geo.ld_s, geo.G, geo.nq, geo.H, geo.nf, tail ? 1 : 0,
@@ -419,7 +463,7 @@ hipError_t launch_score_small(const ScoreGeom &geo, bool tail, hipStream_t s, co
                 static_cast<int32_t>(tps), static_cast<int32_t>(n_tiles), geo.tail_add};
     void *args[] = {&a};
     return hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(static_cast<unsigned>(grid)),
-                           dim3(256), args, 0, s);
+                           dim3(64 * nw), args, 0, s);
 }
 
 }  // namespace qsa

@@ -900,7 +900,9 @@ def test_wide_scorer_many_items(G, nq, H, D, n_tiles):
 
 # 256 queries of one KV head at H = 8 give 16 groups of four query groups,
 # so the block axis is cut into 16 segments of n_tiles/16 tiles: 2, 3, 4 and
-# 6 tiles per segment, K staged one tile per barrier (2, 3) or two (4, 6).
+# 6 tiles per segment, eight waves (two per query group, each taking half of
+# every staged chunk), K staged one tile per wave half and barrier (2, 3, 6)
+# or two (4).
 SMALL_CHUNKS = [32, 48, 64, 96]
 
 
@@ -928,6 +930,39 @@ def test_small_scorer_chunking(n_tiles):
     model = oracle.block_model_f32(w.q16, w.kblk, cfg.nf)
     assert np.array_equal(s_gpu[:, cfg.nf].astype(np.float32).view(np.uint32), model.view(np.uint32))
     check_ids(ids.reshape(cfg.rows, cfg.k).cpu().numpy(), s_gpu, ref, cfg.k, "small chunks")
+
+
+# Slices of 100 queries (4 KV heads) that the small scorer serves with eight
+# waves (segments of two or more tiles): every head packing (H = 2, 4, 5, 8,
+# 12, 16), both head dims, 4-tile chunks (40 and 64 tiles) and 2-tile chunks
+# over a ragged last segment (24 tiles: segments of 3), with and without the
+# partial block.
+EIGHT_WAVES = [(8, 128, 40, True), (8, 128, 24, False), (2, 64, 40, True), (4, 128, 64, True),
+               (16, 128, 40, False), (12, 64, 24, True), (5, 128, 40, True), (8, 64, 16, True)]
+
+
+@pytest.mark.parametrize("H,D,n_tiles,tail", EIGHT_WAVES, ids=lambda v: str(v))
+def test_small_scorer_eight_waves_bitwise(H, D, n_tiles, tail):
+    """The eight-wave small scorer gives the wide scorer's bits: on fp16
+    queries (staged through LDS) and in the phase on fp32 queries (converted
+    on load, the kept fp16 copy exactly the input's bits), tail included."""
+    G, nq, t0, n = 4, 4096, 1500, 100
+    n_kv = n_tiles * 32 * 64 + (9 if tail else 0)
+    cfg = qi.Config("eight_waves", G, nq, H, D, n_kv, 64, 8, "normal", 1400 + 10 * H + n_tiles + D)
+    log(f"small scorer, eight waves: H={H} D={D} tiles={n_tiles} tail={tail}")
+    w = qi.make(cfg)
+    kd = k_dev(w.kblk)
+    nb = cfg.nb
+    whole = qsa.block_scores(q_dev(w.q16), kd, n_kv, cfg.bs)
+    part = qsa.block_scores(q_dev(w.q16[t0:t0 + n]), kd, n_kv, cfg.bs)
+    ws = qsa.PhaseWorkspace(n, G, H, D, n_kv, cfg.bs, cfg.k, dev(), keep_q16=True)
+    q32 = torch.from_numpy(np.ascontiguousarray(w.q32[t0:t0 + n])).to(dev())
+    qsa.select_phase(q32, kd, n_kv, cfg.bs, cfg.k, ws)
+    torch.cuda.synchronize()
+    ref = whole[:, t0:t0 + n].contiguous().view(torch.int32)
+    assert torch.equal(part.contiguous().view(torch.int32), ref)
+    assert torch.equal(ws.scores[:, :, :nb].contiguous().view(torch.int32), ref)
+    assert np.array_equal(ws.q16.cpu().numpy().view(np.uint16), w.q16[t0:t0 + n])
 
 
 def test_wide_scorer_global_store_path():
