@@ -446,10 +446,12 @@ hipError_t launch_score_small(const ScoreGeom &geo, bool tail, hipStream_t s, co
     // waves, which share the staging: 5.21 -> 4.78 us at 128K (per-lane loads
     // with four waves -> staged with eight), 4.11 -> 3.79 at 64K, 7.62 ->
     // 6.53 at 256K; with four waves staging them loses (3.44 -> 4.07 us at
-    // 32K keys, one tile per segment).
+    // 32K keys, one tile per segment).  Sixteen waves (four per query group)
+    // gained 2-3 % at most, and 512 or 128 workgroups of eight waves lost
+    // (5.22 and 6.11 us against 4.90 us at 128K keys).
     const bool rows_fill = geo.nq >= kScoreWaves * qpg;
     const int nw = rows_fill && tps >= 2 ? 8 : 4;
-    const int src = q32 == nullptr ? (nw == 8 ? 3 : 0) : rows_fill ? 2 : 1;
+    const int src = q32 == nullptr ? (nw > 4 ? 3 : 0) : rows_fill ? 2 : 1;
     // A staged chunk is CH tiles per wave half: with eight waves CH = 2 when
     // the segment is a whole number of 4-tile chunks; with four, when it
     // holds an even number of at least four tiles (2 tiles per segment, the
