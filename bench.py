@@ -145,16 +145,24 @@ def scorer_kernel(cfg):
     if cfg.nf > 0 and cfg.nq <= 16 // np_:
         return "score_decode", f"score_decode_kernel<{cfg.D},{np_},true>"
     if cfg.G * -(-cfg.nq // 64) < 256:
-        # K tiles per staged chunk: 2 when a block segment holds an even
-        # number of at least four tiles (segments give about 256 workgroups,
-        # at least one tile each)
+        # block segments give about 256 workgroups, at least one tile each;
+        # fp32 queries are staged in LDS when the rows fill a workgroup's four
+        # query groups, and then eight waves serve segments of two or more
+        # tiles; K tiles per staged chunk and wave half: with eight waves 2
+        # when a segment is a whole number of 4-tile chunks, with four 2 when
+        # it holds an even number of at least four tiles
         n_tiles = -(-cfg.nf // 32)
         base = cfg.G * -(-(-(-cfg.nq // (16 // np_))) // 4)
         segs = min(-(-256 // base) if base < 256 else 1, max(n_tiles, 1))
         tps = -(-n_tiles // segs) if n_tiles else 0
-        ch = 2 if tps >= 4 and tps % 2 == 0 else 1
-        stage = "true" if cfg.nq >= 4 * (16 // np_) else "false"   # fp32 queries staged in LDS
-        return "score_small", f"score_small_kernel<{cfg.D},{np_},true,{ch},{stage}>"
+        rows_fill = cfg.nq >= 4 * (16 // np_)
+        nw = 8 if rows_fill and tps >= 2 else 4
+        if nw == 8:
+            ch = 2 if tps % 4 == 0 else 1
+        else:
+            ch = 2 if tps >= 4 and tps % 2 == 0 else 1
+        stage = "true" if rows_fill else "false"
+        return "score_small", f"score_small_kernel<{cfg.D},{np_},true,{ch},{stage},{nw}>"
     np_ = min(4, (cfg.H + 1) // 2)
     return "score_full", f"score_full_kernel<{cfg.D},{np_},false,true,{tail},true>"
 
