@@ -353,7 +353,17 @@ int oracle_block_keys(const uint16_t *k_tok, int64_t tok_stride, int32_t G, int3
  *   B     = E * (sum_j p_j |v_j| / sum_j p_j) + 2u*|out|,   u = 2^-24
  * (logit errors move each weight by at most delta relatively, in the
  * numerator and the denominator; each fp32 sum is a chain of at most
- * 64 + C additions; each rescale and exp costs a few more roundings). */
+ * 64 + C additions; each rescale and exp costs a few more roundings).
+ *
+ * The device may also take P*V from two fp16 parts of each weight scaled by
+ * 2^14 (hi = fp16(p*2^14), lo = fp16(p*2^14 - hi)), each part times v exact
+ * in fp32, the two parts summed in chains of their own and added once at
+ * the end.  That adds to E the split's 2^-22 = 4u (relative), the lo chain's
+ * (64 + C)u on sums 2^-11 as large, and the final addition's u:
+ *   E    += (5 + (64 + C) / 2048) * u
+ * and where a part falls below fp16's normal range its absolute error is at
+ * most 2^-25 in units of p*2^14, 2^-39 in units of p, so
+ *   B    += 2^-39 * (sum_j |v_j|) / sum_j p_j. */
 int oracle_attention(const uint16_t *q16, int64_t q_tok_stride, const uint16_t *k_tok,
                      const uint16_t *v_tok, int64_t kv_tok_stride, const int32_t *ids,
                      int64_t ld_ids, int32_t G, int32_t nq, int32_t H, int32_t D,
@@ -372,6 +382,7 @@ int oracle_attention(const uint16_t *q16, int64_t q_tok_stride, const uint16_t *
         double *s = (double *)malloc(sizeof(double) * (size_t)(cap > 0 ? cap : 1));
         double *sabs = (double *)malloc(sizeof(double) * (size_t)(cap > 0 ? cap : 1));
         double *kv = (double *)malloc(sizeof(double) * (size_t)D);
+        double *vabs = (double *)malloc(sizeof(double) * (size_t)D);
 #pragma omp for schedule(dynamic, 1)
         for (int64_t r = 0; r < (int64_t)G * nq; ++r) {
             const int64_t g = r / nq, t = r % nq;
@@ -418,9 +429,11 @@ int oracle_attention(const uint16_t *q16, int64_t q_tok_stride, const uint16_t *
                     s[a] = exp(s[a] - m);   /* weight p_a, reusing the logit slot */
                     den += s[a];
                 }
-                const double E = 2.0 * delta + (2.0 * (64.0 + (double)chunks) + 16.0 * (double)chunks + 32.0) * u;
+                const double E = 2.0 * delta +
+                                 (2.0 * (64.0 + (double)chunks) + 16.0 * (double)chunks + 32.0 +
+                                  5.0 + (64.0 + (double)chunks) / 2048.0) * u;
                 for (int32_t i = 0; i < D; ++i)
-                    o[i] = bo[i] = 0.0;
+                    o[i] = bo[i] = vabs[i] = 0.0;
                 for (int64_t a = 0; a < L; ++a) {
                     const uint16_t *vj = v_tok + tok[a] * kv_tok_stride + g * D;
                     for (int32_t i = 0; i < D; ++i)
@@ -428,11 +441,12 @@ int oracle_attention(const uint16_t *q16, int64_t q_tok_stride, const uint16_t *
                     for (int32_t i = 0; i < D; ++i) {
                         o[i] += s[a] * kv[i];
                         bo[i] += s[a] * fabs(kv[i]);
+                        vabs[i] += fabs(kv[i]);
                     }
                 }
                 for (int32_t i = 0; i < D; ++i) {
                     o[i] /= den;
-                    bo[i] = E * (bo[i] / den) + 2.0 * u * fabs(o[i]);
+                    bo[i] = E * (bo[i] / den) + ldexp(vabs[i], -39) / den + 2.0 * u * fabs(o[i]);
                 }
             }
         }
@@ -440,6 +454,7 @@ int oracle_attention(const uint16_t *q16, int64_t q_tok_stride, const uint16_t *
         free(s);
         free(sabs);
         free(kv);
+        free(vabs);
     }
     return 0;
 }

@@ -815,10 +815,13 @@ def test_attention_invariants():
 
 
 def _fp32_device_model(q16, kt, vt, ids, n_kv, bs, no_rescale=False, drop_last=False,
-                       scale_1_over_d=False):
+                       scale_1_over_d=False, split_weights=False, no_unscale=False):
     """The device's algorithm in numpy float32: per row and head, chunks of
     up to 64 tokens in id order, a running maximum, chunk sums of P*V and P
-    added into rescaled running sums."""
+    added into rescaled running sums.  split_weights: P*V from the weights'
+    two fp16 parts scaled by 2^14 (hi = fp16(p*2^14), lo = fp16(p*2^14 -
+    hi)), each part's products and sums in float32 of their own, the two
+    added and unscaled at the end."""
     nq, G, H, D = q16.shape
     Q = q16.view(np.float16).astype(np.float32)
     K = kt.view(np.float16).astype(np.float32)
@@ -834,6 +837,7 @@ def _fp32_device_model(q16, kt, vt, ids, n_kv, bs, no_rescale=False, drop_last=F
                 continue
             m = np.full(H, -np.inf, np.float32)
             acc = np.zeros((H, D), np.float32)
+            acc_lo = np.zeros((H, D), np.float32)
             den = np.zeros(H, np.float32)
             for c0 in range(0, len(toks), 64):
                 ch = toks[c0:c0 + 64]
@@ -843,9 +847,20 @@ def _fp32_device_model(q16, kt, vt, ids, n_kv, bs, no_rescale=False, drop_last=F
                 p = np.exp((s - mn[:, None]).astype(np.float32)).astype(np.float32)
                 if no_rescale:   # the running sums kept at the old maximum's scale
                     a = np.ones_like(a)
-                acc = acc * a[:, None] + (p @ V[ch, g]).astype(np.float32)
+                if split_weights:
+                    p14 = (p * np.float32(16384)).astype(np.float32)
+                    hi = p14.astype(np.float16).astype(np.float32)
+                    lo = (p14 - hi).astype(np.float16).astype(np.float32)
+                    acc = acc * a[:, None] + (hi @ V[ch, g]).astype(np.float32)
+                    acc_lo = acc_lo * a[:, None] + (lo @ V[ch, g]).astype(np.float32)
+                else:
+                    acc = acc * a[:, None] + (p @ V[ch, g]).astype(np.float32)
                 den = den * a + p.sum(axis=1, dtype=np.float32)
                 m = mn
+            if split_weights:
+                acc = (acc + acc_lo).astype(np.float32)
+                if not no_unscale:
+                    acc = (acc * np.float32(1.0 / 16384)).astype(np.float32)
             out[t, g] = acc / den[:, None]
     return out
 
@@ -856,6 +871,14 @@ def test_attention_bound_admits_fp32_model_and_rejects_mistakes():
     good = _fp32_device_model(*case)
     res = oracle.check_attention(good, ref, B)
     assert res.ok, str(res)
+    # the weighted values from the weights' two fp16 parts (the matrix-core
+    # form) are within the same bound
+    split = _fp32_device_model(*case, split_weights=True)
+    res = oracle.check_attention(split, ref, B)
+    assert res.ok, str(res)
+    # and leaving the parts' 2^14 scale in is caught
+    scaled = _fp32_device_model(*case, split_weights=True, no_unscale=True)
+    assert not oracle.check_attention(scaled, ref, B).ok
     for kw in (dict(no_rescale=True), dict(drop_last=True), dict(scale_1_over_d=True)):
         bad = _fp32_device_model(*case, **kw)
         assert not oracle.check_attention(bad, ref, B).ok, kw
