@@ -74,6 +74,11 @@ RANDOM = [
     ("odd_h", 2, 9, 3, 128, 2000, 100, 8, 0.3), ("h12_d64", 3, 7, 12, 64, 777, 32, 12, 0.5),
     ("h16", 1, 5, 16, 128, 640, 64, 10, 0.2), ("h1_bs200", 2, 11, 1, 64, 5000, 200, 9, 1.0),
     ("big_logits", 1, 6, 8, 128, 3000, 64, 20, 1.5),
+    # blocks of several chunks with a ragged last one at D = 128 (the
+    # weighted values on the matrix cores, two passes per chunk), 5 and 6
+    # heads (padded columns)
+    ("d128_bs200_h6", 2, 7, 6, 128, 5003, 200, 9, 0.8), ("d128_bs100_h5", 1, 10, 5, 128, 3001, 100, 12, 1.0),
+    ("d64_bs130_h8", 1, 8, 8, 64, 2600, 130, 10, 1.0),
 ]
 
 
