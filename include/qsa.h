@@ -69,7 +69,7 @@ typedef enum qsa_status {
                                 the library's fixed scratch array */
 } qsa_status;
 
-#define QSA_ABI_VERSION 6
+#define QSA_ABI_VERSION 7
 #define QSA_MAX_K 64
 /* Largest block size qsa_block_keys takes (its sums stay exact in float64). */
 #define QSA_BLOCK_KEYS_MAX_BS 8192
@@ -116,6 +116,20 @@ qsa_status qsa_convert_f32_f16(const float *src, uint16_t *dst, int64_t n, void 
  * writes the scores, then each wave selects its own rows with the
  * selector's row code.  Not accepted by qsa_block_scores. */
 #define QSA_FUSED_SELECT 2u
+
+/* qsa_select_phase / qsa_select_phase_noalloc: the selection streams with the
+ * scoring, and no score is written (the scope of the pages' phase, Strata
+ * pull request #228, part 1: scores, then the per-query top-k; the scores
+ * themselves are only the selection's input).  Where the wide scorer serves
+ * the shape with one workgroup per 64 queries over all blocks (many query
+ * rows, H <= 8, at most 65536 blocks), each wave keeps a running candidate
+ * set per score row in LDS while the block tiles stream by, and selects from
+ * it at the end of the launch: the ids and values are those of the separate
+ * selector over the same scores, bit for bit, and scores_ws is not touched.
+ * Other shapes take the two-launch path (scores written, then selected).
+ * Takes precedence over QSA_FUSED_SELECT where it serves the shape.  Not
+ * accepted by qsa_block_scores. */
+#define QSA_STREAM_SELECT 4u
 
 /*
  * qsa_block_scores -- step 2 of the phase: the score of every (g, t, b)
@@ -248,9 +262,11 @@ int64_t qsa_sparse_attention_ws_floats(int32_t G, int32_t nq, int32_t H, int32_t
  *   scores_ws device fp32 [G*qc][ld_s] workspace, qc = q_chunk > 0 ?
  *             min(q_chunk, nq) : nq; for the chunk of n <= qc queries starting
  *             at query t0, row g*n + t' holds the scores of query t0 + t'
- *             (after the call: those of the last chunk)
+ *             (after the call: those of the last chunk), except where
+ *             QSA_STREAM_SELECT served the shape (then it is not written)
  *   ids, vals as qsa_select_topk with rows = G*nq (vals may be NULL)
- *   flags     QSA_FORCE_TAIL (as qsa_block_scores), QSA_FUSED_SELECT, or 0
+ *   flags     QSA_FORCE_TAIL (as qsa_block_scores), QSA_FUSED_SELECT,
+ *             QSA_STREAM_SELECT (any combination), or 0
  *   other arguments as qsa_block_scores / qsa_select_topk.
  * Workspaces must not overlap the inputs or outputs.  Errors as the three
  * stage entry points; the whole call is validated before the first launch.

@@ -24,10 +24,11 @@ LIB_PATH = os.path.join(_HERE, "libqsa.so")
 QSA_OK, QSA_ERR_ARG, QSA_ERR_UNSUPPORTED, QSA_ERR_HIP, QSA_ERR_TOO_LARGE = 0, 1, 2, 3, 4
 MAX_K = 64
 NOALLOC_SCRATCH_BYTES = 64 << 20   # qsa.h QSA_NOALLOC_SCRATCH_BYTES
-ABI_VERSION = 6   # qsa.h QSA_ABI_VERSION this binding is written for
+ABI_VERSION = 7   # qsa.h QSA_ABI_VERSION this binding is written for
 BLOCK_KEYS_MAX_BS = 8192   # qsa.h QSA_BLOCK_KEYS_MAX_BS
 FORCE_TAIL = 1   # qsa.h QSA_FORCE_TAIL
 FUSED_SELECT = 2   # qsa.h QSA_FUSED_SELECT
+STREAM_SELECT = 4   # qsa.h QSA_STREAM_SELECT
 EXPORTS = ("qsa_abi_version", "qsa_status_string", "qsa_convert_f32_f16", "qsa_block_keys",
            "qsa_block_scores", "qsa_select_topk", "qsa_select_phase", "qsa_select_phase_noalloc",
            "qsa_sparse_attention", "qsa_sparse_attention_ws_floats")
@@ -233,7 +234,7 @@ class PhaseWorkspace:
 def select_phase(q: torch.Tensor, kblk: torch.Tensor, n_kv: int, bs: int, k: int,
                  ws: PhaseWorkspace | None = None, q_chunk: int | None = None,
                  force_tail: bool = False, fused_select: bool = False,
-                 stream: torch.cuda.Stream | None = None):
+                 stream_select: bool = False, stream: torch.cuda.Stream | None = None):
     """The whole phase: (fp32 -> fp16 conversion when q is float32), scores,
     top-k.  Returns ids [G, nq, k] (and vals when the workspace has them).
     fp32 queries are converted by the scorers as they load them; without a
@@ -242,7 +243,10 @@ def select_phase(q: torch.Tensor, kblk: torch.Tensor, n_kv: int, bs: int, k: int
     workspace's when one is given (a different value is refused), else 0.
     force_tail: the forced-tail rule (FORCE_TAIL); fused_select: select inside
     the scorer's launch where the fused scorer serves the shape (FUSED_SELECT),
-    with the same results."""
+    with the same results; stream_select: keep a running selection per row
+    while the scores stream by, writing no score, where the streaming scorer
+    serves the shape (STREAM_SELECT; ws.scores is then left untouched), with
+    the same results."""
     fp32 = q.dtype == torch.float32
     nq, G, H, D, qts = _check_q(q, torch.float32 if fp32 else torch.float16)
     if fp32 and not q.is_contiguous():
@@ -265,18 +269,21 @@ def select_phase(q: torch.Tensor, kblk: torch.Tensor, n_kv: int, bs: int, k: int
                                 _ptr(ws.scores), ws.ld_s, _ptr(ws.ids), ws.ids.stride(1),
                                 _ptr(ws.vals), G, nq, H, D, n_kv, bs, k, ws.q_chunk,
                                 (FORCE_TAIL if force_tail else 0) |
-                                (FUSED_SELECT if fused_select else 0), _stream(stream)))
+                                (FUSED_SELECT if fused_select else 0) |
+                                (STREAM_SELECT if stream_select else 0), _stream(stream)))
     return (ws.ids, ws.vals) if ws.vals is not None else ws.ids
 
 
 def select_phase_noalloc(q: torch.Tensor, kblk: torch.Tensor, n_kv: int, bs: int, k: int,
                          ids: torch.Tensor, vals: torch.Tensor | None = None, q_chunk: int = 0,
                          q16: torch.Tensor | None = None, force_tail: bool = False,
-                         stream: torch.cuda.Stream | None = None):
+                         stream_select: bool = False, stream: torch.cuda.Stream | None = None):
     """The whole phase with no device allocation: scores go to the library's
     fixed per-GPU scratch array (NOALLOC_SCRATCH_BYTES), ids [G, nq, k] and
     optional vals are the caller's.  q is float32 (with an optional fp16
-    buffer q16 that receives the converted queries) or float16."""
+    buffer q16 that receives the converted queries) or float16.
+    stream_select as select_phase (the shapes it serves leave the scratch
+    array untouched)."""
     fp32 = q.dtype == torch.float32
     nq, G, H, D, qts = _check_q(q, torch.float32 if fp32 else torch.float16)
     nb = n_blocks(n_kv, bs)
@@ -293,8 +300,9 @@ def select_phase_noalloc(q: torch.Tensor, kblk: torch.Tensor, n_kv: int, bs: int
     _check("qsa_select_phase_noalloc",
            lib.qsa_select_phase_noalloc(_ptr(q) if fp32 else None, _ptr(qsrc16), qts, _ptr(kblk),
                                         khs, _ptr(ids), ids.stride(1), _ptr(vals), G, nq, H, D,
-                                        n_kv, bs, k, q_chunk, FORCE_TAIL if force_tail else 0,
-                                        _stream(stream)))
+                                        n_kv, bs, k, q_chunk,
+                                        (FORCE_TAIL if force_tail else 0) |
+                                        (STREAM_SELECT if stream_select else 0), _stream(stream)))
     return (ids, vals) if vals is not None else ids
 
 

@@ -251,7 +251,8 @@ qsa_status qsa_select_phase(const float *q32, uint16_t *q16, int64_t q_tok_strid
                             int64_t ld_s, int32_t *ids, int64_t ld_ids, float *vals, int32_t G,
                             int32_t nq, int32_t H, int32_t D, int64_t n_kv, int32_t bs, int32_t k,
                             int64_t q_chunk, uint32_t flags, void *stream) {
-    if (q_chunk < 0 || (flags & ~(QSA_FORCE_TAIL | QSA_FUSED_SELECT))) return QSA_ERR_ARG;
+    if (q_chunk < 0 || (flags & ~(QSA_FORCE_TAIL | QSA_FUSED_SELECT | QSA_STREAM_SELECT)))
+        return QSA_ERR_ARG;
     const int64_t qc = (q_chunk > 0 && q_chunk < nq) ? q_chunk : nq;
     ScoreCheck c;
     // scores are validated for the chunk-sized workspace; the query source
@@ -296,10 +297,13 @@ qsa_status qsa_select_phase(const float *q32, uint16_t *q16, int64_t q_tok_strid
                                                     static_cast<int64_t>(G) * H * D, q_tok_stride, s);
             if (e != hipSuccess) return QSA_ERR_HIP;
         }
-        // with QSA_FUSED_SELECT the shapes the fused scorer serves are
-        // selected inside the scorer's launch
-        const qsa::FusedSelect fsel{ids, ld_ids, vals, k, nq, t0};
-        const qsa::FusedSelect *fs = (flags & QSA_FUSED_SELECT) && k > 0 ? &fsel : nullptr;
+        // with QSA_STREAM_SELECT or QSA_FUSED_SELECT the shapes the
+        // streaming or fused scorer serves are selected inside the scorer's
+        // launch
+        const qsa::FusedSelect fsel{ids, ld_ids, vals, k, nq, t0, (flags & QSA_STREAM_SELECT) != 0,
+                                    (flags & QSA_FUSED_SELECT) != 0};
+        const qsa::FusedSelect *fs =
+            (flags & (QSA_FUSED_SELECT | QSA_STREAM_SELECT)) && k > 0 ? &fsel : nullptr;
         bool selected = false;
         if (c.nb > 0) {
             hipError_t e = fused ? run_scores(geo, c, s, q32 + qoff, q16c, fs, &selected)

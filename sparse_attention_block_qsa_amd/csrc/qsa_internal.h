@@ -87,7 +87,17 @@ struct FusedSelect {
     float *vals;
     int32_t k;
     int64_t dst_group_rows, dst_row0;
+    // streaming form: the running selection of qsa_stream_row.h, no score
+    // written (shapes with one workgroup per query group over all blocks,
+    // one head pass, at most 65536 blocks)
+    bool stream;
+    // the scores written, then selected at the end of the same launch
+    bool fused;
 };
+
+// Whether the streaming selection serves this shape (the decode, small and
+// split-block shapes and more than 8 heads take the two-launch path).
+bool stream_select_serves(const ScoreGeom &g, bool tail);
 
 // With fs set, shapes the fused form serves (one workgroup per query group
 // over all blocks, one head pass, 513-1024 or 2049-2112 blocks) are scored

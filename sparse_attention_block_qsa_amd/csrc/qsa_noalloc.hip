@@ -8,7 +8,9 @@
 // looked up once per device (hipGetSymbolAddress, with that device current)
 // and passed to the phase's kernels like any workspace pointer; the array's
 // name is never used as an address in host code.  Nothing in it has to start
-// at zero: the scorer writes every score cell the selector reads.  Every call
+// at zero: the scorer writes every score cell the selector reads.  With
+// QSA_STREAM_SELECT, shapes the streaming scorer serves do not use it at all.
+// Every call
 // on a GPU uses the same array, so calls that overlap on one GPU (different
 // streams, no ordering between them) race; calls on one stream do not.
 #include "qsa.h"
@@ -57,7 +59,7 @@ qsa_status qsa_select_phase_noalloc(const float *q32, uint16_t *q16, int64_t q_t
                                     int32_t nq, int32_t H, int32_t D, int64_t n_kv, int32_t bs,
                                     int32_t k, int64_t q_chunk, uint32_t flags, void *stream) {
     if (G < 0 || nq < 0 || n_kv < 0 || q_chunk < 0 ||
-        (flags & ~(QSA_FORCE_TAIL | QSA_FUSED_SELECT)))
+        (flags & ~(QSA_FORCE_TAIL | QSA_FUSED_SELECT | QSA_STREAM_SELECT)))
         return QSA_ERR_ARG;
     if (bs < 1) return QSA_ERR_UNSUPPORTED;
     // Rows of the workspace: nb scores rounded up to 32 floats, so that every
@@ -68,6 +70,21 @@ qsa_status qsa_select_phase_noalloc(const float *q32, uint16_t *q16, int64_t q_t
         // nothing to score or select; the phase itself checks the rest
         return qsa_select_phase(q32, q16, q_tok_stride, kblk, kblk_head_stride, nullptr, ld_s,
                                 ids, ld_ids, vals, G, nq, H, D, n_kv, bs, k, 0, flags, stream);
+    }
+    // The streaming selection writes no score: where it serves the whole
+    // shape in one pass, the queries are not chunked for the array (which
+    // is then only the phase's nominal workspace, never written).
+    if ((flags & QSA_STREAM_SELECT) && q_chunk == 0 && k > 0 && nb > 0) {
+        const qsa::ScoreGeom geo{nullptr, q_tok_stride, kblk, kblk_head_stride, nullptr, ld_s,
+                                 G, nq, H, D, n_kv / bs, 0.0f};
+        if (qsa::stream_select_serves(geo, n_kv % bs != 0)) {
+            hipError_t err = hipSuccess;
+            void *ws = scratch_on_current_device(&err);
+            if (!ws) return QSA_ERR_HIP;
+            return qsa_select_phase(q32, q16, q_tok_stride, kblk, kblk_head_stride,
+                                    static_cast<float *>(ws), ld_s, ids, ld_ids, vals, G, nq, H,
+                                    D, n_kv, bs, k, 0, flags, stream);
+        }
     }
     if (ld_s > kScratchBytes / 4 / G) return QSA_ERR_TOO_LARGE;   // not even one query fits
     const int64_t fit = kScratchBytes / (4 * G * ld_s);           // queries per pass

@@ -54,6 +54,7 @@
 //    (qsa_topk_row.h), so the phase needs no selector launch.  The scores
 //    are still written; the selection re-reads them.
 #include "qsa_internal.h"
+#include "qsa_stream_row.h"
 #include "qsa_topk_row.h"
 
 namespace qsa {
@@ -103,7 +104,8 @@ __device__ __forceinline__ float relu_bits(float x) {
     return __builtin_bit_cast(float, max(__builtin_bit_cast(int32_t, x), 0));
 }
 
-template <int D, int NP, bool ACCUM, bool BUF, bool TAIL, bool SRC32, int SEL = 0>
+template <int D, int NP, bool ACCUM, bool BUF, bool TAIL, bool SRC32, int SEL = 0,
+          bool STREAM = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void score_full_kernel(ScoreArgs a) {
     constexpr int KS = D / 16;              // MFMA K-steps per head
@@ -123,7 +125,9 @@ void score_full_kernel(ScoreArgs a) {
     // chunk, interleaved medians: fp16 queries 243 -> 227 us, fp32 queries
     // 267 -> 253 us.  It costs 8 registers, which the accumulating pass and
     // the 64-bit store path do not have to spare (they would spill).
-    constexpr int DIST = (!ACCUM && BUF) ? 3 : 2;
+    // The streaming selection keeps DIST = 2: its candidate buffers need the
+    // LDS of the fourth ring slot, and its state the registers.
+    constexpr int DIST = (!ACCUM && BUF && !STREAM) ? 3 : 2;
     constexpr int NS = DIST + 1;   // ring slots
     __shared__ uint4 kbuf[NS][TILE_U4];
     __shared__ uint4 ktail[TAIL ? CHUNKS : 1];   // the partial block's key
@@ -131,6 +135,15 @@ void score_full_kernel(ScoreArgs a) {
     __shared__ uint64_t sel_slot[SEL > 0 ? kScoreWaves : 1][SEL > 0 ? 128 : 1];
     __shared__ uint32_t sel_stash[SEL > 0 ? kScoreWaves : 1][SEL > 0 ? 64 * SEL : 1];
     static_assert(SEL == 0 || (!ACCUM && BUF), "fused selection: one head pass, buffer stores");
+    // streaming selection: per wave and score row a buffer of kStreamCap
+    // candidates (score bits, block id) in block-id order
+    // (each wave's region ends with one dummy slot per lane)
+    constexpr int kStreamWave = kWaveQueries * kStreamCap + 64;
+    __shared__ uint32_t st_val[STREAM ? kScoreWaves * kStreamWave : 1];
+    __shared__ uint16_t st_id[STREAM ? kScoreWaves * kStreamWave : 1];
+    __shared__ __attribute__((aligned(16))) float st_thr[kScoreWaves][STREAM ? kWaveQueries : 4];
+    __shared__ uint32_t st_kb[kScoreWaves][STREAM ? kWaveQueries : 1];
+    static_assert(!STREAM || (!ACCUM && SEL == 0), "streaming selection: one head pass");
 
     const uint32_t L = xcd_logical_id(blockIdx.x, gridDim.x);
     const int split = static_cast<int>(L % a.n_splits);
@@ -327,6 +340,151 @@ void score_full_kernel(ScoreArgs a) {
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
 
     int slot = 0;   // ring slot of the current tile
+
+    // ---- streaming selection state (STREAM) -------------------------------
+    // Row r of the wave is query t_base + r; in a tile, register u holds row
+    // 8*(u/4) + (u%4) in lanes 0-31 and that row + 4 in lanes 32-63.  Per
+    // row: the candidate count (uniform, in scalar registers), and in LDS its
+    // admission threshold (st_thr) and a key no later number is below
+    // (st_kb), both written only when the row is compacted.
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    uint32_t *wval = st_val + wu * kStreamWave;
+    uint16_t *wid = st_id + wu * kStreamWave;
+    const uint32_t dummy = kWaveQueries * kStreamCap + l;   // this lane's dummy slot
+    float *wthr = st_thr[wu];
+    uint32_t *wkb = st_kb[wu];
+    const bool upper = l >= 32;
+    const int kk = static_cast<int>(min(static_cast<int64_t>(a.k), static_cast<int64_t>(a.nb)));
+    int cnt[kWaveQueries];
+    #pragma unroll
+    for (int r = 0; r < kWaveQueries; ++r) cnt[r] = 0;
+    if constexpr (STREAM) {
+        if (l < kWaveQueries) {
+            wthr[l] = -__builtin_inff();
+            wkb[l] = 0;
+        }
+        wave_lds_sync();
+    }
+    // Compacts the rows in need (and the rows within 40 of full, so that
+    // rows filling together are compacted in one pass).
+    auto stream_compact_rows = [&](uint32_t need) __attribute__((always_inline)) {
+        #pragma unroll
+        for (int r = 0; r < kWaveQueries; ++r)
+            if (cnt[r] > kStreamCap - 40) need |= 1u << r;
+        uint32_t cv = 0;
+        #pragma unroll
+        for (int r = 0; r < kWaveQueries; ++r) cv = lane_set(cv, l, r, cnt[r]);
+        need = uni(need);
+        while (need) {
+            const int r = uni(__builtin_ctz(need));
+            need &= need - 1;
+            uint32_t adm, kb;
+            const int n = stream_compact(wval + r * kStreamCap, wid + r * kStreamCap,
+                                         uni(__builtin_amdgcn_readlane(cv, r)), kk, l, &adm, &kb);
+            cv = lane_set(cv, l, r, n);
+            if (l == 0) {
+                wthr[r] = stream_admit_floor(adm);
+                wkb[r] = kb;
+            }
+        }
+        #pragma unroll
+        for (int r = 0; r < kWaveQueries; ++r) cnt[r] = uni(__builtin_amdgcn_readlane(cv, r));
+        wave_lds_sync();
+    };
+    // This lane's rows' thresholds (rows 4h .. 4h+3 and 8+4h .. 8+4h+3 for
+    // registers 0-3 and 4-7), held in registers and reloaded after each
+    // compaction.
+    float tv[8];
+    auto load_tv = [&]() __attribute__((always_inline)) {
+        const float4 t0 = *reinterpret_cast<const float4 *>(wthr + (upper ? 4 : 0));
+        const float4 t1 = *reinterpret_cast<const float4 *>(wthr + (upper ? 12 : 8));
+        tv[0] = t0.x; tv[1] = t0.y; tv[2] = t0.z; tv[3] = t0.w;
+        tv[4] = t1.x; tv[5] = t1.y; tv[6] = t1.z; tv[7] = t1.w;
+    };
+    if constexpr (STREAM) load_tv();
+    // One tile's scores (tot, columns tile*32 + l%32) into the row buffers.
+    auto stream_tile = [&](int tile, const float (&tot)[8]) __attribute__((always_inline)) {
+        const int bcol = tile * kTileBlocks + bl;
+        const bool colv = bcol < a.nf;   // columns of real blocks
+        const uint64_t colm = ballot_b(colv);
+        // rows that would overflow: compacted before anything is appended
+        uint32_t need = 0;
+        #pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint64_t m = ballot_b(!(tot[u] < tv[u])) & colm;   // NaN passes
+            const int rA = 8 * (u >> 2) + (u & 3);
+            if (cnt[rA] + __popc(static_cast<uint32_t>(m)) > kStreamCap) need |= 1u << rA;
+            if (cnt[rA + 4] + __popc(static_cast<uint32_t>(m >> 32)) > kStreamCap)
+                need |= 1u << (rA + 4);
+        }
+        need = uni(need);
+        if (need) {   // uniform; rare once the thresholds have risen
+            stream_compact_rows(need);
+            load_tv();
+        }
+        // append: lanes of a row write in lane (block) order after the row's
+        // last entry; mbcnt over the 64-lane mask gives the lower half its
+        // position directly and the upper half after the lower half's count,
+        // which the uniform adjustment removes
+        #pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int rA = 8 * (u >> 2) + (u & 3), rB = rA + 4;
+            const bool ge = !(tot[u] < tv[u]);
+            const uint64_t m = ballot_b(ge) & colm;
+            const uint32_t mlo = static_cast<uint32_t>(m), mhi = static_cast<uint32_t>(m >> 32);
+            const int nA = __popc(mlo), nB = __popc(mhi);
+            const int sb = cnt[rA] + rA * kStreamCap;
+            const int adj = cnt[rB] + rB * kStreamCap - nA - sb;
+            const uint32_t b = upper ? static_cast<uint32_t>(adj) : 0u;
+            uint32_t idx = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, b)) + sb;
+            // every lane writes (no branch, so the counts stay scalar): the
+            // lanes that do not pass write their own dummy slot.  The empty
+            // asm keeps the compiler from turning the select into a branch
+            // around the position arithmetic.
+            asm volatile("" : "+v"(idx));
+            const uint32_t at = (ge && colv) ? idx : dummy;
+            wval[at] = __builtin_bit_cast(uint32_t, tot[u]);
+            wid[at] = static_cast<uint16_t>(bcol);
+            cnt[rA] = uni(cnt[rA] + nA);
+            cnt[rB] = uni(cnt[rB] + nB);
+        }
+    };
+    // The tail block's candidate of every row (lane r < 16: row r's score),
+    // appended after compacting the rows whose buffer is full.
+    auto stream_tail = [&](float sum) __attribute__((always_inline)) {
+        uint32_t cv = 0;
+        #pragma unroll
+        for (int r = 0; r < kWaveQueries; ++r) cv = lane_set(cv, l, r, cnt[r]);
+        const bool lr = l < kWaveQueries;
+        wave_lds_sync();
+        bool tp = lr && !(sum < wthr[l & 15]);
+        uint32_t full = uni(static_cast<uint32_t>(ballot_b(tp && cv == static_cast<uint32_t>(kStreamCap))));
+        if (full) {   // uniform
+            while (full) {
+                const int r = uni(__builtin_ctz(full));
+                full &= full - 1;
+                uint32_t adm, kb;
+                const int n = stream_compact(wval + r * kStreamCap, wid + r * kStreamCap, kStreamCap,
+                                             kk, l, &adm, &kb);
+                cv = lane_set(cv, l, r, n);
+                if (l == 0) {
+                    wthr[r] = stream_admit_floor(adm);
+                    wkb[r] = kb;
+                }
+            }
+            wave_lds_sync();
+            tp = lr && !(sum < wthr[l & 15]);
+        }
+        if (tp) {
+            wval[l * kStreamCap + cv] = __builtin_bit_cast(uint32_t, sum);
+            wid[l * kStreamCap + cv] = static_cast<uint16_t>(a.nf);
+        }
+        const uint64_t added = ballot_b(tp);
+        #pragma unroll
+        for (int r = 0; r < kWaveQueries; ++r)
+            cnt[r] = uni(__builtin_amdgcn_readlane(cv, r) + static_cast<int>((added >> r) & 1));
+    };
+
     half8 kf0 = __builtin_bit_cast(half8, kbuf[0][l]);
     half8 kf1 = __builtin_bit_cast(half8, kbuf[0][64 + l]);
 
@@ -410,14 +568,18 @@ void score_full_kernel(ScoreArgs a) {
                 tot[u] = (!ACCUM && p == 0) ? pp : tot[u] + pp;
             }
         }
-        #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            if constexpr (BUF) {
-                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, tot[u]), rs,
-                                                      static_cast<int>(rowoff[u] + coloff), 0,
-                                                      kStoreNT);
-            } else if (rowel[u] >= 0 && coloff != kOut) {
-                __builtin_nontemporal_store(tot[u], srow_base + rowel[u] + bcol);
+        if constexpr (STREAM) {
+            stream_tile(tile, tot);
+        } else {
+            #pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if constexpr (BUF) {
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, tot[u]), rs,
+                                                          static_cast<int>(rowoff[u] + coloff), 0,
+                                                          kStoreNT);
+                } else if (rowel[u] >= 0 && coloff != kOut) {
+                    __builtin_nontemporal_store(tot[u], srow_base + rowel[u] + bcol);
+                }
             }
         }
         __syncthreads();
@@ -477,7 +639,19 @@ void score_full_kernel(ScoreArgs a) {
             for (int c = 0; c < NPC; ++c) red[64 * c + l] = r[c];
             __syncthreads();
             const int t = t_base + l;
-            if (l < kWaveQueries && t < a.nq) {
+            if constexpr (STREAM) {
+                // lane r < 16: row r's tail score, a candidate like any other
+                // (the block of the largest id, so it goes last)
+                float sum = 0.0f;
+                #pragma unroll
+                for (int c = 0; c < NPC; ++c) {
+                    #pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (4 * c + j < a.nh) sum = sum + red[64 * c + 16 * j + (l & 15)];
+                }
+                if (a.tail_add != 0.0f) sum = sum + a.tail_add;   // forced-tail rule
+                stream_tail(sum);
+            } else if (l < kWaveQueries && t < a.nq) {
                 float *cell = srow_base + static_cast<int64_t>(t) * a.ld_s + a.nf;
                 float sum = ACCUM ? *cell : 0.0f;
                 #pragma unroll
@@ -492,12 +666,27 @@ void score_full_kernel(ScoreArgs a) {
         }
     }
 
+    if constexpr (STREAM) {
+        // Each row's selection from its buffer, the wave's rows one after
+        // another (the ring is free: every wave has passed its last barrier).
+        uint64_t *slot = reinterpret_cast<uint64_t *>(&kbuf[1][0]) + wu * 128;
+        const int nrows = min(kWaveQueries, a.nq - t_base);   // uniform
+        uint32_t cv = 0;
+        #pragma unroll
+        for (int r = 0; r < kWaveQueries; ++r) cv = lane_set(cv, l, r, cnt[r]);
+        for (int r = 0; r < nrows; ++r) {
+            const int64_t drow = static_cast<int64_t>(g) * a.dst_group_rows + a.dst_row0 + t_base + r;
+            stream_final(wval + r * kStreamCap, wid + r * kStreamCap,
+                         __builtin_amdgcn_readlane(cv, r), a.k, kk, wkb[r], slot, a.ids + drow * a.ld_ids,
+                         a.vals ? a.vals + drow * a.ld_ids : nullptr, l);
+        }
+    }
+
     if constexpr (SEL > 0) {
         // The wave's score stores (its 16 rows, every block) before its own
         // loads of them: the stores were made by other lanes of this wave.
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        const int wu = __builtin_amdgcn_readfirstlane(w);
         const int nrows = min(kWaveQueries, a.nq - t_base);   // uniform
         auto row = [&](int i) { return srow_base + static_cast<int64_t>(t_base + i) * a.ld_s; };
         auto select = [&](int i, const uint32_t (&x)[SEL]) __attribute__((always_inline)) {
@@ -570,6 +759,30 @@ score_fn pick_sel_ts(int np, bool tail, bool src32) {
     return src32 ? pick_sel_np<D, false, true, SEL>(np) : pick_sel_np<D, false, false, SEL>(np);
 }
 
+// The streaming-selection instances: one head pass (np <= 4).
+template <int D, bool TAIL, bool SRC32>
+score_fn pick_stream_np(int np) {
+    switch (np) {
+        case 1: return score_full_kernel<D, 1, false, true, TAIL, SRC32, 0, true>;
+        case 2: return score_full_kernel<D, 2, false, true, TAIL, SRC32, 0, true>;
+        case 3: return score_full_kernel<D, 3, false, true, TAIL, SRC32, 0, true>;
+        case 4: return score_full_kernel<D, 4, false, true, TAIL, SRC32, 0, true>;
+    }
+    return nullptr;
+}
+
+template <int D>
+score_fn pick_stream_ts(int np, bool tail, bool src32) {
+    if (tail) return src32 ? pick_stream_np<D, true, true>(np) : pick_stream_np<D, true, false>(np);
+    return src32 ? pick_stream_np<D, false, true>(np) : pick_stream_np<D, false, false>(np);
+}
+
+score_fn pick_stream(int D, int np, bool tail, bool src32) {
+    if (D == 128) return pick_stream_ts<128>(np, tail, src32);
+    if (D == 64) return pick_stream_ts<64>(np, tail, src32);
+    return nullptr;
+}
+
 // Columns of the fused selection for nb blocks (0: no fused form).
 int sel_columns(int64_t nb) {
     const int64_t nj = (nb + 63) / 64;
@@ -599,6 +812,19 @@ void split_blocks(int64_t base, int64_t n_tiles, int64_t target, int64_t *splits
 
 }  // namespace
 
+bool stream_select_serves(const ScoreGeom &geo, bool tail) {
+    if (geo.nf <= 0 || geo.nq <= 0 || geo.G <= 0 || geo.H > kHeadsPerPass) return false;
+    if (decode_rows(geo) || small_rows(geo)) return false;
+    // block ids are kept as 16 bits
+    if (geo.nf + (tail ? 1 : 0) > 65536) return false;
+    // one workgroup per query group over all blocks
+    const int64_t n_tiles = (geo.nf + kTileBlocks - 1) / kTileBlocks;
+    const int64_t base = static_cast<int64_t>(geo.G) * ((geo.nq + kGroupQueries - 1) / kGroupQueries);
+    int64_t splits = 1, tps = n_tiles;
+    split_blocks(base, n_tiles, 512, &splits, &tps);
+    return splits == 1 && base <= 0x7fffffffLL;
+}
+
 hipError_t launch_score_full(const ScoreGeom &geo, bool tail, hipStream_t s, const float *q32,
                              uint16_t *q16w, const FusedSelect *fs, bool *selected) {
     if (selected) *selected = false;
@@ -620,7 +846,23 @@ hipError_t launch_score_full(const ScoreGeom &geo, bool tail, hipStream_t s, con
 
     // fused selection: each workgroup scores every block of its query group
     const int64_t nb = geo.nf + (tail ? 1 : 0);
-    const int sel = fs && fs->k > 0 ? sel_columns(nb) : 0;
+    // streaming selection: no score is written
+    if (fs && fs->stream && fs->k > 0 && stream_select_serves(geo, tail)) {
+        const int np = (geo.H + 1) / 2;
+        score_fn fn = pick_stream(geo.D, np, tail, q32 != nullptr);
+        if (!fn) return hipErrorInvalidValue;
+        ScoreArgs a{geo.q16, q32, q32 ? q16w : nullptr, geo.qts, geo.kblk, geo.khs, nullptr,
+                    geo.ld_s, geo.G, geo.nq, geo.H, 0, geo.H, 0, geo.nf,
+                    static_cast<int32_t>(n_qgroups), 1, static_cast<int32_t>(tps),
+                    static_cast<int32_t>(n_tiles), geo.tail_add, fs->ids, fs->ld_ids, fs->vals,
+                    fs->k, static_cast<int32_t>(nb), fs->dst_group_rows, fs->dst_row0};
+        void *args[] = {&a};
+        hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(fn),
+                                       dim3(static_cast<unsigned>(grid)), dim3(256), args, 0, s);
+        if (e == hipSuccess && selected) *selected = true;
+        return e;
+    }
+    const int sel = fs && fs->fused && fs->k > 0 ? sel_columns(nb) : 0;
     if (sel > 0 && splits == 1 && geo.H <= hpp && buf) {
         const int np = (geo.H + 1) / 2;
         score_fn fn = pick_sel(geo.D, np, tail, q32 != nullptr, sel);

@@ -41,7 +41,8 @@ hipError_t launch_score_full(const ScoreGeom &g, bool tail, hipStream_t, const f
     // decides by shape)
     if (selected) *selected = false;
     if (fs) {
-        g_launches.push_back({'F', fs->dst_group_rows, fs->dst_row0, fs->k});
+        g_launches.push_back({'F', fs->dst_group_rows, fs->dst_row0,
+                              fs->k | (fs->stream ? 0x100 : 0) | (fs->fused ? 0x200 : 0)});
         if (selected) *selected = g.nq >= 4096;
     }
     return hipSuccess;
@@ -343,8 +344,18 @@ int main() {
         a.flags = QSA_FUSED_SELECT;
         expect("phase fused select, not taken", QSA_OK, [&] { return a.call(); }, 3);
         CHECK(g_launches[1].kind == 'F' && g_launches[1].a == 256 && g_launches[1].b == 0 &&
-                  g_launches[1].c == 16 && g_launches[2].kind == 'k',
+                  g_launches[1].c == (16 | 0x200) && g_launches[2].kind == 'k',
               "a fused request the scorer declines is followed by the selector launch");
+        a.flags = QSA_STREAM_SELECT;
+        expect("phase stream select, not taken", QSA_OK, [&] { return a.call(); }, 3);
+        CHECK(g_launches[1].kind == 'F' && g_launches[1].c == (16 | 0x100) &&
+                  g_launches[2].kind == 'k',
+              "a streaming request the scorer declines is followed by the selector launch");
+        a.flags = QSA_STREAM_SELECT | QSA_FUSED_SELECT | QSA_FORCE_TAIL;
+        expect("phase all flags", QSA_OK, [&] { return a.call(); }, 3);
+        CHECK(g_launches[0].kind == 'f' && (g_launches[0].c & 8) && g_launches[1].kind == 'F' &&
+                  g_launches[1].c == (16 | 0x300),
+              "every flag reaches the scorer");
         PArgs f;
         f.q16 = nullptr;
         f.flags = QSA_FUSED_SELECT;
@@ -392,7 +403,7 @@ int main() {
     };
     const PCase pcases[] = {
         {"q_chunk<0", [](PArgs &a) { a.q_chunk = -1; }, QSA_ERR_ARG},
-        {"flags=4", [](PArgs &a) { a.flags = 4; }, QSA_ERR_ARG},
+        {"flags=8", [](PArgs &a) { a.flags = 8; }, QSA_ERR_ARG},
         {"k>64", [](PArgs &a) { a.k = 65; a.ld_ids = 65; }, QSA_ERR_UNSUPPORTED},
         {"D=80", [](PArgs &a) { a.D = 80; }, QSA_ERR_UNSUPPORTED},
         {"ids null", [](PArgs &a) { a.ids = nullptr; }, QSA_ERR_ARG},

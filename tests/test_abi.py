@@ -95,7 +95,7 @@ def scores_call(lib, **kw):
     (dict(q16=A16 + 2), UNSUP), (dict(qts=8 * 128 + 4), UNSUP), (dict(kblk=A16 + 8), UNSUP),
     (dict(khs=64 * 128 + 2), UNSUP), (dict(scores=A16 + 2), UNSUP),
     (dict(ld_s=1 << 62, nq=8), ARG),          # row extent overflows int64
-    (dict(flags=2), ARG), (dict(flags=0xFFFFFFFF), ARG),   # only QSA_FORCE_TAIL is defined
+    (dict(flags=2), ARG), (dict(flags=4), ARG), (dict(flags=0xFFFFFFFF), ARG),   # only QSA_FORCE_TAIL is defined
     (dict(flags=3, n_kv=0), ARG),             # refused before the empty early return
 ])
 def test_block_scores_refusals(lib, kw, want):
@@ -154,7 +154,8 @@ def phase_call(lib, **kw):
     (dict(ld_s=10), ARG), (dict(q32=A16 + 2), UNSUP), (dict(H=20), UNSUP),
     # no fp16 buffer: the fp32 rows must be 16-byte aligned
     (dict(q16=None, q32=A16 + 4), UNSUP), (dict(q16=None, qts=8 * 128 + 2), UNSUP),
-    (dict(flags=4), ARG), (dict(flags=1 << 31), ARG),   # QSA_FORCE_TAIL | QSA_FUSED_SELECT only
+    # QSA_FORCE_TAIL | QSA_FUSED_SELECT | QSA_STREAM_SELECT only
+    (dict(flags=8), ARG), (dict(flags=1 << 31), ARG),
 ])
 def test_select_phase_refusals(lib, kw, want):
     assert phase_call(lib, **kw) == want
@@ -177,7 +178,7 @@ def noalloc_call(lib, **kw):
 
 @pytest.mark.parametrize("kw,want", [
     (dict(q_chunk=-1), ARG), (dict(G=-1), ARG), (dict(nq=-1), ARG), (dict(n_kv=-1), ARG),
-    (dict(bs=0), UNSUP), (dict(flags=4), ARG),
+    (dict(bs=0), UNSUP), (dict(flags=8), ARG),
     # one query's score row (17M blocks of one token, 68 MB) exceeds the 64 MiB array
     (dict(n_kv=17 << 20, bs=1, khs=(17 << 20) * 128), TOO_LARGE),
     # four KV heads of 2049 blocks fit 2016 queries per pass, not 4096
