@@ -210,6 +210,9 @@ class Phase:
         # the phase with the selection inside the scorer's launch where the
         # fused scorer serves the shape (QSA_FUSED_SELECT = 2)
         self._phase_fused = (L.qsa_select_phase, phase + (c.k, 0, qsa.FUSED_SELECT))
+        # the phase with the streaming selection where it serves the shape
+        # (QSA_STREAM_SELECT = 4): no score written
+        self._phase_stream = (L.qsa_select_phase, phase + (c.k, 0, qsa.STREAM_SELECT))
 
     def _call(self, fa):
         fn, args = fa
@@ -234,6 +237,9 @@ class Phase:
 
     def step_fused(self):
         self._call(self._phase_fused)
+
+    def step_stream(self):
+        self._call(self._phase_stream)
 
 
 def graph_of(torch, fn, n):
@@ -487,9 +493,15 @@ def measure(cfg, qsa, torch, steps, warmup, w=None, calls_100=False):
         del g
     # the fused form's results are the separate selector's, bit for bit
     fused_same = bool(torch.equal(eager_ids, ph.ws.ids))
+    # and so are the streaming form's
+    ph.ws.ids.fill_(-1)
+    g = graph_of(torch, ph.step_stream, steps)
+    alone["phase_stream_select"] = time_graph(torch, g, steps)
+    del g
+    stream_same = bool(torch.equal(eager_ids, ph.ws.ids))
     med9 = {name: median_of_9(torch, fn) for name, fn in
             (("phase", ph.step), ("scorer", ph.score), ("block_scores_f16", ph.score16),
-             ("phase_fused_select", ph.step_fused))}
+             ("phase_fused_select", ph.step_fused), ("phase_stream_select", ph.step_stream))}
     c100 = ({name: single_call_stats(torch, fn) for name, fn in
              (("phase", ph.step), ("scorer", ph.score), ("block_scores_f16", ph.score16))}
             if calls_100 else None)
@@ -502,6 +514,7 @@ def measure(cfg, qsa, torch, steps, warmup, w=None, calls_100=False):
         "wall_s": wall,
         "graph_replay_matches_eager": same,
         "fused_select_matches": fused_same,
+        "stream_select_matches": stream_same,
         "stages_ms": stages,
         "entry_points_ms": alone,
         "scorer_tflops": flop / (stages["scorer"] * 1e-3) / 1e12 if stages["scorer"] > 0 else 0.0,
@@ -787,6 +800,11 @@ def main():
             "phase_fused_select_ms": pe["phase_fused_select"],
             "phase_fused_select_median_of_9_ms": pr["median_of_9_ms"]["phase_fused_select"],
             "fused_select_matches": pr["fused_select_matches"],
+            # the phase with the streaming selection (QSA_STREAM_SELECT): no
+            # score written, same ids bit for bit
+            "phase_stream_select_ms": pe["phase_stream_select"],
+            "phase_stream_select_median_of_9_ms": pr["median_of_9_ms"]["phase_stream_select"],
+            "stream_select_matches": pr["stream_select_matches"],
             # single launches timed by the pages' protocol (3 warmups, median of 9)
             "median_of_9_ms": pr["median_of_9_ms"],
             "scorer_frac_of_peak_median_of_9":
@@ -802,7 +820,10 @@ def main():
               f"{pr['median_of_9_ms']['block_scores_f16'] * 1e3:.1f} us; fused-select phase "
               f"{pe['phase_fused_select'] * 1e3:.1f} us (graph), "
               f"{pr['median_of_9_ms']['phase_fused_select'] * 1e3:.1f} us (median of 9), same ids "
-              f"{pr['fused_select_matches']}", file=sys.stderr, flush=True)
+              f"{pr['fused_select_matches']}; streaming-select phase "
+              f"{pe['phase_stream_select'] * 1e3:.1f} us (graph), "
+              f"{pr['median_of_9_ms']['phase_stream_select'] * 1e3:.1f} us (median of 9), same ids "
+              f"{pr['stream_select_matches']}", file=sys.stderr, flush=True)
 
     decode = None
     if args.decode_steps > 0 and cfg.name != qi.DECODE.name:
