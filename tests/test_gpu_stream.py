@@ -229,3 +229,23 @@ def test_stream_flag_on_shapes_it_does_not_serve():
         nb = cfg.nb
         assert torch.equal(a.scores[:, :, :nb].view(torch.int32),
                            b.scores[:, :, :nb].view(torch.int32))
+
+
+def test_stream_select_random_geometries():
+    """Seeded random shapes the streaming form serves (and a few it does not):
+    ids and values equal the two-launch phase's, bit for bit."""
+    rng = np.random.default_rng(20261202)
+    for i in range(10):
+        H = int(rng.choice([1, 2, 3, 4, 5, 6, 7, 8]))
+        D = int(rng.choice([64, 128]))
+        G = int(rng.choice([4, 8]))
+        nq = int(rng.integers(4096, 4500) if G == 8 else rng.integers(8192, 8600))
+        nb = int(rng.integers(40, 2500))
+        n_kv = nb * 64 - int(rng.integers(0, 64))
+        k = int(rng.integers(1, 65))
+        cfg = qi.Config(f"rand{i}", G, nq, H, D, n_kv, 64, k, "normal", 6000 + i)
+        w = qi.make(cfg)
+        log(f"random stream geometry {i}: G {G} nq {nq} H {H} D {D} n_kv {n_kv} k {k}")
+        a = _phase(w, cfg, False, fp16=bool(i % 2))
+        b = _phase(w, cfg, True, fp16=bool(i % 2))
+        _same(a, b, cfg.name)
