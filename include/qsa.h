@@ -295,7 +295,9 @@ qsa_status qsa_select_phase(const float *q32, uint16_t *q16, int64_t q_tok_strid
  *            (one pass when they all fit)
  * Results are those of qsa_select_phase with the same q_chunk, bit for bit.
  * Errors: as qsa_select_phase; QSA_ERR_TOO_LARGE (nothing launched) when one
- * query's G score rows, or the q_chunk asked for, exceed the array.
+ * query's G score rows, or the q_chunk asked for, exceed the array.  With
+ * QSA_STREAM_SELECT, a shape the streaming selection serves whole (q_chunk 0
+ * or >= nq) runs in one pass without the array, whatever its size.
  * Calls on one GPU share the array: calls that overlap in time on one GPU
  * (unordered streams) race and give undefined results; calls ordered on one
  * stream are safe.  The array's contents after a call are unspecified.

@@ -72,9 +72,10 @@ qsa_status qsa_select_phase_noalloc(const float *q32, uint16_t *q16, int64_t q_t
                                 ids, ld_ids, vals, G, nq, H, D, n_kv, bs, k, 0, flags, stream);
     }
     // The streaming selection writes no score: where it serves the whole
-    // shape in one pass, the queries are not chunked for the array (which
-    // is then only the phase's nominal workspace, never written).
-    if ((flags & QSA_STREAM_SELECT) && q_chunk == 0 && k > 0 && nb > 0) {
+    // shape in one pass (no q_chunk, or one of at least nq), the queries are
+    // not chunked for the array (which is then only the phase's nominal
+    // workspace, never written), whatever its size.
+    if ((flags & QSA_STREAM_SELECT) && (q_chunk == 0 || q_chunk >= nq) && k > 0 && nb > 0) {
         const qsa::ScoreGeom geo{nullptr, q_tok_stride, kblk, kblk_head_stride, nullptr, ld_s,
                                  G, nq, H, D, n_kv / bs, 0.0f};
         if (qsa::stream_select_serves(geo, n_kv % bs != 0)) {

@@ -204,6 +204,10 @@ def test_stream_select_non_finite_scores():
 
 
 def test_stream_select_noalloc_equals_phase():
+    """The allocation-free entry point with the streaming selection: one pass
+    without the scratch array.  A q_chunk of all the queries, which the array
+    cannot hold (about 2016 queries fit at this shape), is refused without
+    the flag and served with it, so the streaming path is the one taken."""
     cfg = qi.Config("noalloc_stream", 4, 8192, 8, 128, 2049 * 64 - 20, 64, 64, "normal", 5401)
     w = qi.make(cfg)
     a = _phase(w, cfg, False)
@@ -211,10 +215,17 @@ def test_stream_select_noalloc_equals_phase():
     kd = torch.from_numpy(w.kblk.view(np.float16)).to(dev())
     ids = torch.full((cfg.G, cfg.nq, cfg.k), -7, dtype=torch.int32, device=dev())
     vals = torch.full((cfg.G, cfg.nq, cfg.k), float("nan"), device=dev())
-    qsa.select_phase_noalloc(q, kd, cfg.n_kv, cfg.bs, cfg.k, ids, vals, stream_select=True)
-    torch.cuda.synchronize()
-    assert torch.equal(a.ids, ids)
-    assert torch.equal(a.vals.view(torch.int32), vals.view(torch.int32))
+    with pytest.raises(qsa.QSAError) as err:
+        qsa.select_phase_noalloc(q, kd, cfg.n_kv, cfg.bs, cfg.k, ids, vals, q_chunk=cfg.nq)
+    assert err.value.status == qsa.QSA_ERR_TOO_LARGE
+    for q_chunk in (0, cfg.nq):
+        ids.fill_(-7)
+        vals.fill_(float("nan"))
+        qsa.select_phase_noalloc(q, kd, cfg.n_kv, cfg.bs, cfg.k, ids, vals, q_chunk=q_chunk,
+                                 stream_select=True)
+        torch.cuda.synchronize()
+        assert torch.equal(a.ids, ids)
+        assert torch.equal(a.vals.view(torch.int32), vals.view(torch.int32))
 
 
 def test_stream_flag_on_shapes_it_does_not_serve():
