@@ -810,6 +810,24 @@ void split_blocks(int64_t base, int64_t n_tiles, int64_t target, int64_t *splits
     *splits = (n_tiles + *tps - 1) / *tps;
 }
 
+// The wide scorer's grid: groups of 64 queries per workgroup over the KV
+// heads, the block axis split only when the groups cannot fill the CUs twice
+// (512 workgroups).
+struct WideGrid {
+    int64_t n_tiles, n_qgroups, base, splits, tps;
+};
+
+WideGrid wide_grid(const ScoreGeom &geo) {
+    WideGrid w;
+    w.n_tiles = (geo.nf + kTileBlocks - 1) / kTileBlocks;
+    w.n_qgroups = (geo.nq + kGroupQueries - 1) / kGroupQueries;
+    w.base = static_cast<int64_t>(geo.G) * w.n_qgroups;
+    w.splits = 1;
+    w.tps = w.n_tiles;
+    split_blocks(w.base, w.n_tiles, 512, &w.splits, &w.tps);
+    return w;
+}
+
 }  // namespace
 
 bool stream_select_serves(const ScoreGeom &geo, bool tail) {
@@ -818,11 +836,8 @@ bool stream_select_serves(const ScoreGeom &geo, bool tail) {
     // block ids are kept as 16 bits
     if (geo.nf + (tail ? 1 : 0) > 65536) return false;
     // one workgroup per query group over all blocks
-    const int64_t n_tiles = (geo.nf + kTileBlocks - 1) / kTileBlocks;
-    const int64_t base = static_cast<int64_t>(geo.G) * ((geo.nq + kGroupQueries - 1) / kGroupQueries);
-    int64_t splits = 1, tps = n_tiles;
-    split_blocks(base, n_tiles, 512, &splits, &tps);
-    return splits == 1 && base <= 0x7fffffffLL;
+    const WideGrid w = wide_grid(geo);
+    return w.splits == 1 && w.base <= 0x7fffffffLL;
 }
 
 hipError_t launch_score_full(const ScoreGeom &geo, bool tail, hipStream_t s, const float *q32,
@@ -833,15 +848,10 @@ hipError_t launch_score_full(const ScoreGeom &geo, bool tail, hipStream_t s, con
     const int hpp = kHeadsPerPass;
     // buffer stores address one KV head's rows with 32-bit offsets below 2^30
     const bool buf = static_cast<int64_t>(geo.nq) * geo.ld_s * 4 < (int64_t(1) << 30);
-    const int64_t n_tiles = (geo.nf + kTileBlocks - 1) / kTileBlocks;
+    const WideGrid wg = wide_grid(geo);
+    const int64_t n_tiles = wg.n_tiles, n_qgroups = wg.n_qgroups, splits = wg.splits, tps = wg.tps;
     if (n_tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    // Groups of 64 queries per workgroup, split along the block axis only
-    // when the groups cannot fill the CUs twice.
-    const int64_t n_qgroups = (geo.nq + kGroupQueries - 1) / kGroupQueries;
-    const int64_t base = static_cast<int64_t>(geo.G) * n_qgroups;
-    int64_t splits = 1, tps = n_tiles;
-    split_blocks(base, n_tiles, 512, &splits, &tps);
-    const int64_t grid = base * splits;
+    const int64_t grid = wg.base * splits;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
 
     // fused selection: each workgroup scores every block of its query group
