@@ -25,8 +25,8 @@ bool src32_ok(const float *q32, int64_t qts) {
 // given: enough for one workgroup per CU over all rows, but no more than
 // give each of a workgroup's 8 waves one 64-token chunk, and at most 64.
 // Each split costs its own query staging, an 8-wave merge and a workspace
-// round trip: at 256 rows of 64 chunks, four splits per row measured 379 us
-// against 283 us for one.
+// round trip: at 256 rows of 64 chunks (8 heads, D = 128), two splits per row
+// measured 95.5 us and four 111.9 us against 82.5 us for one.
 int64_t attention_splits(int64_t rows, int32_t bs, int32_t k) {
     const int64_t chunks = static_cast<int64_t>(k) * ((static_cast<int64_t>(bs) + 63) / 64);
     int64_t sp = (256 + rows - 1) / rows;
