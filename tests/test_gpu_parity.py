@@ -456,6 +456,21 @@ def topk_cases():
             tt[r, rng.choice(nbt, 150, replace=False)] = 3.0
         cases.append((f"tied_top_{nbt}", tt, nbt))
     cases.append(("all_negative_100", -rng.random((6, 100)).astype(np.float32) - 0.5, 100))
+    # rows of at most 128 blocks, which are sorted whole (one or two
+    # register columns): the special values and ties of the rows above
+    for nbs in (50, 64, 100, 128):
+        s3 = rng.standard_normal((6, nbs)).astype(np.float32)
+        s3[rng.random((6, nbs)) < 0.15] = np.nan
+        s3[rng.random((6, nbs)) < 0.05] = np.inf
+        s3[rng.random((6, nbs)) < 0.05] = -np.inf
+        s3[0, :] = np.nan
+        s3[1, 10:] = np.nan   # fewer numbers than k: NaNs selected, in id order
+        cases.append(("nan_inf", s3, nbs))
+        z3 = rng.integers(-2, 3, (6, nbs)).astype(np.float32)
+        z3[z3 == 0] = np.where(rng.random(int((z3 == 0).sum())) < 0.5, 0.0, -0.0)
+        cases.append(("signed_zero_duplicates", z3, nbs))
+    cases.append(("all_equal", np.full((4, 128), 0.5, np.float32), 128))
+    cases.append(("all_zero", np.zeros((4, 100), np.float32), 100))
     cases.append(("all_negative_2049", -rng.random((4, 2049)).astype(np.float32), 2049))
     return cases
 
