@@ -645,20 +645,25 @@ def config_summary(cfg, r) -> dict:
             "graph_replay_matches_eager": r["graph_replay_matches_eager"]}
 
 
-def _oracle_time(w, cfg, target_s, max_reps=1000) -> tuple[float, int, float]:
+def _oracle_time(w, cfg, target_s, max_reps=1000) -> tuple[float, int, float, float, float]:
     """Seconds per whole-workload oracle pass (scores + S + B, then top-k),
-    repeated until about target_s of wall time."""
+    repeated until about target_s of wall time; also the two stages' seconds
+    per pass (fixture generation excluded)."""
     import oracle
-    reps, tot = 0, 0.0
+    reps, t_scores, t_topk = 0, 0.0, 0.0
     while True:
         t0 = time.perf_counter()
         ref = oracle.scores(w.q16, w.kblk, cfg.nb)
+        t1 = time.perf_counter()
         oracle.topk(ref.score, cfg.k)
-        tot += time.perf_counter() - t0
+        t2 = time.perf_counter()
+        t_scores += t1 - t0
+        t_topk += t2 - t1
         reps += 1
-        if tot >= target_s or reps >= max_reps:
+        if t_scores + t_topk >= target_s or reps >= max_reps:
             break
-    return tot / reps, reps, tot
+    tot = t_scores + t_topk
+    return tot / reps, reps, tot, t_scores / reps, t_topk / reps
 
 
 def cpu_model() -> str | None:
@@ -678,7 +683,7 @@ def cpu_baseline(cfg, target_s, single_thread_cfgs=()):
     import oracle
     import qsa_inputs as qi
     w = qi.make(cfg)
-    per, reps, tot = _oracle_time(w, cfg, target_s)
+    per, reps, tot, per_scores, per_topk = _oracle_time(w, cfg, target_s)
     threads = oracle.max_threads()
     single = {}
     if single_thread_cfgs:
@@ -686,13 +691,15 @@ def cpu_baseline(cfg, target_s, single_thread_cfgs=()):
         try:
             for c in single_thread_cfgs:
                 wc = qi.make(c)
-                p1, n1, _ = _oracle_time(wc, c, 0.5, max_reps=20)
-                single[c.name] = {"ms": p1 * 1e3, "tflops": c.flop / p1 / 1e12, "reps": n1}
+                p1, n1, _, s1, k1 = _oracle_time(wc, c, 0.5, max_reps=20)
+                single[c.name] = {"ms": p1 * 1e3, "scores_ms": s1 * 1e3, "topk_ms": k1 * 1e3,
+                                  "tflops": c.flop / p1 / 1e12, "reps": n1}
         finally:
             oracle.set_threads(threads)
     return {"value": cfg.flop / per / 1e12, "unit": "TFLOP/s", "cores": threads,
             "cores_available": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
             "kind": "oracle", "ms_per_step": per * 1e3,
+            "scores_ms": per_scores * 1e3, "topk_ms": per_topk * 1e3,
             "sample": f"whole {cfg.name} workload ({cfg.rows} rows x {cfg.nb} blocks: scores, "
                       f"S, B in float64 and top-{cfg.k}), {reps} repetition(s), {tot:.1f} s, "
                       f"{threads} OpenMP threads",
