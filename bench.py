@@ -367,8 +367,9 @@ class PowerClock:
 
 def measured_peaks(torch, power=None) -> dict | None:
     """Measured ceilings from libqsa_bench.so: the sustained rate of the
-    scorer's MFMA instruction on register-resident random fp16 operands (and
-    on zeros), and the streaming read bandwidth of a 2 GiB buffer."""
+    scorers' two MFMA instructions on register-resident random fp16 operands
+    (and on zeros), the better of the two being the ceiling, and the
+    streaming read bandwidth of a 2 GiB buffer."""
     import ctypes
     import numpy as np
     path = os.path.join(ROOT, "sparse_attention_block_qsa_amd", "libqsa_bench.so")
@@ -377,6 +378,7 @@ def measured_peaks(torch, power=None) -> dict | None:
     L = ctypes.CDLL(path)
     vp, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     L.qsa_bench_mfma_f16.argtypes = [vp, i64, vp, c_int, c_int, c_int, vp]
+    L.qsa_bench_mfma_f16_16x16x32.argtypes = [vp, i64, vp, c_int, c_int, c_int, vp]
     L.qsa_bench_read.argtypes = [vp, i64, vp, c_int, vp]
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
@@ -384,44 +386,50 @@ def measured_peaks(torch, power=None) -> dict | None:
     rand = torch.from_numpy(
         (rng.standard_normal(4096 * 8) / np.sqrt(128)).astype(np.float16)).to(dev)
     zero = torch.zeros(4096 * 8, dtype=torch.float16, device=dev)
-    res = {"mfma_kernel": "v_mfma_f32_32x32x16_f16 loop, operands in registers, four "
-                          "accumulator chains per wave; 2 and 4 waves per SIMD, runs of ~5 ms "
-                          "after a warm-up run; the better of the two.  'random': four A and four "
-                          "B fragments of N(0,1)/sqrt(128) fp16 in turn (the scorer's operands "
-                          "change as often); 'random_held': one A and one B fragment per wave; "
-                          "'zero': zero operands",
+    res = {"mfma_kernel": "v_mfma_f32_32x32x16_f16 and v_mfma_f32_16x16x32_f16 loops, operands "
+                          "in registers, four (eight) accumulator chains per wave; 2 and 4 waves "
+                          "per SIMD, runs of ~5 ms after a warm-up run; the best of the runs.  "
+                          "'random': four A and four B fragments of N(0,1)/sqrt(128) fp16 in turn "
+                          "(the scorer's operands change as often); 'random_held': one A and one "
+                          "B fragment per wave; 'zero': zero operands",
            "mfma_runs": {}}
+    shapes = {"32x32x16": (L.qsa_bench_mfma_f16, 2 * 32 * 32 * 16, 12000),
+              "16x16x32": (L.qsa_bench_mfma_f16_16x16x32, 2 * 16 * 16 * 32, 24000)}
 
-    def mfma_run(buf, grid, iters, held, out):
-        rc = L.qsa_bench_mfma_f16(ctypes.c_void_p(buf.data_ptr()), buf.numel() // 8,
-                                  ctypes.c_void_p(out.data_ptr()), grid, iters, held,
-                                  ctypes.c_void_p(stream.cuda_stream))
+    def mfma_run(fn, buf, grid, iters, held, out):
+        rc = fn(ctypes.c_void_p(buf.data_ptr()), buf.numel() // 8,
+                ctypes.c_void_p(out.data_ptr()), grid, iters, held,
+                ctypes.c_void_p(stream.cuda_stream))
         assert rc == 0, rc
 
     for name, buf, held in (("random", rand, 0), ("random_held", rand, 1), ("zero", zero, 0)):
         best = 0.0
-        for waves in (2, 4):
-            grid = 256 * waves
-            iters = 12000 // waves
-            out = torch.empty(grid * 256, dtype=torch.float32, device=dev)
-            flop = grid * 4 * iters * L.qsa_bench_mfma_per_iter() * 2 * 32 * 32 * 16
-            ts = []
-            for _ in range(4):
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record()
-                mfma_run(buf, grid, iters, held, out)
-                e1.record()
-                torch.cuda.synchronize()
-                ts.append(e0.elapsed_time(e1))
-            ts = sorted(ts[1:])
-            rate = flop / (ts[len(ts) // 2] * 1e-3) / 1e12
-            run = {"tflops": rate, "ms": ts[len(ts) // 2]}
-            if power is not None and power.ok and waves == 2:
-                run["power_clock"] = power.sample_while(
-                    torch, lambda: mfma_run(buf, grid, iters, held, out), 0.4)
-            res["mfma_runs"][f"{name}_{waves}waves_per_simd"] = run
-            best = max(best, rate)
+        for shape, (fn, flop_per_mfma, iters0) in shapes.items():
+            best_shape = 0.0
+            for waves in (2, 4):
+                grid = 256 * waves
+                iters = iters0 // waves
+                out = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+                flop = grid * 4 * iters * L.qsa_bench_mfma_per_iter() * flop_per_mfma
+                ts = []
+                for _ in range(4):
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    mfma_run(fn, buf, grid, iters, held, out)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    ts.append(e0.elapsed_time(e1))
+                ts = sorted(ts[1:])
+                rate = flop / (ts[len(ts) // 2] * 1e-3) / 1e12
+                run = {"tflops": rate, "ms": ts[len(ts) // 2]}
+                if power is not None and power.ok and waves == 2:
+                    run["power_clock"] = power.sample_while(
+                        torch, lambda: mfma_run(fn, buf, grid, iters, held, out), 0.4)
+                res["mfma_runs"][f"{name}_{shape}_{waves}waves_per_simd"] = run
+                best_shape = max(best_shape, rate)
+            res[f"mfma_f16_{name}_{shape}_tflops"] = best_shape
+            best = max(best, best_shape)
         res[f"mfma_f16_{name}_tflops"] = best
     nbytes = 2 << 30
     src = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)

@@ -47,6 +47,22 @@
 //  * Grid: (KV head, 64-query group, block split), with logical ids laid out
 //    so that each XCD (blockIdx % 8) takes a contiguous range: the splits of
 //    one query group and the query groups of one KV head share that XCD's L2.
+//  * The 16x16x32 form (M16: one head pass with buffer stores, the instances
+//    the prefill scorers run).  The same tile on v_mfma_f32_16x16x32_f16:
+//    A row tiles of 4 queries x 4 heads (lane l holds row l%16 = 4*query +
+//    head of its quad, channels 32s + 8*(l/16) .. +7), B column tiles of 16
+//    blocks read from the same LDS ring (chunk 4s + l/16, block 16c + l%16),
+//    and each lane's four accumulator rows are four heads of one query, so
+//    the relu and the head sum stay lane-local, in the same order.  A D = 128
+//    dot product chained over four 16x16x32 steps has the bits of the eight
+//    32x32x16 steps (a probe over 20,480 dot products, cancellation
+//    included, found no difference), so both forms, the small and the decode
+//    scorer agree bit for bit.  Under the chip's power limit a loop of the
+//    16x16x32 instruction sustains more than one of the 32x32x16 (measured
+//    beside the scorers by the benchmark), and at the prefill chunk the
+//    fp16-input scorer went 227 -> 213 us (fp32 queries 254 -> 252 us).
+//    Lane l stores query t_base + 4*(u/2) + l/16 and block 16*(u%2) + l%16
+//    of the tile for register u: 64-byte row segments.
 //  * Fused selection (SEL > 0, one split per query group): after its last
 //    tile and the partial block, each wave selects the top-k of its own 16
 //    query rows, whose scores (every block, tail included) only it wrote,
@@ -62,6 +78,7 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 struct ScoreArgs {
     const uint16_t *q16;   // query source when q32 is null
@@ -105,10 +122,17 @@ __device__ __forceinline__ float relu_bits(float x) {
 }
 
 template <int D, int NP, bool ACCUM, bool BUF, bool TAIL, bool SRC32, int SEL = 0,
-          bool STREAM = false>
+          bool STREAM = false, bool M16 = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void score_full_kernel(ScoreArgs a) {
     constexpr int KS = D / 16;              // MFMA K-steps per head
+    // M16: the same tile on v_mfma_f32_16x16x32_f16 (row tiles of 4 queries
+    // x 4 heads, two 16-block column tiles); see the design notes above
+    constexpr int KS16 = D / 32;            // its K-steps
+    constexpr int NHH = (2 * NP + 3) / 4;   // head quads in the pass
+    constexpr int RT = 4 * NHH;             // row tiles: 4 query quads x NHH
+    static_assert(!M16 || (!ACCUM && BUF && SEL == 0 && !STREAM),
+                  "the 16x16x32 form: one head pass, buffer stores, no selection");
     constexpr int CHUNKS = D / 8;           // 16-byte chunks per block row
     constexpr int TILE_U4 = CHUNKS * kTileBlocks;
     constexpr int LOADS = TILE_U4 / 256;    // uint4 per thread per tile
@@ -204,40 +228,106 @@ void score_full_kernel(ScoreArgs a) {
     // queries (SRC32) are converted on load; the first split of each query
     // group writes their fp16 bits for the real rows and heads, so every
     // element of the workspace is written exactly once.
-    half8 qa[NP][KS];
+    half8 qa[M16 ? 1 : NP][M16 ? 1 : KS];
+    half8 qa16[M16 ? RT : 1][M16 ? KS16 : 1];
     const int hh = (l >> 4) & 1;   // this lane's head within a pair
     // This lane's row of head hh in the workspace, channel 8*(l/32) (head
     // 2p + hh is 2p*D further on), or null when it writes nothing: the first
     // split of each query group writes the real rows.
     uint16_t *qw = nullptr;
-    {
-        const int tq = l & 15, kc = l >> 5;
-        const int t = t_base + tq;
-        const int64_t trow = static_cast<int64_t>(t < a.nq ? t : 0) * a.qts;
-        int64_t qoff[NP];
-        #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const int h = 2 * p + hh;
-            qoff[p] = trow + static_cast<int64_t>(g * a.H + a.h0 + (h < a.nh ? h : 0)) * D + 8 * kc;
+    if constexpr (!M16) {
+        {
+            const int tq = l & 15, kc = l >> 5;
+            const int t = t_base + tq;
+            const int64_t trow = static_cast<int64_t>(t < a.nq ? t : 0) * a.qts;
+            int64_t qoff[NP];
+            #pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const int h = 2 * p + hh;
+                qoff[p] = trow + static_cast<int64_t>(g * a.H + a.h0 + (h < a.nh ? h : 0)) * D + 8 * kc;
+            }
+            if (SRC32 && a.q16w != nullptr && split == 0 && t < a.nq && hh < a.nh)
+                qw = a.q16w + qoff[0];
+            if constexpr (!SRC32) {
+                #pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    #pragma unroll
+                    for (int p = 0; p < NP; ++p)
+                        qa[p][s] = *reinterpret_cast<const half8 *>(a.q16 + qoff[p] + 16 * s);
+                }
+            } else {
+                // fp32 fragments (8 VGPRs each, twice the fp16 size) in batches
+                // of kQBatch, kQDepth batches in flight: each batch is converted
+                // as it lands and the registers it frees take the next batch's
+                // loads.  Left free, the compiler hoists every load above the
+                // conversions and runs out of registers.
+                constexpr int F = KS * NP;                    // fragments, K-step major
+                // (the accumulating pass with 64-bit store addressing holds more
+                // registers: one batch fewer in flight)
+                constexpr int kQBatch = 4, kQDepth = 3;
+                constexpr int NBAT = (F + kQBatch - 1) / kQBatch;
+                float4 x0[F], x1[F];
+                auto issue = [&](int b) {
+                    #pragma unroll
+                    for (int j = 0; j < kQBatch; ++j) {
+                        const int f = b * kQBatch + j;
+                        if (f < F) {
+                            const float *src = a.q32 + qoff[f % NP] + 16 * (f / NP);
+                            x0[f] = *reinterpret_cast<const float4 *>(src);
+                            x1[f] = *reinterpret_cast<const float4 *>(src + 4);
+                        }
+                    }
+                };
+                #pragma unroll
+                for (int b = 0; b < kQDepth && b < NBAT; ++b) issue(b);
+                #pragma unroll
+                for (int b = 0; b < NBAT; ++b) {
+                    #pragma unroll
+                    for (int j = 0; j < kQBatch; ++j) {
+                        const int f = b * kQBatch + j;
+                        if (f < F) {
+                            const uint4 h = f16x8(x0[f], x1[f]);
+                            qa[f % NP][f / NP] = __builtin_bit_cast(half8, h);
+                            // an empty statement that uses the converted fragment
+                            // and orders memory: the conversion stays before the
+                            // next batch's loads, which cannot move above it
+                            asm volatile("" ::"v"(h.x), "v"(h.y), "v"(h.z), "v"(h.w) : "memory");
+                        }
+                    }
+                    if (b + kQDepth < NBAT) issue(b + kQDepth);
+                }
+            }
+            if (2 * NP > a.nh) {   // uniform
+                #pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    if (hh) qa[NP - 1][s] = half8{};
+            }
         }
-        if (SRC32 && a.q16w != nullptr && split == 0 && t < a.nq && hh < a.nh)
-            qw = a.q16w + qoff[0];
+    } else {
+        // 16x16x32 A fragments: row tile i = (query quad i / NHH, head quad
+        // i % NHH); lane l holds row l%16 = 4*(query in quad) + head in quad,
+        // channels 32s + 8*(l/16) .. +7 of K-step s.  Rows past nq read query
+        // 0 (never stored); heads past the pass are zeroed below.
+        const int m = l & 15, kc = l >> 4;
+        const int qq = m >> 2, hq = m & 3;
+        int64_t qoff[RT];
+        #pragma unroll
+        for (int i = 0; i < RT; ++i) {
+            const int t = t_base + 4 * (i / NHH) + qq;
+            const int h = 4 * (i % NHH) + hq;
+            qoff[i] = static_cast<int64_t>(t < a.nq ? t : 0) * a.qts +
+                      static_cast<int64_t>(g * a.H + a.h0 + (h < a.nh ? h : 0)) * D + 8 * kc;
+        }
         if constexpr (!SRC32) {
             #pragma unroll
-            for (int s = 0; s < KS; ++s) {
+            for (int s = 0; s < KS16; ++s) {
                 #pragma unroll
-                for (int p = 0; p < NP; ++p)
-                    qa[p][s] = *reinterpret_cast<const half8 *>(a.q16 + qoff[p] + 16 * s);
+                for (int i = 0; i < RT; ++i)
+                    qa16[i][s] = *reinterpret_cast<const half8 *>(a.q16 + qoff[i] + 32 * s);
             }
         } else {
-            // fp32 fragments (8 VGPRs each, twice the fp16 size) in batches
-            // of kQBatch, kQDepth batches in flight: each batch is converted
-            // as it lands and the registers it frees take the next batch's
-            // loads.  Left free, the compiler hoists every load above the
-            // conversions and runs out of registers.
-            constexpr int F = KS * NP;                    // fragments, K-step major
-            // (the accumulating pass with 64-bit store addressing holds more
-            // registers: one batch fewer in flight)
+            // batched as above: each batch converted as it lands
+            constexpr int F = KS16 * RT;                  // fragments, K-step major
             constexpr int kQBatch = 4, kQDepth = 3;
             constexpr int NBAT = (F + kQBatch - 1) / kQBatch;
             float4 x0[F], x1[F];
@@ -246,7 +336,7 @@ void score_full_kernel(ScoreArgs a) {
                 for (int j = 0; j < kQBatch; ++j) {
                     const int f = b * kQBatch + j;
                     if (f < F) {
-                        const float *src = a.q32 + qoff[f % NP] + 16 * (f / NP);
+                        const float *src = a.q32 + qoff[f % RT] + 32 * (f / RT);
                         x0[f] = *reinterpret_cast<const float4 *>(src);
                         x1[f] = *reinterpret_cast<const float4 *>(src + 4);
                     }
@@ -261,20 +351,37 @@ void score_full_kernel(ScoreArgs a) {
                     const int f = b * kQBatch + j;
                     if (f < F) {
                         const uint4 h = f16x8(x0[f], x1[f]);
-                        qa[f % NP][f / NP] = __builtin_bit_cast(half8, h);
-                        // an empty statement that uses the converted fragment
-                        // and orders memory: the conversion stays before the
-                        // next batch's loads, which cannot move above it
+                        qa16[f % RT][f / RT] = __builtin_bit_cast(half8, h);
                         asm volatile("" ::"v"(h.x), "v"(h.y), "v"(h.z), "v"(h.w) : "memory");
                     }
                 }
                 if (b + kQDepth < NBAT) issue(b + kQDepth);
             }
+            // the real rows and heads into the fp16 workspace, after the
+            // last load (first split of each query group)
+            if (a.q16w != nullptr && split == 0) {
+                #pragma unroll
+                for (int i = 0; i < RT; ++i) {
+                    const int t = t_base + 4 * (i / NHH) + qq;
+                    const int h = 4 * (i % NHH) + hq;
+                    if (t < a.nq && h < a.nh) {
+                        #pragma unroll
+                        for (int s = 0; s < KS16; ++s)
+                            *reinterpret_cast<uint4 *>(a.q16w + qoff[i] + 32 * s) =
+                                __builtin_bit_cast(uint4, qa16[i][s]);
+                    }
+                }
+            }
         }
-        if (2 * NP > a.nh) {   // uniform
+        // heads past the pass would enter the head sum (odd nh): zero rows
+        if (4 * NHH > a.nh) {   // uniform
             #pragma unroll
-            for (int s = 0; s < KS; ++s)
-                if (hh) qa[NP - 1][s] = half8{};
+            for (int i = 0; i < RT; ++i) {
+                if (4 * (i % NHH) + hq >= a.nh) {
+                    #pragma unroll
+                    for (int s = 0; s < KS16; ++s) qa16[i][s] = half8{};
+                }
+            }
         }
     }
 
@@ -283,7 +390,7 @@ void score_full_kernel(ScoreArgs a) {
     // queries as far as the compiler knows, so a store between the loads
     // would hold back every load after it.  Temporal stores: the 32-byte
     // pieces of each line merge in L2.
-    if constexpr (SRC32) {
+    if constexpr (SRC32 && !M16) {
         if (qw != nullptr) {
             #pragma unroll
             for (int s = 0; s < KS; ++s) {
@@ -297,7 +404,8 @@ void score_full_kernel(ScoreArgs a) {
 
     // ---- output addressing -------------------------------------------------
     // Lane l holds, for register u (0..7), query t_base + 8*(u/4) + 4*(l/32)
-    // + u%4 and block tile*32 + l%32.  With BUF the stores are raw buffer
+    // + u%4 and block tile*32 + l%32 (M16: query t_base + 4*(u/2) + l/16 and
+    // block tile*32 + 16*(u%2) + l%16).  With BUF the stores are raw buffer
     // stores over this KV head's rows: an offset >= 2^30 (past the region,
     // which the host limits to 2^30 bytes) is dropped by the hardware, so
     // masked lanes need no branch.
@@ -310,7 +418,8 @@ void score_full_kernel(ScoreArgs a) {
     int64_t rowel[8];
     #pragma unroll
     for (int u = 0; u < 8; ++u) {
-        const int t = t_base + 8 * (u >> 2) + 4 * (l >> 5) + (u & 3);
+        const int t = M16 ? t_base + 4 * (u >> 1) + (l >> 4)
+                          : t_base + 8 * (u >> 2) + 4 * (l >> 5) + (u & 3);
         if constexpr (BUF)
             rowoff[u] = t < a.nq ? static_cast<uint32_t>(static_cast<int64_t>(t) * a.ld_s * 4) : kOut;
         else
@@ -485,8 +594,13 @@ void score_full_kernel(ScoreArgs a) {
             cnt[r] = uni(__builtin_amdgcn_readlane(cv, r) + static_cast<int>((added >> r) & 1));
     };
 
-    half8 kf0 = __builtin_bit_cast(half8, kbuf[0][l]);
-    half8 kf1 = __builtin_bit_cast(half8, kbuf[0][64 + l]);
+    // This lane's B fragments of a tile's first K-step(s) in the ring: K-steps
+    // 0 and 1 (32x32x16), or column tiles 0 and 1 of K-step 0 (M16: chunk
+    // 4s + l/16, block 16c + l%16, i.e. +128 per K-step).
+    const int fo0 = M16 ? 32 * (l >> 4) + (l & 15) : l;
+    const int fo1 = M16 ? fo0 + 16 : 64 + l;
+    half8 kf0 = __builtin_bit_cast(half8, kbuf[0][fo0]);
+    half8 kf1 = __builtin_bit_cast(half8, kbuf[0][fo1]);
 
     // One tile: its loads go to ld (tile + DIST), and tile + 2 is staged from
     // pw (DIST = 3: loaded by the previous tile) or from ld (DIST = 2).  The
@@ -501,6 +615,14 @@ void score_full_kernel(ScoreArgs a) {
 
         const int bcol = tile * kTileBlocks + bl;
         const uint32_t coloff = bcol < a.nf ? static_cast<uint32_t>(bcol) * 4 : kOut;
+        uint32_t colo[2] = {coloff, coloff};   // M16: column tiles 0 and 1
+        if constexpr (M16) {
+            #pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int bc = tile * kTileBlocks + 16 * c + (l & 15);
+                colo[c] = bc < a.nf ? static_cast<uint32_t>(bc) * 4 : kOut;
+            }
+        }
 
         float tot[8];
         #pragma unroll
@@ -522,50 +644,98 @@ void score_full_kernel(ScoreArgs a) {
         // on a SIMD, the one with MFMAs to issue goes first, and the other
         // runs its epilogue in the gaps (a lasting ping-pong instead of both
         // waves reaching their epilogues together).
-        __builtin_amdgcn_s_setprio(1);
-        const uint4 *kcur = &kbuf[slot][l];
-        floatx16 acc[NP];
-        half8 kf = kf0, kn = kf1;
-        #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            half8 k2 = kn;
-            if (s + 2 < KS) k2 = __builtin_bit_cast(half8, kcur[64 * (s + 2)]);
+        floatx16 acc[M16 ? 1 : NP];
+        floatx4 acc16[M16 ? RT : 1][2];
+        if constexpr (M16) {
+            // every row tile against both column tiles per K-step; the next
+            // K-step's two fragments are read from LDS one step ahead
+            __builtin_amdgcn_s_setprio(1);
+            const uint4 *kcur = &kbuf[slot][0];
+            half8 kb0 = kf0, kb1 = kf1;
             #pragma unroll
-            for (int p = 0; p < NP; ++p) {
-                const floatx16 c = (s == 0) ? floatx16{} : acc[p];
-                acc[p] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[p][s], kf, c, 0, 0, 0);
+            for (int s = 0; s < KS16; ++s) {
+                half8 nb0 = kb0, nb1 = kb1;
+                if (s + 1 < KS16) {
+                    nb0 = __builtin_bit_cast(half8, kcur[fo0 + 128 * (s + 1)]);
+                    nb1 = __builtin_bit_cast(half8, kcur[fo1 + 128 * (s + 1)]);
+                }
+                #pragma unroll
+                for (int i = 0; i < RT; ++i) {
+                    acc16[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        qa16[i][s], kb0, (s == 0) ? floatx4{} : acc16[i][0], 0, 0, 0);
+                    acc16[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        qa16[i][s], kb1, (s == 0) ? floatx4{} : acc16[i][1], 0, 0, 0);
+                }
+                kb0 = nb0;
+                kb1 = nb1;
             }
-            kf = kn;
-            kn = k2;
-        }
-        // Keep the LDS reads a step ahead of their MFMAs (the scheduler would
-        // otherwise sink each read next to its first use).
-        __builtin_amdgcn_sched_group_barrier(0x020, LOADS, 0);   // staging loads
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // fragments 2, 3
-        #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            __builtin_amdgcn_sched_group_barrier(0x008, NP, 0);
-            if (s + 4 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
+            __builtin_amdgcn_sched_group_barrier(0x020, LOADS, 0);   // staging loads
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // K-step 1's fragments
+            #pragma unroll
+            for (int s = 0; s < KS16; ++s) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2 * RT, 0);
+                if (s + 2 < KS16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_s_setprio(0);
+        } else {
+            __builtin_amdgcn_s_setprio(1);
+            const uint4 *kcur = &kbuf[slot][l];
+            half8 kf = kf0, kn = kf1;
+            #pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                half8 k2 = kn;
+                if (s + 2 < KS) k2 = __builtin_bit_cast(half8, kcur[64 * (s + 2)]);
+                #pragma unroll
+                for (int p = 0; p < NP; ++p) {
+                    const floatx16 c = (s == 0) ? floatx16{} : acc[p];
+                    acc[p] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[p][s], kf, c, 0, 0, 0);
+                }
+                kf = kn;
+                kn = k2;
+            }
+            // Keep the LDS reads a step ahead of their MFMAs (the scheduler would
+            // otherwise sink each read next to its first use).
+            __builtin_amdgcn_sched_group_barrier(0x020, LOADS, 0);   // staging loads
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // fragments 2, 3
+            #pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                __builtin_amdgcn_sched_group_barrier(0x008, NP, 0);
+                if (s + 4 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
 
-        __builtin_amdgcn_s_setprio(0);
+            __builtin_amdgcn_s_setprio(0);
+        }
 
         // the next tile was published an iteration ago: fetch its first two
         // fragments now, then stage tile+2 into the free slot
-        kf0 = __builtin_bit_cast(half8, kbuf[nslot][l]);
-        kf1 = __builtin_bit_cast(half8, kbuf[nslot][64 + l]);
+        kf0 = __builtin_bit_cast(half8, kbuf[nslot][fo0]);
+        kf1 = __builtin_bit_cast(half8, kbuf[nslot][fo1]);
         kbuf[wslot][u0] = DIST == 3 ? pw0 : ld0;
         if constexpr (LOADS == 2) kbuf[wslot][u1] = DIST == 3 ? pw1 : ld1;
 
         // epilogue: relu per head; the two heads of a pair are added, then
         // the pair sums in ascending pair order (the head-sum order shared
         // with the small scorer in qsa_small.hip)
-        #pragma unroll
-        for (int p = 0; p < NP; ++p) {
+        if constexpr (M16) {
+            // register u: query quad u/2, column tile u%2; head pair p sits in
+            // rows 2*(p%2), 2*(p%2)+1 of row tile (u/2)*NHH + p/2
             #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float pp = relu_bits(acc[p][u]) + relu_bits(acc[p][u + 8]);   // heads 2p, 2p+1
-                tot[u] = (!ACCUM && p == 0) ? pp : tot[u] + pp;
+            for (int p = 0; p < NP; ++p) {
+                #pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const floatx4 &c4 = acc16[(u >> 1) * NHH + p / 2][u & 1];
+                    const float pp = relu_bits(c4[2 * (p % 2)]) + relu_bits(c4[2 * (p % 2) + 1]);
+                    tot[u] = (p == 0) ? pp : tot[u] + pp;
+                }
+            }
+        } else {
+            #pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                #pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float pp = relu_bits(acc[p][u]) + relu_bits(acc[p][u + 8]);   // heads 2p, 2p+1
+                    tot[u] = (!ACCUM && p == 0) ? pp : tot[u] + pp;
+                }
             }
         }
         if constexpr (STREAM) {
@@ -575,7 +745,7 @@ void score_full_kernel(ScoreArgs a) {
             for (int u = 0; u < 8; ++u) {
                 if constexpr (BUF) {
                     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, tot[u]), rs,
-                                                          static_cast<int>(rowoff[u] + coloff), 0,
+                                                          static_cast<int>(rowoff[u] + colo[M16 ? (u & 1) : 0]), 0,
                                                           kStoreNT);
                 } else if (rowel[u] >= 0 && coloff != kOut) {
                     __builtin_nontemporal_store(tot[u], srow_base + rowel[u] + bcol);
@@ -600,6 +770,81 @@ void score_full_kernel(ScoreArgs a) {
         // channel runs of pair p0 and lanes 32-63 those of pair p1, so lane l
         // runs the chain of query t_base + l%16, head 4c + l/16 (in the pass).
         if (tail_wg) {   // uniform over the workgroup
+          if constexpr (M16) {
+            // The same chains from the 16x16x32 fragments.  In K-step s, lane
+            // group j (lanes 16j .. 16j+15) of row tile i holds channels
+            // 32s + 8j .. +7 of row l%16; a 4x4 transpose over (row tile,
+            // lane group) -- v_permlane32_swap between tiles i and i+2, then
+            // v_permlane16_swap between i and i+1 -- gives lane group j all
+            // 32 channels of its row in tile 4c + j, in channel order.  Lane l
+            // so runs the chain of row l%16 of row tile 4c + l/16: query
+            // 4*((4c + l/16) / NHH) + (l%16)/4 of the wave, head
+            // 4*((4c + l/16) % NHH) + l%4.
+            constexpr int NCH = RT / 4;   // chains per lane
+            uint4 kc[CHUNKS];
+            #pragma unroll
+            for (int c = 0; c < CHUNKS; ++c) kc[c] = ktail[c];   // staged at the prologue
+            float r[NCH];
+            #pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                float acc = 0.0f;
+                #pragma unroll
+                for (int s = 0; s < KS16; ++s) {
+                    const uint4 f0 = __builtin_bit_cast(uint4, qa16[4 * c + 0][s]);
+                    const uint4 f1 = __builtin_bit_cast(uint4, qa16[4 * c + 1][s]);
+                    const uint4 f2 = __builtin_bit_cast(uint4, qa16[4 * c + 2][s]);
+                    const uint4 f3 = __builtin_bit_cast(uint4, qa16[4 * c + 3][s]);
+                    const uint32_t a0[4] = {f0.x, f0.y, f0.z, f0.w}, a1[4] = {f1.x, f1.y, f1.z, f1.w};
+                    const uint32_t a2[4] = {f2.x, f2.y, f2.z, f2.w}, a3[4] = {f3.x, f3.y, f3.z, f3.w};
+                    uint32_t ch[4][4];   // [chunk][dword]
+                    #pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const auto s02 = __builtin_amdgcn_permlane32_swap(a0[e], a2[e], false, false);
+                        const auto s13 = __builtin_amdgcn_permlane32_swap(a1[e], a3[e], false, false);
+                        const auto lo = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+                        const auto hi = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+                        ch[0][e] = lo[0];
+                        ch[1][e] = lo[1];
+                        ch[2][e] = hi[0];
+                        ch[3][e] = hi[1];
+                    }
+                    #pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint4 k4 = kc[4 * s + j];
+                        const uint32_t kw[4] = {k4.x, k4.y, k4.z, k4.w};
+                        #pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float q0 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ch[j][e] & 0xffffu)));
+                            const float q1 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ch[j][e] >> 16)));
+                            const float k0f = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(kw[e] & 0xffffu)));
+                            const float k1f = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(kw[e] >> 16)));
+                            acc = __builtin_fmaf(k0f, q0, acc);
+                            acc = __builtin_fmaf(k1f, q1, acc);
+                        }
+                    }
+                }
+                r[c] = acc > 0.0f ? acc : 0.0f;
+            }
+            // head sum across lanes, through the ring (free after the last
+            // barrier): the wave's (query, head) results at 8*query + head
+            float *red = reinterpret_cast<float *>(&kbuf[0][0]) + w * (8 * kWaveQueries);
+            #pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int i = 4 * c + (l >> 4);
+                red[8 * (4 * (i / NHH) + ((l & 15) >> 2)) + 4 * (i % NHH) + (l & 3)] = r[c];
+            }
+            __syncthreads();
+            const int t = t_base + l;
+            if (l < kWaveQueries && t < a.nq) {
+                float *cell = srow_base + static_cast<int64_t>(t) * a.ld_s + a.nf;
+                float sum = 0.0f;
+                #pragma unroll
+                for (int h = 0; h < 4 * NHH; ++h)
+                    if (h < a.nh) sum = sum + red[8 * l + h];
+                if (a.tail_add != 0.0f) sum = sum + a.tail_add;   // forced-tail rule
+                *cell = sum;
+            }
+          } else {
             constexpr int NPC = (NP + 1) / 2;
             uint4 kc[CHUNKS];
             #pragma unroll
@@ -663,6 +908,7 @@ void score_full_kernel(ScoreArgs a) {
                 if (a.tail_add != 0.0f) sum = sum + a.tail_add;   // forced-tail rule
                 *cell = sum;
             }
+          }
         }
     }
 
@@ -716,13 +962,14 @@ typedef void (*score_fn)(ScoreArgs);
 // per SIMD; more heads take a second, accumulating pass.
 constexpr int kHeadsPerPass = 8;
 
+// One head pass with buffer stores takes the 16x16x32 form (M16 = BUF).
 template <int D, bool BUF, bool TAIL, bool SRC32>
 score_fn pick_d(int np, bool accum) {
     switch (np) {
-        case 1: return accum ? score_full_kernel<D, 1, true, BUF, TAIL, SRC32> : score_full_kernel<D, 1, false, BUF, TAIL, SRC32>;
-        case 2: return accum ? score_full_kernel<D, 2, true, BUF, TAIL, SRC32> : score_full_kernel<D, 2, false, BUF, TAIL, SRC32>;
-        case 3: return accum ? score_full_kernel<D, 3, true, BUF, TAIL, SRC32> : score_full_kernel<D, 3, false, BUF, TAIL, SRC32>;
-        case 4: return accum ? score_full_kernel<D, 4, true, BUF, TAIL, SRC32> : score_full_kernel<D, 4, false, BUF, TAIL, SRC32>;
+        case 1: return accum ? score_full_kernel<D, 1, true, BUF, TAIL, SRC32> : score_full_kernel<D, 1, false, BUF, TAIL, SRC32, 0, false, BUF>;
+        case 2: return accum ? score_full_kernel<D, 2, true, BUF, TAIL, SRC32> : score_full_kernel<D, 2, false, BUF, TAIL, SRC32, 0, false, BUF>;
+        case 3: return accum ? score_full_kernel<D, 3, true, BUF, TAIL, SRC32> : score_full_kernel<D, 3, false, BUF, TAIL, SRC32, 0, false, BUF>;
+        case 4: return accum ? score_full_kernel<D, 4, true, BUF, TAIL, SRC32> : score_full_kernel<D, 4, false, BUF, TAIL, SRC32, 0, false, BUF>;
     }
     return nullptr;
 }
