@@ -164,7 +164,7 @@ def scorer_kernel(cfg):
         stage = "true" if rows_fill else "false"
         return "score_small", f"score_small_kernel<{cfg.D},{np_},true,{ch},{stage},{nw}>"
     np_ = min(4, (cfg.H + 1) // 2)
-    return "score_full", f"score_full_kernel<{cfg.D},{np_},false,true,{tail},true>"
+    return "score_full", f"score_full_kernel<{cfg.D},{np_},false,true,{tail},true,0,false,true>"
 
 
 class Phase:
