@@ -818,8 +818,8 @@ def test_wide_and_small_scorers_agree_bitwise():
 
 # H, D: every row packing of the small scorer (head pairs 1, 2, 4, 8 per MFMA
 # row block, padded heads for odd H), both head dims, one or two wide passes
-SMALL_VS_WIDE = [(1, 128), (2, 64), (3, 128), (4, 64), (5, 128), (8, 128), (8, 64), (12, 128),
-                 (16, 64)]
+SMALL_VS_WIDE = [(1, 128), (2, 64), (3, 128), (4, 64), (5, 128), (6, 128), (7, 64), (8, 128),
+                 (8, 64), (12, 128), (16, 64)]
 
 
 @pytest.mark.parametrize("H,D", SMALL_VS_WIDE, ids=lambda v: str(v))
@@ -870,8 +870,11 @@ def test_wide_scorer_tile_counts(D, n_tiles, H):
 # More (KV head, query group) items than two workgroups per CU: the wide
 # scorer's grid runs in more than one round of workgroups (520 to 1536 items,
 # odd tile counts, one tile, partial query groups).
+# (odd H and H = 6: heads zeroed or left out of the wide scorer's head quads,
+# and the kept fp16 copy written for the real heads only)
 MANY_ITEMS = [(8, 4100, 8, 128, 3), (16, 4096, 4, 64, 5), (17, 4000, 8, 128, 1),
-              (12, 8192, 2, 128, 2)]
+              (12, 8192, 2, 128, 2), (8, 4096, 3, 128, 2), (4, 4100, 7, 64, 3),
+              (4, 4096, 6, 128, 2), (8, 4096, 5, 64, 1), (4, 4096, 1, 128, 2)]
 
 
 @pytest.mark.parametrize("G,nq,H,D,n_tiles", MANY_ITEMS, ids=lambda v: str(v))
