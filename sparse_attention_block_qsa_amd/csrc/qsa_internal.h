@@ -7,7 +7,8 @@
 
 namespace qsa {
 
-// Blocks per MFMA scorer tile: the N extent of v_mfma_f32_32x32x16_f16.
+// Blocks per MFMA scorer tile: the N extent of v_mfma_f32_32x32x16_f16 (two
+// 16-block column tiles in the wide scorer's v_mfma_f32_16x16x32_f16 form).
 constexpr int kTileBlocks = 32;
 // Queries per wave (M = 32 rows = 16 queries x 2 heads) and waves per group.
 constexpr int kWaveQueries = 16;
