@@ -97,6 +97,7 @@ KERNEL_FILES = {
     "score_full": ("qsa_score.hip", "qsa_internal.h"),
     "topk": ("qsa_topk.hip", "qsa_topk_row.h", "qsa_internal.h"),
     "score_decode": ("qsa_decode.hip", "qsa_internal.h"),
+    "convert": ("qsa_convert.hip", "qsa_internal.h"),
 }
 
 
@@ -817,6 +818,9 @@ def main():
             "scorer_kernel": scorer_kernel(pc)[1],
             "scorer_traffic_bytes": read_traffic(scorer_kernel(pc)[0], pc.name),
             "convert_gbs": hbm["convert"] / (pe["convert"] * 1e-3) / 1e9,
+            "convert_traffic_bytes": read_traffic("convert", pc.name),
+            "convert_gbs_counters": (read_traffic("convert", pc.name) / (pe["convert"] * 1e-3) / 1e9
+                                     if read_traffic("convert", pc.name) else None),
             "block_scores_f16_frac_of_peak":
                 pc.flop / (pe["block_scores_f16"] * 1e-3) / 1e12 / PEAK_FP16_TFLOPS,
             "topk_gbs": hbm["topk"] / (ps["topk"] * 1e-3) / 1e9,
