@@ -61,8 +61,9 @@
 //    16x16x32 instruction sustains more than one of the 32x32x16 (measured
 //    beside the scorers by the benchmark), and at the prefill chunk the
 //    fp16-input scorer went 227 -> 213 us (fp32 queries 254 -> 252 us).
-//    Lane l stores query t_base + 4*(u/2) + l/16 and block 16*(u%2) + l%16
-//    of the tile for register u: 64-byte row segments.
+//    After the epilogue, one v_permlane16_swap per register pair turns the
+//    two 16-block column tiles of a query quad into 32-block rows, so the
+//    stores write whole 128-byte row segments (+1.2 % with 64-byte ones).
 //  * Fused selection (SEL > 0, one split per query group): after its last
 //    tile and the partial block, each wave selects the top-k of its own 16
 //    query rows, whose scores (every block, tail included) only it wrote,
@@ -404,8 +405,8 @@ void score_full_kernel(ScoreArgs a) {
 
     // ---- output addressing -------------------------------------------------
     // Lane l holds, for register u (0..7), query t_base + 8*(u/4) + 4*(l/32)
-    // + u%4 and block tile*32 + l%32 (M16: query t_base + 4*(u/2) + l/16 and
-    // block tile*32 + 16*(u%2) + l%16).  With BUF the stores are raw buffer
+    // + u%4 and block tile*32 + l%32 (M16, after the epilogue's lane swap:
+    // query t_base + 4*(u/2) + u%2 + 2*(l/32) and the same block).  With BUF the stores are raw buffer
     // stores over this KV head's rows: an offset >= 2^30 (past the region,
     // which the host limits to 2^30 bytes) is dropped by the hardware, so
     // masked lanes need no branch.
@@ -418,7 +419,7 @@ void score_full_kernel(ScoreArgs a) {
     int64_t rowel[8];
     #pragma unroll
     for (int u = 0; u < 8; ++u) {
-        const int t = M16 ? t_base + 4 * (u >> 1) + (l >> 4)
+        const int t = M16 ? t_base + 4 * (u >> 1) + (u & 1) + 2 * (l >> 5)
                           : t_base + 8 * (u >> 2) + 4 * (l >> 5) + (u & 3);
         if constexpr (BUF)
             rowoff[u] = t < a.nq ? static_cast<uint32_t>(static_cast<int64_t>(t) * a.ld_s * 4) : kOut;
@@ -615,14 +616,6 @@ void score_full_kernel(ScoreArgs a) {
 
         const int bcol = tile * kTileBlocks + bl;
         const uint32_t coloff = bcol < a.nf ? static_cast<uint32_t>(bcol) * 4 : kOut;
-        uint32_t colo[2] = {coloff, coloff};   // M16: column tiles 0 and 1
-        if constexpr (M16) {
-            #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const int bc = tile * kTileBlocks + 16 * c + (l & 15);
-                colo[c] = bc < a.nf ? static_cast<uint32_t>(bc) * 4 : kOut;
-            }
-        }
 
         float tot[8];
         #pragma unroll
@@ -728,6 +721,17 @@ void score_full_kernel(ScoreArgs a) {
                     tot[u] = (p == 0) ? pp : tot[u] + pp;
                 }
             }
+            // v_permlane16_swap of each query quad's two column tiles: lanes
+            // 0-31 then hold one query's 32 blocks and lanes 32-63 another's
+            // (queries 4*qd + u%2 and 4*qd + u%2 + 2), so every store writes
+            // two whole 128-byte row segments, as the 32x32x16 form does
+            #pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const auto sw = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, tot[2 * qd]),
+                                                                 __builtin_bit_cast(uint32_t, tot[2 * qd + 1]), false, false);
+                tot[2 * qd] = __builtin_bit_cast(float, static_cast<uint32_t>(sw[0]));
+                tot[2 * qd + 1] = __builtin_bit_cast(float, static_cast<uint32_t>(sw[1]));
+            }
         } else {
             #pragma unroll
             for (int p = 0; p < NP; ++p) {
@@ -745,7 +749,7 @@ void score_full_kernel(ScoreArgs a) {
             for (int u = 0; u < 8; ++u) {
                 if constexpr (BUF) {
                     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, tot[u]), rs,
-                                                          static_cast<int>(rowoff[u] + colo[M16 ? (u & 1) : 0]), 0,
+                                                          static_cast<int>(rowoff[u] + coloff), 0,
                                                           kStoreNT);
                 } else if (rowel[u] >= 0 && coloff != kOut) {
                     __builtin_nontemporal_store(tot[u], srow_base + rowel[u] + bcol);
