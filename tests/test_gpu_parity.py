@@ -877,6 +877,44 @@ MANY_ITEMS = [(8, 4100, 8, 128, 3), (16, 4096, 4, 64, 5), (17, 4000, 8, 128, 1),
               (4, 4096, 6, 128, 2), (8, 4096, 5, 64, 1), (4, 4096, 1, 128, 2)]
 
 
+@pytest.mark.parametrize("H", [8, 5])
+def test_wide_scorer_chunked_phase_keeps_q16(H):
+    """A phase over 4 KV heads x 8300 queries in chunks of 4160: each chunk,
+    the ragged second one (4140 queries) too, is 260 groups of 64 queries and
+    takes the wide scorer, its fp32 queries converted on load and kept in the
+    fp16 copy.  Ids, values and the kept copy are bit for bit those of one
+    pass (and the copy the inputs' fp16 bits), the workspace holds the last
+    chunk's scores, and every tail cell is the fixed-order model."""
+    G, nq, D, bs, k, qc = 4, 8300, 128, 64, 64, 4160
+    cfg = qi.Config("wide_chunked", G, nq, H, D, 40 * 64 + 11, bs, k, "normal", 1500 + H)
+    log(f"wide scorer, chunked phase with the fp16 copy kept: H={H}")
+    w = qi.make(cfg)
+    q = torch.from_numpy(w.q32).to(dev())
+    kb = k_dev(w.kblk)
+
+    def run(chunk):
+        ws = qsa.PhaseWorkspace(nq, G, H, D, cfg.n_kv, bs, k, dev(), with_vals=True,
+                                q_chunk=chunk, keep_q16=True)
+        ids, vals = qsa.select_phase(q, kb, cfg.n_kv, bs, k, ws)
+        torch.cuda.synchronize()
+        return ws, ids.cpu().numpy(), vals.cpu().numpy()
+
+    ws1, ids1, v1 = run(0)
+    wsc, idsc, vc = run(qc)
+    nb = cfg.nb
+    assert wsc.chunk_rows == qc
+    assert np.array_equal(idsc, ids1)
+    assert np.array_equal(vc.view(np.uint32), v1.view(np.uint32))
+    assert np.array_equal(ws1.q16.cpu().numpy().view(np.uint16), w.q16)
+    assert np.array_equal(wsc.q16.cpu().numpy().view(np.uint16), w.q16)
+    n = nq - qc
+    last = wsc.scores.reshape(-1, wsc.ld_s)[:G * n].reshape(G, n, wsc.ld_s)[:, :, :nb]
+    assert torch.equal(last.view(torch.int32), ws1.scores[:, qc:, :nb].view(torch.int32))
+    s_all = ws1.scores[:, :, :nb].reshape(cfg.rows, nb)
+    model = oracle.block_model_f32(w.q16, w.kblk, cfg.nf)
+    assert np.array_equal(s_all[:, cfg.nf].cpu().numpy().view(np.uint32), model.view(np.uint32))
+
+
 @pytest.mark.parametrize("G,nq,H,D,n_tiles", MANY_ITEMS, ids=lambda v: str(v))
 def test_wide_scorer_many_items(G, nq, H, D, n_tiles):
     """The wide scorer over more work items than one round of workgroups:
